@@ -1,0 +1,238 @@
+"""CPU oracle for the batch-1 fine-grained MoE decode step (TEST INFRASTRUCTURE).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg
+import this package. The GPU library never imports, links or calls it, and the two
+share no source. The arithmetic lives in ``oracle.c`` (plain fp64 loops); this
+module builds it with gcc, marshals numpy arrays into it and wires the stacked
+decode step out of its routines.
+
+Inputs are numpy arrays in storage formats: bf16 as uint16 bits, FP8 as uint8
+OCP E4M3FN codes, scales as float32. Sources and readings are listed in
+``oracle.c`` next to each routine; the stack wiring is described in
+``stack_step`` below.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-std=gnu11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-fno-fast-math", "-ffp-contract=off"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP). Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            L = ctypes.CDLL(_LIB)
+            P = ctypes.c_void_p
+            I = ctypes.c_int
+            L.oracle_fp8_e4m3.restype = ctypes.c_double
+            L.oracle_fp8_e4m3.argtypes = [ctypes.c_uint8]
+            L.oracle_bf16.restype = ctypes.c_double
+            L.oracle_bf16.argtypes = [ctypes.c_uint16]
+            L.oracle_bf16_round.restype = ctypes.c_uint16
+            L.oracle_bf16_round.argtypes = [ctypes.c_double]
+            L.oracle_gelu_tanh.restype = ctypes.c_double
+            L.oracle_gelu_tanh.argtypes = [ctypes.c_double]
+            L.oracle_router.restype = None
+            L.oracle_router.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
+            L.oracle_moe_layer.restype = None
+            L.oracle_moe_layer.argtypes = [I] * 7 + [P] * 21
+            L.oracle_lm_head.restype = None
+            L.oracle_lm_head.argtypes = [I, I, I, P, P, P, P, P, P]
+            L.oracle_lm_head_rows.restype = None
+            L.oracle_lm_head_rows.argtypes = [I, I, I, P, P, P, P, P]
+            L.oracle_spec_accept.restype = I
+            L.oracle_spec_accept.argtypes = [I, P, P, P]
+            L.oracle_add_rmsnorm.restype = None
+            L.oracle_add_rmsnorm.argtypes = [I, I, P, P, P, P, ctypes.c_double, P, P]
+            L.oracle_num_threads.restype = I
+            L.oracle_num_threads.argtypes = []
+            _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def fp8_e4m3(code: int) -> float:
+    return lib().oracle_fp8_e4m3(int(code))
+
+
+def bf16(bits: int) -> float:
+    return lib().oracle_bf16(int(bits))
+
+
+def bf16_round(v: float) -> int:
+    return lib().oracle_bf16_round(float(v))
+
+
+def gelu_tanh(z: float) -> float:
+    return lib().oracle_gelu_tanh(float(z))
+
+
+def router(u, W, bias, K):
+    """u uint16 [M][H], W uint16 [H][E], bias f32 [E] or None -> dict(idx, w, gap, logits)."""
+    u = _c(u, np.uint16)
+    W = _c(W, np.uint16)
+    bias = _c(bias, np.float32)
+    M, H = u.shape
+    E = W.shape[1]
+    logits = np.empty((M, E), np.float64)
+    idx = np.empty((M, K), np.int32)
+    wts = np.empty((M, K), np.float64)
+    gap = np.empty(M, np.float64)
+    lib().oracle_router(M, H, E, K, _p(u), _p(W), _p(bias), _p(logits), _p(idx), _p(wts), _p(gap))
+    return {"idx": idx, "w": wts, "gap": gap, "logits": logits}
+
+
+def moe_layer(u, w: dict, K: int):
+    """One MoE layer. u uint16 [M][H]; w: synth.weights_to_host(layer_weights(...)).
+
+    Returns dict(idx [M][K] ascending, w [M][K], gap [M], logits [M][E],
+    y fp64 [M][H], y_bf16 uint16 [M][H]).
+    """
+    u = _c(u, np.uint16)
+    M, H = u.shape
+    wtype = 0 if w["expert_dtype"] == "fp8" else 1
+    edt = np.uint8 if wtype == 0 else np.uint16
+    G = _c(w["gate_w"], edt)
+    E, D, _ = G.shape
+    shG = _c(w["sh_gate_w"], edt)
+    Ds = 0 if shG is None else shG.shape[0]
+    args = dict(
+        router_w=_c(w["router_w"], np.uint16), router_b=_c(w["router_b"], np.float32),
+        G=G, U=_c(w["up_w"], edt), Dn=_c(w["down_w"], edt),
+        gs=_c(w["gate_s"], np.float32), us=_c(w["up_s"], np.float32),
+        ds=_c(w["down_s"], np.float32),
+        shG=shG, shU=_c(w["sh_up_w"], edt), shD=_c(w["sh_down_w"], edt),
+        shgs=_c(w["sh_gate_s"], np.float32), shus=_c(w["sh_up_s"], np.float32),
+        shds=_c(w["sh_down_s"], np.float32))
+    E_r = args["router_w"].shape[1]
+    assert E_r == E
+    idx = np.empty((M, K), np.int32)
+    wts = np.empty((M, K), np.float64)
+    gap = np.empty(M, np.float64)
+    logits = np.empty((M, E), np.float64)
+    y = np.empty((M, H), np.float64)
+    yb = np.empty((M, H), np.uint16)
+    lib().oracle_moe_layer(
+        M, H, E, K, D, Ds, wtype, _p(u), _p(args["router_w"]), _p(args["router_b"]),
+        _p(args["G"]), _p(args["U"]), _p(args["Dn"]), _p(args["gs"]), _p(args["us"]),
+        _p(args["ds"]), _p(args["shG"]), _p(args["shU"]), _p(args["shD"]),
+        _p(args["shgs"]), _p(args["shus"]), _p(args["shds"]),
+        _p(idx), _p(wts), _p(gap), _p(logits), _p(y), _p(yb))
+    return {"idx": idx, "w": wts, "gap": gap, "logits": logits, "y": y, "y_bf16": yb}
+
+
+def lm_head_argmax(x, Q, s):
+    """x uint16 [M][H], Q uint8 [V][H], s f32 [V] -> (tok int32 [M], max_logit f64 [M], gap f64 [M])."""
+    x = _c(x, np.uint16)
+    Q = _c(Q, np.uint8)
+    s = _c(s, np.float32)
+    M, H = x.shape
+    V = Q.shape[0]
+    tok = np.empty(M, np.int32)
+    ml = np.empty(M, np.float64)
+    gap = np.empty(M, np.float64)
+    lib().oracle_lm_head(M, H, V, _p(x), _p(Q), _p(s), _p(tok), _p(ml), _p(gap))
+    return tok, ml, gap
+
+
+def lm_head_rows(x, Q, s, rows):
+    """Logits of the given vocab rows only: f64 [M][len(rows)]."""
+    x = _c(x, np.uint16)
+    Q = _c(Q, np.uint8)
+    s = _c(s, np.float32)
+    rows = _c(rows, np.int32)
+    M, H = x.shape
+    out = np.empty((M, len(rows)), np.float64)
+    lib().oracle_lm_head_rows(M, H, len(rows), _p(rows), _p(x), _p(Q), _p(s), _p(out))
+    return out
+
+
+def spec_accept(draft, target):
+    """draft int32 [gamma], target int32 [gamma+1] -> (n, out int32 [gamma+1])."""
+    target = _c(target, np.int32)
+    gamma = len(target) - 1
+    draft = _c(draft, np.int32) if gamma > 0 else np.zeros(1, np.int32)
+    out = np.empty(gamma + 1, np.int32)
+    n = lib().oracle_spec_accept(gamma, _p(draft), _p(target), _p(out))
+    return n, out
+
+
+def add_rmsnorm(h, a0, a1, g, eps=1e-6):
+    """h, a0, a1 uint16 [M][H] (a1 may be None), g uint16 [H] -> (h_out, u) uint16 [M][H]."""
+    h = _c(h, np.uint16)
+    a0 = _c(a0, np.uint16)
+    a1 = _c(a1, np.uint16)
+    g = _c(g, np.uint16)
+    M, H = h.shape
+    ho = np.empty_like(h)
+    uo = np.empty_like(h)
+    lib().oracle_add_rmsnorm(M, H, _p(h), _p(a0), _p(a1), _p(g), float(eps), _p(ho), _p(uo))
+    return ho, uo
+
+
+def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None):
+    """One decode step through a stack of MoE layers, then lm_head, argmax, acceptance.
+
+    Wiring (the pages omit attention; the stacked workload replaces it by a residual
+    add of noise and puts an RMSNorm before every layer and before the lm_head):
+        h = x
+        for l: h, u_l = add_rmsnorm(h, noise_l, y_{l-1}, g_l); y_l = moe_layer(u_l)
+        h, x_f = add_rmsnorm(h, y_{L-1}, None, g_L)
+        tok = argmax(lm_head(x_f)); (n, out) = spec_accept(draft, tok)
+    layers: a list of host weight dicts (or a callable l -> dict, to fetch lazily).
+    Returns per-layer u, routing, gaps and y, plus the final tokens and gaps.
+    """
+    L = len(noise)
+    h = np.ascontiguousarray(x, np.uint16)
+    y_prev = None
+    per = []
+    for l in range(L):
+        w = layers(l) if callable(layers) else layers[l]
+        h, u = add_rmsnorm(h, noise[l], y_prev, gains[l], eps)
+        r = moe_layer(u, w, K)
+        per.append({"u": u, "idx": r["idx"], "w": r["w"], "gap": r["gap"],
+                    "y": r["y"], "y_bf16": r["y_bf16"]})
+        y_prev = r["y_bf16"]
+    h, xf = add_rmsnorm(h, y_prev, None, gains[L], eps)
+    tok, ml, gap = lm_head_argmax(xf, lm_w, lm_s)
+    out = {"layers": per, "x_final": xf, "h_final": h, "tok": tok, "max_logit": ml,
+           "lm_gap": gap}
+    if draft is not None:
+        n, acc = spec_accept(draft, tok)
+        out["accepted"] = n
+        out["out_tokens"] = acc
+    return out

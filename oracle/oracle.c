@@ -1,0 +1,396 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU reference of the batch-1 fine-grained MoE
+ * decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library. The GPU library never includes, links or
+ * calls it, and it shares no source with the GPU library.
+ *
+ * Every routine is the plain definition written out: straight loops, fp64
+ * accumulation in index order, a library sort where a sort is a step. Values
+ * enter in their storage formats (bf16 bits, OCP E4M3FN code bytes, fp32
+ * scales) and are decoded here from the format definitions. The only roundings
+ * to a narrow type are those where the boundary stores a bf16 tensor.
+ *
+ * Sources (web pages; quoted by address and section):
+ *  [LLMD] "LLM decoding", us-homepage.pages.dev/blog/llm-decoding
+ *    - "The exact architecture, and why it rules out 4-bit": top 8 of 128 routed
+ *      experts plus one always-on shared expert; expert width 704, hidden 2816,
+ *      tied 262,144-row lm_head.
+ *    - "Where the 7.36 GB goes": gate, up and down matrices per expert; the
+ *      router; the always-on shared MLP; the lm_head read once per token.
+ *    - "Lever 1: fewer bytes (FP8 weights)": FP8 weight-only storage, each
+ *      weight decoded to a wider type for the math.
+ *    - "Lever 2: fewer passes (native MTP)" and "What we learned": the target
+ *      verifies drafted tokens in one pass and keeps exactly the tokens it would
+ *      have produced itself (greedy = exact token equality).
+ *  Readings where the pages are silent (gating function, activation, tie
+ *  breaks, scale placement, norm form) are listed next to each routine.
+ *
+ * Parity pins: each routine is checked by tests against closed forms, library
+ * routines (torch FP8/bf16 conversion, numpy dense evaluation), brute force and
+ * invariants. "Fidelity to the real Gemma-4 numerics" is parity unpinned: the
+ * pages do not give the real router function, activation or norm.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------------------------------------------------------------- formats */
+
+/* OCP 8-bit floating point E4M3FN: 1 sign, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent 0 is subnormal (m/8 * 2^-6); 0x7F/0xFF are NaN; no infinity. */
+double oracle_fp8_e4m3(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* bf16 is the top half of an IEEE binary32. */
+double oracle_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bf16 (ties to even), in one rounding.
+ * bf16 keeps 8 significant bits and the binary32 exponent range; below 2^-126
+ * the quantum stays 2^-133 (subnormals). */
+uint16_t oracle_bf16_round(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    double a = fabs(v);
+    double r;
+    if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int k;
+        frexp(a, &k);              /* a = f * 2^k, f in [0.5, 1): a in [2^(k-1), 2^k) */
+        int ex = k - 1;            /* unbiased exponent of a */
+        if (ex < -126)
+            ex = -126;
+        double q = ldexp(1.0, ex - 7);       /* spacing of bf16 values near a */
+        r = nearbyint(a / q) * q;            /* default rounding mode: ties to even */
+        if (r >= ldexp(1.0, 128))
+            r = INFINITY;
+    }
+    float f = (float)(v < 0 ? -r : r);       /* exact: r is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* GELU, tanh form: 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))).
+ * The pages do not name the expert activation; the tanh-approximated GELU gate
+ * of the workload definition is used. */
+double oracle_gelu_tanh(double z)
+{
+    const double c = sqrt(2.0 / M_PI);
+    return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
+}
+
+/* Decode element i of an expert weight matrix stored as FP8 codes (wtype 0) or
+ * bf16 bits (wtype 1). */
+static double wget(const void *w, int wtype, size_t i)
+{
+    if (wtype == 0)
+        return oracle_fp8_e4m3(((const uint8_t *)w)[i]);
+    return oracle_bf16(((const uint16_t *)w)[i]);
+}
+
+/* ------------------------------------------------------------------ router */
+
+typedef struct { double v; int i; } vi_t;
+
+/* Larger logit first; equal logits: lower expert id first. */
+static int by_logit_desc(const void *a, const void *b)
+{
+    const vi_t *x = a, *y = b;
+    if (x->v > y->v) return -1;
+    if (x->v < y->v) return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+static int int_asc(const void *a, const void *b)
+{
+    int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Router GEMV, softmax, top-K, renormalise ([LLMD] "The exact architecture":
+ * top 8 of 128 routed experts).
+ *   logits[m][e] = sum_c u[m][c] * W[c][e] (+ bias[e])     W row-major [H][E]
+ *   p = softmax(logits[m]) over all E experts
+ *   S = the K largest logits (ties: lower expert id)        -- softmax is monotone
+ *   w_k = p_k / sum_{j in S} p_j
+ * Reading: the pages do not give the gating function; softmax over all experts,
+ * keep K, renormalise over the K is taken. idx is written in ascending expert id
+ * with wts aligned to it. gap[m] = K-th largest logit minus (K+1)-th (INFINITY when
+ * K == E): the margin of the selection decision.
+ */
+void oracle_router(int M, int H, int E, int K, const uint16_t *u, const uint16_t *W,
+                   const float *bias, double *logits, int32_t *idx, double *wts,
+                   double *gap)
+{
+    vi_t *order = malloc(sizeof(vi_t) * (size_t)E);
+    int *sel = malloc(sizeof(int) * (size_t)K);
+    for (int m = 0; m < M; ++m) {
+        double *l = logits + (size_t)m * E;
+        for (int e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += oracle_bf16(u[(size_t)m * H + c]) * oracle_bf16(W[(size_t)c * E + e]);
+            if (bias)
+                acc += (double)bias[e];
+            l[e] = acc;
+        }
+        double lmax = l[0];
+        for (int e = 1; e < E; ++e)
+            if (l[e] > lmax) lmax = l[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp(l[e] - lmax);
+        for (int e = 0; e < E; ++e) {
+            order[e].v = l[e];
+            order[e].i = e;
+        }
+        qsort(order, (size_t)E, sizeof(vi_t), by_logit_desc);
+        for (int k = 0; k < K; ++k)
+            sel[k] = order[k].i;
+        gap[m] = (K < E) ? order[K - 1].v - order[K].v : INFINITY;
+        qsort(sel, (size_t)K, sizeof(int), int_asc);
+        double ps = 0.0;
+        for (int k = 0; k < K; ++k)
+            ps += exp(l[sel[k]] - lmax) / z;
+        for (int k = 0; k < K; ++k) {
+            idx[(size_t)m * K + k] = sel[k];
+            wts[(size_t)m * K + k] = (exp(l[sel[k]] - lmax) / z) / ps;
+        }
+    }
+    free(order);
+    free(sel);
+}
+
+/* ------------------------------------------------------------- expert FFN */
+
+/*
+ * One expert applied to one token ([LLMD] "Where the 7.36 GB goes": gate, up and
+ * down matrices per expert; "Lever 1": weights decoded to a wider type, scale per
+ * output channel applied after the dot product):
+ *   a_j = sg[j] * sum_c G[j][c] u[c]     G row-major [F][H]
+ *   b_j = su[j] * sum_c U[j][c] u[c]     U row-major [F][H]
+ *   h_j = gelu_tanh(a_j) * b_j
+ *   o_c = sd[c] * sum_j Dn[c][j] h_j     Dn row-major [H][F]
+ * Scales are NULL for bf16 weights (factor 1).
+ */
+static void expert_apply(int H, int F, int wtype, const uint16_t *u,
+                         const void *G, const void *U, const void *Dn,
+                         const float *sg, const float *su, const float *sd,
+                         double *hbuf, double *o)
+{
+    int j, c;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < F; ++j) {
+        double a = 0.0, b = 0.0;
+        for (int cc = 0; cc < H; ++cc) {
+            double x = oracle_bf16(u[cc]);
+            a += wget(G, wtype, (size_t)j * H + cc) * x;
+            b += wget(U, wtype, (size_t)j * H + cc) * x;
+        }
+        if (sg) a *= (double)sg[j];
+        if (su) b *= (double)su[j];
+        hbuf[j] = oracle_gelu_tanh(a) * b;
+    }
+#pragma omp parallel for schedule(static)
+    for (c = 0; c < H; ++c) {
+        double acc = 0.0;
+        for (int jj = 0; jj < F; ++jj)
+            acc += wget(Dn, wtype, (size_t)c * F + jj) * hbuf[jj];
+        if (sd) acc *= (double)sd[c];
+        o[c] = acc;
+    }
+}
+
+/*
+ * One MoE layer for M tokens: router (above), then for each token
+ *   y[m] = sum_{e in S_m, ascending e} w_{m,e} * expert_e(u[m]) + shared(u[m])
+ * The shared expert is always on with weight 1 ([LLMD] "The exact architecture":
+ * one always-on shared expert); it is not renormalised with the routed experts.
+ * y is returned in fp64 and rounded once to bf16 (y_bf16), the boundary's type.
+ * Expert weights: G, U [E][D][H], Dn [E][H][D]; shared [Ds][H], [Ds][H], [H][Ds]
+ * (Ds == 0: no shared expert).
+ */
+void oracle_moe_layer(int M, int H, int E, int K, int D, int Ds, int wtype,
+                      const uint16_t *u, const uint16_t *router_w, const float *router_b,
+                      const void *G, const void *U, const void *Dn,
+                      const float *gs, const float *us, const float *ds,
+                      const void *shG, const void *shU, const void *shD,
+                      const float *shgs, const float *shus, const float *shds,
+                      int32_t *idx, double *wts, double *gap, double *logits,
+                      double *y, uint16_t *y_bf16)
+{
+    size_t esz = wtype == 0 ? 1 : 2;
+    int F = D > Ds ? D : Ds;
+    double *hbuf = malloc(sizeof(double) * (size_t)(F > 0 ? F : 1));
+    double *o = malloc(sizeof(double) * (size_t)H);
+    oracle_router(M, H, E, K, u, router_w, router_b, logits, idx, wts, gap);
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *um = u + (size_t)m * H;
+        double *ym = y + (size_t)m * H;
+        for (int c = 0; c < H; ++c)
+            ym[c] = 0.0;
+        for (int k = 0; k < K; ++k) {
+            int e = idx[(size_t)m * K + k];
+            double w = wts[(size_t)m * K + k];
+            size_t off = (size_t)e * D * H;
+            expert_apply(H, D, wtype, um,
+                         (const char *)G + off * esz, (const char *)U + off * esz,
+                         (const char *)Dn + off * esz,
+                         gs ? gs + (size_t)e * D : NULL, us ? us + (size_t)e * D : NULL,
+                         ds ? ds + (size_t)e * H : NULL, hbuf, o);
+            for (int c = 0; c < H; ++c)
+                ym[c] += w * o[c];
+        }
+        if (Ds > 0) {
+            expert_apply(H, Ds, wtype, um, shG, shU, shD, shgs, shus, shds, hbuf, o);
+            for (int c = 0; c < H; ++c)
+                ym[c] += o[c];
+        }
+        for (int c = 0; c < H; ++c)
+            y_bf16[(size_t)m * H + c] = oracle_bf16_round(ym[c]);
+    }
+    free(hbuf);
+    free(o);
+}
+
+/* ----------------------------------------------------------------- lm_head */
+
+/*
+ * Tied lm_head GEMV and greedy argmax ([LLMD] "Where the 7.36 GB goes": the
+ * 2816 x 262,144 output projection read once per token to produce logits over the
+ * whole vocabulary; the greedy (temperature 0) decoding of the measurements):
+ *   logit[m][v] = s[v] * sum_c Q[v][c] x[m][c]        Q row-major [V][H] FP8
+ *   tok[m] = argmax_v logit[m][v], ties: lower v
+ * max_logit[m] = logit at tok; gap[m] = best minus second best (INFINITY if V == 1).
+ */
+void oracle_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *Q,
+                    const float *s, int32_t *tok, double *max_logit, double *gap)
+{
+    double *lg = malloc(sizeof(double) * (size_t)V);
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xm = x + (size_t)m * H;
+        int v;
+#pragma omp parallel for schedule(static)
+        for (v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += oracle_fp8_e4m3(Q[(size_t)v * H + c]) * oracle_bf16(xm[c]);
+            lg[v] = (double)s[v] * acc;
+        }
+        int best = 0;
+        for (int vv = 1; vv < V; ++vv)
+            if (lg[vv] > lg[best])
+                best = vv;
+        double second = -INFINITY;
+        for (int vv = 0; vv < V; ++vv)
+            if (vv != best && lg[vv] > second)
+                second = lg[vv];
+        tok[m] = best;
+        max_logit[m] = lg[best];
+        gap[m] = V > 1 ? lg[best] - second : INFINITY;
+    }
+    free(lg);
+}
+
+/* Logits of selected rows only: out[m][r] = s[rows[r]] * sum_c Q[rows[r]][c] x[m][c]. */
+void oracle_lm_head_rows(int M, int H, int nrows, const int32_t *rows, const uint16_t *x,
+                         const uint8_t *Q, const float *s, double *out)
+{
+    for (int m = 0; m < M; ++m)
+        for (int r = 0; r < nrows; ++r) {
+            size_t v = (size_t)rows[r];
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += oracle_fp8_e4m3(Q[v * H + c]) * oracle_bf16(x[(size_t)m * H + c]);
+            out[(size_t)m * nrows + r] = (double)s[v] * acc;
+        }
+}
+
+/* --------------------------------------------------------- spec acceptance */
+
+/*
+ * Greedy speculative acceptance ([LLMD] "Lever 2: fewer passes": the target checks
+ * the drafted tokens in one pass and keeps the ones it would have produced;
+ * "What we learned": the output equals ordinary decoding).
+ * draft[0..gamma-1] = d_1..d_gamma; target[0..gamma] = t_0..t_gamma, where t_i is
+ * the target's token after the prefix extended by d_1..d_i.
+ *   n = the largest j <= gamma with d_i == t_{i-1} for every i <= j
+ *   out[0..n] = t_0..t_n (n accepted drafts, then the bonus token t_n); out[i > n] = -1
+ * Returns n.
+ */
+int oracle_spec_accept(int gamma, const int32_t *draft, const int32_t *target, int32_t *out)
+{
+    int n = 0;
+    while (n < gamma && draft[n] == target[n])
+        ++n;
+    for (int i = 0; i <= gamma; ++i)
+        out[i] = i <= n ? target[i] : -1;
+    return n;
+}
+
+/* ----------------------------------------------------------- residual norm */
+
+/*
+ * Residual add and RMSNorm between MoE layers (the pages omit attention; the
+ * stacked workload replaces it by a residual add of noise):
+ *   h'[c] = bf16(h[c] + a0[c] + a1[c])              a1 may be NULL
+ *   r     = 1 / sqrt(mean_c h'[c]^2 + eps)
+ *   u[c]  = bf16(h'[c] * r * g[c])
+ * Reading: the gain multiplies directly (not 1 + g); one rounding of the sum.
+ */
+void oracle_add_rmsnorm(int M, int H, const uint16_t *h, const uint16_t *a0,
+                        const uint16_t *a1, const uint16_t *g, double eps,
+                        uint16_t *h_out, uint16_t *u_out)
+{
+    for (int m = 0; m < M; ++m) {
+        size_t o = (size_t)m * H;
+        double ss = 0.0;
+        for (int c = 0; c < H; ++c) {
+            double v = oracle_bf16(h[o + c]) + oracle_bf16(a0[o + c]);
+            if (a1)
+                v += oracle_bf16(a1[o + c]);
+            h_out[o + c] = oracle_bf16_round(v);
+            double hv = oracle_bf16(h_out[o + c]);
+            ss += hv * hv;
+        }
+        double r = 1.0 / sqrt(ss / (double)H + eps);
+        for (int c = 0; c < H; ++c)
+            u_out[o + c] = oracle_bf16_round(oracle_bf16(h_out[o + c]) * r * oracle_bf16(g[c]));
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,245 @@
+"""Seeded synthetic weights and inputs for the batch-1 fine-grained MoE decode step.
+
+This module is the only code that both the CPU oracle tests and the GPU path use.
+It draws random numbers with seeded torch generators and stores them in the
+formats the decode step consumes:
+
+* bf16 tensors (router weights, hidden vectors, RMSNorm gains, noise),
+* OCP E4M3FN code bytes with one fp32 scale per output row (expert matrices and the
+  tied lm_head), made the way a load-time FP8 weight-only quantiser makes them:
+  scale = row absmax / 448, code = round-to-nearest-even E4M3FN of (w / scale),
+  done by torch's own float8 conversion.
+
+It holds none of the decode step's arithmetic (no routing, no GEMV, no argmax,
+no acceptance). Random draws are keyed by (seed, tag, kind, layer, index) through
+SHA-256, so any block can be regenerated on its own. The same key on a different
+device gives different numbers (torch's CPU and GPU generators differ); a test
+generates on one device and copies to the other.
+
+Shapes follow the Gemma-4-26B-A4B description on the page 'LLM decoding'
+(us-homepage.pages.dev/blog/llm-decoding), section "The exact architecture, and
+why it rules out 4-bit": hidden 2816, 128 experts, top-8 plus one shared expert,
+expert width 704, 30 layers, tied vocabulary 262,144.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import Optional
+
+import numpy as np
+import torch
+
+FP8_MAX = 448.0  # largest finite OCP E4M3FN magnitude
+
+
+@dataclasses.dataclass(frozen=True)
+class Shape:
+    hidden: int
+    experts: int
+    top_k: int
+    width: int          # routed expert FFN width
+    shared_width: int   # shared expert FFN width (0: no shared expert)
+    vocab: int
+    layers: int = 1
+
+    def with_(self, **kw) -> "Shape":
+        return dataclasses.replace(self, **kw)
+
+
+# Gemma-4-26B-A4B-shaped layer (shared expert at the routed width; the page's
+# 2112-wide dense MLP is available through with_(shared_width=2112)).
+GEMMA4_26B_A4B = Shape(hidden=2816, experts=128, top_k=8, width=704,
+                       shared_width=704, vocab=262144, layers=30)
+# Tiny parity shape: hidden 256, 16 experts top-2 plus shared, width 64, vocab 4096.
+TINY = Shape(hidden=256, experts=16, top_k=2, width=64, shared_width=64,
+             vocab=4096, layers=1)
+
+ROUTER_STD = 0.05
+EXPERT_STD = 0.02
+LM_HEAD_STD = 0.02
+NOISE_STD = 0.1
+GAIN_MEAN, GAIN_STD = 1.0, 0.1
+
+
+def seed_of(*key) -> int:
+    """A 63-bit seed from an arbitrary tuple key (stable across runs and hosts)."""
+    digest = hashlib.sha256(repr(key).encode()).digest()
+    return int.from_bytes(digest[:8], "little") & ((1 << 63) - 1)
+
+
+def _gen(device, *key) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of(*key))
+    return g
+
+
+def normal(shape, std, device, *key, mean=0.0) -> torch.Tensor:
+    g = _gen(device, *key)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t
+
+
+def quantize_rows_fp8(w: torch.Tensor):
+    """Per-output-row FP8 (E4M3FN) codes and fp32 scales of a float32 matrix.
+
+    Rows are the last-but-one axis: w[..., row, col]. Returns (codes uint8, scales fp32).
+    An all-zero row gets scale 0 and code 0.
+    """
+    amax = w.abs().amax(dim=-1)
+    scale = amax / FP8_MAX
+    safe = torch.where(scale > 0, scale, torch.ones_like(scale))
+    q = (w / safe.unsqueeze(-1)).clamp_(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), scale.contiguous()
+
+
+def _fp8_matrix(shape, std, device, *key):
+    """Draw N(0, std) and quantise per row; done in slices to bound temporaries."""
+    lead = shape[0]
+    codes = torch.empty(shape, dtype=torch.uint8, device=device)
+    scales = torch.empty(shape[:-1], dtype=torch.float32, device=device)
+    per = max(1, (1 << 27) // max(1, int(np.prod(shape[1:]))))
+    for i0 in range(0, lead, per):
+        i1 = min(lead, i0 + per)
+        w = normal((i1 - i0,) + tuple(shape[1:]), std, device, *key, i0)
+        codes[i0:i1], scales[i0:i1] = quantize_rows_fp8(w)
+        del w
+    return codes, scales
+
+
+def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
+                  tag: str = "moe", expert_dtype: str = "fp8",
+                  router_bias: Optional[torch.Tensor] = None) -> dict:
+    """Weights of one MoE layer in the boundary's logical row-major layout.
+
+    router_w  bf16 [H][E]            N(0, 0.05)
+    router_b  fp32 [E] or None
+    gate_w/up_w  [E][D][H], down_w [E][H][D]: uint8 FP8 codes (expert_dtype="fp8",
+              with fp32 per-row scales gate_s/up_s [E][D], down_s [E][H]) or bf16
+              (expert_dtype="bf16", scales None); values N(0, 0.02) before quantisation.
+    sh_*      the shared expert: [Ds][H], [Ds][H], [H][Ds] (None when Ds == 0).
+    """
+    H, E, D, Ds = shape.hidden, shape.experts, shape.width, shape.shared_width
+    k = (seed, tag, layer)
+    out = {"router_w": normal((H, E), ROUTER_STD, device, *k, "router").to(torch.bfloat16),
+           "router_b": None if router_bias is None else router_bias.to(device=device, dtype=torch.float32)}
+
+    def mat(shp, name):
+        if expert_dtype == "fp8":
+            return _fp8_matrix(shp, EXPERT_STD, device, *k, name)
+        if expert_dtype == "bf16":
+            w = torch.empty(shp, dtype=torch.bfloat16, device=device)
+            for i in range(shp[0]):
+                w[i] = normal(tuple(shp[1:]), EXPERT_STD, device, *k, name, i).to(torch.bfloat16)
+            return w, None
+        raise ValueError(expert_dtype)
+
+    out["gate_w"], out["gate_s"] = mat((E, D, H), "gate")
+    out["up_w"], out["up_s"] = mat((E, D, H), "up")
+    out["down_w"], out["down_s"] = mat((E, H, D), "down")
+    if Ds > 0:
+        for name, shp in (("gate", (Ds, H)), ("up", (Ds, H)), ("down", (H, Ds))):
+            w, s = mat((1,) + shp, "shared_" + name)
+            out["sh_%s_w" % name] = w[0]
+            out["sh_%s_s" % name] = None if s is None else s[0]
+    else:
+        for name in ("gate", "up", "down"):
+            out["sh_%s_w" % name] = None
+            out["sh_%s_s" % name] = None
+    out["expert_dtype"] = expert_dtype
+    return out
+
+
+def lm_head(shape: Shape, device="cpu", seed: int = 0, tag: str = "lm_head"):
+    """Tied lm_head [V][H]: FP8 codes from N(0, 0.02) with per-row fp32 scales."""
+    return _fp8_matrix((shape.vocab, shape.hidden), LM_HEAD_STD, device, seed, tag)
+
+
+def hidden_inputs(shape: Shape, M: int, step: int, sub: int = 0, device="cpu",
+                  seed: int = 0, tag: str = "x") -> torch.Tensor:
+    """M fresh bf16 hidden vectors N(0, 1) for one decode step (sub: resample index)."""
+    return normal((M, shape.hidden), 1.0, device, seed, tag, step, sub).to(torch.bfloat16)
+
+
+def stack_noise(shape: Shape, M: int, step: int, sub: int = 0, device="cpu",
+                seed: int = 0) -> torch.Tensor:
+    """Per-layer residual noise N(0, 0.1), bf16 [L][M][H] (stands in for attention)."""
+    return normal((shape.layers, M, shape.hidden), NOISE_STD, device, seed, "noise",
+                  step, sub).to(torch.bfloat16)
+
+
+def rmsnorm_gains(shape: Shape, device="cpu", seed: int = 0) -> torch.Tensor:
+    """bf16 gains N(1, 0.1): one per layer plus the final norm, [L + 1][H]."""
+    return normal((shape.layers + 1, shape.hidden), GAIN_STD, device, seed, "gain",
+                  mean=GAIN_MEAN).to(torch.bfloat16)
+
+
+def zipf_router_bias(experts: int, s: float = 1.1, seed: int = 0) -> torch.Tensor:
+    """Router bias that makes expert popularity Zipf-like: b_e = -s * ln(rank_e).
+
+    rank is a seeded permutation of 1..E, so exp(b_e) is proportional to rank_e^-s.
+    """
+    g = _gen("cpu", seed, "zipf_rank", experts)
+    rank = torch.randperm(experts, generator=g).to(torch.float64) + 1.0
+    return (-s * torch.log(rank)).to(torch.float32)
+
+
+def match_probability(step: int, seed: int = 0, lo: float = 0.5, hi: float = 0.9) -> float:
+    """Per-step draft-match probability, uniform on [lo, hi]."""
+    g = _gen("cpu", seed, "match_p", step)
+    return lo + (hi - lo) * float(torch.rand((), generator=g, dtype=torch.float64))
+
+
+def drafts(reference_tokens, p: float, vocab: int, step: int, seed: int = 0) -> np.ndarray:
+    """gamma = len(reference_tokens) - 1 draft ids.
+
+    Draft i (1-based) equals reference_tokens[i-1] with probability p, and is
+    otherwise a uniform id different from it. reference_tokens are the tokens an
+    independent run (the oracle) produced for this step, so the drafts never depend
+    on the code under test.
+    """
+    ref = np.asarray(reference_tokens, dtype=np.int64)
+    gamma = len(ref) - 1
+    g = _gen("cpu", seed, "drafts", step)
+    coin = torch.rand((max(gamma, 1),), generator=g, dtype=torch.float64).numpy()
+    other = torch.randint(0, vocab - 1, (max(gamma, 1),), generator=g).numpy()
+    out = np.empty(gamma, dtype=np.int32)
+    for i in range(gamma):
+        if coin[i] < p:
+            out[i] = ref[i]
+        else:  # uniform over the vocab minus ref[i]
+            out[i] = other[i] + (1 if other[i] >= ref[i] else 0)
+    return out
+
+
+def bits16(t: torch.Tensor) -> np.ndarray:
+    """Host numpy uint16 view of a bf16 tensor's bits."""
+    return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def bytes8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").contiguous().view(torch.uint8).numpy()
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").contiguous().to(torch.float32).numpy()
+
+
+def weights_to_host(w: dict) -> dict:
+    """Numpy copies of a layer_weights() dict (bf16 as uint16 bits, FP8 as uint8)."""
+    out = {}
+    for k, v in w.items():
+        if isinstance(v, torch.Tensor):
+            if v.dtype == torch.bfloat16:
+                out[k] = bits16(v)
+            elif v.dtype == torch.uint8:
+                out[k] = bytes8(v)
+            else:
+                out[k] = f32(v)
+        else:
+            out[k] = v
+    return out
