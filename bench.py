@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: the stacked batch-1 decode step of a Gemma-4-26B-A4B-shaped
+fine-grained MoE on one MI355X.
+
+A step is one pass of the whole hot path over one batch of M tokens: for each of
+30 MoE layers the residual add + RMSNorm, the router GEMV with softmax top-8 of 128,
+the union of selected experts, the FP8 gate/up GEMVs with the GELU-tanh gate, the
+FP8 down GEMV with the weighted combine and the always-on shared expert; then the
+final norm, the tied 262,144-row FP8 lm_head GEMV with argmax, and greedy
+acceptance of M-1 draft tokens. M=1 is plain decoding, M=5 the verify step of
+speculative decoding with 4 drafts.
+
+Weights (23.8 GB of FP8 experts and lm_head, every expert at its own address) and
+all step inputs are seeded synthetic data resident in HBM before timing. Each
+step is captured once in a HIP graph; W warm-up steps are replayed, then exactly K
+steps are timed with HIP events on the replay stream, bracketed by
+device synchronisations. Bytes per step are the algorithmic bytes of the routing
+the GPU actually took (each selected expert counted once per step).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--M", type=str, default="1,5", help="tokens per step; the first is the headline")
+    ap.add_argument("--layers", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=8, help="oracle sample: layers per step")
+    ap.add_argument("--cpu-steps", type=int, default=40, help="oracle sample: steps")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the decode step is a single-GPU kernel path "
+              "(see the sharding notes); --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import budget, native
+    from fine_grained_moe_router_amd.stack import DecodeStack
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    Ms = [int(m) for m in args.M.split(",")]
+    sh = synth.GEMMA4_26B_A4B.with_(layers=args.layers)
+    K, W = args.steps, args.warmup
+
+    t0 = time.time()
+    layers = [synth.layer_weights(sh, l, dev, seed=args.seed, tag="stack") for l in range(sh.layers)]
+    gains = synth.rmsnorm_gains(sh, dev, seed=args.seed)
+    Q, s = synth.lm_head(sh, dev, seed=args.seed)
+    torch.cuda.synchronize()
+    log("weights generated in %.1fs (%.2f GB resident)" % (time.time() - t0, torch.cuda.memory_allocated() / 1e9))
+    st = DecodeStack(sh, layers, gains, Q, s, max_M=max(Ms))
+
+    results = {}
+    for M in Ms:
+        n = K + W
+        xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="bench_x") for i in range(n)]
+        noises = [synth.stack_noise(sh, M, i, device=dev, seed=args.seed) for i in range(n)]
+        g = torch.Generator().manual_seed(synth.seed_of(args.seed, "bench_drafts", M))
+        drafts = [torch.randint(0, sh.vocab, (max(M - 1, 1),), generator=g, dtype=torch.int32).to(dev)
+                  for _ in range(n)]
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(stream):
+            st.step(xs[0], noises[0], drafts[0], M)
+            torch.cuda.synchronize()
+            for i in range(n):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    st.step(xs[i], noises[i], drafts[i], M)
+                graphs.append(gr)
+        torch.cuda.synchronize()
+        log("M=%d: %d step graphs captured" % (M, n))
+
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                graphs[i].replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            w0 = time.perf_counter()
+            e0.record(stream)
+            for i in range(W, n):
+                graphs[i].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - w0
+            ms_total = e0.elapsed_time(e1)
+
+            # per-step latency distribution and the routing each step took
+            per_step, uniq = [], []
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+            ev[0].record(stream)
+            for j, i in enumerate(range(W, n)):
+                graphs[i].replay()
+                ev[j + 1].record(stream)
+            torch.cuda.synchronize()
+            per_step = [ev[j].elapsed_time(ev[j + 1]) for j in range(K)]
+            for i in range(W, n):
+                graphs[i].replay()
+                torch.cuda.synchronize()
+                idx = st.topk_idx[:, :M].cpu().numpy()
+                uniq.append([len(np.unique(idx[l])) for l in range(sh.layers)])
+
+        bytes_steps = [budget.step_bytes(sh, u, M) for u in uniq]
+        ms = ms_total / K
+        bps = float(np.mean(bytes_steps))
+        results[M] = {
+            "steps_per_s": K / (ms_total / 1e3), "ms_per_step": ms, "wall_s": wall,
+            "p50_ms": float(np.percentile(per_step, 50)), "p99_ms": float(np.percentile(per_step, 99)),
+            "bytes_per_step": bps, "hbm_gbs": bps / (ms / 1e3) / 1e9,
+            "hbm_frac": bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "mean_unique_experts_per_layer": float(np.mean(uniq)),
+        }
+        log("M=%d: %.3f ms/step, %.1f steps/s, %.1f GB/s (%.1f%% of 8 TB/s), p50 %.3f p99 %.3f ms" % (
+            M, ms, results[M]["steps_per_s"], results[M]["hbm_gbs"], 100 * results[M]["hbm_frac"],
+            results[M]["p50_ms"], results[M]["p99_ms"]))
+        del graphs
+        torch.cuda.synchronize()
+
+    # lm_head roofline: the largest single launch of the step, timed alone with HIP
+    # events on the stream it is launched on, over K launches on resident inputs
+    M0 = Ms[0]
+    lm_bytes = budget.lm_head_bytes(sh.vocab, sh.hidden)
+    xs_lm = [synth.hidden_inputs(sh, M0, i, device=dev, tag="bench_lm") for i in range(8)]
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for i in range(3):
+            native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, st.tok[:M0], st.max_logit[:M0],
+                                  st.lm_ws, st.lm_ws_bytes)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(K):
+            native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, st.tok[:M0], st.max_logit[:M0],
+                                  st.lm_ws, st.lm_ws_bytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    lm_ms = e0.elapsed_time(e1) / K
+    lm_gbs = lm_bytes / (lm_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_lmhead (lm_head_argmax, M=%d)" % M0,
+                "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
+    log("lm_head alone: %.1f us, %.1f GB/s" % (lm_ms * 1e3, lm_gbs))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, sh, layers, gains, Q, s, Ms[0])
+
+    head = results[Ms[0]]
+    line = {
+        "metric": "decode steps/s + achieved HBM GB/s (% peak), 26B-A4B MoE stack, M=1 & M=5",
+        "value": round(head["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,.) weights quantised to FP8 E4M3FN, N(0,1) inputs)",
+        "config": {"workload": "Gemma-4-26B-A4B-shaped MoE stack: 30 layers x (router 2816x128 bf16, "
+                               "top-8 of 128 + shared expert, width 704, FP8) + tied 262144x2816 FP8 "
+                               "lm_head + argmax + greedy accept, M=%d tokens/step" % Ms[0],
+                   "M": Ms[0], "layers": sh.layers, "hidden": sh.hidden, "experts": sh.experts,
+                   "top_k": sh.top_k, "expert_width": sh.width, "vocab": sh.vocab},
+        "hbm_gbs": round(head["hbm_gbs"], 1),
+        "hbm_frac": round(head["hbm_frac"], 4),
+        "bytes_per_step": int(head["bytes_per_step"]),
+        "p50_ms": round(head["p50_ms"], 4),
+        "p99_ms": round(head["p99_ms"], 4),
+        "per_M": {str(M): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                  for M, r in results.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, sh, layers, gains, Q, s, M):
+    """The oracle (plain fp64 C, OpenMP over output rows) on a bounded sample of the
+    same workload: the first cpu_layers layers for cpu_steps step inputs, plus the
+    full lm_head once per step; scaled to a whole 30-layer step."""
+    import oracle
+    import synth
+    import torch
+    t0 = time.time()
+    host = [synth.weights_to_host(layers[l]) for l in range(args.cpu_layers)]
+    gh = synth.bits16(gains)
+    Qh, sh_ = synth.bytes8(Q), synth.f32(s)
+    log("oracle sample: host copies in %.1fs" % (time.time() - t0))
+    t_layers = 0.0
+    t_lm = 0.0
+    for i in range(args.cpu_steps):
+        x = synth.bits16(synth.hidden_inputs(sh, M, i, tag="bench_x"))
+        noise = synth.bits16(synth.stack_noise(sh, M, i))
+        t = time.perf_counter()
+        h = x
+        y = None
+        for l in range(args.cpu_layers):
+            h, u = oracle.add_rmsnorm(h, noise[l], y, gh[l])
+            y = oracle.moe_layer(u, host[l], sh.top_k)["y_bf16"]
+        t_layers += time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.lm_head_argmax(u, Qh, sh_)
+        t_lm += time.perf_counter() - t
+    per_step = (t_layers / args.cpu_layers * sh.layers + t_lm) / args.cpu_steps
+    log("oracle: %.2f s per full step (sample %.1f s)" % (per_step, t_layers + t_lm))
+    return {"value": round(1.0 / per_step, 5), "unit": "steps/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "M=%d, %d step inputs x (layers 0-%d of the 30-layer stack + the full 262144-row "
+                      "lm_head), scaled to 30 layers; %.1f s of CPU time" % (
+                          M, args.cpu_steps, args.cpu_layers - 1, t_layers + t_lm)}
+
+
+if __name__ == "__main__":
+    main()

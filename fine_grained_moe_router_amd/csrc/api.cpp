@@ -1,0 +1,151 @@
+// api.cpp -- the C ABI: argument validation, workspace carving, and hand-off to
+// the launchers in kernels.hip. Plain C++ with no HIP headers, so the validation
+// can be built and exercised on a host without a GPU.
+#include <stdint.h>
+
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_layer_desc(const moe_layer_desc *d) {
+    if (!d) return MOE_EINVAL;
+    if (d->hidden < 256 || d->hidden > kMaxHidden || d->hidden % 256) return MOE_EINVAL;
+    if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOE_EINVAL;
+    if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > kMaxTopK) return MOE_EINVAL;
+    if (d->expert_width < 64 || d->expert_width > kMaxWidth || d->expert_width % 64) return MOE_EINVAL;
+    if (d->shared_width < 0 || d->shared_width > kMaxWidth || d->shared_width % 64) return MOE_EINVAL;
+    if (d->wtype != MOE_W_FP8_E4M3 && d->wtype != MOE_W_BF16) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+// A required device pointer: NULL -> EINVAL, misaligned -> EALIGN.
+int need(const void *p) {
+    if (!p) return MOE_EINVAL;
+    return aligned16(p) ? MOE_OK : MOE_EALIGN;
+}
+
+#define CHECK(expr)                 \
+    do {                            \
+        int st_ = (expr);           \
+        if (st_ != MOE_OK) return st_; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_strerror(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (size out of range or required pointer NULL)";
+    case MOE_EALIGN: return "pointer not 16-byte aligned";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M) {
+    if (check_layer_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
+    return layer_ws(*desc, max_M).total;
+}
+
+int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
+                     const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    CHECK(check_layer_desc(desc));
+    if (!w || M < 1 || M > kMaxM) return MOE_EINVAL;
+    const bool fp8 = desc->wtype == MOE_W_FP8_E4M3;
+    CHECK(need(w->router_w));
+    if (w->router_bias && !aligned16(w->router_bias)) return MOE_EALIGN;
+    CHECK(need(w->gate_w));
+    CHECK(need(w->up_w));
+    CHECK(need(w->down_w));
+    if (fp8) {
+        CHECK(need(w->gate_s));
+        CHECK(need(w->up_s));
+        CHECK(need(w->down_s));
+    }
+    if (desc->shared_width > 0) {
+        CHECK(need(w->sh_gate_w));
+        CHECK(need(w->sh_up_w));
+        CHECK(need(w->sh_down_w));
+        if (fp8) {
+            CHECK(need(w->sh_gate_s));
+            CHECK(need(w->sh_up_s));
+            CHECK(need(w->sh_down_s));
+        }
+    }
+    CHECK(need(x));
+    CHECK(need(y));
+    if (((uintptr_t)topk_idx | (uintptr_t)topk_w) & 3u) return MOE_EALIGN;
+    const LayerWs L = layer_ws(*desc, M);
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total)
+        return MOE_EWORKSPACE;
+    if (!fp8) return MOE_EUNSUPPORTED;
+    return launch_moe_layer(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, L, stream);
+}
+
+size_t lm_head_argmax_workspace(int max_M, int H, int V) {
+    if (max_M < 1 || max_M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 ||
+        V % 64 || V > (1 << 30))
+        return 0;
+    return lm_ws_bytes(max_M, V);
+}
+
+int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
+                   int32_t *token, float *max_logit, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||
+        V > (1 << 30))
+        return MOE_EINVAL;
+    CHECK(need(x));
+    CHECK(need(w));
+    CHECK(need(w_s));
+    CHECK(need(token));
+    if (max_logit && !aligned16(max_logit)) return MOE_EALIGN;
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lm_ws_bytes(M, V))
+        return MOE_EWORKSPACE;
+    return launch_lm_head(M, H, V, x, w, w_s, token, max_logit, (char *)workspace, stream);
+}
+
+int spec_accept(int num_draft, const int32_t *draft, const int32_t *target,
+                int32_t *accepted_len, int32_t *out_tokens, void *stream) {
+    if (num_draft < 0 || num_draft > kMaxM - 1) return MOE_EINVAL;
+    if (num_draft > 0 && !draft) return MOE_EINVAL;
+    if (!target || !accepted_len || !out_tokens) return MOE_EINVAL;
+    if (((uintptr_t)draft | (uintptr_t)target | (uintptr_t)accepted_len |
+         (uintptr_t)out_tokens) & 3u)
+        return MOE_EALIGN;
+    return launch_spec_accept(num_draft, draft, target, accepted_len, out_tokens, stream);
+}
+
+int moe_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *add0,
+                    const uint16_t *add1, const uint16_t *gain, float eps, uint16_t *h_out,
+                    uint16_t *u_out, void *stream) {
+    if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256) return MOE_EINVAL;
+    if (!(eps >= 0.0f)) return MOE_EINVAL;
+    CHECK(need(h_in));
+    CHECK(need(add0));
+    if (add1 && !aligned16(add1)) return MOE_EALIGN;
+    CHECK(need(gain));
+    CHECK(need(h_out));
+    CHECK(need(u_out));
+    return launch_add_rmsnorm(M, H, h_in, add0, add1, gain, eps, h_out, u_out, stream);
+}
+
+int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,
+                   void *stream) {
+    if (n < 4 || n > (1 << 20) || n % 4) return MOE_EINVAL;
+    CHECK(need(codes));
+    CHECK(need(out_via_bf16));
+    CHECK(need(out_via_f32));
+    return launch_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream);
+}
+
+}  // extern "C"

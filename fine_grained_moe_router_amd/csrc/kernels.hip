@@ -1,0 +1,761 @@
+// kernels.hip -- gfx950 (CDNA4) kernels of the batch-1 fine-grained MoE decode step.
+//
+// Every weight matrix is streamed from HBM once per call with 16-byte loads, for all
+// the tokens that need it. FP8 codes are decoded in registers by the gfx950
+// conversion instructions (two codes per instruction) and multiplied against bf16
+// activations held in LDS with the packed bf16 dot product, accumulating in fp32
+// (page "LLM decoding", "Lever 1: fewer bytes (FP8 weights)": the 8-bit format only
+// saves HBM bytes; the arithmetic runs in a wider type). Per-output-row scales are
+// applied in fp32 after the dot product. Reductions across the lanes that share a
+// row use DPP row operations in a fixed order, so results are deterministic and a
+// token's output never depends on the other tokens of the call.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ scalar helpers
+
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Two E4M3FN codes (bytes 0-1 or 2-3 of v) to two bf16, exactly (scale 1).
+template <bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI);
+}
+
+// Two E4M3FN codes (word HI of v) to two fp32.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t v) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, HI);
+}
+
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// 16 codes (one uint4) -> 8 bf16 pairs in column order.
+__device__ __forceinline__ void decode16_bf16(const uint4 q, bf16x2 (&w)[8]) {
+    w[0] = fp8x2_to_bf16<false>(q.x); w[1] = fp8x2_to_bf16<true>(q.x);
+    w[2] = fp8x2_to_bf16<false>(q.y); w[3] = fp8x2_to_bf16<true>(q.y);
+    w[4] = fp8x2_to_bf16<false>(q.z); w[5] = fp8x2_to_bf16<true>(q.z);
+    w[6] = fp8x2_to_bf16<false>(q.w); w[7] = fp8x2_to_bf16<true>(q.w);
+}
+
+// 8 bf16 weight pairs . 16 bf16 activations (two uint4), accumulated into acc.
+__device__ __forceinline__ float dot16(const bf16x2 (&w)[8], const uint4 x0, const uint4 x1, float acc) {
+    acc = dot2(w[0], as_bf2(x0.x), acc);
+    acc = dot2(w[1], as_bf2(x0.y), acc);
+    acc = dot2(w[2], as_bf2(x0.z), acc);
+    acc = dot2(w[3], as_bf2(x0.w), acc);
+    acc = dot2(w[4], as_bf2(x1.x), acc);
+    acc = dot2(w[5], as_bf2(x1.y), acc);
+    acc = dot2(w[6], as_bf2(x1.z), acc);
+    acc = dot2(w[7], as_bf2(x1.w), acc);
+    return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 4 lanes of a quad; every lane of the quad gets the same bits.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = quad_sum(v);
+    v += dpp<0x141>(v);  // row_half_mirror: combines the two quads of each half row
+    v += dpp<0x140>(v);  // row_mirror: combines the two half rows
+    return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+}
+
+// -------------------------------------------------------------------- router
+
+struct RouterArgs {
+    const uint16_t *x;   // [M][H]
+    const uint16_t *w;   // [H][E]
+    float *partial;      // [NB][M][E]
+    int M, H, E;
+};
+
+// Partial router logits of one block of kRouterRows rows of W: thread (grp, e)
+// accumulates rows grp, grp + G, ... of its column; groups are summed in order.
+__global__ __launch_bounds__(256) void k_router(RouterArgs a) {
+    __shared__ float xs[kMaxM][kRouterRows];
+    __shared__ float red[256][kMaxM];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int r0 = b * kRouterRows;
+    const int nr = min(kRouterRows, a.H - r0);
+    for (int i = tid; i < a.M * kRouterRows; i += 256) {
+        const int m = i / kRouterRows, r = i % kRouterRows;
+        xs[m][r] = r < nr ? bf2f(a.x[(size_t)m * a.H + r0 + r]) : 0.0f;
+    }
+    __syncthreads();
+    const int E = a.E, G = 256 / E;
+    const int e = tid % E, grp = tid / E;
+    float acc[kMaxM];
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m) acc[m] = 0.0f;
+    if (grp < G) {
+        for (int r = grp; r < nr; r += G) {
+            const float wv = bf2f(a.w[(size_t)(r0 + r) * E + e]);
+#pragma unroll
+            for (int m = 0; m < kMaxM; ++m)
+                if (m < a.M) acc[m] = fmaf(xs[m][r], wv, acc[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m) red[tid][m] = acc[m];
+    __syncthreads();
+    if (tid < E) {
+        for (int m = 0; m < a.M; ++m) {
+            float s = 0.0f;
+            for (int g = 0; g < G; ++g) s += red[g * E + tid][m];
+            a.partial[((size_t)b * a.M + m) * E + tid] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------- top-K and union
+
+struct TopkArgs {
+    const float *partial;  // [NB][M][E]
+    const float *bias;     // [E] or null
+    int32_t *topk_idx;     // [M][K] or null
+    float *topk_w;         // [M][K] or null
+    int32_t *n_slots;
+    int32_t *slot_expert;
+    uint32_t *slot_mask;
+    float *slot_w;         // [S][M]
+    int M, E, K, NB, shared;
+};
+
+// One workgroup: wave m selects token m's top K (K rounds of a wave argmax with
+// ties to the lower id), then all threads build the union of selected experts in
+// ascending id, each with its token mask and combine weights; the shared expert
+// (id E) is appended last with weight 1 for every token.
+__global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
+    __shared__ float wsel[kMaxM][kMaxExperts];
+    __shared__ int sel_e[kMaxM][kMaxTopK];
+    __shared__ float sel_l[kMaxM][kMaxTopK];
+    __shared__ int wave_cnt[4];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int E = a.E, K = a.K, M = a.M;
+    for (int i = tid; i < kMaxM * kMaxExperts; i += 512) (&wsel[0][0])[i] = 0.0f;
+    __syncthreads();
+    if (wave < M) {
+        const int m = wave;
+        float l[4];
+        bool taken[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            taken[i] = false;
+            if (e < E) {
+                float s = 0.0f;
+                for (int b = 0; b < a.NB; ++b) s += a.partial[((size_t)b * M + m) * E + e];
+                if (a.bias) s += a.bias[e];
+                l[i] = s;
+            } else {
+                l[i] = -INFINITY;
+            }
+        }
+        for (int k = 0; k < K; ++k) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !taken[i] && (l[i] > bv || (l[i] == bv && e < bi))) {
+                    bv = l[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane + 64 * i == bi) taken[i] = true;
+            if (lane == 0) {
+                sel_e[m][k] = bi;
+                sel_l[m][k] = bv;
+            }
+        }
+        if (lane == 0) {
+            // renormalised softmax over the selected logits (the full-softmax
+            // denominator cancels); sel_l[m][0] is the largest logit
+            const float lmax = sel_l[m][0];
+            float z = 0.0f;
+            for (int k = 0; k < K; ++k) z += expf(sel_l[m][k] - lmax);
+            // ascending expert id (insertion sort of K <= 16 entries)
+            for (int k = 1; k < K; ++k) {
+                const int ek = sel_e[m][k];
+                const float lk = sel_l[m][k];
+                int j = k - 1;
+                while (j >= 0 && sel_e[m][j] > ek) {
+                    sel_e[m][j + 1] = sel_e[m][j];
+                    sel_l[m][j + 1] = sel_l[m][j];
+                    --j;
+                }
+                sel_e[m][j + 1] = ek;
+                sel_l[m][j + 1] = lk;
+            }
+            for (int k = 0; k < K; ++k) {
+                const float wk = expf(sel_l[m][k] - lmax) / z;
+                wsel[m][sel_e[m][k]] = wk;
+                if (a.topk_idx) a.topk_idx[m * K + k] = sel_e[m][k];
+                if (a.topk_w) a.topk_w[m * K + k] = wk;
+            }
+        }
+    }
+    __syncthreads();
+    // union over tokens, slots in ascending expert id
+    uint32_t mask = 0;
+    if (tid < 256 && tid < E) {
+        for (int m = 0; m < M; ++m)
+            for (int k = 0; k < K; ++k)
+                if (sel_e[m][k] == tid) mask |= 1u << m;
+    }
+    const unsigned long long bal = __ballot(mask != 0);
+    if (tid < 256 && lane == 0) wave_cnt[wave] = __popcll(bal);
+    __syncthreads();
+    if (tid < 256 && mask) {
+        int base = 0;
+        for (int w = 0; w < wave; ++w) base += wave_cnt[w];
+        const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
+        a.slot_expert[slot] = tid;
+        a.slot_mask[slot] = mask;
+        for (int m = 0; m < M; ++m) a.slot_w[slot * M + m] = wsel[m][tid];
+    }
+    if (tid == 0) {
+        const int nr = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+        int ns = nr;
+        if (a.shared) {
+            a.slot_expert[ns] = E;
+            a.slot_mask[ns] = (1u << M) - 1u;
+            for (int m = 0; m < M; ++m) a.slot_w[ns * M + m] = 1.0f;
+            ++ns;
+        }
+        *a.n_slots = ns;
+    }
+}
+
+// ------------------------------------------------------------ expert gate/up
+
+struct ExpertArgs {
+    const uint16_t *x;        // [M][H] layer input
+    const uint8_t *gate, *up, *down;          // routed [E][D][H], [E][D][H], [E][H][D]
+    const float *gate_s, *up_s, *down_s;      // [E][D], [E][D], [E][H]
+    const uint8_t *sh_gate, *sh_up, *sh_down;
+    const float *sh_gate_s, *sh_up_s, *sh_down_s;
+    const int32_t *n_slots;
+    const int32_t *slot_expert;
+    const uint32_t *slot_mask;
+    const float *slot_w;      // [S][M]
+    float *h;                 // [S][M][F]
+    float *ypart;             // [S][M][H]
+    int M, H, E, D, Ds, F;
+    int down_lds;             // bytes of dynamic LDS given to k_down
+};
+
+constexpr int kGateUpRows = 16;   // rows of gate (and of up) per workgroup
+constexpr int kGateUpUnroll = 6;  // 16-byte chunks per lane in flight, per matrix
+
+// Workgroup (row block, slot): 4 waves x 4 groups of 16 lanes; each group owns one
+// row j of gate and up; lane li reads bytes [256 i + 16 li, +16) of the row for
+// i = 0..H/256-1 (each load instruction reads 4 rows x 256 contiguous bytes).
+// h[slot][t][j] = gelu_tanh(s_g[j] (G_j . x_t)) * (s_u[j] (U_j . x_t)).
+__global__ __launch_bounds__(256) void k_gateup(ExpertArgs a) {
+    extern __shared__ uint4 xs[];  // [ntok][H/8]
+    const int s = blockIdx.y;
+    if (s >= *a.n_slots) return;
+    const int e = a.slot_expert[s];
+    const bool shared = e == a.E;
+    const int F = shared ? a.Ds : a.D;
+    const int row0 = blockIdx.x * kGateUpRows;
+    if (row0 >= F) return;
+    const uint32_t mask = a.slot_mask[s];
+    const int ntok = __popc(mask);
+    const int H = a.H, hv = H / 8;
+    {
+        uint32_t mm = mask;
+        for (int t = 0; mm; mm &= mm - 1u, ++t) {
+            const int tok = __ffs(mm) - 1;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)tok * H);
+            for (int i = threadIdx.x; i < hv; i += 256) xs[t * hv + i] = src[i];
+        }
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    const int row = row0 + wave * 4 + g;
+    const size_t eoff = (size_t)e * a.D * H;
+    const uint8_t *gw = (shared ? a.sh_gate : a.gate + eoff) + (size_t)row * H + li * 16;
+    const uint8_t *uw = (shared ? a.sh_up : a.up + eoff) + (size_t)row * H + li * 16;
+    float accg[kMaxM], accu[kMaxM];
+#pragma unroll
+    for (int t = 0; t < kMaxM; ++t) accg[t] = accu[t] = 0.0f;
+    const int NC = H / 256;
+    for (int i0 = 0; i0 < NC; i0 += kGateUpUnroll) {
+        uint4 qg[kGateUpUnroll], qu[kGateUpUnroll];
+#pragma unroll
+        for (int k = 0; k < kGateUpUnroll; ++k) {
+            if (i0 + k < NC) {
+                qg[k] = *reinterpret_cast<const uint4 *>(gw + (size_t)(i0 + k) * 256);
+                qu[k] = *reinterpret_cast<const uint4 *>(uw + (size_t)(i0 + k) * 256);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kGateUpUnroll; ++k) {
+            if (i0 + k < NC) {
+                bf16x2 wg[8], wu[8];
+                decode16_bf16(qg[k], wg);
+                decode16_bf16(qu[k], wu);
+                const int xv = ((i0 + k) * 256 + li * 16) / 8;
+#pragma unroll
+                for (int t = 0; t < kMaxM; ++t) {
+                    if (t < ntok) {
+                        const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
+                        accg[t] = dot16(wg, x0, x1, accg[t]);
+                        accu[t] = dot16(wu, x0, x1, accu[t]);
+                    }
+                }
+            }
+        }
+    }
+    const float sg = (shared ? a.sh_gate_s : a.gate_s + (size_t)e * a.D)[row];
+    const float su = (shared ? a.sh_up_s : a.up_s + (size_t)e * a.D)[row];
+#pragma unroll
+    for (int t = 0; t < kMaxM; ++t) {
+        if (t < ntok) {
+            const float ga = row16_sum(accg[t]);
+            const float ub = row16_sum(accu[t]);
+            if (li == 0)
+                a.h[((size_t)s * a.M + t) * a.F + row] = gelu_tanh(sg * ga) * (su * ub);
+        }
+    }
+}
+
+// --------------------------------------------------------------- expert down
+
+constexpr int kDownRows = 64;    // output rows per workgroup
+constexpr int kDownUnroll = 6;
+constexpr int kDownLdsBytes = 64 * 1024;
+
+// Workgroup (row block, slot): wave w owns rows c0 + 16 w .. +16, 4 lanes per row;
+// lane q reads bytes [64 i + 16 q, +16) of the row (i = 0..F/64-1). h of the slot's
+// tokens is staged in LDS (fp32). ypart[slot][m][c] = w[slot][m] * s_d[c] (Dn_c . h).
+__global__ __launch_bounds__(256) void k_down(ExpertArgs a) {
+    extern __shared__ float4 hs4[];  // [tp][F/4]
+    const int s = blockIdx.y;
+    if (s >= *a.n_slots) return;
+    const int e = a.slot_expert[s];
+    const bool shared = e == a.E;
+    const int F = shared ? a.Ds : a.D;
+    const uint32_t mask = a.slot_mask[s];
+    const int ntok = __popc(mask);
+    const int H = a.H;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int q = lane & 3;
+    const int c = blockIdx.x * kDownRows + wave * 16 + (lane >> 2);
+    const uint8_t *dw = (shared ? a.sh_down : a.down + (size_t)e * H * a.D) + (size_t)c * F + q * 16;
+    const float sd = (shared ? a.sh_down_s : a.down_s + (size_t)e * H)[c];
+    const int f4 = F / 4;
+    const int tp = min(ntok, a.down_lds / (F * 4));
+    const int NI = F / 64;
+    uint32_t mrem = mask;
+    for (int t0 = 0; t0 < ntok; t0 += tp) {
+        const int tn = min(tp, ntok - t0);
+        __syncthreads();
+        for (int i = threadIdx.x; i < tn * f4; i += 256) {
+            const int t = i / f4, j = i % f4;
+            hs4[t * f4 + j] = reinterpret_cast<const float4 *>(a.h + ((size_t)s * a.M + t0 + t) * a.F)[j];
+        }
+        __syncthreads();
+        float acc[kMaxM];
+#pragma unroll
+        for (int t = 0; t < kMaxM; ++t) acc[t] = 0.0f;
+        for (int i0 = 0; i0 < NI; i0 += kDownUnroll) {
+            uint4 qd[kDownUnroll];
+#pragma unroll
+            for (int k = 0; k < kDownUnroll; ++k)
+                if (i0 + k < NI) qd[k] = *reinterpret_cast<const uint4 *>(dw + (size_t)(i0 + k) * 64);
+#pragma unroll
+            for (int k = 0; k < kDownUnroll; ++k) {
+                if (i0 + k < NI) {
+                    float wv[16];
+                    const uint32_t qw[4] = {qd[k].x, qd[k].y, qd[k].z, qd[k].w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const f32x2 lo = fp8x2_to_f32<false>(qw[u]);
+                        const f32x2 hi = fp8x2_to_f32<true>(qw[u]);
+                        wv[4 * u + 0] = lo.x; wv[4 * u + 1] = lo.y;
+                        wv[4 * u + 2] = hi.x; wv[4 * u + 3] = hi.y;
+                    }
+                    const int cv = ((i0 + k) * 64 + q * 16) / 4;
+#pragma unroll
+                    for (int t = 0; t < kMaxM; ++t) {
+                        if (t < tn) {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const float4 hv = hs4[t * f4 + cv + u];
+                                acc[t] = fmaf(wv[4 * u + 0], hv.x, acc[t]);
+                                acc[t] = fmaf(wv[4 * u + 1], hv.y, acc[t]);
+                                acc[t] = fmaf(wv[4 * u + 2], hv.z, acc[t]);
+                                acc[t] = fmaf(wv[4 * u + 3], hv.w, acc[t]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kMaxM; ++t) {
+            if (t < tn) {
+                const int m = __ffs(mrem) - 1;
+                mrem &= mrem - 1u;
+                const float v = quad_sum(acc[t]);
+                if (q == 0)
+                    a.ypart[((size_t)s * a.M + m) * H + c] = a.slot_w[s * a.M + m] * (sd * v);
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------- combine
+
+struct CombineArgs {
+    const int32_t *n_slots;
+    const uint32_t *slot_mask;
+    const float *ypart;  // [S][M][H]
+    uint16_t *y;         // [M][H]
+    int M, H;
+};
+
+// y[m][c] = bf16( sum over the slots of token m, ascending expert id, shared last ).
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int m = blockIdx.y;
+    const int ns = *a.n_slots;
+    float acc = 0.0f;
+    for (int s = 0; s < ns; ++s)
+        if ((a.slot_mask[s] >> m) & 1u) acc += a.ypart[((size_t)s * a.M + m) * a.H + c];
+    a.y[(size_t)m * a.H + c] = f2bf(acc);
+}
+
+// ------------------------------------------------------------------- lm_head
+
+struct LmArgs {
+    const uint16_t *x;  // [M][H]
+    const uint8_t *w;   // [V][H]
+    const float *s;     // [V]
+    float *best_v;      // [grid][M]
+    int32_t *best_i;    // [grid][M]
+    int32_t *token;
+    float *max_logit;
+    int M, H, V, nwg;
+};
+
+constexpr int kLmRowsPerLane = 4;
+constexpr int kLmUnroll = 2;
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+// Workgroups stride over 64-row blocks. Lane (wave w, group g, li) owns rows
+// blk*64 + 16 w + 4 g + r (r = 0..3) and reads the same 16-byte column chunk of all
+// four, so each bf16 activation chunk read from LDS serves 4 rows. Row sums go
+// through the 16-lane DPP reduction; each group keeps its running best per token.
+__global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
+    extern __shared__ uint4 xs[];  // [M][H/8]; reused at the end for the per-group bests
+    const int H = a.H, hv = H / 8, M = a.M;
+    for (int i = threadIdx.x; i < M * hv; i += 256)
+        xs[i] = reinterpret_cast<const uint4 *>(a.x)[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, li = lane & 15;
+    float bv[kMaxM];
+    int bi[kMaxM];
+#pragma unroll
+    for (int t = 0; t < kMaxM; ++t) {
+        bv[t] = -INFINITY;
+        bi[t] = 0x7fffffff;
+    }
+    const int NC = H / 256;
+    const int nblk = a.V / kLmRowsPerWG;
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int rbase = blk * kLmRowsPerWG + wave * 16 + g * 4;
+        const uint8_t *wr = a.w + (size_t)rbase * H + li * 16;
+        float acc[kLmRowsPerLane][kMaxM];
+#pragma unroll
+        for (int r = 0; r < kLmRowsPerLane; ++r)
+#pragma unroll
+            for (int t = 0; t < kMaxM; ++t) acc[r][t] = 0.0f;
+        for (int i0 = 0; i0 < NC; i0 += kLmUnroll) {
+            uint4 q[kLmUnroll][kLmRowsPerLane];
+#pragma unroll
+            for (int k = 0; k < kLmUnroll; ++k)
+#pragma unroll
+                for (int r = 0; r < kLmRowsPerLane; ++r)
+                    if (i0 + k < NC)
+                        q[k][r] = *reinterpret_cast<const uint4 *>(wr + (size_t)r * H + (size_t)(i0 + k) * 256);
+#pragma unroll
+            for (int k = 0; k < kLmUnroll; ++k) {
+                if (i0 + k < NC) {
+                    bf16x2 wv[kLmRowsPerLane][8];
+#pragma unroll
+                    for (int r = 0; r < kLmRowsPerLane; ++r) decode16_bf16(q[k][r], wv[r]);
+                    const int xv = ((i0 + k) * 256 + li * 16) / 8;
+#pragma unroll
+                    for (int t = 0; t < kMaxM; ++t) {
+                        if (t < M) {
+                            const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
+#pragma unroll
+                            for (int r = 0; r < kLmRowsPerLane; ++r) acc[r][t] = dot16(wv[r], x0, x1, acc[r][t]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kLmRowsPerLane; ++r) {
+            const int v = rbase + r;
+            const float sc = a.s[v];
+#pragma unroll
+            for (int t = 0; t < kMaxM; ++t) {
+                if (t < M) {
+                    const float lg = sc * row16_sum(acc[r][t]);
+                    if (better(lg, v, bv[t], bi[t])) {
+                        bv[t] = lg;
+                        bi[t] = v;
+                    }
+                }
+            }
+        }
+    }
+    // 16 groups x M (value, row) pairs = 128 M bytes <= the M * H * 2 bytes of xs
+    __syncthreads();
+    float *gv = reinterpret_cast<float *>(xs);
+    int *gi = reinterpret_cast<int *>(xs) + 16 * M;
+    if (li == 0) {
+#pragma unroll
+        for (int t = 0; t < kMaxM; ++t) {
+            if (t < M) {
+                gv[(wave * 4 + g) * M + t] = bv[t];
+                gi[(wave * 4 + g) * M + t] = bi[t];
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+        const int t = threadIdx.x;
+        float v = gv[t];
+        int i = gi[t];
+        for (int k = 1; k < 16; ++k)
+            if (better(gv[k * M + t], gi[k * M + t], v, i)) {
+                v = gv[k * M + t];
+                i = gi[k * M + t];
+            }
+        a.best_v[blockIdx.x * M + t] = v;
+        a.best_i[blockIdx.x * M + t] = i;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_argmax_final(LmArgs a) {
+    __shared__ float rv[256];
+    __shared__ int ri[256];
+    for (int t = 0; t < a.M; ++t) {
+        float v = -INFINITY;
+        int i = 0x7fffffff;
+        for (int k = threadIdx.x; k < a.nwg; k += 256) {
+            const float kv = a.best_v[k * a.M + t];
+            const int ki = a.best_i[k * a.M + t];
+            if (better(kv, ki, v, i)) {
+                v = kv;
+                i = ki;
+            }
+        }
+        rv[threadIdx.x] = v;
+        ri[threadIdx.x] = i;
+        __syncthreads();
+        for (int off = 128; off >= 1; off >>= 1) {
+            if (threadIdx.x < off && better(rv[threadIdx.x + off], ri[threadIdx.x + off], rv[threadIdx.x], ri[threadIdx.x])) {
+                rv[threadIdx.x] = rv[threadIdx.x + off];
+                ri[threadIdx.x] = ri[threadIdx.x + off];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            a.token[t] = ri[0];
+            if (a.max_logit) a.max_logit[t] = rv[0];
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------- acceptance
+
+__global__ void k_spec_accept(int gamma, const int32_t *draft, const int32_t *target,
+                              int32_t *accepted_len, int32_t *out_tokens) {
+    if (threadIdx.x != 0) return;
+    int n = 0;
+    while (n < gamma && draft[n] == target[n]) ++n;
+    for (int i = 0; i <= gamma; ++i) out_tokens[i] = i <= n ? target[i] : -1;
+    *accepted_len = n;
+}
+
+// ------------------------------------------------------- residual + RMSNorm
+
+// One workgroup per token: h_out = bf16(h_in + a0 + a1); u = bf16(h_out * rsqrt(mean h_out^2 + eps) * g).
+__global__ __launch_bounds__(256) void k_add_rmsnorm(int H, const uint16_t *h_in, const uint16_t *a0,
+                                                     const uint16_t *a1, const uint16_t *gain,
+                                                     float eps, uint16_t *h_out, uint16_t *u) {
+    __shared__ float wsum[4];
+    const int m = blockIdx.x;
+    const size_t o = (size_t)m * H;
+    float ss = 0.0f;
+    for (int c = threadIdx.x; c < H; c += 256) {
+        float v = bf2f(h_in[o + c]) + bf2f(a0[o + c]);
+        if (a1) v += bf2f(a1[o + c]);
+        const uint16_t hb = f2bf(v);
+        h_out[o + c] = hb;
+        const float hf = bf2f(hb);
+        ss = fmaf(hf, hf, ss);
+    }
+    // fixed-order reduction: DPP rows, then the four rows of a wave, then waves
+    ss = row16_sum(ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    const float r = rsqrtf(tot / (float)H + eps);
+    for (int c = threadIdx.x; c < H; c += 256)
+        u[o + c] = f2bf(bf2f(h_out[o + c]) * r * bf2f(gain[c]));
+}
+
+// Each thread decodes 4 codes through both conversion paths of the GEMV kernels.
+__global__ __launch_bounds__(256) void k_fp8_decode(int n, const uint32_t *codes, float4 *via_bf16,
+                                                    float4 *via_f32) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i * 4 >= n) return;
+    const uint32_t v = codes[i];
+    const bf16x2 lo = fp8x2_to_bf16<false>(v), hi = fp8x2_to_bf16<true>(v);
+    const uint32_t ulo = __builtin_bit_cast(uint32_t, lo), uhi = __builtin_bit_cast(uint32_t, hi);
+    via_bf16[i] = make_float4(bf2f(ulo & 0xffffu), bf2f(ulo >> 16), bf2f(uhi & 0xffffu), bf2f(uhi >> 16));
+    const f32x2 flo = fp8x2_to_f32<false>(v), fhi = fp8x2_to_f32<true>(v);
+    via_f32[i] = make_float4(flo.x, flo.y, fhi.x, fhi.y);
+}
+
+inline hipStream_t S(void *p) { return reinterpret_cast<hipStream_t>(p); }
+
+inline int launched() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH; }
+
+}  // namespace
+
+int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
+                     const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
+                     char *ws, const LayerWs &L, void *stream) {
+    (void)hipGetLastError();
+    const int H = d.hidden, E = d.num_experts;
+    RouterArgs ra{x, w.router_w, reinterpret_cast<float *>(ws + L.partial), M, H, E};
+    hipLaunchKernelGGL(k_router, dim3(L.nb), dim3(256), 0, S(stream), ra);
+    TopkArgs ta{reinterpret_cast<const float *>(ws + L.partial), w.router_bias, topk_idx, topk_w,
+                reinterpret_cast<int32_t *>(ws + L.n_slots), reinterpret_cast<int32_t *>(ws + L.slot_expert),
+                reinterpret_cast<uint32_t *>(ws + L.slot_mask), reinterpret_cast<float *>(ws + L.slot_w),
+                M, E, d.top_k, L.nb, d.shared_width > 0 ? 1 : 0};
+    hipLaunchKernelGGL(k_topk, dim3(1), dim3(512), 0, S(stream), ta);
+    const int S_ = max_slots(M, d.top_k, E, d.shared_width);
+    ExpertArgs ea{x,
+                  static_cast<const uint8_t *>(w.gate_w), static_cast<const uint8_t *>(w.up_w),
+                  static_cast<const uint8_t *>(w.down_w), w.gate_s, w.up_s, w.down_s,
+                  static_cast<const uint8_t *>(w.sh_gate_w), static_cast<const uint8_t *>(w.sh_up_w),
+                  static_cast<const uint8_t *>(w.sh_down_w), w.sh_gate_s, w.sh_up_s, w.sh_down_s,
+                  reinterpret_cast<const int32_t *>(ws + L.n_slots),
+                  reinterpret_cast<const int32_t *>(ws + L.slot_expert),
+                  reinterpret_cast<const uint32_t *>(ws + L.slot_mask),
+                  reinterpret_cast<const float *>(ws + L.slot_w),
+                  reinterpret_cast<float *>(ws + L.h), reinterpret_cast<float *>(ws + L.ypart),
+                  M, H, E, d.expert_width, d.shared_width, L.F,
+                  min(M, kDownLdsBytes / (L.F * 4)) * L.F * 4};
+    hipLaunchKernelGGL(k_gateup, dim3(L.F / kGateUpRows, S_), dim3(256), (size_t)M * H * 2, S(stream), ea);
+    hipLaunchKernelGGL(k_down, dim3(H / kDownRows, S_), dim3(256), (size_t)ea.down_lds, S(stream), ea);
+    CombineArgs ca{reinterpret_cast<const int32_t *>(ws + L.n_slots),
+                   reinterpret_cast<const uint32_t *>(ws + L.slot_mask),
+                   reinterpret_cast<const float *>(ws + L.ypart), y, M, H};
+    hipLaunchKernelGGL(k_combine, dim3(H / 256, M), dim3(256), 0, S(stream), ca);
+    return launched();
+}
+
+int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
+                   int32_t *token, float *max_logit, char *ws, void *stream) {
+    (void)hipGetLastError();
+    const int nwg = lm_grid(V);
+    LmArgs a{x, w, s, reinterpret_cast<float *>(ws),
+             reinterpret_cast<int32_t *>(ws + align256((size_t)nwg * M * sizeof(float))),
+             token, max_logit, M, H, V, nwg};
+    hipLaunchKernelGGL(k_lmhead, dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
+    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, S(stream), a);
+    return launched();
+}
+
+int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,
+                       int32_t *accepted_len, int32_t *out_tokens, void *stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_spec_accept, dim3(1), dim3(64), 0, S(stream), gamma, draft, target,
+                       accepted_len, out_tokens);
+    return launched();
+}
+
+int launch_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *a0, const uint16_t *a1,
+                       const uint16_t *g, float eps, uint16_t *h_out, uint16_t *u, void *stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_add_rmsnorm, dim3(M), dim3(256), 0, S(stream), H, h_in, a0, a1, g, eps, h_out, u);
+    return launched();
+}
+
+int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream) {
+    (void)hipGetLastError();
+    const int threads = n / 4;
+    hipLaunchKernelGGL(k_fp8_decode, dim3((threads + 255) / 256), dim3(256), 0, S(stream), n,
+                       reinterpret_cast<const uint32_t *>(codes), reinterpret_cast<float4 *>(via_bf16),
+                       reinterpret_cast<float4 *>(via_f32));
+    return launched();
+}
+
+}  // namespace moe

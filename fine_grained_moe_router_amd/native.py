@@ -1,0 +1,154 @@
+"""Thin ctypes binding of libmoedecode.so (the C ABI in include/moe_decode.h).
+
+Argument marshalling only: every step of the decode path runs in the library's
+HIP kernels. Tensors are torch device tensors (torch provides device memory and
+streams); each wrapper passes their data pointers and the current HIP stream. A
+missing library raises at first use: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoedecode.so")
+_lib = None
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
+MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
+
+# Every symbol include/moe_decode.h declares.
+EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "lm_head_argmax_workspace",
+           "lm_head_argmax", "spec_accept", "moe_add_rmsnorm", "moe_fp8_decode", "moe_strerror")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__("%s failed: %s (%d)" % (fn, strerror(status), status))
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int), ("num_experts", ctypes.c_int), ("top_k", ctypes.c_int),
+                ("expert_width", ctypes.c_int), ("shared_width", ctypes.c_int), ("wtype", ctypes.c_int)]
+
+
+_P = ctypes.c_void_p
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("router_w", "router_bias", "gate_w", "up_w", "down_w", "gate_s",
+                                  "up_s", "down_s", "sh_gate_w", "sh_up_w", "sh_down_w",
+                                  "sh_gate_s", "sh_up_s", "sh_down_s")]
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libmoedecode.so is not built (%s); run "
+                               "python -m fine_grained_moe_router_amd.build" % _LIB_PATH)
+        L = ctypes.CDLL(_LIB_PATH)
+        I, S = ctypes.c_int, ctypes.c_size_t
+        L.moe_decode_layer_workspace.restype = S
+        L.moe_decode_layer_workspace.argtypes = [ctypes.POINTER(LayerDesc), I]
+        L.moe_decode_layer.restype = I
+        L.moe_decode_layer.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), I,
+                                       _P, _P, _P, _P, _P, S, _P]
+        L.lm_head_argmax_workspace.restype = S
+        L.lm_head_argmax_workspace.argtypes = [I, I, I]
+        L.lm_head_argmax.restype = I
+        L.lm_head_argmax.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P, S, _P]
+        L.spec_accept.restype = I
+        L.spec_accept.argtypes = [I, _P, _P, _P, _P, _P]
+        L.moe_add_rmsnorm.restype = I
+        L.moe_add_rmsnorm.argtypes = [I, I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
+        L.moe_fp8_decode.restype = I
+        L.moe_fp8_decode.argtypes = [I, _P, _P, _P, _P]
+        L.moe_strerror.restype = ctypes.c_char_p
+        L.moe_strerror.argtypes = [I]
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().moe_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+def layer_desc(shape, expert_dtype: str = "fp8") -> LayerDesc:
+    return LayerDesc(shape.hidden, shape.experts, shape.top_k, shape.width, shape.shared_width,
+                     MOE_W_FP8_E4M3 if expert_dtype == "fp8" else MOE_W_BF16)
+
+
+def layer_weights(w: dict) -> LayerWeights:
+    """LayerWeights from a dict of device tensors (keys as synth.layer_weights)."""
+    keys = ("router_w", "router_b", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
+            "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s")
+    return LayerWeights(*[_ptr(w.get(k)) for k in keys])
+
+
+def moe_decode_layer_workspace(desc: LayerDesc, max_M: int) -> int:
+    return lib().moe_decode_layer_workspace(ctypes.byref(desc), int(max_M))
+
+
+def moe_decode_layer(desc: LayerDesc, weights: LayerWeights, M: int, x, y, topk_idx, topk_w,
+                     workspace, workspace_bytes: int, stream=None):
+    st = lib().moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), int(M), _ptr(x), _ptr(y),
+                                _ptr(topk_idx), _ptr(topk_w), _ptr(workspace), int(workspace_bytes),
+                                _stream(stream))
+    _check("moe_decode_layer", st)
+
+
+def lm_head_argmax_workspace(max_M: int, H: int, V: int) -> int:
+    return lib().lm_head_argmax_workspace(int(max_M), int(H), int(V))
+
+
+def lm_head_argmax(M, H, V, x, w, w_s, token, max_logit, workspace, workspace_bytes, stream=None):
+    st = lib().lm_head_argmax(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), _ptr(token),
+                              _ptr(max_logit), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("lm_head_argmax", st)
+
+
+def spec_accept(num_draft, draft, target, accepted_len, out_tokens, stream=None):
+    st = lib().spec_accept(int(num_draft), _ptr(draft), _ptr(target), _ptr(accepted_len),
+                           _ptr(out_tokens), _stream(stream))
+    _check("spec_accept", st)
+
+
+def moe_add_rmsnorm(M, H, h_in, add0, add1, gain, eps, h_out, u_out, stream=None):
+    st = lib().moe_add_rmsnorm(int(M), int(H), _ptr(h_in), _ptr(add0), _ptr(add1), _ptr(gain),
+                               float(eps), _ptr(h_out), _ptr(u_out), _stream(stream))
+    _check("moe_add_rmsnorm", st)
+
+
+def moe_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream=None):
+    st = lib().moe_fp8_decode(int(n), _ptr(codes), _ptr(out_via_bf16), _ptr(out_via_f32),
+                              _stream(stream))
+    _check("moe_fp8_decode", st)
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zeroed device buffer of nbytes (torch allocations are 256-byte aligned)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)

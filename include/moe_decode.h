@@ -1,0 +1,188 @@
+/*
+ * moe_decode.h -- C ABI of the MI355X (gfx950) batch-1 fine-grained MoE decode step.
+ *
+ * One decode step of a Gemma-4-26B-A4B-shaped mixture-of-experts model at batch 1,
+ * including the small verify batch of speculative decoding (M <= 8 tokens that
+ * share one pass over the weights). Shapes and the structure of the step follow
+ * the page "LLM decoding" (us-homepage.pages.dev/blog/llm-decoding):
+ *   - "The exact architecture, and why it rules out 4-bit": each layer routes to
+ *     the top 8 of 128 experts plus one always-on shared expert; expert width 704,
+ *     hidden 2816; tied lm_head over a 262,144-token vocabulary.
+ *   - "Where the 7.36 GB goes": per expert a gate, an up and a down matrix; a
+ *     router; the lm_head read once per token.
+ *   - "Lever 1: fewer bytes (FP8 weights)": weights stored in 8 bits and decoded
+ *     to a wider type for the arithmetic.
+ *   - "Lever 2: fewer passes (native MTP)": the target checks the drafted tokens
+ *     in a single pass and keeps the ones it would have produced.
+ *
+ * Conventions for every entry point
+ *   - Device pointers are owned by the caller; the library allocates nothing,
+ *     never synchronises and keeps no global mutable state. Calls with distinct
+ *     workspaces may run concurrently on different streams.
+ *   - `stream` is a hipStream_t (NULL: the default stream). Work is enqueued
+ *     asynchronously; calls are hipGraph-capturable (no memset nodes are used).
+ *   - Matrices are row-major [rows][cols]. bf16 values are passed as their 16-bit
+ *     patterns (uint16_t). FP8 values are OCP E4M3FN code bytes (bias 7, max 448,
+ *     NaN = 0x7F/0xFF), each output row with one fp32 scale applied after its dot
+ *     product: out[r] = scale[r] * sum_c decode(Q[r][c]) * x[c].
+ *   - Arguments are validated on the host before anything is enqueued. A
+ *     failure returns a negative moe_status and enqueues nothing; MOE_ELAUNCH
+ *     means the runtime refused a launch (work already enqueued by the same call
+ *     may have run). Faults inside kernels surface at the caller's next
+ *     synchronisation.
+ *   - Arithmetic: products of FP8/bf16 values are exact in fp32; sums are fp32.
+ *     The router logits, the expert intermediates and the combine stay fp32;
+ *     the only rounding to bf16 is that of each output tensor.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,        /* a size or count out of range, or a required pointer is NULL */
+    MOE_EALIGN = -2,        /* a pointer is not 16-byte aligned                              */
+    MOE_EWORKSPACE = -3,    /* workspace NULL or smaller than the *_workspace() size         */
+    MOE_EUNSUPPORTED = -4,  /* a valid request this build does not implement                 */
+    MOE_ELAUNCH = -5        /* the HIP runtime rejected a kernel launch                      */
+} moe_status;
+
+typedef enum moe_wtype {
+    MOE_W_FP8_E4M3 = 0,     /* expert weights: FP8 E4M3FN codes + fp32 per-row scales        */
+    MOE_W_BF16 = 1          /* expert weights: bf16, no scales                               */
+} moe_wtype;
+
+/* Shape of one MoE layer.
+ *   hidden        H: a multiple of 256, at most 4096            (Gemma-4-26B-A4B: 2816)
+ *   num_experts   E: 1..256                                      (128)
+ *   top_k         K: 1..min(E, 16)                               (8)
+ *   expert_width  D: a multiple of 64, 64..4096                  (704)
+ *   shared_width  Ds: 0 (no shared expert) or a multiple of 64 up to 4096 (704; the
+ *                 page's dense MLP is 2112 wide)
+ *   wtype         a moe_wtype for the routed and shared expert matrices */
+typedef struct moe_layer_desc {
+    int hidden;
+    int num_experts;
+    int top_k;
+    int expert_width;
+    int shared_width;
+    int wtype;
+} moe_layer_desc;
+
+/* Weights of one MoE layer (device pointers, 16-byte aligned).
+ *   router_w     bf16 [H][E]
+ *   router_bias  fp32 [E], added to the logits before the softmax; NULL for none
+ *   gate_w, up_w [E][D][H]   down_w [E][H][D]   (FP8 codes or bf16 per wtype)
+ *   gate_s, up_s fp32 [E][D] down_s fp32 [E][H] (FP8 only; ignored for bf16)
+ *   sh_*         the shared expert: gate/up [Ds][H], down [H][Ds], scales [Ds],[Ds],[H];
+ *                ignored when shared_width == 0 */
+typedef struct moe_layer_weights {
+    const uint16_t *router_w;
+    const float *router_bias;
+    const void *gate_w;
+    const void *up_w;
+    const void *down_w;
+    const float *gate_s;
+    const float *up_s;
+    const float *down_s;
+    const void *sh_gate_w;
+    const void *sh_up_w;
+    const void *sh_down_w;
+    const float *sh_gate_s;
+    const float *sh_up_s;
+    const float *sh_down_s;
+} moe_layer_weights;
+
+/* Bytes of device workspace moe_decode_layer needs for up to max_M tokens
+ * (0 if desc is invalid or max_M is outside 1..8). */
+size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M);
+
+/*
+ * One MoE layer for M tokens (1 <= M <= 8; the batch-1 decode step is M = 1, the
+ * speculative verify step with gamma drafts is M = gamma + 1).
+ *   logits[m][e] = sum_c x[m][c] * router_w[c][e] (+ router_bias[e])
+ *   S_m          = the K experts with the largest logits (equal logits: lower id)
+ *   w[m][e]      = softmax(logits[m])[e] / sum_{j in S_m} softmax(logits[m])[j]
+ *   expert_e(v)  = down_e( gelu_tanh(gate_e v) * (up_e v) ),
+ *                  gelu_tanh(z) = 0.5 z (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3)))
+ *   y[m]         = sum_{e in S_m, ascending e} w[m][e] expert_e(x[m]) + shared(x[m])
+ * The shared expert is always on with weight 1. Every selected expert's weights
+ * are read once per call however many of the M tokens selected it. y[m] depends
+ * only on x[m]: identical tokens give bit-identical rows, and a row does not
+ * change with M or with the other tokens in the call.
+ *   x          bf16 [M][H], the (already normalised) layer input
+ *   y          bf16 [M][H], the MoE branch output (the residual is NOT added)
+ *   topk_idx   int32 [M][K], S_m in ascending expert id, or NULL (4-byte aligned)
+ *   topk_w     fp32 [M][K], the weights aligned with topk_idx, or NULL (4-byte aligned)
+ *   workspace  at least moe_decode_layer_workspace(desc, M) bytes, 256-byte aligned
+ */
+int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
+                     const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace lm_head_argmax needs (0 for invalid sizes). */
+size_t lm_head_argmax_workspace(int max_M, int H, int V);
+
+/*
+ * Tied lm_head GEMV and greedy argmax for M rows (page "LLM decoding", "Where the
+ * 7.36 GB goes": the output projection read once per token over the whole vocabulary).
+ *   logit[m][v] = w_s[v] * sum_c decode(w[v][c]) * x[m][c]
+ *   token[m]    = argmax_v logit[m][v] (equal logits: lower v); max_logit[m] = that logit
+ * The V x H matrix is streamed once per call for all M rows.
+ *   M 1..8; H a multiple of 256 up to 4096; V a multiple of 64, 64..2^30
+ *   x bf16 [M][H]; w FP8 codes [V][H]; w_s fp32 [V]; token int32 [M];
+ *   max_logit fp32 [M] or NULL; workspace >= lm_head_argmax_workspace(M, H, V) bytes
+ */
+int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
+                   int32_t *token, float *max_logit, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/*
+ * Greedy speculative acceptance (page "LLM decoding", "Lever 2: fewer passes" and
+ * "What we learned": a drafted token is kept only if it is the token the target
+ * itself produces, so the output equals ordinary greedy decoding).
+ *   draft   int32 [num_draft]      d_1..d_gamma (gamma = num_draft, 0..7)
+ *   target  int32 [num_draft + 1]  t_0..t_gamma, the target's argmax at each verify row
+ *   accepted_len int32 [1]: n = the largest j <= gamma with d_i == t_{i-1} for all i <= j
+ *   out_tokens   int32 [num_draft + 1]: t_0..t_n (the n accepted drafts and the bonus
+ *                token t_n), then -1
+ * Draft ids outside the vocabulary simply never match. draft may be NULL when
+ * num_draft == 0.
+ */
+int spec_accept(int num_draft, const int32_t *draft, const int32_t *target,
+                int32_t *accepted_len, int32_t *out_tokens, void *stream);
+
+/*
+ * Residual add and RMSNorm between layers of the stacked step (attention is not
+ * part of this step; a stacked workload adds noise in its place):
+ *   h_out[m][c] = bf16(h_in[m][c] + add0[m][c] + add1[m][c])      (add1 may be NULL)
+ *   u_out[m][c] = bf16(h_out[m][c] * rsqrt(mean_c h_out[m][c]^2 + eps) * gain[c])
+ *   M 1..8; H a multiple of 256 up to 4096; all tensors bf16 [M][H] (gain [H]);
+ *   h_out may equal h_in (in place); u_out must not alias the inputs.
+ */
+int moe_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *add0,
+                    const uint16_t *add1, const uint16_t *gain, float eps, uint16_t *h_out,
+                    uint16_t *u_out, void *stream);
+
+/*
+ * Diagnostic: decode n FP8 E4M3FN codes with the two conversions the GEMV kernels
+ * use (codes -> bf16 pairs for the bf16 dot products; codes -> fp32 pairs for the
+ * fp32 FMAs) and write both as fp32. n a multiple of 4, 4..2^20; codes, out_via_bf16,
+ * out_via_f32 16-byte aligned.
+ */
+int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,
+                   void *stream);
+
+/* A static string describing a moe_status value. */
+const char *moe_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_DECODE_H */

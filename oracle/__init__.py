@@ -222,15 +222,17 @@ def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None):
     per = []
     for l in range(L):
         w = layers(l) if callable(layers) else layers[l]
+        h_in = h
         h, u = add_rmsnorm(h, noise[l], y_prev, gains[l], eps)
         r = moe_layer(u, w, K)
-        per.append({"u": u, "idx": r["idx"], "w": r["w"], "gap": r["gap"],
+        per.append({"h_in": h_in, "h": h, "u": u, "idx": r["idx"], "w": r["w"], "gap": r["gap"],
                     "y": r["y"], "y_bf16": r["y_bf16"]})
         y_prev = r["y_bf16"]
+    h_last = h
     h, xf = add_rmsnorm(h, y_prev, None, gains[L], eps)
     tok, ml, gap = lm_head_argmax(xf, lm_w, lm_s)
-    out = {"layers": per, "x_final": xf, "h_final": h, "tok": tok, "max_logit": ml,
-           "lm_gap": gap}
+    out = {"layers": per, "h_last": h_last, "x_final": xf, "h_final": h, "tok": tok,
+           "max_logit": ml, "lm_gap": gap}
     if draft is not None:
         n, acc = spec_accept(draft, tok)
         out["accepted"] = n

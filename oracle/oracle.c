@@ -105,12 +105,28 @@ double oracle_gelu_tanh(double z)
     return 0.5 * z * (1.0 + tanh(c * (z + 0.044715 * z * z * z)));
 }
 
+/* The 256 values of oracle_fp8_e4m3, tabulated once so the matrix loops below do
+ * not call ldexp per element (speed only; the values are those of the routine). */
+static double fp8_tab[256];
+static int fp8_tab_ready;
+
+static void fp8_tab_init(void)
+{
+    if (fp8_tab_ready)
+        return;
+    for (int c = 0; c < 256; ++c)
+        fp8_tab[c] = oracle_fp8_e4m3((uint8_t)c);
+    fp8_tab_ready = 1;
+}
+
+static inline double fp8(uint8_t code) { return fp8_tab[code]; }
+
 /* Decode element i of an expert weight matrix stored as FP8 codes (wtype 0) or
  * bf16 bits (wtype 1). */
 static double wget(const void *w, int wtype, size_t i)
 {
     if (wtype == 0)
-        return oracle_fp8_e4m3(((const uint8_t *)w)[i]);
+        return fp8(((const uint8_t *)w)[i]);
     return oracle_bf16(((const uint16_t *)w)[i]);
 }
 
@@ -250,6 +266,7 @@ void oracle_moe_layer(int M, int H, int E, int K, int D, int Ds, int wtype,
     int F = D > Ds ? D : Ds;
     double *hbuf = malloc(sizeof(double) * (size_t)(F > 0 ? F : 1));
     double *o = malloc(sizeof(double) * (size_t)H);
+    fp8_tab_init();
     oracle_router(M, H, E, K, u, router_w, router_b, logits, idx, wts, gap);
     for (int m = 0; m < M; ++m) {
         const uint16_t *um = u + (size_t)m * H;
@@ -294,6 +311,7 @@ void oracle_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *Q,
                     const float *s, int32_t *tok, double *max_logit, double *gap)
 {
     double *lg = malloc(sizeof(double) * (size_t)V);
+    fp8_tab_init();
     for (int m = 0; m < M; ++m) {
         const uint16_t *xm = x + (size_t)m * H;
         int v;
@@ -301,7 +319,7 @@ void oracle_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *Q,
         for (v = 0; v < V; ++v) {
             double acc = 0.0;
             for (int c = 0; c < H; ++c)
-                acc += oracle_fp8_e4m3(Q[(size_t)v * H + c]) * oracle_bf16(xm[c]);
+                acc += fp8(Q[(size_t)v * H + c]) * oracle_bf16(xm[c]);
             lg[v] = (double)s[v] * acc;
         }
         int best = 0;
@@ -323,12 +341,13 @@ void oracle_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *Q,
 void oracle_lm_head_rows(int M, int H, int nrows, const int32_t *rows, const uint16_t *x,
                          const uint8_t *Q, const float *s, double *out)
 {
+    fp8_tab_init();
     for (int m = 0; m < M; ++m)
         for (int r = 0; r < nrows; ++r) {
             size_t v = (size_t)rows[r];
             double acc = 0.0;
             for (int c = 0; c < H; ++c)
-                acc += oracle_fp8_e4m3(Q[v * H + c]) * oracle_bf16(x[(size_t)m * H + c]);
+                acc += fp8(Q[v * H + c]) * oracle_bf16(x[(size_t)m * H + c]);
             out[(size_t)m * nrows + r] = (double)s[v] * acc;
         }
 }

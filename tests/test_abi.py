@@ -1,0 +1,173 @@
+"""The C-ABI library loads and exports every symbol include/*.h declares, and the
+host-side validation rejects bad arguments before anything is enqueued (no GPU:
+every call here fails validation, so no HIP call is made)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from fine_grained_moe_router_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, re.M):
+            if m.group(1) not in ("if", "sizeof"):
+                names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == set(native.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = native.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", native._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    dyn = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert declared_functions() <= dyn
+
+
+def test_strerror():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert native.strerror(st) and native.strerror(st) != "unknown status"
+    assert native.strerror(42) == "unknown status"
+
+
+GEMMA = native.LayerDesc(2816, 128, 8, 704, 704, native.MOE_W_FP8_E4M3)
+FAKE = 1 << 20          # a 16-byte-aligned non-null address (never dereferenced)
+
+
+def fake_weights(**over):
+    w = {k: FAKE for k, _ in native.LayerWeights._fields_}
+    w["router_bias"] = None
+    w.update(over)
+    return native.LayerWeights(*[w[k] for k, _ in native.LayerWeights._fields_])
+
+
+def call_layer(desc=GEMMA, weights=None, M=1, x=FAKE, y=FAKE, idx=None, wts=None, ws=FAKE,
+               ws_bytes=None):
+    L = native.lib()
+    if weights is None:
+        weights = fake_weights()
+    if ws_bytes is None:
+        ws_bytes = L.moe_decode_layer_workspace(ctypes.byref(desc), max(1, min(M, 8))) or 1 << 30
+    return L.moe_decode_layer(ctypes.byref(desc), ctypes.byref(weights), M, x, y, idx, wts, ws,
+                              ws_bytes, None)
+
+
+def test_workspace_sizes():
+    L = native.lib()
+    w1 = L.moe_decode_layer_workspace(ctypes.byref(GEMMA), 1)
+    w8 = L.moe_decode_layer_workspace(ctypes.byref(GEMMA), 8)
+    assert 0 < w1 < w8 and w1 % 256 == 0 and w8 % 256 == 0
+    assert L.moe_decode_layer_workspace(ctypes.byref(GEMMA), 0) == 0
+    assert L.moe_decode_layer_workspace(ctypes.byref(GEMMA), 9) == 0
+    assert L.moe_decode_layer_workspace(None, 1) == 0
+    assert L.lm_head_argmax_workspace(5, 2816, 262144) > 0
+    assert L.lm_head_argmax_workspace(5, 2817, 262144) == 0
+    assert L.lm_head_argmax_workspace(5, 2816, 100) == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("hidden", 0), ("hidden", 2800), ("hidden", 8192), ("num_experts", 0), ("num_experts", 257),
+    ("top_k", 0), ("top_k", 17), ("expert_width", 700), ("expert_width", 0),
+    ("shared_width", -64), ("shared_width", 100), ("wtype", 7)])
+def test_layer_desc_validation(field, value):
+    d = native.LayerDesc(*[getattr(GEMMA, f) for f, _ in native.LayerDesc._fields_])
+    setattr(d, field, value)
+    assert call_layer(desc=d, ws_bytes=1 << 30) == native.MOE_EINVAL
+
+
+def test_top_k_above_experts_rejected():
+    d = native.LayerDesc(256, 4, 5, 64, 64, 0)
+    assert call_layer(desc=d, ws_bytes=1 << 30) == native.MOE_EINVAL
+
+
+@pytest.mark.parametrize("M", [0, -1, 9, 100])
+def test_token_count_validation(M):
+    assert call_layer(M=M, ws_bytes=1 << 30) == native.MOE_EINVAL
+
+
+def test_layer_pointer_validation():
+    assert call_layer(x=None) == native.MOE_EINVAL
+    assert call_layer(y=None) == native.MOE_EINVAL
+    assert call_layer(x=FAKE + 8) == native.MOE_EALIGN
+    assert call_layer(idx=FAKE + 2) == native.MOE_EALIGN
+    assert call_layer(wts=FAKE + 1) == native.MOE_EALIGN
+    assert call_layer(weights=fake_weights(gate_w=None)) == native.MOE_EINVAL
+    assert call_layer(weights=fake_weights(down_s=FAKE + 2)) == native.MOE_EALIGN
+    assert call_layer(weights=fake_weights(router_bias=FAKE + 4)) == native.MOE_EALIGN
+    assert call_layer(weights=fake_weights(sh_up_w=None)) == native.MOE_EINVAL
+    L = native.lib()
+    assert L.moe_decode_layer(ctypes.byref(GEMMA), None, 1, FAKE, FAKE, None, None, FAKE,
+                              1 << 30, None) == native.MOE_EINVAL
+
+
+def test_layer_workspace_validation():
+    need = native.lib().moe_decode_layer_workspace(ctypes.byref(GEMMA), 5)
+    assert call_layer(M=5, ws_bytes=need - 1) == native.MOE_EWORKSPACE
+    assert call_layer(M=5, ws=None) == native.MOE_EWORKSPACE
+    assert call_layer(M=5, ws=FAKE + 16) == native.MOE_EWORKSPACE     # not 256-byte aligned
+
+
+def test_bf16_experts_are_reported_unsupported_after_validation():
+    d = native.LayerDesc(2816, 128, 8, 704, 704, native.MOE_W_BF16)
+    need = native.lib().moe_decode_layer_workspace(ctypes.byref(d), 1)
+    # bf16 weights need no scales: NULL scales pass validation
+    w = fake_weights(gate_s=None, up_s=None, down_s=None, sh_gate_s=None, sh_up_s=None, sh_down_s=None)
+    st = call_layer(desc=d, weights=w, ws_bytes=need)
+    assert st in (native.MOE_EUNSUPPORTED,)
+
+
+def test_lm_head_validation():
+    L = native.lib()
+    ws = L.lm_head_argmax_workspace(5, 2816, 262144)
+    f = lambda **k: L.lm_head_argmax(k.get("M", 5), k.get("H", 2816), k.get("V", 262144),
+                                     k.get("x", FAKE), k.get("w", FAKE), k.get("s", FAKE),
+                                     k.get("tok", FAKE), k.get("ml", None), k.get("ws", FAKE),
+                                     k.get("wsb", ws), None)
+    assert f(M=0) == native.MOE_EINVAL and f(M=9) == native.MOE_EINVAL
+    assert f(H=100) == native.MOE_EINVAL and f(V=65) == native.MOE_EINVAL
+    assert f(x=None) == native.MOE_EINVAL and f(tok=None) == native.MOE_EINVAL
+    assert f(w=FAKE + 1) == native.MOE_EALIGN and f(ml=FAKE + 4) == native.MOE_EALIGN
+    assert f(wsb=ws - 1) == native.MOE_EWORKSPACE and f(ws=None) == native.MOE_EWORKSPACE
+
+
+def test_spec_accept_validation():
+    L = native.lib()
+    assert L.spec_accept(-1, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.spec_accept(8, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.spec_accept(2, None, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.spec_accept(2, FAKE, None, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.spec_accept(2, FAKE + 2, FAKE, FAKE, FAKE, None) == native.MOE_EALIGN
+
+
+def test_add_rmsnorm_validation():
+    L = native.lib()
+    f = lambda **k: L.moe_add_rmsnorm(k.get("M", 1), k.get("H", 2816), k.get("h", FAKE),
+                                      k.get("a0", FAKE), k.get("a1", None), k.get("g", FAKE),
+                                      k.get("eps", 1e-6), k.get("ho", FAKE), k.get("u", FAKE), None)
+    assert f(M=0) == native.MOE_EINVAL and f(H=2800) == native.MOE_EINVAL
+    assert f(eps=-1.0) == native.MOE_EINVAL and f(eps=float("nan")) == native.MOE_EINVAL
+    assert f(h=None) == native.MOE_EINVAL and f(a1=FAKE + 2) == native.MOE_EALIGN
+    assert f(ho=None) == native.MOE_EINVAL and f(u=FAKE + 8) == native.MOE_EALIGN
+
+
+def test_fp8_decode_validation():
+    L = native.lib()
+    assert L.moe_fp8_decode(0, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_fp8_decode(6, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_fp8_decode(256, None, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_fp8_decode(256, FAKE, FAKE + 4, FAKE, None) == native.MOE_EALIGN
