@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=8, help="oracle sample: layers per step")
     ap.add_argument("--cpu-steps", type=int, default=40, help="oracle sample: steps")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--path", choices=("fused", "layers"), default="fused",
+                    help="fused: one moe_decode_step launch per step; layers: per-layer entry points "
+                         "captured in a HIP graph per step")
     return ap.parse_args()
 
 
@@ -60,7 +63,7 @@ def main():
     import torch
     import synth
     from fine_grained_moe_router_amd import budget, native
-    from fine_grained_moe_router_amd.stack import DecodeStack
+    from fine_grained_moe_router_amd.stack import DecodeStack, FusedDecodeStep
 
     native.lib()   # fail loudly if the HIP library is missing
     dev = "cuda"
@@ -74,7 +77,10 @@ def main():
     Q, s = synth.lm_head(sh, dev, seed=args.seed)
     torch.cuda.synchronize()
     log("weights generated in %.1fs (%.2f GB resident)" % (time.time() - t0, torch.cuda.memory_allocated() / 1e9))
-    st = DecodeStack(sh, layers, gains, Q, s, max_M=max(Ms))
+    if args.path == "fused":
+        runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=max(Ms))
+    else:
+        runner = DecodeStack(sh, layers, gains, Q, s, max_M=max(Ms))
 
     results = {}
     for M in Ms:
@@ -86,46 +92,57 @@ def main():
                   for _ in range(n)]
         stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
-        graphs = []
-        with torch.cuda.stream(stream):
-            st.step(xs[0], noises[0], drafts[0], M)
+        if args.path == "fused":
+            def launch(i, outputs=False):
+                runner.step(xs[i], noises[i], drafts[i], M, stream=stream, outputs=outputs)
+        else:
+            graphs = []
+            with torch.cuda.stream(stream):
+                runner.step(xs[0], noises[0], drafts[0], M)
+                torch.cuda.synchronize()
+                for i in range(n):
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr, stream=stream):
+                        runner.step(xs[i], noises[i], drafts[i], M)
+                    graphs.append(gr)
             torch.cuda.synchronize()
-            for i in range(n):
-                gr = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gr, stream=stream):
-                    st.step(xs[i], noises[i], drafts[i], M)
-                graphs.append(gr)
-        torch.cuda.synchronize()
-        log("M=%d: %d step graphs captured" % (M, n))
+            log("M=%d: %d step graphs captured" % (M, n))
+
+            def launch(i, outputs=False):
+                graphs[i].replay()
 
         with torch.cuda.stream(stream):
             for i in range(W):
-                graphs[i].replay()
+                launch(i)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             w0 = time.perf_counter()
             e0.record(stream)
             for i in range(W, n):
-                graphs[i].replay()
+                launch(i)
             e1.record(stream)
             torch.cuda.synchronize()
             wall = time.perf_counter() - w0
             ms_total = e0.elapsed_time(e1)
 
             # per-step latency distribution and the routing each step took
-            per_step, uniq = [], []
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
             ev[0].record(stream)
             for j, i in enumerate(range(W, n)):
-                graphs[i].replay()
+                launch(i)
                 ev[j + 1].record(stream)
             torch.cuda.synchronize()
             per_step = [ev[j].elapsed_time(ev[j + 1]) for j in range(K)]
+            uniq = []
             for i in range(W, n):
-                graphs[i].replay()
+                launch(i, outputs=True)
                 torch.cuda.synchronize()
-                idx = st.topk_idx[:, :M].cpu().numpy()
+                idx = (runner.topk_idx(M) if args.path == "fused" else runner.topk_idx[:, :M]).cpu().numpy()
                 uniq.append([len(np.unique(idx[l])) for l in range(sh.layers)])
+        if args.path == "fused":
+            st_code = runner.status()
+            if st_code != native.MOE_OK:
+                raise RuntimeError("fused step reported %s" % native.strerror(st_code))
 
         bytes_steps = [budget.step_bytes(sh, u, M) for u in uniq]
         ms = ms_total / K
@@ -140,40 +157,48 @@ def main():
         log("M=%d: %.3f ms/step, %.1f steps/s, %.1f GB/s (%.1f%% of 8 TB/s), p50 %.3f p99 %.3f ms" % (
             M, ms, results[M]["steps_per_s"], results[M]["hbm_gbs"], 100 * results[M]["hbm_frac"],
             results[M]["p50_ms"], results[M]["p99_ms"]))
-        del graphs
+        if args.path != "fused":
+            del graphs
         torch.cuda.synchronize()
 
-    # lm_head roofline: the largest single launch of the step, timed alone with HIP
-    # events on the stream it is launched on, over K launches on resident inputs
     M0 = Ms[0]
-    lm_bytes = budget.lm_head_bytes(sh.vocab, sh.hidden)
-    xs_lm = [synth.hidden_inputs(sh, M0, i, device=dev, tag="bench_lm") for i in range(8)]
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        for i in range(3):
-            native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, st.tok[:M0], st.max_logit[:M0],
-                                  st.lm_ws, st.lm_ws_bytes)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(K):
-            native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, st.tok[:M0], st.max_logit[:M0],
-                                  st.lm_ws, st.lm_ws_bytes)
-        e1.record(stream)
-        torch.cuda.synchronize()
-    lm_ms = e0.elapsed_time(e1) / K
-    lm_gbs = lm_bytes / (lm_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "k_lmhead (lm_head_argmax, M=%d)" % M0,
-                "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
-    log("lm_head alone: %.1f us, %.1f GB/s" % (lm_ms * 1e3, lm_gbs))
+    head = results[M0]
+    if args.path == "fused":
+        # the step is one kernel launch: its average duration over the timed region
+        roofline = {"bound": "hbm", "kernel": "k_step (moe_decode_step, M=%d)" % M0,
+                    "achieved": round(head["hbm_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(head["hbm_frac"], 4), "traffic": None,
+                    "bytes_per_launch": int(head["bytes_per_step"]),
+                    "avg_launch_us": round(head["ms_per_step"] * 1e3, 2)}
+    else:
+        # the largest single launch of the per-layer path, timed alone with HIP events
+        lm_bytes = budget.lm_head_bytes(sh.vocab, sh.hidden)
+        xs_lm = [synth.hidden_inputs(sh, M0, i, device=dev, tag="bench_lm") for i in range(8)]
+        stream = torch.cuda.Stream()
+        with torch.cuda.stream(stream):
+            for i in range(3):
+                native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, runner.tok[:M0],
+                                      runner.max_logit[:M0], runner.lm_ws, runner.lm_ws_bytes)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(K):
+                native.lm_head_argmax(M0, sh.hidden, sh.vocab, xs_lm[i % 8], Q, s, runner.tok[:M0],
+                                      runner.max_logit[:M0], runner.lm_ws, runner.lm_ws_bytes)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        lm_ms = e0.elapsed_time(e1) / K
+        lm_gbs = lm_bytes / (lm_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": "k_lmhead (lm_head_argmax, M=%d)" % M0,
+                    "achieved": round(lm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(lm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
+        log("lm_head alone: %.1f us, %.1f GB/s" % (lm_ms * 1e3, lm_gbs))
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, sh, layers, gains, Q, s, Ms[0])
 
-    head = results[Ms[0]]
     line = {
         "metric": "decode steps/s + achieved HBM GB/s (% peak), 26B-A4B MoE stack, M=1 & M=5",
         "value": round(head["steps_per_s"], 2),
@@ -190,6 +215,7 @@ def main():
         "config": {"workload": "Gemma-4-26B-A4B-shaped MoE stack: 30 layers x (router 2816x128 bf16, "
                                "top-8 of 128 + shared expert, width 704, FP8) + tied 262144x2816 FP8 "
                                "lm_head + argmax + greedy accept, M=%d tokens/step" % Ms[0],
+                   "path": args.path,
                    "M": Ms[0], "layers": sh.layers, "hidden": sh.hidden, "experts": sh.experts,
                    "top_k": sh.top_k, "expert_width": sh.width, "vocab": sh.vocab},
         "hbm_gbs": round(head["hbm_gbs"], 1),

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoedecode.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "kernels.hip")]
+SOURCES = [os.path.join(CSRC, "api.cpp"), os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "step.hip")]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -48,10 +48,10 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def device_asm(out_path: str) -> str:
-    """Write the gfx950 assembly of kernels.hip to out_path (for inspection)."""
+def device_asm(out_path: str, source: str = "kernels.hip") -> str:
+    """Write the gfx950 assembly of one source file to out_path (for inspection)."""
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "--cuda-device-only", "-S",
-           "-I" + INCLUDE, "-I" + CSRC, *DEVICE_FLAGS, os.path.join(CSRC, "kernels.hip"),
+           "-I" + INCLUDE, "-I" + CSRC, *DEVICE_FLAGS, os.path.join(CSRC, source),
            "-o", out_path]
     subprocess.run(cmd, check=True, capture_output=True)
     return out_path

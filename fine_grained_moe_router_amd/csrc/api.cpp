@@ -14,7 +14,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 int check_layer_desc(const moe_layer_desc *d) {
     if (!d) return MOE_EINVAL;
     if (d->hidden < 256 || d->hidden > kMaxHidden || d->hidden % 256) return MOE_EINVAL;
-    if (d->num_experts < 1 || d->num_experts > kMaxExperts) return MOE_EINVAL;
+    if (d->num_experts < 2 || d->num_experts > kMaxExperts || d->num_experts % 2) return MOE_EINVAL;
     if (d->top_k < 1 || d->top_k > d->num_experts || d->top_k > kMaxTopK) return MOE_EINVAL;
     if (d->expert_width < 64 || d->expert_width > kMaxWidth || d->expert_width % 64) return MOE_EINVAL;
     if (d->shared_width < 0 || d->shared_width > kMaxWidth || d->shared_width % 64) return MOE_EINVAL;
@@ -34,32 +34,8 @@ int need(const void *p) {
         if (st_ != MOE_OK) return st_; \
     } while (0)
 
-}  // namespace
-
-extern "C" {
-
-const char *moe_strerror(int status) {
-    switch (status) {
-    case MOE_OK: return "ok";
-    case MOE_EINVAL: return "invalid argument (size out of range or required pointer NULL)";
-    case MOE_EALIGN: return "pointer not 16-byte aligned";
-    case MOE_EWORKSPACE: return "workspace missing or too small";
-    case MOE_EUNSUPPORTED: return "unsupported configuration";
-    case MOE_ELAUNCH: return "kernel launch failed";
-    default: return "unknown status";
-    }
-}
-
-size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M) {
-    if (check_layer_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
-    return layer_ws(*desc, max_M).total;
-}
-
-int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
-                     const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
-                     void *workspace, size_t workspace_bytes, void *stream) {
-    CHECK(check_layer_desc(desc));
-    if (!w || M < 1 || M > kMaxM) return MOE_EINVAL;
+int check_weights(const moe_layer_desc *desc, const moe_layer_weights *w) {
+    if (!w) return MOE_EINVAL;
     const bool fp8 = desc->wtype == MOE_W_FP8_E4M3;
     CHECK(need(w->router_w));
     if (w->router_bias && !aligned16(w->router_bias)) return MOE_EALIGN;
@@ -81,12 +57,58 @@ int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int
             CHECK(need(w->sh_down_s));
         }
     }
+    return MOE_OK;
+}
+
+int check_step_desc(const moe_step_desc *d) {
+    if (!d) return MOE_EINVAL;
+    CHECK(check_layer_desc(&d->layer));
+    if (d->layer.hidden > kStepMaxHidden) return MOE_EINVAL;
+    if (d->num_layers < 1 || d->num_layers > kMaxLayers) return MOE_EINVAL;
+    if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
+    if (d->max_tokens < 1 || d->max_tokens > kMaxM) return MOE_EINVAL;
+    if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+bool ws_ok(const void *ws, size_t bytes, size_t need_bytes) {
+    return ws && !((uintptr_t)ws & 255u) && bytes >= need_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_strerror(int status) {
+    switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (size out of range or required pointer NULL)";
+    case MOE_EALIGN: return "pointer not 16-byte aligned";
+    case MOE_EWORKSPACE: return "workspace missing or too small";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    case MOE_ETIMEOUT: return "a device-side wait of the fused step gave up";
+    default: return "unknown status";
+    }
+}
+
+size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M) {
+    if (check_layer_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
+    return layer_ws(*desc, max_M).total;
+}
+
+int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
+                     const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    CHECK(check_layer_desc(desc));
+    if (!w || M < 1 || M > kMaxM) return MOE_EINVAL;
+    const bool fp8 = desc->wtype == MOE_W_FP8_E4M3;
+    CHECK(check_weights(desc, w));
     CHECK(need(x));
     CHECK(need(y));
     if (((uintptr_t)topk_idx | (uintptr_t)topk_w) & 3u) return MOE_EALIGN;
     const LayerWs L = layer_ws(*desc, M);
-    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < L.total)
-        return MOE_EWORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
     if (!fp8) return MOE_EUNSUPPORTED;
     return launch_moe_layer(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, L, stream);
 }
@@ -137,6 +159,55 @@ int moe_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *add0,
     CHECK(need(h_out));
     CHECK(need(u_out));
     return launch_add_rmsnorm(M, H, h_in, add0, add1, gain, eps, h_out, u_out, stream);
+}
+
+size_t moe_decode_step_workspace(const moe_step_desc *desc) {
+    if (check_step_desc(desc) != MOE_OK) return 0;
+    return step_ws(*desc).total;
+}
+
+int moe_decode_step_prepare(const moe_step_desc *desc, const moe_layer_weights *layers,
+                            void *workspace, size_t workspace_bytes) {
+    CHECK(check_step_desc(desc));
+    if (!layers) return MOE_EINVAL;
+    for (int l = 0; l < desc->num_layers; ++l) CHECK(check_weights(&desc->layer, &layers[l]));
+    const StepWs W = step_ws(*desc);
+    if (!ws_ok(workspace, workspace_bytes, W.total)) return MOE_EWORKSPACE;
+    if (desc->layer.wtype != MOE_W_FP8_E4M3) return MOE_EUNSUPPORTED;
+    return step_prepare(W, layers, (char *)workspace);
+}
+
+int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
+                    const uint8_t *lm_w, const float *lm_s, const uint16_t *x,
+                    const uint16_t *noise, const int32_t *draft, int32_t *token,
+                    float *max_logit, int32_t *accepted_len, int32_t *out_tokens,
+                    uint16_t *y_layers, int32_t *topk_idx, float *topk_w, uint16_t *x_final,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    CHECK(check_step_desc(desc));
+    if (M < 1 || M > desc->max_tokens) return MOE_EINVAL;
+    CHECK(need(gains));
+    CHECK(need(lm_w));
+    CHECK(need(lm_s));
+    CHECK(need(x));
+    CHECK(need(noise));
+    if (M > 1 && !draft) return MOE_EINVAL;
+    if (!token || !accepted_len || !out_tokens) return MOE_EINVAL;
+    if (((uintptr_t)draft | (uintptr_t)token | (uintptr_t)accepted_len | (uintptr_t)out_tokens |
+         (uintptr_t)max_logit | (uintptr_t)topk_idx | (uintptr_t)topk_w) & 3u)
+        return MOE_EALIGN;
+    if ((y_layers && !aligned16(y_layers)) || (x_final && !aligned16(x_final))) return MOE_EALIGN;
+    const StepWs W = step_ws(*desc);
+    if (!ws_ok(workspace, workspace_bytes, W.total)) return MOE_EWORKSPACE;
+    if (desc->layer.wtype != MOE_W_FP8_E4M3) return MOE_EUNSUPPORTED;
+    return launch_step(*desc, W, M, gains, lm_w, lm_s, x, noise, draft, token, max_logit,
+                       accepted_len, out_tokens, y_layers, topk_idx, topk_w, x_final,
+                       (char *)workspace, stream);
+}
+
+int moe_decode_step_status(const moe_step_desc *desc, void *workspace) {
+    CHECK(check_step_desc(desc));
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MOE_EWORKSPACE;
+    return step_status(step_ws(*desc), (char *)workspace);
 }
 
 int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,

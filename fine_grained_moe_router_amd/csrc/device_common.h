@@ -1,0 +1,90 @@
+// device_common.h -- gfx950 device helpers shared by the kernels: FP8 and bf16
+// conversions, packed bf16 dot products, and fixed-order DPP reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+namespace dev {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------ scalar helpers
+
+__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ bf16x2 as_bf2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+// Two E4M3FN codes (bytes 0-1 or 2-3 of v) to two bf16, exactly (scale 1).
+template <bool HI>
+__device__ __forceinline__ bf16x2 fp8x2_to_bf16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, HI);
+}
+
+// Two E4M3FN codes (word HI of v) to two fp32.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t v) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, HI);
+}
+
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// 16 codes (one uint4) -> 8 bf16 pairs in column order.
+__device__ __forceinline__ void decode16_bf16(const uint4 q, bf16x2 (&w)[8]) {
+    w[0] = fp8x2_to_bf16<false>(q.x); w[1] = fp8x2_to_bf16<true>(q.x);
+    w[2] = fp8x2_to_bf16<false>(q.y); w[3] = fp8x2_to_bf16<true>(q.y);
+    w[4] = fp8x2_to_bf16<false>(q.z); w[5] = fp8x2_to_bf16<true>(q.z);
+    w[6] = fp8x2_to_bf16<false>(q.w); w[7] = fp8x2_to_bf16<true>(q.w);
+}
+
+// 8 bf16 weight pairs . 16 bf16 activations (two uint4), accumulated into acc.
+__device__ __forceinline__ float dot16(const bf16x2 (&w)[8], const uint4 x0, const uint4 x1, float acc) {
+    acc = dot2(w[0], as_bf2(x0.x), acc);
+    acc = dot2(w[1], as_bf2(x0.y), acc);
+    acc = dot2(w[2], as_bf2(x0.z), acc);
+    acc = dot2(w[3], as_bf2(x0.w), acc);
+    acc = dot2(w[4], as_bf2(x1.x), acc);
+    acc = dot2(w[5], as_bf2(x1.y), acc);
+    acc = dot2(w[6], as_bf2(x1.z), acc);
+    acc = dot2(w[7], as_bf2(x1.w), acc);
+    return acc;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 4 lanes of a quad; every lane of the quad gets the same bits.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    return v;
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = quad_sum(v);
+    v += dpp<0x141>(v);  // row_half_mirror: combines the two quads of each half row
+    v += dpp<0x140>(v);  // row_mirror: combines the two half rows
+    return v;
+}
+
+__device__ __forceinline__ float gelu_tanh(float z) {
+    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+    return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+}
+
+}  // namespace dev
+}  // namespace moe

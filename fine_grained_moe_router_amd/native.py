@@ -16,11 +16,14 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoedeco
 _lib = None
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
+MOE_ETIMEOUT = -6
 MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "lm_head_argmax_workspace",
-           "lm_head_argmax", "spec_accept", "moe_add_rmsnorm", "moe_fp8_decode", "moe_strerror")
+           "lm_head_argmax", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
+           "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
+           "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -41,6 +44,11 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("router_w", "router_bias", "gate_w", "up_w", "down_w", "gate_s",
                                   "up_s", "down_s", "sh_gate_w", "sh_up_w", "sh_down_w",
                                   "sh_gate_s", "sh_up_s", "sh_down_s")]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("layer", LayerDesc), ("num_layers", ctypes.c_int), ("vocab", ctypes.c_int),
+                ("max_tokens", ctypes.c_int), ("eps", ctypes.c_float), ("spin_limit", ctypes.c_uint)]
 
 
 def lib() -> ctypes.CDLL:
@@ -66,6 +74,14 @@ def lib() -> ctypes.CDLL:
         L.moe_add_rmsnorm.argtypes = [I, I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
         L.moe_fp8_decode.restype = I
         L.moe_fp8_decode.argtypes = [I, _P, _P, _P, _P]
+        L.moe_decode_step_workspace.restype = S
+        L.moe_decode_step_workspace.argtypes = [ctypes.POINTER(StepDesc)]
+        L.moe_decode_step_prepare.restype = I
+        L.moe_decode_step_prepare.argtypes = [ctypes.POINTER(StepDesc), ctypes.POINTER(LayerWeights), _P, S]
+        L.moe_decode_step.restype = I
+        L.moe_decode_step.argtypes = [ctypes.POINTER(StepDesc), I] + [_P] * 14 + [_P, S, _P]
+        L.moe_decode_step_status.restype = I
+        L.moe_decode_step_status.argtypes = [ctypes.POINTER(StepDesc), _P]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_strerror.argtypes = [I]
         _lib = L
@@ -147,6 +163,37 @@ def moe_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream=None):
     st = lib().moe_fp8_decode(int(n), _ptr(codes), _ptr(out_via_bf16), _ptr(out_via_f32),
                               _stream(stream))
     _check("moe_fp8_decode", st)
+
+
+def step_desc(shape, max_tokens: int, eps: float = 1e-6, spin_limit: int = 0,
+              expert_dtype: str = "fp8") -> StepDesc:
+    return StepDesc(layer_desc(shape, expert_dtype), shape.layers, shape.vocab, max_tokens, eps, spin_limit)
+
+
+def moe_decode_step_workspace(desc: StepDesc) -> int:
+    return lib().moe_decode_step_workspace(ctypes.byref(desc))
+
+
+def moe_decode_step_prepare(desc: StepDesc, layers, workspace, workspace_bytes: int):
+    """layers: a sequence of LayerWeights (host structs holding device pointers)."""
+    arr = (LayerWeights * len(layers))(*layers)
+    st = lib().moe_decode_step_prepare(ctypes.byref(desc), arr, _ptr(workspace), int(workspace_bytes))
+    _check("moe_decode_step_prepare", st)
+
+
+def moe_decode_step(desc: StepDesc, M, gains, lm_w, lm_s, x, noise, draft, token, max_logit,
+                    accepted_len, out_tokens, y_layers, topk_idx, topk_w, x_final, workspace,
+                    workspace_bytes, stream=None):
+    st = lib().moe_decode_step(ctypes.byref(desc), int(M), _ptr(gains), _ptr(lm_w), _ptr(lm_s), _ptr(x),
+                               _ptr(noise), _ptr(draft), _ptr(token), _ptr(max_logit), _ptr(accepted_len),
+                               _ptr(out_tokens), _ptr(y_layers), _ptr(topk_idx), _ptr(topk_w),
+                               _ptr(x_final), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("moe_decode_step", st)
+
+
+def moe_decode_step_status(desc: StepDesc, workspace) -> int:
+    """MOE_OK or MOE_ETIMEOUT (synchronous; clears the flag)."""
+    return lib().moe_decode_step_status(ctypes.byref(desc), _ptr(workspace))
 
 
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:

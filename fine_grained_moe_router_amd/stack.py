@@ -66,3 +66,59 @@ class DecodeStack:
                               self.max_logit[:M], self.lm_ws, self.lm_ws_bytes, stream)
         native.spec_accept(M - 1, drafts if M > 1 else None, self.tok[:M], self.accepted,
                            self.out_tokens[:M], stream)
+
+
+class FusedDecodeStep:
+    """The same step as DecodeStack, run by the library's single-launch entry point
+    moe_decode_step (one persistent kernel per step)."""
+
+    def __init__(self, shape, layers, gains, lm_w, lm_s, max_M: int, eps: float = 1e-6,
+                 spin_limit: int = 0, device="cuda"):
+        self.shape = shape
+        self.L = len(layers)
+        self.max_M = max_M
+        self.layers = layers
+        self.gains, self.lm_w, self.lm_s = gains, lm_w, lm_s
+        self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit)
+        self.ws_bytes = native.moe_decode_step_workspace(self.desc)
+        if self.ws_bytes == 0:
+            raise ValueError("unsupported shape for the fused decode step")
+        self.ws = native.workspace(self.ws_bytes, device)
+        native.moe_decode_step_prepare(self.desc, [native.layer_weights(w) for w in layers], self.ws,
+                                       self.ws_bytes)
+        H, K, L = shape.hidden, shape.top_k, self.L
+        z = lambda n, dt: torch.zeros(n, dtype=dt, device=device)
+        self._y = z(L * max_M * H, torch.bfloat16)
+        self._idx = z(L * max_M * K, torch.int32)
+        self._w = z(L * max_M * K, torch.float32)
+        self.x_final = torch.zeros(max_M, H, dtype=torch.bfloat16, device=device)
+        self.tok = z(max_M, torch.int32)
+        self.max_logit = z(max_M, torch.float32)
+        self.accepted = z(4, torch.int32)
+        self.out_tokens = z(max_M, torch.int32)
+        self.M = max_M
+
+    def y(self, M=None):
+        M = M or self.M
+        return self._y[: self.L * M * self.shape.hidden].view(self.L, M, self.shape.hidden)
+
+    def topk_idx(self, M=None):
+        M = M or self.M
+        return self._idx[: self.L * M * self.shape.top_k].view(self.L, M, self.shape.top_k)
+
+    def topk_w(self, M=None):
+        M = M or self.M
+        return self._w[: self.L * M * self.shape.top_k].view(self.L, M, self.shape.top_k)
+
+    def step(self, x, noise, drafts, M: int, stream=None, outputs: bool = True):
+        """One step for M tokens; outputs=False skips the per-layer diagnostic outputs."""
+        self.M = M
+        native.moe_decode_step(self.desc, M, self.gains, self.lm_w, self.lm_s, x, noise,
+                               drafts if M > 1 else None, self.tok[:M], self.max_logit[:M],
+                               self.accepted, self.out_tokens[:M],
+                               self._y if outputs else None, self._idx if outputs else None,
+                               self._w if outputs else None, self.x_final if outputs else None,
+                               self.ws, self.ws_bytes, stream)
+
+    def status(self) -> int:
+        return native.moe_decode_step_status(self.desc, self.ws)

@@ -50,7 +50,8 @@ typedef enum moe_status {
     MOE_EALIGN = -2,        /* a pointer is not 16-byte aligned                              */
     MOE_EWORKSPACE = -3,    /* workspace NULL or smaller than the *_workspace() size         */
     MOE_EUNSUPPORTED = -4,  /* a valid request this build does not implement                 */
-    MOE_ELAUNCH = -5        /* the HIP runtime rejected a kernel launch                      */
+    MOE_ELAUNCH = -5,       /* the HIP runtime rejected a kernel launch                      */
+    MOE_ETIMEOUT = -6       /* a device-side wait of moe_decode_step gave up                 */
 } moe_status;
 
 typedef enum moe_wtype {
@@ -60,7 +61,7 @@ typedef enum moe_wtype {
 
 /* Shape of one MoE layer.
  *   hidden        H: a multiple of 256, at most 4096            (Gemma-4-26B-A4B: 2816)
- *   num_experts   E: 1..256                                      (128)
+ *   num_experts   E: even, 2..256                                (128)
  *   top_k         K: 1..min(E, 16)                               (8)
  *   expert_width  D: a multiple of 64, 64..4096                  (704)
  *   shared_width  Ds: 0 (no shared expert) or a multiple of 64 up to 4096 (704; the
@@ -178,6 +179,73 @@ int moe_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *add0,
  */
 int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,
                    void *stream);
+
+/* ------------------------------------------------------------------------------
+ * The whole stacked decode step in one launch.
+ *
+ * num_layers MoE layers, each preceded by a residual add and RMSNorm, then the
+ * final norm, the tied lm_head with argmax and greedy acceptance:
+ *   h_0 = bf16(x + noise_0),                  u_0 = rmsnorm(h_0; gain_0)
+ *   y_l = moe_layer_l(u_l)                     (as moe_decode_layer)
+ *   h_l = bf16(h_{l-1} + noise_l + y_{l-1}),   u_l = rmsnorm(h_l; gain_l)   (l >= 1)
+ *   h_L = bf16(h_{L-1} + y_{L-1}),             x_f = rmsnorm(h_L; gain_L)
+ *   token[m] = argmax_v logit(x_f[m])[v];      (n, out) = spec_accept(draft, token)
+ * rmsnorm(h; g) = bf16(h * rsqrt(mean(h^2) + eps) * g). (Attention is not part of
+ * this step; the stacked workload adds noise in its place.)
+ *
+ * The step runs as one kernel of persistent workgroups that take work items in a
+ * fixed order (per layer: router row blocks, gate/up row blocks, down row blocks;
+ * then lm_head row blocks) and hand data to later items through device-memory
+ * counters; every weight byte the step needs is read once.
+ * ---------------------------------------------------------------------------- */
+
+typedef struct moe_step_desc {
+    moe_layer_desc layer;   /* shape of every layer (wtype MOE_W_FP8_E4M3; hidden <= 3072)   */
+    int num_layers;         /* L, 1..64                                                        */
+    int vocab;              /* V, a multiple of 64, 64..2^30                                   */
+    int max_tokens;         /* largest M the workspace serves, 1..8                            */
+    float eps;              /* RMSNorm epsilon, >= 0                                           */
+    unsigned spin_limit;    /* polls of a device-side wait before it gives up and flags a
+                               timeout (0: a default of about a quarter second)                    */
+} moe_step_desc;
+
+/* Bytes of workspace for moe_decode_step (0 if desc is invalid). */
+size_t moe_decode_step_workspace(const moe_step_desc *desc);
+
+/*
+ * Prepare a workspace for moe_decode_step (synchronous; not capturable). Validates
+ * the L weight sets in `layers` (a HOST array of moe_layer_weights holding device
+ * pointers, checked as in moe_decode_layer), zeroes the workspace and copies the
+ * weight table into it. Call again if any weight pointer changes.
+ */
+int moe_decode_step_prepare(const moe_step_desc *desc, const moe_layer_weights *layers,
+                            void *workspace, size_t workspace_bytes);
+
+/*
+ * One stacked decode step for M tokens (1 <= M <= desc->max_tokens), asynchronous on
+ * `stream` and capturable. Concurrent steps must use distinct workspaces.
+ *   gains      bf16 [L+1][H]            lm_w FP8 [V][H], lm_s fp32 [V]
+ *   x          bf16 [M][H]              noise bf16 [L][M][H]
+ *   draft      int32 [M-1] (NULL when M == 1)
+ *   token      int32 [M]; max_logit fp32 [M] or NULL; accepted_len int32 [1];
+ *   out_tokens int32 [M] (as spec_accept)
+ *   y_layers   bf16 [L][M][H], every layer's MoE output y_l, or NULL
+ *   topk_idx   int32 [L][M][K] or NULL; topk_w fp32 [L][M][K] or NULL
+ *   x_final    bf16 [M][H], the lm_head input, or NULL
+ */
+int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
+                    const uint8_t *lm_w, const float *lm_s, const uint16_t *x,
+                    const uint16_t *noise, const int32_t *draft, int32_t *token,
+                    float *max_logit, int32_t *accepted_len, int32_t *out_tokens,
+                    uint16_t *y_layers, int32_t *topk_idx, float *topk_w, uint16_t *x_final,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Synchronous: MOE_OK, or MOE_ETIMEOUT if a device-side wait of a step run on this
+ * workspace since the last call gave up (its results are then invalid). Clears the
+ * flag. Call after the stream has been synchronised.
+ */
+int moe_decode_step_status(const moe_step_desc *desc, void *workspace);
 
 /* A static string describing a moe_status value. */
 const char *moe_strerror(int status);

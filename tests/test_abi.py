@@ -171,3 +171,64 @@ def test_fp8_decode_validation():
     assert L.moe_fp8_decode(6, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
     assert L.moe_fp8_decode(256, None, FAKE, FAKE, None) == native.MOE_EINVAL
     assert L.moe_fp8_decode(256, FAKE, FAKE + 4, FAKE, None) == native.MOE_EALIGN
+
+
+# ------------------------------------------------------------------ fused step
+
+def step_desc(**over):
+    import synth
+    d = native.step_desc(synth.GEMMA4_26B_A4B, max_tokens=5)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_step_workspace_and_desc_validation():
+    L = native.lib()
+    d = step_desc()
+    assert native.moe_decode_step_workspace(d) > 0
+    for k, v in (("num_layers", 0), ("num_layers", 65), ("vocab", 100), ("max_tokens", 9), ("max_tokens", 0),
+                 ("eps", -1.0)):
+        assert native.moe_decode_step_workspace(step_desc(**{k: v})) == 0, k
+    wide = step_desc()
+    wide.layer.hidden = 4096                       # the fused step holds H <= 3072 per lane
+    assert native.moe_decode_step_workspace(wide) == 0
+    assert L.moe_decode_step_workspace(None) == 0
+
+
+def test_step_prepare_validation():
+    d = step_desc()
+    need = native.moe_decode_step_workspace(d)
+    good = [fake_weights() for _ in range(d.num_layers)]
+    with pytest.raises(native.MoeError) as e:
+        native.moe_decode_step_prepare(d, good[:-1] + [fake_weights(up_w=None)], FAKE, need)
+    assert e.value.status == native.MOE_EINVAL
+    with pytest.raises(native.MoeError) as e:
+        native.moe_decode_step_prepare(d, good, FAKE, need - 1)
+    assert e.value.status == native.MOE_EWORKSPACE
+
+
+def test_step_call_validation_through_the_binding():
+    d = step_desc()
+    need = native.moe_decode_step_workspace(d)
+
+    def call(**k):
+        args = dict(M=1, gains=FAKE, lm_w=FAKE, lm_s=FAKE, x=FAKE, noise=FAKE, draft=None, token=FAKE,
+                    max_logit=None, accepted_len=FAKE, out_tokens=FAKE, y_layers=None, topk_idx=None,
+                    topk_w=None, x_final=None, workspace=FAKE, workspace_bytes=need, stream=0)
+        args.update(k)
+        with pytest.raises(native.MoeError) as e:
+            native.moe_decode_step(d, **args)
+        return e.value.status
+
+    assert call(M=0) == native.MOE_EINVAL and call(M=6) == native.MOE_EINVAL
+    assert call(M=2) == native.MOE_EINVAL                       # drafts required for M > 1
+    assert call(x=None) == native.MOE_EINVAL and call(token=None) == native.MOE_EINVAL
+    assert call(x=FAKE + 2) == native.MOE_EALIGN and call(token=FAKE + 1) == native.MOE_EALIGN
+    assert call(y_layers=FAKE + 8) == native.MOE_EALIGN
+    assert call(workspace_bytes=need - 1) == native.MOE_EWORKSPACE
+
+
+def test_step_status_validation():
+    assert native.lib().moe_decode_step_status(None, FAKE) == native.MOE_EINVAL
+    assert native.moe_decode_step_status(step_desc(), None) == native.MOE_EWORKSPACE

@@ -178,3 +178,62 @@ def test_verify_batch_equals_sequential_steps(stack):
         torch.cuda.synchronize()
         assert int(st.tok[0]) == int(tok5[m])
         assert torch.equal(st.y[:, 0], y5[:, m])
+
+
+# ------------------------------------------------- the single-launch step (moe_decode_step)
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_fused_step_each_layer_on_oracle_inputs(stack, oracle_steps, M):
+    """The fused kernel run as a one-layer step on every layer's weights, with the
+    oracle's residual h_l as its input (noise 0, gains g_l and g_L): the layer's
+    expert ids and y_l must match the oracle's."""
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+    sh, st, host, gains_h, Qh, sh_ = stack
+    x, noise, drafts, res = oracle_steps[M]
+    one = sh.with_(layers=1)
+    zero = torch.zeros(1, M, sh.hidden, dtype=torch.bfloat16, device=DEV)
+    d = torch.zeros(max(M - 1, 1), dtype=torch.int32, device=DEV)
+    worst = 0.0
+    for l in range(sh.layers):
+        r = res["layers"][l]
+        g2 = torch.stack([st.gains[l], st.gains[sh.layers]]).contiguous()
+        fs = FusedDecodeStep(one, [st.layers[l]], g2, st.lm_w, st.lm_s, max_M=M)
+        fs.step(dev16(r["h"]), zero, d if M > 1 else None, M)
+        torch.cuda.synchronize()
+        assert fs.status() == native.MOE_OK
+        assert (fs.topk_idx(M)[0].cpu().numpy() == r["idx"]).all(), "layer %d expert ids" % l
+        err, _ = check_bf16_output(synth.bits16(fs.y(M)[0]), r["y"], None, "fused y layer %d" % l)
+        worst = max(worst, err)
+        del fs
+    say("M=%d fused, layer by layer: all 30 layers match; worst y rel-L2 %.3g" % (M, worst))
+
+
+@pytest.mark.parametrize("M", [1, 5])
+def test_fused_step_full_stack(stack, oracle_steps, M):
+    """The benchmark's configuration: the 30-layer step in one launch. Layer 0 (fed by
+    the seeded input) matches the oracle; repeated launches are bitwise identical; the
+    chained divergence from the oracle is reported."""
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+    sh, st, host, gains_h, Qh, sh_ = stack
+    x, noise, drafts, res = oracle_steps[M]
+    fs = FusedDecodeStep(sh, st.layers, st.gains, st.lm_w, st.lm_s, max_M=8)
+    xd, nd = x.to(DEV), noise.to(DEV)
+    dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV) if M > 1 else None
+    fs.step(xd, nd, dd, M)
+    torch.cuda.synchronize()
+    assert fs.status() == native.MOE_OK
+    ref = (fs.y(M).clone(), fs.topk_idx(M).clone(), fs.tok[:M].clone(), fs.accepted.clone())
+    for rep in range(3):
+        fs.step(xd, nd, dd, M)
+        torch.cuda.synchronize()
+        assert torch.equal(fs.y(M), ref[0]) and torch.equal(fs.topk_idx(M), ref[1])
+        assert torch.equal(fs.tok[:M], ref[2]) and torch.equal(fs.accepted, ref[3]), rep
+    assert fs.status() == native.MOE_OK
+    r0 = res["layers"][0]
+    assert (fs.topk_idx(M)[0].cpu().numpy() == r0["idx"]).all()
+    check_bf16_output(synth.bits16(fs.y(M)[0]), r0["y"], None, "fused y layer 0")
+    div = [rel_l2(bf16_f64(synth.bits16(fs.y(M)[l])), res["layers"][l]["y"]) for l in range(sh.layers)]
+    same = [float((fs.topk_idx(M)[l].cpu().numpy() == res["layers"][l]["idx"]).all()) for l in range(sh.layers)]
+    say("M=%d fused chained: y rel-L2 by layer %s" % (M, " ".join("%.1e" % v for v in div)))
+    say("M=%d fused chained: identical routing %d/30, tokens equal %s" % (
+        M, int(sum(same)), bool((fs.tok[:M].cpu().numpy() == res["tok"]).all())))
