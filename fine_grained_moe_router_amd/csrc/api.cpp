@@ -64,6 +64,8 @@ int check_step_desc(const moe_step_desc *d) {
     if (!d) return MOE_EINVAL;
     CHECK(check_layer_desc(&d->layer));
     if (d->layer.hidden > kStepMaxHidden) return MOE_EINVAL;
+    if (d->layer.expert_width > kStepMaxWidth) return MOE_EINVAL;
+    if (step_nseg(d->layer.shared_width) > kStepMaxSharedSeg) return MOE_EINVAL;
     if (d->num_layers < 1 || d->num_layers > kMaxLayers) return MOE_EINVAL;
     if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
     if (d->max_tokens < 1 || d->max_tokens > kMaxM) return MOE_EINVAL;
@@ -174,7 +176,7 @@ int moe_decode_step_prepare(const moe_step_desc *desc, const moe_layer_weights *
     const StepWs W = step_ws(*desc);
     if (!ws_ok(workspace, workspace_bytes, W.total)) return MOE_EWORKSPACE;
     if (desc->layer.wtype != MOE_W_FP8_E4M3) return MOE_EUNSUPPORTED;
-    return step_prepare(W, layers, (char *)workspace);
+    return step_prepare(W, desc->layer, layers, (char *)workspace);
 }
 
 int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,

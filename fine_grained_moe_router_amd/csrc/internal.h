@@ -70,62 +70,70 @@ inline size_t lm_ws_bytes(int M, int V) {
 // ---------------------------------------------------------------- fused step
 
 constexpr int kMaxLayers = 64;
-constexpr int kStepMaxHidden = 3072;  // the fused step keeps 12 16-byte chunks of a row per lane
+constexpr int kStepMaxHidden = 3072;  // the fused step keeps 12 256-column chunks of a row per lane
+constexpr int kStepMaxWidth = 768;    // routed expert width: one 64-row down unit covers a whole row
+constexpr int kStepMaxSharedSeg = 8;  // column segments of the shared expert's down rows
+constexpr int kStepMaxGrid = 2048;    // persistent workgroups
 constexpr int kCtrStride = 16;        // ints between counters (64 bytes)
 constexpr unsigned kDefaultSpin = 1u << 18;   // about a quarter second of polling
-// counter slots: exit count, lm_head top-level count, error flag, lm_head group counts
-constexpr int kLmGroups = 32;
-constexpr int kExit = 0, kLmTop = 1, kError = 2, kLmSub = 3, kCtrFixed = kLmSub + kLmGroups;
+
+// Column segments of a down row of width F: the fewest that divide the F / 64 chunks
+// into at most 12 chunks each.
+inline int step_nseg(int F) {
+    if (F <= 0) return 0;
+    const int c = F / 64;
+    for (int n = (c + 11) / 12; n < c; ++n)
+        if (c % n == 0) return n;
+    return c;
+}
 
 struct StepWs {
     size_t table;        // moe_layer_weights [L]
-    size_t ctr;          // int counters, kCtrStride apart
-    size_t lmkey;        // uint64 [kLmGroups][kMaxM]: packed (logit, row) maxima per group
-    size_t hres;         // bf16 [L+1][Mx][H] residual after each layer's add
-    size_t u;            // bf16 [L][Mx][H] normalised layer inputs
-    size_t sumsq;        // fp32 [L+1][ND][Mx] per row block sums of squares of hres
-    size_t partial;      // fp32 [L][Mx][E][NB] router partial logits
-    size_t nslots;       // int [L], kCtrStride apart
-    size_t slot_expert;  // int [L][Sx]
-    size_t slot_mask;    // uint32 [L][Sx]
-    size_t slot_w;       // fp32 [L][Sx][Mx]
-    size_t h;            // fp32 [L][Sx][Mx][F]
-    size_t ypart;        // fp32 [L][Sx][Mx][H]
-    size_t y;            // bf16 [L][Mx][H] (used when the caller passes no y_layers)
+    size_t rt;           // bf16 [L][E][H]: router weights re-laid out one expert per row
+    size_t ctr;          // int [kCtrStride]: the error flag
+    size_t flags;        // uint32: lm_head workgroup done [kStepMaxGrid], then the epoch
+    // Hand-off words (uint64): the value in the low 32 bits, the step's tag in the high 32.
+    size_t logits;       // [L][Mx][E] router logits (fp32)
+    size_t hres;         // [L+1][Mx][H/2] residual stream entering each layer (2 x bf16); [0] unused
+    size_t hact;         // [L][Sx][Mx][F] gelu(gate) * up per slot and token (fp32)
+    size_t ypart;        // [L][NSUBx][Mx][H] weighted down output per sub-slot and token (fp32)
+    size_t lmbest;       // uint64 [kStepMaxGrid][kMaxM] per-workgroup best (logit, row) keys
     size_t total;
-    int L, Mx, Sx, NB, ND, F, nctr;
+    int L, Mx, Sx, NR, ND, UGx, NSUBx, F, segFmax, nseg_r, nseg_s;
+    int f_lm, f_epoch, nflags;
 };
-
-// Counters after the fixed ones (step.hip indexes them): router arrivals [L], routing
-// published [L], layer output done [L], gate/up arrivals [L][Sx], down arrivals [L][ND].
 
 inline StepWs step_ws(const moe_step_desc &d) {
     StepWs W{};
     const moe_layer_desc &ld = d.layer;
     const int H = ld.hidden, E = ld.num_experts, L = d.num_layers, Mx = d.max_tokens;
+    const int D = ld.expert_width, Ds = ld.shared_width, has_sh = Ds > 0 ? 1 : 0;
     W.L = L;
     W.Mx = Mx;
-    W.Sx = max_slots(Mx, ld.top_k, E, ld.shared_width);
-    W.NB = (H + kRouterRows - 1) / kRouterRows;
+    W.Sx = max_slots(Mx, ld.top_k, E, Ds);
+    W.NR = (E + 7) / 8;
     W.ND = H / 64;
-    W.F = ld.expert_width > ld.shared_width ? ld.expert_width : ld.shared_width;
-    W.nctr = kCtrFixed + 3 * L + L * W.Sx + L * W.ND;
+    W.nseg_r = step_nseg(D);
+    W.nseg_s = step_nseg(Ds);
+    W.UGx = (W.Sx - has_sh) * (D / 8) + Ds / 8;
+    W.NSUBx = (W.Sx - has_sh) * W.nseg_r + W.nseg_s;
+    W.F = D > Ds ? D : Ds;
+    W.segFmax = D / W.nseg_r;
+    if (Ds > 0 && Ds / W.nseg_s > W.segFmax) W.segFmax = Ds / W.nseg_s;
+    W.f_lm = 0;
+    W.f_epoch = kStepMaxGrid;
+    W.nflags = W.f_epoch + 16;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
     W.table = take(sizeof(moe_layer_weights) * (size_t)L);
-    W.ctr = take(sizeof(int) * (size_t)kCtrStride * W.nctr);
-    W.lmkey = take(8 * (size_t)kLmGroups * kMaxM);
-    W.hres = take(2 * (size_t)(L + 1) * Mx * H);
-    W.u = take(2 * (size_t)L * Mx * H);
-    W.sumsq = take(4 * (size_t)(L + 1) * W.ND * Mx);
-    W.partial = take(4 * (size_t)L * Mx * E * W.NB);
-    W.nslots = take(sizeof(int) * (size_t)kCtrStride * L);
-    W.slot_expert = take(4 * (size_t)L * W.Sx);
-    W.slot_mask = take(4 * (size_t)L * W.Sx);
-    W.slot_w = take(4 * (size_t)L * W.Sx * Mx);
-    W.h = take(4 * (size_t)L * W.Sx * Mx * W.F);
-    W.ypart = take(4 * (size_t)L * W.Sx * Mx * H);
-    W.y = take(2 * (size_t)L * Mx * H);
+    W.rt = take(2 * (size_t)L * E * H);
+    W.ctr = take(sizeof(int) * (size_t)kCtrStride);
+    W.flags = take(4 * (size_t)W.nflags);
+    W.logits = take(8 * (size_t)L * Mx * E);
+    W.hres = take(8 * (size_t)(L + 1) * Mx * (H / 2));
+    W.hact = take(8 * (size_t)L * W.Sx * Mx * W.F);
+    W.ypart = take(8 * (size_t)L * W.NSUBx * Mx * H);
+    W.lmbest = take(8 * (size_t)kStepMaxGrid * kMaxM);
     W.total = o;
     return W;
 }
@@ -146,7 +154,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
                 const int32_t *draft, int32_t *token, float *max_logit, int32_t *accepted_len,
                 int32_t *out_tokens, uint16_t *y_layers, int32_t *topk_idx, float *topk_w,
                 uint16_t *x_final, char *ws, void *stream);
-int step_prepare(const StepWs &W, const moe_layer_weights *layers, char *ws);
+int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weights *layers, char *ws);
 int step_status(const StepWs &W, char *ws);
 int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream);
 

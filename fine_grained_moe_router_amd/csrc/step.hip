@@ -1,40 +1,45 @@
 // step.hip -- the stacked batch-1 decode step as one persistent gfx950 kernel.
 //
-// A decode step at batch 1 is a chain of small, memory-bound GEMV phases (page "LLM
+// A decode step at batch 1 is a chain of small, memory-bound GEMVs (page "LLM
 // decoding", us-homepage.pages.dev/blog/llm-decoding: "First principles" and the
-// remark under "Where the 7.36 GB goes" that a fine-grained MoE step launches
-// thousands of tiny kernels, which graph replay only partly hides). Here the whole
-// step is one launch of G co-resident workgroups. The work is a fixed list of items:
+// remark under "Where the 7.36 GB goes" that a fine-grained MoE step is thousands of
+// tiny kernels, which graph replay only partly hides). Here the whole step is one
+// launch of G co-resident workgroups (the compute units times the occupancy), and
+// every workgroup takes part in every phase of every layer:
 //
-//   per layer l:  NB router row blocks | S x NG gate/up row blocks | S x ND down row blocks
-//   then:         NLM lm_head row blocks
+//  router   workgroups 0..NR-1 each own 8 experts (router weights re-laid out as
+//           [E][H] at prepare time, loaded before the wait). Each forms the whole
+//           normalised input u_l as soon as the previous layer's residual rows are
+//           in, and writes its experts' logits for all tokens.
+//  route    every workgroup reads the E x M logits and selects the top K per token
+//           itself (one wave per token, K rounds of a wave-wide maximum, ties to the
+//           lower id), so nothing stands between the logits and the expert weight
+//           loads. The union of selected experts becomes the slot list: the shared
+//           expert first, then the routed experts in ascending id.
+//  units    the layer's work is a list: 8-row gate/up units (gate and up rows of one
+//           slot), 64-row down units (one slot, one row block), then 64-row combine
+//           units. Unit i belongs to workgroup i mod G, which keeps two of its units'
+//           weights in flight. A gate/up unit writes h = gelu_tanh(gate) * up for the
+//           slot's tokens; a down unit reads the slot's h, multiplies and writes its
+//           weighted partial sums; a combine unit sums a row block's sub-slots in a
+//           fixed order into y_l, adds the residual and the next layer's noise and
+//           writes the next residual rows.
+//  lm_head  every workgroup forms x_f itself, streams an equal share of the
+//           vocabulary rows with three steps in flight, and leaves its per-token best
+//           (ordered logit, inverted row) key; workgroup 0 reduces the keys, writes
+//           the tokens and runs the greedy acceptance.
 //
-// (S = the most expert slots M tokens can select, plus the shared expert; slots the
-// routing did not fill are skipped.) Workgroup w takes items w, w + G, w + 2G, ... in
-// order, and an item waits only on items earlier in the list, so the earliest
-// unfinished item can always run: with every workgroup resident the step cannot
-// deadlock, and every wait is bounded anyway (a timed-out wait raises the error flag
-// instead of hanging).
-//
-// Hand-off between items goes through device memory with relaxed agent-scope atomic
-// loads and stores (coherent across the XCDs without writing back or invalidating the
-// L2): a producer's waves wait for their stores to complete, then thread 0 bumps a
-// counter; a consumer's thread 0 polls the counter and the workgroup then reads.
-//
-//  router item (l, b): residual add + RMSNorm of rows 64b.., router partial logits of
-//     those rows. The last router item of the layer sums the partials in block order,
-//     selects the top K per token and builds the union of selected experts (slots in
-//     ascending expert id, the shared expert last).
-//  gate/up item (l, s, rb): waves 0-1 stream 8 rows of the slot's gate matrix, waves
-//     2-3 the same 8 rows of up, for the slot's tokens; h = gelu_tanh(gate) * up.
-//  down item (l, s, cb): 64 rows of the slot's down matrix (loaded before h is ready),
-//     weighted by the token's combine weight. The last down item of a row block sums
-//     the slots in fixed order into y_l (bf16), adds the residual and the next noise
-//     and leaves the row block's sum of squares for the next layer's norm.
-//  lm_head item (i): 64 vocabulary rows for all M tokens; per-token maxima are merged
-//     with 64-bit atomic maxima of (ordered logit, inverted row) in 32 groups -- order
-//     independent, ties to the lower row. The last item writes the tokens and runs the
-//     greedy acceptance.
+// Hand-off data between workgroups travels as 64-bit words: the value in the low half,
+// the step's tag (epoch + 1) in the high half, written and read with relaxed
+// agent-scope atomics (coherent across the XCDs without writing back or invalidating
+// the L2). A consumer polls the words it needs until every tag is current, so a
+// producer never waits for its own stores and there are no separate flags inside a
+// layer. Every unit waits only on units that come earlier in the list, and a
+// workgroup runs its units in list order, so with all workgroups resident the earliest
+// unfinished unit can always run: the step cannot deadlock. Every poll is also bounded
+// (one that exceeds the spin limit raises the error flag and moves on, so the step
+// always ends). The epoch, read by every workgroup when it starts, is advanced by
+// workgroup 0 at the very end, after every workgroup has signalled its lm_head share.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -50,6 +55,7 @@ using namespace dev;
 
 struct StepArgs {
     const moe_layer_weights *layers;   // device table [L]
+    const uint16_t *rt;                // router weights re-laid out [L][E][H]
     const uint16_t *gains;             // [L+1][H]
     const uint16_t *x;                 // [M][H]
     const uint16_t *noise;             // [L][M][H]
@@ -60,23 +66,27 @@ struct StepArgs {
     float *max_logit;
     int32_t *accepted;
     int32_t *out_tokens;
-    uint16_t *y;                       // layer l, token m at y + l * y_ls + m * H
+    uint16_t *y;                       // layer l, token m at y + l * y_ls + m * H, or null
     int32_t *topk_idx;                 // [L][M][K] or null
     float *topk_w;
     uint16_t *x_final;                 // [M][H] or null
     char *ws;
-    size_t o_ctr, o_lmkey, o_hres, o_u, o_sumsq, o_partial, o_nslots, o_sexp, o_smask, o_sw, o_h, o_ypart;
+    size_t o_ctr, o_flags, o_logits, o_hres, o_hact, o_ypart, o_lmbest;
     size_t y_ls;
-    int M, Mx, H, E, K, D, Ds, F, L, V, S, Sx, NB, NG, ND, NLM, P, T, nctr;
+    int f_lm, f_epoch;                 // uint32 offsets inside the flag region
+    int l_scr, l_slot;                 // LDS offsets (bytes) of the scratch and slot areas
+    int M, Mx, H, E, K, D, Ds, L, V, Sx, NR, ND, NSUBx, Fmax, nseg_r, nseg_s, NLU;
     float eps;
     unsigned spin_limit;
 };
 
 constexpr int kWG = 256;
+constexpr int kNC = kStepMaxHidden / 256;       // 12: 256-column chunks of a row of H
+constexpr int kW = kStepMaxHidden / 2 / kWG;    // 6: residual words (2 x bf16) of a row per thread
 
-// The item functions are inlined into the kernel and read the kernel arguments on
+// The phase functions are inlined into the kernel and read the kernel arguments on
 // demand through a pointer into the kernel-argument segment, made opaque to the
-// optimiser per item so that argument fields are not held in registers across items.
+// optimiser per layer so that argument fields are not held in registers across phases.
 typedef const __attribute__((address_space(4))) StepArgs *AP;
 
 __device__ __forceinline__ AP uniform(AP p) {
@@ -88,108 +98,132 @@ __device__ __forceinline__ AP uniform(AP p) {
 
 extern __shared__ __align__(16) char smem[];
 
+// The thread index, made opaque so that values derived from it are formed where a
+// phase needs them rather than hoisted out of the layer loop and kept live (in
+// registers, or spilled) across every phase.
+__device__ __forceinline__ int ltid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // -------------------------------------------------------- coherent hand-off access
 
 __device__ __forceinline__ void st32(void *p, uint32_t v) {
     __hip_atomic_store(reinterpret_cast<uint32_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st64(void *p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t ld32(const void *p) {
     return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void stf(float *p, float v) { st32(p, __float_as_uint(v)); }
-__device__ __forceinline__ float ldf(const float *p) { return __uint_as_float(ld32(p)); }
-__device__ __forceinline__ int ldi(const int *p) { return (int)ld32(p); }
 __device__ __forceinline__ uint64_t ld64(const void *p) {
     return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// The hand-off loads are atomic, so the compiler waits for each before its first use;
-// code below issues them in unrolled batches (loads first, uses after) so that a batch
-// costs one memory latency.
+// Hand-off words are read with these atomic loads: a plain load can hit a line that the
+// reading XCD's L2 still holds from before the write (the L2s of different XCDs are not
+// kept coherent). The compiler waits for each atomic load before its first use, so the
+// code below issues them in unrolled batches (loads first, uses after): a batch costs
+// one memory latency.
+__device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return ((uint64_t)tag << 32) | v; }
+__device__ __forceinline__ bool current(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 __device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 // ------------------------------------------------------------ workspace views
 
+constexpr int kErrCtr = 0;
+
 __device__ __forceinline__ int *ctr(AP a, int i) {
     return reinterpret_cast<int *>(a->ws + a->o_ctr) + (size_t)i * kCtrStride;
 }
-__device__ __forceinline__ unsigned long long *lmkey(AP a, int grp, int m) {
-    return reinterpret_cast<unsigned long long *>(a->ws + a->o_lmkey) + (size_t)grp * kMaxM + m;
+__device__ __forceinline__ uint32_t *flags(AP a) { return reinterpret_cast<uint32_t *>(a->ws + a->o_flags); }
+__device__ __forceinline__ uint64_t *logits(AP a, int l) {
+    return reinterpret_cast<uint64_t *>(a->ws + a->o_logits) + (size_t)l * a->Mx * a->E;
 }
-__device__ __forceinline__ uint16_t *hres(AP a, int l, int m) {
-    return reinterpret_cast<uint16_t *>(a->ws + a->o_hres) + ((size_t)l * a->Mx + m) * a->H;
+__device__ __forceinline__ uint64_t *hres(AP a, int l, int m) {   // words of bf16 pairs
+    return reinterpret_cast<uint64_t *>(a->ws + a->o_hres) + ((size_t)l * a->Mx + m) * (a->H / 2);
 }
-__device__ __forceinline__ uint16_t *uin(AP a, int l, int m) {
-    return reinterpret_cast<uint16_t *>(a->ws + a->o_u) + ((size_t)l * a->Mx + m) * a->H;
+__device__ __forceinline__ uint64_t *hact(AP a, int l, int s, int m) {
+    return reinterpret_cast<uint64_t *>(a->ws + a->o_hact) + (((size_t)l * a->Sx + s) * a->Mx + m) * a->Fmax;
 }
-__device__ __forceinline__ float *sumsq(AP a, int l, int cb) {
-    return reinterpret_cast<float *>(a->ws + a->o_sumsq) + ((size_t)l * a->ND + cb) * a->Mx;
+__device__ __forceinline__ uint64_t *ypart(AP a, int l, int js, int m) {
+    return reinterpret_cast<uint64_t *>(a->ws + a->o_ypart) + (((size_t)l * a->NSUBx + js) * a->Mx + m) * a->H;
 }
-__device__ __forceinline__ float *partial(AP a, int l, int m, int e) {
-    return reinterpret_cast<float *>(a->ws + a->o_partial) + (((size_t)l * a->Mx + m) * a->E + e) * a->NB;
-}
-__device__ __forceinline__ int *nslots(AP a, int l) {
-    return reinterpret_cast<int *>(a->ws + a->o_nslots) + (size_t)l * kCtrStride;
-}
-__device__ __forceinline__ int *slot_expert(AP a, int l) {
-    return reinterpret_cast<int *>(a->ws + a->o_sexp) + (size_t)l * a->Sx;
-}
-__device__ __forceinline__ unsigned *slot_mask(AP a, int l) {
-    return reinterpret_cast<unsigned *>(a->ws + a->o_smask) + (size_t)l * a->Sx;
-}
-__device__ __forceinline__ float *slot_w(AP a, int l, int s) {
-    return reinterpret_cast<float *>(a->ws + a->o_sw) + ((size_t)l * a->Sx + s) * a->Mx;
-}
-__device__ __forceinline__ float *hbuf(AP a, int l, int s, int t) {
-    return reinterpret_cast<float *>(a->ws + a->o_h) + (((size_t)l * a->Sx + s) * a->Mx + t) * a->F;
-}
-__device__ __forceinline__ float *ypart(AP a, int l, int s, int m) {
-    return reinterpret_cast<float *>(a->ws + a->o_ypart) + (((size_t)l * a->Sx + s) * a->Mx + m) * a->H;
+__device__ __forceinline__ uint64_t *lmbest(AP a, int w) {
+    return reinterpret_cast<uint64_t *>(a->ws + a->o_lmbest) + (size_t)w * kMaxM;
 }
 
-// counter slots after the fixed ones (their count is StepWs::nctr)
-__device__ __forceinline__ int ctr_router(int l) { return kCtrFixed + l; }
-__device__ __forceinline__ int ctr_routed(int L, int l) { return kCtrFixed + L + l; }
-__device__ __forceinline__ int ctr_ydone(int L, int l) { return kCtrFixed + 2 * L + l; }
-__device__ __forceinline__ int ctr_h(int L, int Sx, int l, int s) { return kCtrFixed + 3 * L + l * Sx + s; }
-__device__ __forceinline__ int ctr_rb(int L, int Sx, int ND, int l, int cb) {
-    return kCtrFixed + 3 * L + L * Sx + l * ND + cb;
-}
+// ------------------------------------------------------------ LDS
 
-// ------------------------------------------------------------ wait / publish
-
-struct Shared {
-    int slot;       // broadcast of an atomic's result
+// The slot area: the routing of the current layer, as every workgroup computes it.
+constexpr int kMaxSub = 24;   // sub-slots (slot, column segment) per token: K + shared segments
+struct SlotLds {
+    int se[kMaxSlots + 3];                 // expert of slot s (E: the shared expert)
+    unsigned sm[kMaxSlots + 3];            // bit m: token m uses slot s
+    float sw[kMaxSlots + 3][kMaxM];        // combine weight of token m in slot s
+    int tsub[kMaxM][kMaxSub];              // token m's sub-slots, in summation order
+    unsigned long long bal[kMaxM][4];      // bit e % 64 of word e / 64: token m selected e
+    float red[4][kMaxM];                   // per-wave partial sums of squares
 };
-__shared__ Shared g_sh;
 
-// Every thread: wait until *c >= target (thread 0 polls). A wait that exceeds the spin
-// limit sets the error flag and gives up, so the step always finishes.
-__device__ __forceinline__ void wg_wait(AP a, int *c, int target) {
-    if (threadIdx.x == 0) {
-        unsigned n = 0;
-        while (ldi(c) < target) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++n >= a->spin_limit) {
-                st32(ctr(a, kError), 1u);
-                break;
-            }
+__device__ __forceinline__ SlotLds &slots(AP a) { return *reinterpret_cast<SlotLds *>(smem + a->l_slot); }
+__device__ __forceinline__ uint16_t *ulds() { return reinterpret_cast<uint16_t *>(smem); }   // [M][H] bf16
+__device__ __forceinline__ char *scratch(AP a) { return smem + a->l_scr; }
+
+// ------------------------------------------------------------ polling
+
+// A wave's polling loop: done() is true once every lane's words are current (or the
+// spin limit is reached, which raises the error flag); otherwise it sleeps briefly and
+// the loop reloads.
+struct Poll {
+    unsigned spins = 0;
+    __device__ __forceinline__ bool done(AP a, bool ok) {
+        if (__all(ok)) return true;
+        if (++spins >= a->spin_limit) {
+            if ((ltid() & 63) == 0) st32(ctr(a, kErrCtr), 1u);
+            return true;
         }
+        __builtin_amdgcn_s_sleep(1);
+        return false;
+    }
+};
+
+// Wait until all n flags hold a value >= tgt (wrap-safe); wave 0 polls.
+__device__ __forceinline__ void wait_flags(AP a, const uint32_t *f, int n, uint32_t tgt) {
+    const int tid = ltid();
+    if (tid < 64) {
+        const int lane = tid;
+        Poll pl;
+        bool ok;
+        do {
+            ok = true;
+            for (int i0 = 0; i0 < n; i0 += 64 * 8) {
+                uint32_t v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int i = i0 + lane + 64 * k;
+                    v[k] = i < n ? ld32(f + i) : tgt;
+                }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) ok = ok && (int)(v[k] - tgt) >= 0;
+            }
+        } while (!pl.done(a, ok));
     }
     __syncthreads();
 }
 
-// Every thread: wait for this wave's memory operations (its hand-off stores) to
-// complete, then thread 0 adds 1 to *c; returns the old value to every thread.
-__device__ __forceinline__ int wg_publish(int *c) {
+// Every thread: once every wave's outstanding memory operations (its stores among
+// them) are complete, thread 0 raises the flag.
+__device__ __forceinline__ void publish(uint32_t *f, uint32_t tgt) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __syncthreads();
-    if (threadIdx.x == 0)
-        g_sh.slot = __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    return g_sh.slot;
+    if (ltid() == 0) st32(f, tgt);
 }
+
+// ------------------------------------------------------------ cross-lane helpers
 
 // Order-preserving map of a float onto uint32 (larger float -> larger integer).
 __device__ __forceinline__ uint32_t ordered(float v) {
@@ -200,700 +234,888 @@ __device__ __forceinline__ float unordered(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// ------------------------------------------------------------------ router
+// Cross-lane reductions use DPP and readlane only (no LDS round trips).
 
-constexpr int kRowsPerThread = 16;   // router rows prefetched per thread (E <= 128: all of them)
-constexpr int kMaxRouterBlocks = kStepMaxHidden / kRouterRows;   // 48: partial logits per expert
-constexpr int kQuadsPerThread = kStepMaxHidden / 4 / kWG;         // 3: bf16 quads of a row per thread
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
 
-__device__ __forceinline__ void router_topk(AP a, int l);
+// Sum over the 64 lanes in a fixed order; the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
+}
 
-// Router partial logits of rows 64 b .. 64 b + 63 for every token. Thread (grp, p)
-// owns experts 2p, 2p+1 (one 4-byte load per row) and rows grp, grp + G, ...
-__device__ __forceinline__ void item_router(AP a0, int l, int b) {
-    const AP a = uniform(a0);
-    const int H = a->H, E = a->E, M = a->M, tid = threadIdx.x;
-    const int r0 = b * kRouterRows;   // H is a multiple of 256: every block has 64 rows
-    const moe_layer_weights &w = a->layers[l];
-    const uint32_t *Wr = reinterpret_cast<const uint32_t *>(w.router_w);   // [H][E/2] pairs
-    const int E2 = E / 2, G = kWG / E2, p = tid % E2, grp = tid / E2;
-    const bool act = grp < G;
-    uint32_t wv[kRowsPerThread];
+// Sum over each half-wave (32 lanes); valid in lanes 16..31 and 48..63.
+__device__ __forceinline__ float half_sum(float v) {
+    v = row16_sum(v);
+    // row_bcast:15 into rows 1 and 3 only: lane 15 of the row below
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void kmax_step(uint32_t &hi, uint32_t &lo, uint32_t oh, uint32_t ol) {
+    const bool gt = oh > hi || (oh == hi && ol > lo);
+    hi = gt ? oh : hi;
+    lo = gt ? ol : lo;
+}
+
+// Largest 64-bit key over the 64 lanes (all lanes active); wave-uniform result.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+    kmax_step(hi, lo, dppu<0xB1>(hi), dppu<0xB1>(lo));     // quad_perm [1,0,3,2]
+    kmax_step(hi, lo, dppu<0x4E>(hi), dppu<0x4E>(lo));     // quad_perm [2,3,0,1]
+    kmax_step(hi, lo, dppu<0x141>(hi), dppu<0x141>(lo));   // row_half_mirror
+    kmax_step(hi, lo, dppu<0x140>(hi), dppu<0x140>(lo));   // row_mirror
+    uint64_t best = 0;
 #pragma unroll
-    for (int k = 0; k < kRowsPerThread; ++k) {
-        const int r = grp + G * k;
-        wv[k] = (act && r < kRouterRows) ? Wr[(size_t)(r0 + r) * E2 + p] : 0u;
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        best = v > best ? v : best;
     }
-    float *xs = reinterpret_cast<float *>(smem);             // [M][64] u of this block (fp32)
-    float *rsum = xs + kMaxM * kRouterRows;                  // [M] norm factors
-    float *red = rsum + kMaxM;                               // [256][2][M] / [ND][M]
-    if (l > 0) wg_wait(a, ctr(a, ctr_ydone(a->L, l - 1)), a->ND);
+    return best;
+}
 
-    // norm factor r_m = rsqrt(mean(h^2) + eps)
-    if (l == 0) {
-        // h_0 = bf16(x + noise_0): the whole row is needed for the sum of squares
-        for (int m = 0; m < M; ++m) {
-            const uint16_t *xm = a->x + (size_t)m * H, *nm = a->noise + (size_t)m * H;
-            float ss = 0.0f;
-            for (int c = tid; c < H; c += kWG) {
-                const float hv = bf2f(f2bf(bf2f(xm[c]) + bf2f(nm[c])));
-                ss = fmaf(hv, hv, ss);
-            }
-            red[tid * kMaxM + m] = ss;
-        }
-        __syncthreads();
-        if (tid < M) {
-            float ss = 0.0f;
-            for (int t = 0; t < kWG; ++t) ss += red[t * kMaxM + tid];
-            rsum[tid] = rsqrtf(ss / (float)H + a->eps);
-        }
-    } else {
-        for (int i = tid; i < a->ND * M; i += kWG) {
-            const int cb = i / M, m = i % M;
-            red[cb * kMaxM + m] = ldf(sumsq(a, l, cb) + m);
-        }
-        __syncthreads();
-        if (tid < M) {
-            float ss = 0.0f;
-            for (int cb = 0; cb < a->ND; ++cb) ss += red[cb * kMaxM + tid];
-            rsum[tid] = rsqrtf(ss / (float)H + a->eps);
-        }
-    }
-    __syncthreads();
-    // u rows of this block, two rows per thread: bf16(h * r * g), kept in LDS (fp32)
-    // and published for the expert items
-    const uint16_t *g = a->gains + (size_t)l * H;
-    for (int i = tid; i < M * (kRouterRows / 2); i += kWG) {
-        const int m = i / (kRouterRows / 2), r = 2 * (i % (kRouterRows / 2)), c = r0 + r;
-        uint16_t h0, h1;
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// ------------------------------------------------------------ norm
+
+// h_0 = bf16(x + noise_0) for the pair of columns (2 word, 2 word + 1) of token m
+__device__ __forceinline__ uint32_t h0_pair(AP a, int m, int word) {
+    const uint32_t xv = *reinterpret_cast<const uint32_t *>(a->x + (size_t)m * a->H + 2 * word);
+    const uint32_t nv = *reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * a->H + 2 * word);
+    return pack2(f2bf(bf2f(xv & 0xffffu) + bf2f(nv & 0xffffu)), f2bf(bf2f(xv >> 16) + bf2f(nv >> 16)));
+}
+
+// u = bf16(h_l * rsqrt(mean(h_l^2) + eps) * g) for the M tokens, into the u area of
+// LDS. h_0 comes from the inputs; h_l (l >= 1) from the residual words, polled until
+// current, four tokens at a time. Thread t owns words t, t+256, ... of every token and
+// the sums of squares are reduced in a fixed order, so every workgroup forms
+// bit-identical u. h is staged in the u area and rewritten in place.
+constexpr int kNormTok = 4;
+template <int MT>
+__device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint32_t tgt) {
+    const int H = a->H, M = MT, tid = ltid(), hw = H / 2, lane = tid & 63, wave = tid >> 6;
+    uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][H/2] bf16 pairs
+    float ss[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) ss[m] = 0.0f;
+#pragma unroll
+    for (int m0 = 0; m0 < MT; m0 += kNormTok) {
+        if (m0 >= M) break;
+        uint32_t hp[kNormTok][kW];
         if (l == 0) {
-            h0 = f2bf(bf2f(a->x[(size_t)m * H + c]) + bf2f(a->noise[(size_t)m * H + c]));
-            h1 = f2bf(bf2f(a->x[(size_t)m * H + c + 1]) + bf2f(a->noise[(size_t)m * H + c + 1]));
-            st32(hres(a, 0, m) + c, pack2(h0, h1));
+            uint32_t xv[kNormTok][kW], nv[kNormTok][kW];
+#pragma unroll
+            for (int mm = 0; mm < kNormTok; ++mm)
+#pragma unroll
+                for (int k = 0; k < kW; ++k) {
+                    const int m = m0 + mm, q = tid + k * kWG;
+                    if (m < M && q < hw) {
+                        xv[mm][k] = *reinterpret_cast<const uint32_t *>(a->x + (size_t)m * H + 2 * q);
+                        nv[mm][k] = *reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * H + 2 * q);
+                    }
+                }
+#pragma unroll
+            for (int mm = 0; mm < kNormTok; ++mm)
+#pragma unroll
+                for (int k = 0; k < kW; ++k)
+                    hp[mm][k] = pack2(f2bf(bf2f(xv[mm][k] & 0xffffu) + bf2f(nv[mm][k] & 0xffffu)),
+                                      f2bf(bf2f(xv[mm][k] >> 16) + bf2f(nv[mm][k] >> 16)));
         } else {
-            const uint32_t hp = ld32(hres(a, l, m) + c);
-            h0 = (uint16_t)(hp & 0xffffu);
-            h1 = (uint16_t)(hp >> 16);
-        }
-        const uint16_t u0 = f2bf(bf2f(h0) * rsum[m] * bf2f(g[c]));
-        const uint16_t u1 = f2bf(bf2f(h1) * rsum[m] * bf2f(g[c + 1]));
-        st32(uin(a, l, m) + c, pack2(u0, u1));
-        xs[m * kRouterRows + r] = bf2f(u0);
-        xs[m * kRouterRows + r + 1] = bf2f(u1);
-    }
-    __syncthreads();
-    float acc0[kMaxM], acc1[kMaxM];
+            Poll pl;
+            bool ok;
+            do {
+                uint64_t v[kNormTok][kW];
 #pragma unroll
-    for (int m = 0; m < kMaxM; ++m) acc0[m] = acc1[m] = 0.0f;
-    if (act) {
+                for (int mm = 0; mm < kNormTok; ++mm)
 #pragma unroll
-        for (int k = 0; k < kRowsPerThread; ++k) {
-            const int r = grp + G * k;
-            if (r < kRouterRows) {
-                const float w0 = bf2f(wv[k] & 0xffffu), w1 = bf2f(wv[k] >> 16);
-#pragma unroll
-                for (int m = 0; m < kMaxM; ++m) {
-                    if (m < M) {
-                        acc0[m] = fmaf(xs[m * kRouterRows + r], w0, acc0[m]);
-                        acc1[m] = fmaf(xs[m * kRouterRows + r], w1, acc1[m]);
+                    for (int k = 0; k < kW; ++k) {
+                        const int m = m0 + mm, q = tid + k * kWG;
+                        if (m < M && q < hw) v[mm][k] = ld64(hres(a, l, m) + q);
                     }
-                }
-            }
-        }
-        // rows beyond the prefetched ones (E > 128)
-        for (int r = grp + G * kRowsPerThread; r < kRouterRows; r += G) {
-            const uint32_t wp = Wr[(size_t)(r0 + r) * E2 + p];
-            const float w0 = bf2f(wp & 0xffffu), w1 = bf2f(wp >> 16);
+                ok = true;
 #pragma unroll
-            for (int m = 0; m < kMaxM; ++m) {
-                if (m < M) {
-                    acc0[m] = fmaf(xs[m * kRouterRows + r], w0, acc0[m]);
-                    acc1[m] = fmaf(xs[m * kRouterRows + r], w1, acc1[m]);
-                }
-            }
-        }
-    }
-    __syncthreads();
+                for (int mm = 0; mm < kNormTok; ++mm)
 #pragma unroll
-    for (int m = 0; m < kMaxM; ++m) {
-        red[(tid * 2 + 0) * kMaxM + m] = acc0[m];
-        red[(tid * 2 + 1) * kMaxM + m] = acc1[m];
-    }
-    __syncthreads();
-    if (tid < E) {
-        const int pp = tid >> 1, half = tid & 1;
-        for (int m = 0; m < M; ++m) {
-            float sum = 0.0f;
-            for (int q = 0; q < G; ++q) sum += red[((q * E2 + pp) * 2 + half) * kMaxM + m];
-            stf(partial(a, l, m, tid) + b, sum);
-        }
-    }
-    if (wg_publish(ctr(a, ctr_router(l))) != a->NB - 1) return;
-    router_topk(a, l);
-}
-
-// The last router item of a layer: logits = partials summed in block order (+ bias);
-// per token the K largest (wave argmax K times, ties to the lower id); weights are
-// the softmax renormalised over the K (the full softmax denominator cancels); the
-// union of selected experts becomes the slot table (ascending id, shared expert last).
-__device__ __forceinline__ void router_topk(AP a, int l) {
-    const int E = a->E, M = a->M, K = a->K, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    float *wsel = reinterpret_cast<float *>(smem);                       // [M][E]
-    int *sel_e = reinterpret_cast<int *>(wsel + kMaxM * kMaxExperts);   // [M][16]
-    float *sel_l = reinterpret_cast<float *>(sel_e + kMaxM * kMaxTopK);
-    int *wave_cnt = reinterpret_cast<int *>(sel_l + kMaxM * kMaxTopK);
-    __syncthreads();
-    for (int i = tid; i < kMaxM * kMaxExperts; i += kWG) wsel[i] = 0.0f;
-    __syncthreads();
-    const float *bias = a->layers[l].router_bias;
-    const int NB = a->NB;
-    for (int m = wave; m < M; m += 4) {
-        float lg[4];
-        bool taken[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ee = lane + 64 * i;
-            taken[i] = false;
-            lg[i] = -INFINITY;
-            if (ee < E) {
-                const float *pp = partial(a, l, m, ee);
-                uint64_t v[kMaxRouterBlocks / 2];
-#pragma unroll
-                for (int q = 0; q < kMaxRouterBlocks / 2; ++q)
-                    if (2 * q < NB) v[q] = ld64(pp + 2 * q);
-                float sum = 0.0f;
-#pragma unroll
-                for (int q = 0; q < kMaxRouterBlocks / 2; ++q) {
-                    if (2 * q < NB) sum += __uint_as_float((uint32_t)v[q]);
-                    if (2 * q + 1 < NB) sum += __uint_as_float((uint32_t)(v[q] >> 32));
-                }
-                if (bias) sum += bias[ee];
-                lg[i] = sum;
-            }
-        }
-        for (int k = 0; k < K; ++k) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ee = lane + 64 * i;
-                if (ee < E && !taken[i] && (lg[i] > bv || (lg[i] == bv && ee < bi))) {
-                    bv = lg[i];
-                    bi = ee;
-                }
-            }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane + 64 * i == bi) taken[i] = true;
-            if (lane == 0) {
-                sel_e[m * kMaxTopK + k] = bi;
-                sel_l[m * kMaxTopK + k] = bv;
-            }
-        }
-        if (lane == 0) {
-            int *se = sel_e + m * kMaxTopK;
-            float *sl = sel_l + m * kMaxTopK;
-            const float lmax = sl[0];
-            float z = 0.0f;
-            for (int k = 0; k < K; ++k) z += expf(sl[k] - lmax);
-            for (int k = 1; k < K; ++k) {
-                const int ek = se[k];
-                const float lk = sl[k];
-                int j = k - 1;
-                while (j >= 0 && se[j] > ek) {
-                    se[j + 1] = se[j];
-                    sl[j + 1] = sl[j];
-                    --j;
-                }
-                se[j + 1] = ek;
-                sl[j + 1] = lk;
-            }
-            for (int k = 0; k < K; ++k) {
-                const float wk = expf(sl[k] - lmax) / z;
-                wsel[m * kMaxExperts + se[k]] = wk;
-                if (a->topk_idx) a->topk_idx[((size_t)l * M + m) * K + k] = se[k];
-                if (a->topk_w) a->topk_w[((size_t)l * M + m) * K + k] = wk;
-            }
-        }
-    }
-    __syncthreads();
-    unsigned mask = 0;
-    if (tid < E)
-        for (int m = 0; m < M; ++m)
-            for (int k = 0; k < K; ++k)
-                if (sel_e[m * kMaxTopK + k] == tid) mask |= 1u << m;
-    const unsigned long long bal = __ballot(mask != 0);
-    if (lane == 0) wave_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    int *se_out = slot_expert(a, l);
-    unsigned *sm_out = slot_mask(a, l);
-    if (mask) {
-        int base = 0;
-        for (int q = 0; q < wave; ++q) base += wave_cnt[q];
-        const int slot = base + __popcll(bal & ((1ull << lane) - 1ull));
-        st32(se_out + slot, (uint32_t)tid);
-        st32(sm_out + slot, mask);
-        for (int m = 0; m < M; ++m) stf(slot_w(a, l, slot) + m, wsel[m * kMaxExperts + tid]);
-    }
-    if (tid == 0) {
-        int ns = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
-        if (a->Ds > 0) {
-            st32(se_out + ns, (uint32_t)E);
-            st32(sm_out + ns, (1u << M) - 1u);
-            for (int m = 0; m < M; ++m) stf(slot_w(a, l, ns) + m, 1.0f);
-            ++ns;
-        }
-        st32(nslots(a, l), (uint32_t)ns);
-    }
-    wg_publish(ctr(a, ctr_routed(a->L, l)));
-}
-
-// ----------------------------------------------------------------- gate / up
-
-constexpr int kGURows = 8;      // rows of gate and of up per item
-constexpr int kGUChunks = 12;   // 16-byte chunks of a row per lane held in registers (H <= 3072)
-
-struct SlotInfo {
-    int ns, e, F, ntok;
-    unsigned mask;
-    bool shared;
-};
-
-__device__ __forceinline__ SlotInfo read_slot(AP a, int l, int s) {
-    SlotInfo si;
-    // s < S <= Sx, so the slot's entries can be read before knowing whether s is used
-    const int ns = ldi(nslots(a, l));
-    const int e = ldi(slot_expert(a, l) + s);
-    const unsigned mask = ld32(slot_mask(a, l) + s);
-    si.ns = ns;
-    si.e = 0;
-    si.mask = 0;
-    si.F = 0;
-    si.ntok = 0;
-    si.shared = false;
-    if (s < ns) {
-        // clamped so that even a stale table (after a timed-out wait) names an existing expert
-        si.e = min(max(e, 0), a->Ds > 0 ? a->E : a->E - 1);
-        si.mask = mask & ((1u << a->M) - 1u);
-        si.shared = si.e == a->E;
-        si.F = si.shared ? a->Ds : a->D;
-        si.ntok = __popc(si.mask);
-    }
-    return si;
-}
-
-// Gate/up item: waves 0-1 stream rows row0..row0+7 of the gate matrix, waves 2-3 the
-// same rows of up (16 lanes per row, 256 contiguous bytes per row per load), so each
-// lane holds one row's H/256 chunks.
-__device__ __forceinline__ void item_gateup(AP a0, int l, int s, int rb) {
-    const AP a = uniform(a0);
-    wg_wait(a, ctr(a, ctr_routed(a->L, l)), 1);
-    const SlotInfo si = read_slot(a, l, s);
-    const int row0 = rb * kGURows;
-    if (s >= si.ns || row0 >= si.F) return;
-    const int H = a->H, hv = H / 8, hw = H / 2, NC = H / 256;
-    (void)hw;
-    const moe_layer_weights &w = a->layers[l];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int g = lane >> 4, li = lane & 15, up = wave >> 1;
-    const int rloc = (wave & 1) * 4 + g, row = row0 + rloc;
-    const size_t eoff = (size_t)si.e * a->D * H;
-    const uint8_t *mat = up ? (si.shared ? (const uint8_t *)w.sh_up_w : (const uint8_t *)w.up_w + eoff)
-                            : (si.shared ? (const uint8_t *)w.sh_gate_w : (const uint8_t *)w.gate_w + eoff);
-    const uint8_t *wp = mat + (size_t)row * H + li * 16;
-    uint4 q[kGUChunks];
-#pragma unroll
-    for (int k = 0; k < kGUChunks; ++k)
-        if (k < NC) q[k] = *reinterpret_cast<const uint4 *>(wp + (size_t)k * 256);
-    const float *sc = up ? (si.shared ? w.sh_up_s : w.up_s + (size_t)si.e * a->D)
-                         : (si.shared ? w.sh_gate_s : w.gate_s + (size_t)si.e * a->D);
-    const float srow = sc[row];
-    uint32_t *xw = reinterpret_cast<uint32_t *>(smem);                      // [ntok][H/2] bf16 pairs
-    float *red = reinterpret_cast<float *>(smem + (size_t)a->Mx * H * 2);   // [2][8][M]
-    {
-        // token t's row is H/4 quads; thread i loads quads i, i + 256, ... of every token
-        const int hq = H / 4;
-        int toks[kMaxM];
-        {
-            unsigned mm = si.mask;
-#pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
-                toks[t] = mm ? __ffs(mm) - 1 : 0;
-                mm &= mm - 1u;
-            }
-        }
-        uint64_t v[kMaxM][kQuadsPerThread];
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t)
-#pragma unroll
-            for (int k = 0; k < kQuadsPerThread; ++k) {
-                const int i = threadIdx.x + k * kWG;
-                if (t < si.ntok && i < hq) v[t][k] = ld64(uin(a, l, toks[t]) + 4 * i);
-            }
-        uint64_t *xq = reinterpret_cast<uint64_t *>(xw);
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t)
-#pragma unroll
-            for (int k = 0; k < kQuadsPerThread; ++k) {
-                const int i = threadIdx.x + k * kWG;
-                if (t < si.ntok && i < hq) xq[t * hq + i] = v[t][k];
-            }
-    }
-    __syncthreads();
-    const uint4 *xs = reinterpret_cast<const uint4 *>(xw);
-    float acc[kMaxM];
-#pragma unroll
-    for (int t = 0; t < kMaxM; ++t) acc[t] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kGUChunks; ++k) {
-        if (k < NC) {
-            bf16x2 wv[8];
-            decode16_bf16(q[k], wv);
-            const int xv = (k * 256 + li * 16) / 8;
-#pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
-                if (t < si.ntok) {
-                    const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
-                    acc[t] = dot16(wv, x0, x1, acc[t]);
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxM; ++t) {
-        if (t < si.ntok) {
-            const float v = row16_sum(acc[t]);
-            if (li == 0) red[(up * kGURows + rloc) * kMaxM + t] = srow * v;
-        }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < kGURows * si.ntok; i += kWG) {
-        const int r = i / si.ntok, t = i % si.ntok;
-        stf(hbuf(a, l, s, t) + row0 + r, gelu_tanh(red[r * kMaxM + t]) * red[(kGURows + r) * kMaxM + t]);
-    }
-    wg_publish(ctr(a, ctr_h(a->L, a->Sx, l, s)));
-}
-
-// --------------------------------------------------------------------- down
-
-constexpr int kDNRows = 64;
-constexpr int kDNChunks = 11;   // 16-byte chunks per lane in registers (F = 704: the whole row)
-constexpr int kDownLdsBytes = 32 * 1024;   // h of the slot's tokens staged per pass
-
-__device__ __forceinline__ void item_down(AP a0, int l, int s, int cb) {
-    const AP a = uniform(a0);
-    wg_wait(a, ctr(a, ctr_routed(a->L, l)), 1);
-    const SlotInfo si = read_slot(a, l, s);
-    if (s >= si.ns) return;
-    const int H = a->H, F = si.F, NI = F / 64, f4 = F / 4;
-    const moe_layer_weights &w = a->layers[l];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane & 3;
-    const int c = cb * kDNRows + wave * 16 + (lane >> 2);
-    const uint8_t *dw = (si.shared ? (const uint8_t *)w.sh_down_w
-                                   : (const uint8_t *)w.down_w + (size_t)si.e * H * a->D) +
-                        (size_t)c * F + q * 16;
-    // the first block of this lane's chunks is loaded before h is ready
-    uint4 qd[kDNChunks];
-#pragma unroll
-    for (int k = 0; k < kDNChunks; ++k)
-        if (k < NI) qd[k] = *reinterpret_cast<const uint4 *>(dw + (size_t)k * 64);
-    const float sd = (si.shared ? w.sh_down_s : w.down_s + (size_t)si.e * H)[c];
-    wg_wait(a, ctr(a, ctr_h(a->L, a->Sx, l, s)), F / kGURows);
-
-    float4 *hs4 = reinterpret_cast<float4 *>(smem);
-    float *hsf = reinterpret_cast<float *>(smem);
-    const int tp = min(si.ntok, (int)(kDownLdsBytes / (F * 4)));
-    // the combine weights of the slot's tokens
-    float cw[kMaxM];
-    {
-        const float *swp = slot_w(a, l, s);
-        uint32_t v[kMaxM];
-#pragma unroll
-        for (int m = 0; m < kMaxM; ++m)
-            if (m < a->M) v[m] = ld32(swp + m);
-#pragma unroll
-        for (int m = 0; m < kMaxM; ++m) cw[m] = m < a->M ? __uint_as_float(v[m]) : 0.0f;
-    }
-    unsigned mrem = si.mask;
-    bool fresh = true;   // qd holds chunks 0.. of the row
-    for (int t0 = 0; t0 < si.ntok; t0 += tp) {
-        const int tn = min(tp, si.ntok - t0);
-        __syncthreads();
-        {
-            // tn * F / 2 float pairs (at most kDownLdsBytes / 8): thread i takes pairs i, i + 256, ...
-            const int F2 = F / 2, np = tn * F2;
-            uint64_t *hq = reinterpret_cast<uint64_t *>(hsf);
-#pragma unroll 1
-            for (int k0 = 0; k0 * kWG < np; k0 += 8) {   // rounds of 8 loads per thread
-                uint64_t v[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int i = threadIdx.x + (k0 + k) * kWG;
-                    if (i < np) v[k] = ld64(hbuf(a, l, s, t0 + i / F2) + 2 * (i % F2));
-                }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int i = threadIdx.x + (k0 + k) * kWG;
-                    if (i < np) hq[i] = v[k];
-                }
-            }
-        }
-        __syncthreads();
-        float acc[kMaxM];
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t) acc[t] = 0.0f;
-        for (int i0 = 0; i0 < NI; i0 += kDNChunks) {
-            if (!fresh || i0 > 0) {
-#pragma unroll
-                for (int k = 0; k < kDNChunks; ++k)
-                    if (i0 + k < NI) qd[k] = *reinterpret_cast<const uint4 *>(dw + (size_t)(i0 + k) * 64);
-            }
-            fresh = false;
-#pragma unroll
-            for (int k = 0; k < kDNChunks; ++k) {
-                if (i0 + k < NI) {
-                    float wv[16];
-                    const uint32_t qw[4] = {qd[k].x, qd[k].y, qd[k].z, qd[k].w};
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const f32x2 lo = fp8x2_to_f32<false>(qw[u]);
-                        const f32x2 hi = fp8x2_to_f32<true>(qw[u]);
-                        wv[4 * u + 0] = lo.x;
-                        wv[4 * u + 1] = lo.y;
-                        wv[4 * u + 2] = hi.x;
-                        wv[4 * u + 3] = hi.y;
-                    }
-                    const int cv = ((i0 + k) * 64 + q * 16) / 4;
-#pragma unroll
-                    for (int t = 0; t < kMaxM; ++t) {
-                        if (t < tn) {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                const float4 hv = hs4[t * f4 + cv + u];
-                                acc[t] = fmaf(wv[4 * u + 0], hv.x, acc[t]);
-                                acc[t] = fmaf(wv[4 * u + 1], hv.y, acc[t]);
-                                acc[t] = fmaf(wv[4 * u + 2], hv.z, acc[t]);
-                                acc[t] = fmaf(wv[4 * u + 3], hv.w, acc[t]);
-                            }
+                    for (int k = 0; k < kW; ++k) {
+                        const int m = m0 + mm, q = tid + k * kWG;
+                        if (m < M && q < hw) {
+                            hp[mm][k] = (uint32_t)v[mm][k];
+                            ok = ok && current(v[mm][k], tgt);
                         }
                     }
+            } while (!pl.done(a, ok));
+        }
+#pragma unroll
+        for (int mm = 0; mm < kNormTok; ++mm) {
+            const int m = m0 + mm;
+#pragma unroll
+            for (int k = 0; k < kW; ++k) {
+                const int q = tid + k * kWG;
+                if (m < M && q < hw) {
+                    const float f0 = bf2f(hp[mm][k] & 0xffffu), f1 = bf2f(hp[mm][k] >> 16);
+                    ss[m0 + mm] = fmaf(f0, f0, ss[m0 + mm]);
+                    ss[m0 + mm] = fmaf(f1, f1, ss[m0 + mm]);
+                    uw[(size_t)m * hw + q] = hp[mm][k];
                 }
             }
         }
+    }
+    SlotLds &S = slots(a);
 #pragma unroll
-        for (int t = 0; t < kMaxM; ++t) {
-            if (t < tn) {
-                const int m = __ffs(mrem) - 1;
-                mrem &= mrem - 1u;
-                const float v = quad_sum(acc[t]);
-                float wm = 0.0f;
+    for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+            const float t = wave_sum(ss[m]);
+            if (lane == 0) S.red[wave][m] = t;
+        }
+    }
+    __syncthreads();
 #pragma unroll
-                for (int mm = 0; mm < kMaxM; ++mm)
-                    if (mm == m) wm = cw[mm];
-                if (q == 0) stf(ypart(a, l, s, m) + c, wm * (sd * v));
+    for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+            const float r = rsqrtf((S.red[0][m] + S.red[1][m] + S.red[2][m] + S.red[3][m]) / (float)H + a->eps);
+#pragma unroll
+            for (int k = 0; k < kW; ++k) {
+                const int q = tid + k * kWG;
+                if (q < hw) {
+                    const uint32_t gv = *reinterpret_cast<const uint32_t *>(g + 2 * q);
+                    const uint32_t hv = uw[(size_t)m * hw + q];
+                    const uint16_t u0 = f2bf(bf2f(hv & 0xffffu) * r * bf2f(gv & 0xffffu));
+                    const uint16_t u1 = f2bf(bf2f(hv >> 16) * r * bf2f(gv >> 16));
+                    uw[(size_t)m * hw + q] = pack2(u0, u1);
+                }
             }
         }
     }
-    if (wg_publish(ctr(a, ctr_rb(a->L, a->Sx, a->ND, l, cb))) != si.ns - 1) return;
+    __syncthreads();
+}
 
-    // ---- the last down item of row block cb: combine, residual, next norm's partial sum
-    const int M = a->M, tid = threadIdx.x;
-    unsigned *masks = reinterpret_cast<unsigned *>(smem);           // [ns <= kMaxSlots]
-    int *slist = reinterpret_cast<int *>(masks + kMaxSlots);        // [M][kMaxTopK + 1]
-    int *scount = slist + kMaxM * (kMaxTopK + 1);                   // [M]
-    float *sq = reinterpret_cast<float *>(scount + kMaxM);          // [M][64]
-    __syncthreads();
-    {
-        uint32_t v[kMaxSlots / kWG + 1];
+// ------------------------------------------------------------------ router
+
+// Router workgroup j's weights for layer l: experts 8j .. 8j+7, one half-wave (32
+// lanes) per expert, each lane 8 bf16 of every 256-column chunk of the expert's row.
+__device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]) {
+    const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
+    const int e = min(8 * j + (tid >> 5), E - 1);
+    const uint16_t *wr = a->rt + ((size_t)l * E + e) * H + (tid & 31) * 8;
 #pragma unroll
-        for (int k = 0; k < kMaxSlots / kWG + 1; ++k)
-            if (tid + k * kWG < si.ns) v[k] = ld32(slot_mask(a, l) + tid + k * kWG);
+    for (int k = 0; k < kNC; ++k)
+        if (k < NC) wq[k] = *reinterpret_cast<const uint4 *>(wr + k * 256);
+}
+
+// Router workgroup j, layer l: u_l, then the logits of experts 8j .. 8j+7 for every
+// token (weights already in wq).
+template <int MT>
+__device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&wq)[kNC], uint32_t tgt) {
+    const AP a = uniform(a0);
+    const int H = a->H, E = a->E, M = MT, NC = H / 256, tid = ltid(), lane32 = tid & 31;
+    const int e = 8 * j + (tid >> 5);
+    const bool valid = e < E;
+    norm_to_lds<MT>(a, l, a->gains + (size_t)l * H, tgt);
+    const uint16_t *u = ulds();
+    float acc[MT];
 #pragma unroll
-        for (int k = 0; k < kMaxSlots / kWG + 1; ++k)
-            if (tid + k * kWG < si.ns) masks[tid + k * kWG] = v[k];
-    }
-    __syncthreads();
-    if (tid < M) {   // the slots of token tid in ascending order (K routed + the shared one)
-        int n = 0;
-        for (int s2 = 0; s2 < si.ns; ++s2)
-            if (((masks[s2] >> tid) & 1u) && n < kMaxTopK + 1) slist[tid * (kMaxTopK + 1) + n++] = s2;
-        scount[tid] = n;
-    }
-    __syncthreads();
-    const bool last_layer = l == a->L - 1;
-    for (int i = tid; i < M * (kDNRows / 2); i += kWG) {
-        const int m = i / (kDNRows / 2), r = 2 * (i % (kDNRows / 2)), cc = cb * kDNRows + r;
-        const int n = scount[m];
-        uint64_t v[kMaxTopK + 1];
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kMaxTopK + 1; ++j)
-            if (j < n) v[j] = ld64(ypart(a, l, slist[m * (kMaxTopK + 1) + j], m) + cc);
-        float acc0 = 0.0f, acc1 = 0.0f;
+    for (int k = 0; k < kNC; ++k) {
+        if (k < NC) {
 #pragma unroll
-        for (int j = 0; j < kMaxTopK + 1; ++j) {
-            if (j < n) {
-                acc0 += __uint_as_float((uint32_t)v[j]);
-                acc1 += __uint_as_float((uint32_t)(v[j] >> 32));
+            for (int m = 0; m < MT; ++m) {
+                if (m < M) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(u + (size_t)m * H + k * 256 + lane32 * 8);
+                    acc[m] = dot2(as_bf2(wq[k].x), as_bf2(xv.x), acc[m]);
+                    acc[m] = dot2(as_bf2(wq[k].y), as_bf2(xv.y), acc[m]);
+                    acc[m] = dot2(as_bf2(wq[k].z), as_bf2(xv.z), acc[m]);
+                    acc[m] = dot2(as_bf2(wq[k].w), as_bf2(xv.w), acc[m]);
+                }
             }
         }
-        const uint16_t y0 = f2bf(acc0), y1 = f2bf(acc1);
-        *reinterpret_cast<uint32_t *>(a->y + (size_t)l * a->y_ls + (size_t)m * H + cc) = pack2(y0, y1);
-        const uint32_t hp = ld32(hres(a, l, m) + cc);
-        float hv0 = bf2f(hp & 0xffffu), hv1 = bf2f(hp >> 16);
-        if (!last_layer) {
-            const uint16_t *nz = a->noise + ((size_t)(l + 1) * M + m) * H + cc;
-            hv0 += bf2f(nz[0]);
-            hv1 += bf2f(nz[1]);
+    }
+    const float *bias = a->layers[l].router_bias;
+    const float bv = (bias && valid) ? bias[e] : 0.0f;
+    uint64_t *lg = logits(a, l);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        if (m < M) {
+            const float v = half_sum(acc[m]);
+            if (lane32 == 16 && valid) st64(lg + (size_t)m * E + e, tagged(__float_as_uint(v + bv), tgt));
         }
-        const uint16_t hn0 = f2bf(hv0 + bf2f(y0)), hn1 = f2bf(hv1 + bf2f(y1));
-        st32(hres(a, l + 1, m) + cc, pack2(hn0, hn1));
-        const float f0 = bf2f(hn0), f1 = bf2f(hn1);
-        sq[m * kDNRows + r] = f0 * f0;
-        sq[m * kDNRows + r + 1] = f1 * f1;
+    }
+}
+
+// ------------------------------------------------------------------ route
+
+constexpr int kEI = kMaxExperts / 64;   // experts per lane in the top-K selection
+
+// Every workgroup, layer l: route. Wave w selects the top K of tokens w, w+4: each lane
+// holds the (ordered logit, inverted id) keys of experts lane, lane+64, ..., and K
+// rounds of a wave-wide maximum take the largest remaining key (ties to the lower id).
+// The selected experts' softmax weights are renormalised over the K (the full softmax
+// denominator cancels). Then every thread e builds expert e's slot from the per-token
+// selection masks: the slot list is the shared expert, then the union of selected
+// experts in ascending id. Returns the number of slots.
+template <int MT>
+__device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outputs) {
+    const AP a = uniform(a0);
+    const int E = a->E, M = MT, K = a->K, tid = ltid(), lane = tid & 63, wave = tid >> 6;
+    SlotLds &S = slots(a);
+    float *wt = reinterpret_cast<float *>(scratch(a));   // [M][E] weight of expert e for token m
+    const uint64_t *src = logits(a, l);
+    for (int m = wave; m < M; m += 4) {
+        float lgv[kEI];
+        {
+            Poll pl;
+            bool ok;
+            do {
+                uint64_t v[kEI];
+#pragma unroll
+                for (int i = 0; i < kEI; ++i)
+                    if (lane + 64 * i < E) v[i] = ld64(src + (size_t)m * E + lane + 64 * i);
+                ok = true;
+#pragma unroll
+                for (int i = 0; i < kEI; ++i) {
+                    lgv[i] = 0.0f;
+                    if (lane + 64 * i < E) {
+                        lgv[i] = __uint_as_float((uint32_t)v[i]);
+                        ok = ok && current(v[i], tgt);
+                    }
+                }
+            } while (!pl.done(a, ok));
+        }
+        uint64_t key[kEI];
+        bool sel[kEI];
+#pragma unroll
+        for (int i = 0; i < kEI; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = e < E ? ((uint64_t)ordered(lgv[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+            sel[i] = false;
+        }
+        float lmax = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            uint64_t best = key[0];
+#pragma unroll
+            for (int i = 1; i < kEI; ++i) best = key[i] > best ? key[i] : best;
+            const uint64_t W = wave_max_key(best);
+            if (k == 0) lmax = unordered((uint32_t)(W >> 32));
+#pragma unroll
+            for (int i = 0; i < kEI; ++i) {
+                if (key[i] == W) {
+                    sel[i] = true;
+                    key[i] = 0ull;
+                }
+            }
+        }
+        float ev[kEI], zl = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kEI; ++i) {
+            ev[i] = sel[i] ? expf(lgv[i] - lmax) : 0.0f;
+            zl += ev[i];
+        }
+        const float z = wave_sum(zl);
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < kEI; ++i) {
+            const unsigned long long bm = __ballot(sel[i]);
+            if (lane == 0) S.bal[m][i] = bm;
+            if (sel[i]) {
+                const int e = lane + 64 * i, pos = before + lanes_below(bm);
+                const float wv = ev[i] / z;
+                wt[m * E + e] = wv;
+                if (outputs) {
+                    if (a->topk_idx) a->topk_idx[((size_t)l * M + m) * K + pos] = e;
+                    if (a->topk_w) a->topk_w[((size_t)l * M + m) * K + pos] = wv;
+                }
+            }
+            before += __popcll(bm);
+        }
     }
     __syncthreads();
-    if (tid < M) {
-        float ss = 0.0f;
-        for (int r = 0; r < kDNRows; ++r) ss += sq[tid * kDNRows + r];
-        stf(sumsq(a, l + 1, cb) + tid, ss);
+    const int has_sh = a->Ds > 0, nsh = has_sh ? a->nseg_s : 0, nsr = a->nseg_r;
+    // union of the selections; register arrays are only indexed by constants
+    unsigned long long U[kEI];
+#pragma unroll
+    for (int i = 0; i < kEI; ++i) {
+        U[i] = 0ull;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+            if (m < M) U[i] |= S.bal[m][i];
     }
-    wg_publish(ctr(a, ctr_ydone(a->L, l)));
+    int ns = has_sh;
+#pragma unroll
+    for (int i = 0; i < kEI; ++i) ns += __popcll(U[i]);
+    if (tid < E) {
+        // expert tid = lane + 64 * wave
+        unsigned long long Bw[MT];
+        unsigned um = 0;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            Bw[m] = m < M ? S.bal[m][wave] : 0ull;
+            um |= (unsigned)((Bw[m] >> lane) & 1ull) << m;
+        }
+        if (um) {
+            int slot = has_sh;
+            unsigned long long Uw = 0ull;
+#pragma unroll
+            for (int q = 0; q < kEI; ++q) {
+                if (q < wave) slot += __popcll(U[q]);
+                if (q == wave) Uw = U[q];
+            }
+            slot += lanes_below(Uw);
+            S.se[slot] = tid;
+            S.sm[slot] = um;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                S.sw[slot][m] = ((um >> m) & 1u) ? wt[m * E + tid] : 0.0f;
+                if ((um >> m) & 1u) {
+                    // expert tid's place in token m's list (ascending id)
+                    int pos = lanes_below(Bw[m]);
+                    for (int q = 0; q < wave; ++q) pos += __popcll(S.bal[m][q]);
+                    for (int sg = 0; sg < nsr; ++sg) S.tsub[m][nsh + pos * nsr + sg] = nsh + (slot - has_sh) * nsr + sg;
+                }
+            }
+        }
+    }
+    if (tid < M) {
+        for (int sg = 0; sg < nsh; ++sg) S.tsub[tid][sg] = sg;
+        if (has_sh) S.sw[0][tid] = 1.0f;
+    }
+    if (tid == 0 && has_sh) {
+        S.se[0] = E;
+        S.sm[0] = (1u << M) - 1u;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(ns);
+}
+
+// ----------------------------------------------------------------- units
+
+// A unit's weights: gate/up units hold the gate row's chunks in w[0..11] and the up
+// row's in w[12..23]; down units hold row c's chunks in w[0..11] and row c + 32's in
+// w[12..23]. sc holds the two rows' scales.
+struct UnitBuf {
+    uint2 w[2 * kNC];
+    float sc[2];
+};
+
+enum { kGU = 0, kDN = 1, kCMB = 2 };
+
+struct UnitRef {
+    int kind;
+    int s;       // slot (gate/up, down)
+    int row0;    // gate/up: the first of its 8 rows
+    int js;      // down: sub-slot
+    int seg;     // down: column segment
+    int cb;      // down, combine: 64-row block
+};
+
+// The layer's unit list: the shared expert's gate/up units, its down units, the routed
+// slots' gate/up units, their down units, then the combine units. The shared expert's
+// units come first so that their place in the list does not depend on the routing.
+struct UnitList {
+    int sh_gu, sh_dn, r_gu, r_dn, U;   // ends of the five ranges
+    int nsub;                           // sub-slots
+};
+
+__device__ __forceinline__ UnitList unit_list(AP a, int ns) {
+    UnitList L;
+    const int has_sh = a->Ds > 0, nr = ns - has_sh;
+    L.sh_gu = has_sh ? a->Ds / 8 : 0;
+    L.sh_dn = L.sh_gu + (has_sh ? a->nseg_s * a->ND : 0);
+    L.r_gu = L.sh_dn + nr * (a->D / 8);
+    L.r_dn = L.r_gu + nr * a->nseg_r * a->ND;
+    L.U = L.r_dn + a->ND;
+    L.nsub = (has_sh ? a->nseg_s : 0) + nr * a->nseg_r;
+    return L;
+}
+
+__device__ __forceinline__ UnitRef decode_unit(AP a, int q, const UnitList &L) {
+    UnitRef u;
+    const int has_sh = a->Ds > 0;
+    u.s = u.row0 = u.js = u.seg = u.cb = 0;
+    if (q < L.sh_gu) {
+        u.kind = kGU;
+        u.row0 = 8 * q;
+    } else if (q < L.sh_dn) {
+        const int r = q - L.sh_gu;
+        u.kind = kDN;
+        u.js = u.seg = r / a->ND;
+        u.cb = r % a->ND;
+    } else if (q < L.r_gu) {
+        const int r = q - L.sh_dn, D8 = a->D / 8;
+        u.kind = kGU;
+        u.s = has_sh + r / D8;
+        u.row0 = 8 * (r % D8);
+    } else if (q < L.r_dn) {
+        const int r = q - L.r_gu, jr = r / a->ND;
+        u.kind = kDN;
+        u.cb = r % a->ND;
+        u.js = (has_sh ? a->nseg_s : 0) + jr;
+        u.s = has_sh + jr / a->nseg_r;
+        u.seg = jr % a->nseg_r;
+    } else {
+        u.kind = kCMB;
+        u.cb = q - L.r_dn;
+    }
+    return u;
+}
+
+// Request a unit's weights. Before the routing is known (pre_route) only the shared
+// expert's units can be loaded.
+__device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf &b, bool pre_route) {
+    if (u.kind == kCMB) return;
+    const moe_layer_weights &w = a->layers[l];
+    const SlotLds &S = slots(a);
+    const int e = pre_route ? a->E : S.se[u.s], tid = ltid(), H = a->H;
+    const bool shared = e == a->E;
+    if (u.kind == kGU) {
+        const int NC = H / 256, j = tid & 31, row = u.row0 + (tid >> 5);
+        const size_t eoff = (size_t)e * a->D;
+        const uint8_t *gp = (shared ? (const uint8_t *)w.sh_gate_w : (const uint8_t *)w.gate_w + eoff * H) +
+                            (size_t)row * H + j * 8;
+        const uint8_t *vp = (shared ? (const uint8_t *)w.sh_up_w : (const uint8_t *)w.up_w + eoff * H) +
+                            (size_t)row * H + j * 8;
+#pragma unroll
+        for (int k = 0; k < kNC; ++k)
+            if (k < NC) b.w[k] = *reinterpret_cast<const uint2 *>(gp + k * 256);
+#pragma unroll
+        for (int k = 0; k < kNC; ++k)
+            if (k < NC) b.w[kNC + k] = *reinterpret_cast<const uint2 *>(vp + k * 256);
+        b.sc[0] = (shared ? w.sh_gate_s : w.gate_s + eoff)[row];
+        b.sc[1] = (shared ? w.sh_up_s : w.up_s + eoff)[row];
+    } else {
+        const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NCd = segF / 64;
+        const int j = tid & 7, c0 = u.cb * 64 + (tid >> 3);
+        const uint8_t *dp = (shared ? (const uint8_t *)w.sh_down_w : (const uint8_t *)w.down_w + (size_t)e * H * a->D) +
+                            (size_t)c0 * F + u.seg * segF + j * 8;
+#pragma unroll
+        for (int k = 0; k < kNC; ++k)
+            if (k < NCd) b.w[k] = *reinterpret_cast<const uint2 *>(dp + k * 64);
+#pragma unroll
+        for (int k = 0; k < kNC; ++k)
+            if (k < NCd) b.w[kNC + k] = *reinterpret_cast<const uint2 *>(dp + (size_t)32 * F + k * 64);
+        const float *ds = shared ? w.sh_down_s : w.down_s + (size_t)e * H;
+        b.sc[0] = ds[c0];
+        b.sc[1] = ds[c0 + 32];
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void slot_tokens(unsigned mask, int (&toks)[MT]) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        toks[t] = mask ? __ffs(mask) - 1 : 0;
+        mask &= mask - 1u;
+    }
+}
+
+// Gate/up unit: 8 rows of the slot's gate and up matrices; half-wave r computes row
+// row0 + r of both (32 lanes, 8 columns of every 256-column chunk per lane).
+template <int MT>
+__device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
+    const SlotLds &S = slots(a);
+    const int H = a->H, NC = H / 256, tid = ltid(), j = tid & 31, row = u.row0 + (tid >> 5);
+    const unsigned mask = S.sm[u.s];
+    const int ntok = __popc(mask);
+    int toks[MT];
+    slot_tokens<MT>(mask, toks);
+    const uint16_t *ul = ulds();
+    float ag[MT], au[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+        if (k < NC) {
+            const uint2 g = b.w[k], v = b.w[kNC + k];
+            const bf16x2 g0 = fp8x2_to_bf16<false>(g.x), g1 = fp8x2_to_bf16<true>(g.x);
+            const bf16x2 g2 = fp8x2_to_bf16<false>(g.y), g3 = fp8x2_to_bf16<true>(g.y);
+            const bf16x2 v0 = fp8x2_to_bf16<false>(v.x), v1 = fp8x2_to_bf16<true>(v.x);
+            const bf16x2 v2 = fp8x2_to_bf16<false>(v.y), v3 = fp8x2_to_bf16<true>(v.y);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < ntok) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(ul + (size_t)toks[t] * H + k * 256 + j * 8);
+                    ag[t] = dot2(g0, as_bf2(xv.x), ag[t]);
+                    ag[t] = dot2(g1, as_bf2(xv.y), ag[t]);
+                    ag[t] = dot2(g2, as_bf2(xv.z), ag[t]);
+                    ag[t] = dot2(g3, as_bf2(xv.w), ag[t]);
+                    au[t] = dot2(v0, as_bf2(xv.x), au[t]);
+                    au[t] = dot2(v1, as_bf2(xv.y), au[t]);
+                    au[t] = dot2(v2, as_bf2(xv.z), au[t]);
+                    au[t] = dot2(v3, as_bf2(xv.w), au[t]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < ntok) {
+            const float gs = half_sum(ag[t]);
+            const float us = half_sum(au[t]);
+            if (j == 16)
+                st64(hact(a, l, u.s, toks[t]) + row,
+                     tagged(__float_as_uint(gelu_tanh(b.sc[0] * gs) * (b.sc[1] * us)), tgt));
+        }
+    }
+}
+
+constexpr int kStage = 8;    // h words per thread per staging round of a down unit
+constexpr int kCmbChunk = 12;   // sub-slot words per poll of a combine unit
+
+// Down unit: rows c0 = 64 cb + (tid >> 3) and c0 + 32 of the slot's down matrix over
+// one column segment (8 lanes per row pair, 8 columns of every 64-column chunk per
+// lane), for the slot's tokens, weighted by their combine weights.
+template <int MT>
+__device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
+    const SlotLds &S = slots(a);
+    const int e = S.se[u.s], tid = ltid(), j = tid & 7;
+    const bool shared = e == a->E;
+    const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NCd = segF / 64;
+    const unsigned mask = S.sm[u.s];
+    const int ntok = __popc(mask);
+    int toks[MT];
+    slot_tokens<MT>(mask, toks);
+    // the slot's h for this segment, [ntok][segF] in LDS, polled until current
+    float *hs = reinterpret_cast<float *>(scratch(a));
+    {
+        const int np = ntok * segF;
+#pragma unroll 1
+        for (int k0 = 0; k0 * kWG < np; k0 += kStage) {
+            float pv[kStage];
+            Poll pl;
+            bool ok;
+            do {
+                uint64_t v[kStage];
+#pragma unroll
+                for (int k = 0; k < kStage; ++k) {
+                    const int i = tid + (k0 + k) * kWG;
+                    if (i < np) {
+                        int t = 0;
+#pragma unroll
+                        for (int tt = 1; tt < MT; ++tt) t += i >= tt * segF;
+                        int m = toks[0];
+#pragma unroll
+                        for (int tt = 1; tt < MT; ++tt) m = t == tt ? toks[tt] : m;
+                        v[k] = ld64(hact(a, l, u.s, m) + u.seg * segF + (i - t * segF));
+                    }
+                }
+                ok = true;
+#pragma unroll
+                for (int k = 0; k < kStage; ++k) {
+                    const int i = tid + (k0 + k) * kWG;
+                    if (i < np) {
+                        pv[k] = __uint_as_float((uint32_t)v[k]);
+                        ok = ok && current(v[k], tgt);
+                    }
+                }
+            } while (!pl.done(a, ok));
+#pragma unroll
+            for (int k = 0; k < kStage; ++k) {
+                const int i = tid + (k0 + k) * kWG;
+                if (i < np) hs[i] = pv[k];
+            }
+        }
+    }
+    __syncthreads();
+    float a0[MT], a1[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) a0[t] = a1[t] = 0.0f;
+    const float4 *hs4 = reinterpret_cast<const float4 *>(hs);
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+        if (k < NCd) {
+            const f32x2 p0 = fp8x2_to_f32<false>(b.w[k].x), p1 = fp8x2_to_f32<true>(b.w[k].x);
+            const f32x2 p2 = fp8x2_to_f32<false>(b.w[k].y), p3 = fp8x2_to_f32<true>(b.w[k].y);
+            const f32x2 q0 = fp8x2_to_f32<false>(b.w[kNC + k].x), q1 = fp8x2_to_f32<true>(b.w[kNC + k].x);
+            const f32x2 q2 = fp8x2_to_f32<false>(b.w[kNC + k].y), q3 = fp8x2_to_f32<true>(b.w[kNC + k].y);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                if (t < ntok) {
+                    const int o = (t * segF + k * 64 + j * 8) / 4;
+                    const float4 h0 = hs4[o], h1 = hs4[o + 1];
+                    float s0 = a0[t], s1 = a1[t];
+                    s0 = fmaf(p0.x, h0.x, s0); s0 = fmaf(p0.y, h0.y, s0);
+                    s0 = fmaf(p1.x, h0.z, s0); s0 = fmaf(p1.y, h0.w, s0);
+                    s0 = fmaf(p2.x, h1.x, s0); s0 = fmaf(p2.y, h1.y, s0);
+                    s0 = fmaf(p3.x, h1.z, s0); s0 = fmaf(p3.y, h1.w, s0);
+                    s1 = fmaf(q0.x, h0.x, s1); s1 = fmaf(q0.y, h0.y, s1);
+                    s1 = fmaf(q1.x, h0.z, s1); s1 = fmaf(q1.y, h0.w, s1);
+                    s1 = fmaf(q2.x, h1.x, s1); s1 = fmaf(q2.y, h1.y, s1);
+                    s1 = fmaf(q3.x, h1.z, s1); s1 = fmaf(q3.y, h1.w, s1);
+                    a0[t] = s0;
+                    a1[t] = s1;
+                }
+            }
+        }
+    }
+    const int c0 = u.cb * 64 + (tid >> 3);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < ntok) {
+            float v0 = quad_sum(a0[t]);
+            v0 += dpp<0x141>(v0);   // row_half_mirror: the two quads of each 8-lane group
+            float v1 = quad_sum(a1[t]);
+            v1 += dpp<0x141>(v1);
+            if (j == 0) {
+                const float cw = S.sw[u.s][toks[t]];
+                uint64_t *yp = ypart(a, l, u.js, toks[t]);
+                st64(yp + c0, tagged(__float_as_uint(cw * (b.sc[0] * v0)), tgt));
+                st64(yp + c0 + 32, tagged(__float_as_uint(cw * (b.sc[1] * v1)), tgt));
+            }
+        }
+    }
+    // hs is reused by the next down unit
+    __syncthreads();
+}
+
+// Combine unit cb: y_l rows = bf16 of the token's sub-slots summed in order;
+// h_{l+1} = bf16(h_l + noise_{l+1} + y_l) (no noise after the last layer). In pass p,
+// thread t owns row 64 cb + (i & 63) of token i >> 6, i = 256 p + t; neighbouring
+// lanes hold a row pair and trade values through DPP.
+template <int MT>
+__device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
+    const SlotLds &S = slots(a);
+    const int M = MT, H = a->H, tid = ltid();
+    const int n = (a->Ds > 0 ? a->nseg_s : 0) + a->K * a->nseg_r;
+    for (int p = 0; p * kWG < M * 64; ++p) {
+        const int i = p * kWG + tid, m = i >> 6, c = cb * 64 + (i & 63);
+        const bool act = m < M, odd = (i & 1) != 0;
+        float s = 0.0f;
+        uint32_t hp = 0;
+        for (int k0 = 0; k0 < n; k0 += kCmbChunk) {
+            // sub-slots k0 .. k0 + 11 (and, with the first chunk, the residual word)
+            float sc = 0.0f;
+            Poll pl;
+            bool ok;
+            do {
+                uint64_t v[kCmbChunk], hv = 0;
+#pragma unroll
+                for (int k = 0; k < kCmbChunk; ++k)
+                    if (act && k0 + k < n) v[k] = ld64(ypart(a, l, S.tsub[m][k0 + k], m) + c);
+                if (act && l > 0 && k0 == 0) hv = ld64(hres(a, l, m) + c / 2);
+                ok = true;
+                sc = s;
+#pragma unroll
+                for (int k = 0; k < kCmbChunk; ++k) {
+                    if (act && k0 + k < n) {
+                        sc += __uint_as_float((uint32_t)v[k]);
+                        ok = ok && current(v[k], tgt);
+                    }
+                }
+                if (act && l > 0 && k0 == 0) {
+                    hp = (uint32_t)hv;
+                    ok = ok && current(hv, tgt);
+                }
+            } while (!pl.done(a, ok));
+            s = sc;
+        }
+        if (act && l == 0) hp = h0_pair(a, m, c / 2);
+        const uint16_t y = f2bf(s);
+        float hv = bf2f(odd ? hp >> 16 : hp & 0xffffu);
+        if (act && l + 1 < a->L) hv += bf2f(a->noise[((size_t)(l + 1) * M + m) * H + c]);
+        const uint16_t hn = f2bf(hv + bf2f(y));
+        // the pair partner's values (quad_perm [1,0,3,2])
+        const uint32_t yo = dppu<0xB1>(y), ho = dppu<0xB1>(hn);
+        if (act && !odd) {
+            if (a->y) *reinterpret_cast<uint32_t *>(a->y + (size_t)l * a->y_ls + (size_t)m * H + c) = pack2(y, (uint16_t)yo);
+            st64(hres(a, l + 1, m) + c / 2, tagged(pack2(hn, (uint16_t)ho), tgt));
+        }
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
+    if (u.kind == kGU) run_gu<MT>(a, l, u, b, tgt);
+    else if (u.kind == kDN) run_dn<MT>(a, l, u, b, tgt);
+    else run_cmb<MT>(a, l, u.cb, tgt);
+}
+
+// Unit workgroup w (0 <= w < GU), layer l: u_l, the routing, then its units w, w + GU,
+// ..., two in flight. A shared-expert unit's weights are requested before the routing
+// is known.
+template <int MT>
+__device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32_t tgt) {
+    const AP a = uniform(a0);
+    norm_to_lds<MT>(a, l, a->gains + (size_t)l * a->H, tgt);
+    // the shared expert's units sit at fixed places at the head of the list
+    const UnitList L0 = unit_list(a, a->Ds > 0 ? 1 : 0);
+    UnitBuf A, B;
+    const bool early = w < L0.sh_dn;
+    if (early) load_unit(a, l, decode_unit(a, w, L0), A, true);
+    const int ns = route_phase<MT>(a, l, tgt, w == 0);
+    const UnitList L = unit_list(a, ns);
+    if (!early && w < L.U) load_unit(a, l, decode_unit(a, w, L), A, false);
+    if (w + GU < L.U) load_unit(a, l, decode_unit(a, w + GU, L), B, false);
+    for (int i = w; i < L.U; i += 2 * GU) {
+        run_unit<MT>(a, l, decode_unit(a, i, L), A, tgt);
+        if (i + 2 * GU < L.U) load_unit(a, l, decode_unit(a, i + 2 * GU, L), A, false);
+        if (i + GU < L.U) {
+            run_unit<MT>(a, l, decode_unit(a, i + GU, L), B, tgt);
+            if (i + 3 * GU < L.U) load_unit(a, l, decode_unit(a, i + 3 * GU, L), B, false);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ lm_head
 
 constexpr int kLmRows = 4;   // rows per lane (same column chunk)
 
-__device__ __forceinline__ void item_lm(AP a0, int i) {
-    const AP a = uniform(a0);
-    const int H = a->H, hv = H / 8, M = a->M, NC = H / 256, tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6, g = lane >> 4, li = lane & 15;
-    const int rbase = i * kLmRowsPerWG + wave * 16 + g * kLmRows;
-    const uint8_t *wr = a->lm_w + (size_t)rbase * H + li * 16;
-    uint4 pre[kLmRows];
-#pragma unroll
-    for (int r = 0; r < kLmRows; ++r) pre[r] = *reinterpret_cast<const uint4 *>(wr + (size_t)r * H);
-    wg_wait(a, ctr(a, ctr_ydone(a->L, a->L - 1)), a->ND);
+struct LmBuf {
+    uint4 q[kLmRows];
+};
 
-    // x_f = bf16(h_L * rsqrt(mean h_L^2 + eps) * g_L), staged in LDS
-    uint32_t *xw = reinterpret_cast<uint32_t *>(smem);              // [M][H/2] bf16 pairs
-    float *rs = reinterpret_cast<float *>(xw + (size_t)M * (H / 2));  // [M]
-    float *tmp = rs + kMaxM;                                          // [ND][M]
-    for (int j = tid; j < a->ND * M; j += kWG) tmp[(j / M) * kMaxM + j % M] = ldf(sumsq(a, a->L, j / M) + j % M);
-    __syncthreads();
-    if (tid < M) {
-        float ss = 0.0f;
-        for (int cb = 0; cb < a->ND; ++cb) ss += tmp[cb * kMaxM + tid];
-        rs[tid] = rsqrtf(ss / (float)H + a->eps);
+template <int MT>
+struct LmAcc {
+    float acc[kLmRows][MT];
+    float sc[kLmRows];
+    unsigned long long best[MT];
+};
+
+// step st of this workgroup's row stream: 64-row unit u0 + st / NC, chunk st % NC
+__device__ __forceinline__ void lm_load(AP a, int u0, int nst, int st, LmBuf &b) {
+    if (st < nst) {
+        const int t = ltid(), NC = a->H / 256, lane = t & 63, wave = t >> 6;
+        const int unit = u0 + st / NC, k = st % NC;
+        const size_t row = (size_t)unit * 64 + wave * 16 + (lane >> 4) * kLmRows;
+        const uint8_t *p = a->lm_w + row * a->H + k * 256 + (lane & 15) * 16;
+#pragma unroll
+        for (int r = 0; r < kLmRows; ++r) b.q[r] = *reinterpret_cast<const uint4 *>(p + (size_t)r * a->H);
     }
-    __syncthreads();
-    const uint16_t *gL = a->gains + (size_t)a->L * H;
-    {
-        // M * H / 4 quads of h_L: thread tid takes quads tid, tid + 256, ...
-        const int hq = H / 4, nq = M * hq;
-        uint64_t v[kMaxM * kQuadsPerThread];
+}
+
+template <int MT>
+__device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmBuf &b, LmAcc<MT> &A) {
+    if (st >= nst) return;
+    const int tid = ltid(), H = a->H, NC = H / 256, M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
+    const int k = st % NC;
+    const uint16_t *xl = ulds();
+    bf16x2 wv[kLmRows][8];
 #pragma unroll
-        for (int k = 0; k < kMaxM * kQuadsPerThread; ++k) {
-            const int j = tid + k * kWG;
-            if (j < nq) v[k] = ld64(hres(a, a->L, j / hq) + 4 * (j % hq));
+    for (int r = 0; r < kLmRows; ++r) decode16_bf16(b.q[r], wv[r]);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < M) {
+            const uint4 *xs = reinterpret_cast<const uint4 *>(xl + (size_t)t * H + k * 256 + li * 16);
+            const uint4 x0 = xs[0], x1 = xs[1];
+#pragma unroll
+            for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = dot16(wv[r], x0, x1, A.acc[r][t]);
         }
+    }
+    if (k == NC - 1) {
+        const int unit = u0 + st / NC;
+        const int row = unit * 64 + wave * 16 + (lane >> 4) * kLmRows;
 #pragma unroll
-        for (int k = 0; k < kMaxM * kQuadsPerThread; ++k) {
-            const int j = tid + k * kWG;
-            if (j < nq) {
-                const int m = j / hq, c = 4 * (j % hq);
-                uint16_t xq[4];
+        for (int r = 0; r < kLmRows; ++r) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    xq[u] = f2bf(bf2f((uint32_t)(v[k] >> (16 * u)) & 0xffffu) * rs[m] * bf2f(gL[c + u]));
-                const uint32_t p0 = pack2(xq[0], xq[1]), p1 = pack2(xq[2], xq[3]);
-                xw[2 * j] = p0;
-                xw[2 * j + 1] = p1;
-                if (i == 0 && a->x_final) {
-                    uint32_t *xo = reinterpret_cast<uint32_t *>(a->x_final + (size_t)m * H + c);
-                    xo[0] = p0;
-                    xo[1] = p1;
+            for (int t = 0; t < MT; ++t) {
+                if (t < M) {
+                    const float lgv = A.sc[r] * row16_sum(A.acc[r][t]);
+                    const unsigned long long key = ((unsigned long long)ordered(lgv) << 32) |
+                                                   (unsigned long long)(0xffffffffu - (uint32_t)(row + r));
+                    A.best[t] = key > A.best[t] ? key : A.best[t];
                 }
+                A.acc[r][t] = 0.0f;
             }
         }
-    }
-    __syncthreads();
-    const uint4 *xs4 = reinterpret_cast<const uint4 *>(xw);
-    float acc[kLmRows][kMaxM];
+        if (st + 1 < nst) {   // the next unit's scales
 #pragma unroll
-    for (int r = 0; r < kLmRows; ++r)
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t) acc[r][t] = 0.0f;
-    for (int k = 0; k < NC; ++k) {
-        uint4 qv[kLmRows];
-#pragma unroll
-        for (int r = 0; r < kLmRows; ++r)
-            qv[r] = (k == 0) ? pre[r] : *reinterpret_cast<const uint4 *>(wr + (size_t)r * H + (size_t)k * 256);
-        bf16x2 wv[kLmRows][8];
-#pragma unroll
-        for (int r = 0; r < kLmRows; ++r) decode16_bf16(qv[r], wv[r]);
-        const int xv = (k * 256 + li * 16) / 8;
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t) {
-            if (t < M) {
-                const uint4 x0 = xs4[t * hv + xv], x1 = xs4[t * hv + xv + 1];
-#pragma unroll
-                for (int r = 0; r < kLmRows; ++r) acc[r][t] = dot16(wv[r], x0, x1, acc[r][t]);
-            }
+            for (int r = 0; r < kLmRows; ++r) A.sc[r] = a->lm_s[row + 64 + r];
         }
     }
-    unsigned long long best[kMaxM];
+}
+
+template <int MT>
+__device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
+    const AP a = uniform(a0);
+    const int H = a->H, M = MT, NC = H / 256, tid = ltid(), lane = tid & 63, wave = tid >> 6;
+    const int u0 = (int)((long long)w * a->NLU / G), u1 = (int)((long long)(w + 1) * a->NLU / G);
+    const int nst = (u1 - u0) * NC;
+    LmBuf b0, b1, b2;
+    lm_load(a, u0, nst, 0, b0);
+    lm_load(a, u0, nst, 1, b1);
+    lm_load(a, u0, nst, 2, b2);
+    LmAcc<MT> A;
 #pragma unroll
-    for (int t = 0; t < kMaxM; ++t) best[t] = 0ull;
+    for (int t = 0; t < MT; ++t) {
+        A.best[t] = 0ull;
 #pragma unroll
-    for (int r = 0; r < kLmRows; ++r) {
-        const int v = rbase + r;
-        const float sc = a->lm_s[v];
-#pragma unroll
-        for (int t = 0; t < kMaxM; ++t) {
-            if (t < M) {
-                const float lg = sc * row16_sum(acc[r][t]);
-                const unsigned long long key =
-                    ((unsigned long long)ordered(lg) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)v);
-                best[t] = key > best[t] ? key : best[t];
-            }
-        }
+        for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = 0.0f;
     }
-    // reduce the 16 lane groups of the workgroup, then one atomic max per token into
-    // this item's group slot
+#pragma unroll
+    for (int r = 0; r < kLmRows; ++r) A.sc[r] = 0.0f;
+    if (nst > 0) {
+        const int row = u0 * 64 + wave * 16 + (lane >> 4) * kLmRows;
+#pragma unroll
+        for (int r = 0; r < kLmRows; ++r) A.sc[r] = a->lm_s[row + r];
+    }
+    norm_to_lds<MT>(a, a->L, a->gains + (size_t)a->L * H, tgt);
+    if (w == 0 && a->x_final) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(ulds());
+        uint4 *dst = reinterpret_cast<uint4 *>(a->x_final);
+        for (int i = tid; i < M * H / 8; i += kWG) dst[i] = src[i];
+    }
+    for (int st = 0; st < nst; st += 3) {
+        lm_step<MT>(a, u0, nst, st, b0, A);
+        lm_load(a, u0, nst, st + 3, b0);
+        lm_step<MT>(a, u0, nst, st + 1, b1, A);
+        lm_load(a, u0, nst, st + 4, b1);
+        lm_step<MT>(a, u0, nst, st + 2, b2, A);
+        lm_load(a, u0, nst, st + 5, b2);
+    }
+    // the workgroup's best per token: 16 lane groups, then one key per token
+    unsigned long long *gb = reinterpret_cast<unsigned long long *>(scratch(a));   // [16][MT]
+    if ((lane & 15) == 0) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) gb[(wave * 4 + (lane >> 4)) * kMaxM + t] = A.best[t];
+    }
     __syncthreads();
-    unsigned long long *gb = reinterpret_cast<unsigned long long *>(smem);  // [16][M]
-    if (li == 0)
-        for (int t = 0; t < M; ++t) gb[(wave * 4 + g) * kMaxM + t] = best[t];
-    __syncthreads();
-    const int grp = i % kLmGroups;
     if (tid < M) {
         unsigned long long bk = gb[tid];
         for (int k = 1; k < 16; ++k) bk = gb[k * kMaxM + tid] > bk ? gb[k * kMaxM + tid] : bk;
-        __hip_atomic_fetch_max(lmkey(a, grp, tid), bk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        st64(lmbest(a, w) + tid, bk);
     }
-    const int in_grp = (a->NLM - grp + kLmGroups - 1) / kLmGroups;
-    if (wg_publish(ctr(a, kLmSub + grp)) != in_grp - 1) return;
-    const int ngroups = min(a->NLM, kLmGroups);
-    if (wg_publish(ctr(a, kLmTop)) != ngroups - 1) return;
+    publish(flags(a) + a->f_lm + w, tgt);
+    if (w != 0) return;
+
+    // workgroup 0: every workgroup's keys -> tokens, greedy acceptance, next epoch
+    wait_flags(a, flags(a) + a->f_lm, G, tgt);
+    unsigned long long kb[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) kb[t] = 0ull;
+    for (int i0 = 0; i0 < G; i0 += kWG) {
+        const int i = i0 + tid;
+        if (i < G) {
+            uint64_t v[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                if (t < M) v[t] = ld64(lmbest(a, i) + t);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+                if (t < M) kb[t] = v[t] > kb[t] ? v[t] : kb[t];
+        }
+    }
+    __syncthreads();
+    unsigned long long *wb = reinterpret_cast<unsigned long long *>(scratch(a));   // [4][MT]
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        if (t < M) {
+            const unsigned long long v = wave_max_key(kb[t]);
+            if (lane == 0) wb[wave * kMaxM + t] = v;
+        }
+    }
+    __syncthreads();
     if (tid == 0) {
-        int tok[kMaxM];
+        int tok[MT];
         for (int t = 0; t < M; ++t) {
-            unsigned long long key = 0ull;
-            for (int q = 0; q < ngroups; ++q) {
-                const unsigned long long kq =
-                    __hip_atomic_load(lmkey(a, q, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                key = kq > key ? kq : key;
-            }
+            unsigned long long key = wb[t];
+            for (int q = 1; q < 4; ++q) key = wb[q * kMaxM + t] > key ? wb[q * kMaxM + t] : key;
             tok[t] = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
             a->token[t] = tok[t];
             if (a->max_logit) a->max_logit[t] = unordered((uint32_t)(key >> 32));
@@ -903,6 +1125,7 @@ __device__ __forceinline__ void item_lm(AP a0, int i) {
         while (n < gamma && a->draft[n] == tok[n]) ++n;
         for (int t = 0; t < M; ++t) a->out_tokens[t] = t <= n ? tok[t] : -1;
         *a->accepted = n;
+        st32(flags(a) + a->f_epoch, tgt);   // every workgroup has read the epoch by now
     }
 }
 
@@ -911,71 +1134,95 @@ __device__ __forceinline__ void item_lm(AP a0, int i) {
 #ifndef MOE_STEP_MIN_BLOCKS
 #define MOE_STEP_MIN_BLOCKS 2
 #endif
+template <int MT>
 __global__ __launch_bounds__(256, MOE_STEP_MIN_BLOCKS) void k_step(StepArgs args) {
     (void)args;
     const AP base = (AP)__builtin_amdgcn_kernarg_segment_ptr();
-    for (int t = blockIdx.x;; t += gridDim.x) {
-        // The argument pointer is made opaque each iteration so that argument fields
-        // are re-read by each item instead of being held in registers across items.
-        AP a = base;
-        asm volatile("" : "+s"(a));
-        const int T = a->T, L = a->L, P = a->P, NB = a->NB, S = a->S, NG = a->NG, ND = a->ND;
-        if (t >= T) break;
-        if (t < L * P) {
-            const int l = t / P, i = t % P;
-            if (i < NB) {
-                item_router(a, l, i);
-            } else if (i < NB + S * NG) {
-                const int j = i - NB;
-                item_gateup(a, l, j / NG, j % NG);
-            } else {
-                const int j = i - NB - S * NG;
-                item_down(a, l, j / ND, j % ND);
-            }
-        } else {
-            item_lm(a, t - L * P);
+    const int w = blockIdx.x, G = gridDim.x, GU = G - base->NR;
+    const uint32_t tgt = __builtin_amdgcn_readfirstlane(ld32(flags(base) + base->f_epoch)) + 1u;
+    if (w >= GU) {
+        // router workgroup: each layer's weights are requested as soon as the previous
+        // layer's logits are out
+        uint4 wq[kNC];
+        router_load(base, 0, w - GU, wq);
+        for (int l = 0;; ++l) {
+            AP a = base;
+            asm volatile("" : "+s"(a));
+            if (l >= a->L) break;
+            router_phase<MT>(a, l, w - GU, wq, tgt);
+            if (l + 1 < a->L) router_load(a, l + 1, w - GU, wq);
         }
-        __syncthreads();
+    } else {
+        for (int l = 0;; ++l) {
+            // The argument pointer is made opaque each layer so that argument fields are
+            // re-read by each phase instead of being held in registers across phases.
+            AP a = base;
+            asm volatile("" : "+s"(a));
+            if (l >= a->L) break;
+            expert_phase<MT>(a, l, w, GU, tgt);
+        }
     }
-    // the last workgroup to leave returns every counter to zero for the next step
-    const AP a = base;
-    if (wg_publish(ctr(a, kExit)) != (int)gridDim.x - 1) return;
-    const int nctr = a->nctr;
-    for (int i = threadIdx.x; i < nctr; i += kWG)
-        if (i != kError) st32(ctr(a, i), 0u);
-    for (int i = threadIdx.x; i < kLmGroups * kMaxM; i += kWG)
-        __hip_atomic_store(lmkey(a, i / kMaxM, i % kMaxM), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    AP a = base;
+    asm volatile("" : "+s"(a));
+    lm_phase<MT>(a, w, G, tgt);
+}
+
+// Router weights [H][E] -> [E][H] (once, at prepare time).
+__global__ void k_router_transpose(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst, int H, int E) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)H * E) return;
+    const int e = (int)(i / H), h = (int)(i % H);
+    dst[i] = src[(size_t)h * E + e];
 }
 
 inline hipStream_t Sm(void *p) { return reinterpret_cast<hipStream_t>(p); }
 
-size_t step_lds_bytes(const moe_step_desc &d, const StepWs &W) {
-    const int H = d.layer.hidden, Mx = d.max_tokens;
-    size_t router = sizeof(float) * (kMaxM * kRouterRows + kMaxM + 2 * kWG * kMaxM);
-    size_t topk = sizeof(float) * kMaxM * kMaxExperts + 2 * sizeof(int) * kMaxM * kMaxTopK + 16;
-    size_t gu = (size_t)Mx * H * 2 + sizeof(float) * 2 * kGURows * kMaxM;
-    // a slot of width F stages min(ntok, kDownLdsBytes / (4 F)) tokens of h
-    size_t dn = std::min((size_t)Mx * W.F * 4, (size_t)kDownLdsBytes);
-    size_t comb = sizeof(unsigned) * kMaxSlots + sizeof(int) * (kMaxM * (kMaxTopK + 1) + kMaxM) +
-                  sizeof(float) * kMaxM * kDNRows;
-    size_t lm = (size_t)Mx * H * 2 + sizeof(float) * (kMaxM + (size_t)W.ND * kMaxM);
-    size_t mx = router;
-    for (size_t v : {topk, gu, dn, comb, lm, (size_t)16 * kMaxM * 8}) mx = v > mx ? v : mx;
-    return (mx + 15) & ~(size_t)15;
+// Every workgroup must be resident at once (units wait on other workgroups' units): the
+// grid is the occupancy of the step kernel for M tokens times the compute units.
+template <int MT>
+int launch_mt(const StepArgs &a, size_t lds, int NR, void *stream) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<MT>, kWG, lds) != hipSuccess || per_cu < 1)
+        return MOE_ELAUNCH;
+    const int grid = std::min(cus * per_cu, kStepMaxGrid);
+    if (grid <= NR) return MOE_ELAUNCH;   // the last NR workgroups only route
+    hipLaunchKernelGGL(k_step<MT>, dim3(grid), dim3(kWG), lds, Sm(stream), a);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+size_t step_lds_bytes(const moe_step_desc &d, const StepWs &W, int *l_scr, int *l_slot) {
+    const int H = d.layer.hidden, Mx = d.max_tokens, E = d.layer.num_experts;
+    const size_t u = ((size_t)Mx * H * 2 + 15) & ~(size_t)15;
+    size_t scr = (size_t)Mx * W.segFmax * 4;
+    scr = std::max(scr, (size_t)Mx * E * 4);
+    scr = std::max(scr, (size_t)16 * kMaxM * 8);
+    scr = (scr + 15) & ~(size_t)15;
+    *l_scr = (int)u;
+    *l_slot = (int)(u + scr);
+    return u + scr + ((sizeof(SlotLds) + 15) & ~(size_t)15);
 }
 
 }  // namespace
 
-int step_prepare(const StepWs &W, const moe_layer_weights *layers, char *ws) {
+int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weights *layers, char *ws) {
     if (hipMemset(ws, 0, W.total) != hipSuccess) return MOE_ELAUNCH;
     if (hipMemcpy(ws + W.table, layers, sizeof(moe_layer_weights) * W.L, hipMemcpyHostToDevice) != hipSuccess)
         return MOE_ELAUNCH;
+    const int H = ld.hidden, E = ld.num_experts;
+    const size_t n = (size_t)H * E;
+    for (int l = 0; l < W.L; ++l) {
+        hipLaunchKernelGGL(k_router_transpose, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr,
+                           layers[l].router_w, reinterpret_cast<uint16_t *>(ws + W.rt) + (size_t)l * n, H, E);
+        if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    }
     return hipDeviceSynchronize() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
 int step_status(const StepWs &W, char *ws) {
     int err = 0;
-    char *flag = ws + W.ctr + sizeof(int) * kCtrStride * kError;
+    char *flag = ws + W.ctr + sizeof(int) * kCtrStride * kErrCtr;
     if (hipMemcpy(&err, flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ELAUNCH;
     if (!err) return MOE_OK;
     const int zero = 0;
@@ -992,6 +1239,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     const moe_layer_desc &ld = d.layer;
     StepArgs a{};
     a.layers = reinterpret_cast<const moe_layer_weights *>(ws + W.table);
+    a.rt = reinterpret_cast<const uint16_t *>(ws + W.rt);
     a.gains = gains;
     a.x = x;
     a.noise = noise;
@@ -1002,24 +1250,21 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.max_logit = max_logit;
     a.accepted = accepted_len;
     a.out_tokens = out_tokens;
-    a.y = y_layers ? y_layers : reinterpret_cast<uint16_t *>(ws + W.y);
-    a.y_ls = y_layers ? (size_t)M * ld.hidden : (size_t)W.Mx * ld.hidden;
+    a.y = y_layers;
+    a.y_ls = (size_t)M * ld.hidden;
     a.topk_idx = topk_idx;
     a.topk_w = topk_w;
     a.x_final = x_final;
     a.ws = ws;
     a.o_ctr = W.ctr;
-    a.o_lmkey = W.lmkey;
+    a.o_flags = W.flags;
+    a.o_logits = W.logits;
     a.o_hres = W.hres;
-    a.o_u = W.u;
-    a.o_sumsq = W.sumsq;
-    a.o_partial = W.partial;
-    a.o_nslots = W.nslots;
-    a.o_sexp = W.slot_expert;
-    a.o_smask = W.slot_mask;
-    a.o_sw = W.slot_w;
-    a.o_h = W.h;
+    a.o_hact = W.hact;
     a.o_ypart = W.ypart;
+    a.o_lmbest = W.lmbest;
+    a.f_lm = W.f_lm;
+    a.f_epoch = W.f_epoch;
     a.M = M;
     a.Mx = W.Mx;
     a.H = ld.hidden;
@@ -1027,33 +1272,31 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.K = ld.top_k;
     a.D = ld.expert_width;
     a.Ds = ld.shared_width;
-    a.F = W.F;
     a.L = d.num_layers;
     a.V = d.vocab;
-    a.S = max_slots(M, ld.top_k, ld.num_experts, ld.shared_width);
     a.Sx = W.Sx;
-    a.NB = W.NB;
-    a.NG = W.F / kGURows;
+    a.NR = W.NR;
     a.ND = W.ND;
-    a.NLM = d.vocab / kLmRowsPerWG;
-    a.P = a.NB + a.S * a.NG + a.S * a.ND;
-    a.T = a.L * a.P + a.NLM;
-    a.nctr = W.nctr;
+    a.NSUBx = W.NSUBx;
+    a.Fmax = W.F;
+    a.nseg_r = W.nseg_r;
+    a.nseg_s = W.nseg_s;
+    a.NLU = d.vocab / 64;
     a.eps = d.eps;
     a.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpin;
 
-    // every workgroup must be resident at once (items wait on other workgroups'
-    // items): the grid is the occupancy of this kernel times the compute units
-    const size_t lds = step_lds_bytes(d, W);
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step, kWG, lds) != hipSuccess || per_cu < 1)
-        return MOE_ELAUNCH;
-    int grid = cus * per_cu;
-    if (grid > a.T) grid = a.T;
-    hipLaunchKernelGGL(k_step, dim3(grid), dim3(kWG), lds, Sm(stream), a);
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+    const size_t lds = step_lds_bytes(d, W, &a.l_scr, &a.l_slot);
+    switch (M) {   // one kernel per token count: token loops are unrolled exactly
+    case 1: return launch_mt<1>(a, lds, W.NR, stream);
+    case 2: return launch_mt<2>(a, lds, W.NR, stream);
+    case 3: return launch_mt<3>(a, lds, W.NR, stream);
+    case 4: return launch_mt<4>(a, lds, W.NR, stream);
+    case 5: return launch_mt<5>(a, lds, W.NR, stream);
+    case 6: return launch_mt<6>(a, lds, W.NR, stream);
+    case 7: return launch_mt<7>(a, lds, W.NR, stream);
+    case 8: return launch_mt<8>(a, lds, W.NR, stream);
+    default: return MOE_EINVAL;
+    }
 }
 
 }  // namespace moe
