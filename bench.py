@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=8, help="oracle sample: layers per step")
     ap.add_argument("--cpu-steps", type=int, default=40, help="oracle sample: steps")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
+                    help="only run a plain device-to-device copy of MB megabytes 5 times (a known "
+                         "byte count for calibrating hardware traffic counters) and exit")
     ap.add_argument("--path", choices=("fused", "layers"), default="fused",
                     help="fused: one moe_decode_step launch per step; layers: per-layer entry points "
                          "captured in a HIP graph per step")
@@ -61,6 +64,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
+        return
     import synth
     from fine_grained_moe_router_amd import budget, native
     from fine_grained_moe_router_amd.stack import DecodeStack, FusedDecodeStep

@@ -717,52 +717,40 @@ __device__ __forceinline__ void slot_tokens(unsigned mask, int (&toks)[MT]) {
 }
 
 // Gate/up unit: 8 rows of the slot's gate and up matrices; half-wave r computes row
-// row0 + r of both (32 lanes, 8 columns of every 256-column chunk per lane).
+// row0 + r of both (32 lanes, 8 columns of every 256-column chunk per lane). Tokens are
+// taken one at a time in a loop (the FP8 codes are decoded again per token: one
+// instruction per pair) so that the code does not grow with the token count.
 template <int MT>
 __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
     const SlotLds &S = slots(a);
     const int H = a->H, NC = H / 256, tid = ltid(), j = tid & 31, row = u.row0 + (tid >> 5);
-    const unsigned mask = S.sm[u.s];
-    const int ntok = __popc(mask);
-    int toks[MT];
-    slot_tokens<MT>(mask, toks);
     const uint16_t *ul = ulds();
-    float ag[MT], au[MT];
+    unsigned mm = S.sm[u.s];
+#pragma unroll 1
+    while (mm) {
+        const int m = __ffs(mm) - 1;
+        mm &= mm - 1u;
+        float ag = 0.0f, au = 0.0f;
+        const uint16_t *um = ul + (size_t)m * H + j * 8;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) ag[t] = au[t] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-        if (k < NC) {
-            const uint2 g = b.w[k], v = b.w[kNC + k];
-            const bf16x2 g0 = fp8x2_to_bf16<false>(g.x), g1 = fp8x2_to_bf16<true>(g.x);
-            const bf16x2 g2 = fp8x2_to_bf16<false>(g.y), g3 = fp8x2_to_bf16<true>(g.y);
-            const bf16x2 v0 = fp8x2_to_bf16<false>(v.x), v1 = fp8x2_to_bf16<true>(v.x);
-            const bf16x2 v2 = fp8x2_to_bf16<false>(v.y), v3 = fp8x2_to_bf16<true>(v.y);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if (t < ntok) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(ul + (size_t)toks[t] * H + k * 256 + j * 8);
-                    ag[t] = dot2(g0, as_bf2(xv.x), ag[t]);
-                    ag[t] = dot2(g1, as_bf2(xv.y), ag[t]);
-                    ag[t] = dot2(g2, as_bf2(xv.z), ag[t]);
-                    ag[t] = dot2(g3, as_bf2(xv.w), ag[t]);
-                    au[t] = dot2(v0, as_bf2(xv.x), au[t]);
-                    au[t] = dot2(v1, as_bf2(xv.y), au[t]);
-                    au[t] = dot2(v2, as_bf2(xv.z), au[t]);
-                    au[t] = dot2(v3, as_bf2(xv.w), au[t]);
-                }
+        for (int k = 0; k < kNC; ++k) {
+            if (k < NC) {
+                const uint2 g = b.w[k], v = b.w[kNC + k];
+                const uint4 xv = *reinterpret_cast<const uint4 *>(um + k * 256);
+                ag = dot2(fp8x2_to_bf16<false>(g.x), as_bf2(xv.x), ag);
+                ag = dot2(fp8x2_to_bf16<true>(g.x), as_bf2(xv.y), ag);
+                ag = dot2(fp8x2_to_bf16<false>(g.y), as_bf2(xv.z), ag);
+                ag = dot2(fp8x2_to_bf16<true>(g.y), as_bf2(xv.w), ag);
+                au = dot2(fp8x2_to_bf16<false>(v.x), as_bf2(xv.x), au);
+                au = dot2(fp8x2_to_bf16<true>(v.x), as_bf2(xv.y), au);
+                au = dot2(fp8x2_to_bf16<false>(v.y), as_bf2(xv.z), au);
+                au = dot2(fp8x2_to_bf16<true>(v.y), as_bf2(xv.w), au);
             }
         }
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t < ntok) {
-            const float gs = half_sum(ag[t]);
-            const float us = half_sum(au[t]);
-            if (j == 16)
-                st64(hact(a, l, u.s, toks[t]) + row,
-                     tagged(__float_as_uint(gelu_tanh(b.sc[0] * gs) * (b.sc[1] * us)), tgt));
-        }
+        const float gs = half_sum(ag);
+        const float us = half_sum(au);
+        if (j == 16)
+            st64(hact(a, l, u.s, m) + row, tagged(__float_as_uint(gelu_tanh(b.sc[0] * gs) * (b.sc[1] * us)), tgt));
     }
 }
 
@@ -824,52 +812,44 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
         }
     }
     __syncthreads();
-    float a0[MT], a1[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) a0[t] = a1[t] = 0.0f;
     const float4 *hs4 = reinterpret_cast<const float4 *>(hs);
-#pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-        if (k < NCd) {
-            const f32x2 p0 = fp8x2_to_f32<false>(b.w[k].x), p1 = fp8x2_to_f32<true>(b.w[k].x);
-            const f32x2 p2 = fp8x2_to_f32<false>(b.w[k].y), p3 = fp8x2_to_f32<true>(b.w[k].y);
-            const f32x2 q0 = fp8x2_to_f32<false>(b.w[kNC + k].x), q1 = fp8x2_to_f32<true>(b.w[kNC + k].x);
-            const f32x2 q2 = fp8x2_to_f32<false>(b.w[kNC + k].y), q3 = fp8x2_to_f32<true>(b.w[kNC + k].y);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                if (t < ntok) {
-                    const int o = (t * segF + k * 64 + j * 8) / 4;
-                    const float4 h0 = hs4[o], h1 = hs4[o + 1];
-                    float s0 = a0[t], s1 = a1[t];
-                    s0 = fmaf(p0.x, h0.x, s0); s0 = fmaf(p0.y, h0.y, s0);
-                    s0 = fmaf(p1.x, h0.z, s0); s0 = fmaf(p1.y, h0.w, s0);
-                    s0 = fmaf(p2.x, h1.x, s0); s0 = fmaf(p2.y, h1.y, s0);
-                    s0 = fmaf(p3.x, h1.z, s0); s0 = fmaf(p3.y, h1.w, s0);
-                    s1 = fmaf(q0.x, h0.x, s1); s1 = fmaf(q0.y, h0.y, s1);
-                    s1 = fmaf(q1.x, h0.z, s1); s1 = fmaf(q1.y, h0.w, s1);
-                    s1 = fmaf(q2.x, h1.x, s1); s1 = fmaf(q2.y, h1.y, s1);
-                    s1 = fmaf(q3.x, h1.z, s1); s1 = fmaf(q3.y, h1.w, s1);
-                    a0[t] = s0;
-                    a1[t] = s1;
-                }
-            }
-        }
-    }
     const int c0 = u.cb * 64 + (tid >> 3);
+#pragma unroll 1
+    for (int t = 0; t < ntok; ++t) {
+        const int m = toks[0];
+        float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t < ntok) {
-            float v0 = quad_sum(a0[t]);
-            v0 += dpp<0x141>(v0);   // row_half_mirror: the two quads of each 8-lane group
-            float v1 = quad_sum(a1[t]);
-            v1 += dpp<0x141>(v1);
-            if (j == 0) {
-                const float cw = S.sw[u.s][toks[t]];
-                uint64_t *yp = ypart(a, l, u.js, toks[t]);
-                st64(yp + c0, tagged(__float_as_uint(cw * (b.sc[0] * v0)), tgt));
-                st64(yp + c0 + 32, tagged(__float_as_uint(cw * (b.sc[1] * v1)), tgt));
+        for (int k = 0; k < kNC; ++k) {
+            if (k < NCd) {
+                const f32x2 p0 = fp8x2_to_f32<false>(b.w[k].x), p1 = fp8x2_to_f32<true>(b.w[k].x);
+                const f32x2 p2 = fp8x2_to_f32<false>(b.w[k].y), p3 = fp8x2_to_f32<true>(b.w[k].y);
+                const f32x2 q0 = fp8x2_to_f32<false>(b.w[kNC + k].x), q1 = fp8x2_to_f32<true>(b.w[kNC + k].x);
+                const f32x2 q2 = fp8x2_to_f32<false>(b.w[kNC + k].y), q3 = fp8x2_to_f32<true>(b.w[kNC + k].y);
+                const int o = (t * segF + k * 64 + j * 8) / 4;
+                const float4 h0 = hs4[o], h1 = hs4[o + 1];
+                s0 = fmaf(p0.x, h0.x, s0); s0 = fmaf(p0.y, h0.y, s0);
+                s0 = fmaf(p1.x, h0.z, s0); s0 = fmaf(p1.y, h0.w, s0);
+                s0 = fmaf(p2.x, h1.x, s0); s0 = fmaf(p2.y, h1.y, s0);
+                s0 = fmaf(p3.x, h1.z, s0); s0 = fmaf(p3.y, h1.w, s0);
+                s1 = fmaf(q0.x, h0.x, s1); s1 = fmaf(q0.y, h0.y, s1);
+                s1 = fmaf(q1.x, h0.z, s1); s1 = fmaf(q1.y, h0.w, s1);
+                s1 = fmaf(q2.x, h1.x, s1); s1 = fmaf(q2.y, h1.y, s1);
+                s1 = fmaf(q3.x, h1.z, s1); s1 = fmaf(q3.y, h1.w, s1);
             }
         }
+        float v0 = quad_sum(s0);
+        v0 += dpp<0x141>(v0);   // row_half_mirror: the two quads of each 8-lane group
+        float v1 = quad_sum(s1);
+        v1 += dpp<0x141>(v1);
+        if (j == 0) {
+            const float cw = S.sw[u.s][m];
+            uint64_t *yp = ypart(a, l, u.js, m);
+            st64(yp + c0, tagged(__float_as_uint(cw * (b.sc[0] * v0)), tgt));
+            st64(yp + c0 + 32, tagged(__float_as_uint(cw * (b.sc[1] * v1)), tgt));
+        }
+        // the next token of the slot
+#pragma unroll
+        for (int q = 0; q + 1 < MT; ++q) toks[q] = toks[q + 1];
     }
     // hs is reused by the next down unit
     __syncthreads();
@@ -938,8 +918,10 @@ __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const Un
 }
 
 // Unit workgroup w (0 <= w < GU), layer l: u_l, the routing, then its units w, w + GU,
-// ..., two in flight. A shared-expert unit's weights are requested before the routing
-// is known.
+// ..., two in flight (about 45 MB requested across the chip; a measured sweep of
+// scattered 45 KB reads on MI355X peaks at one to two units per workgroup and loses a
+// third of the bandwidth at three). A shared-expert unit's weights are requested
+// before the routing is known.
 template <int MT>
 __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32_t tgt) {
     const AP a = uniform(a0);
