@@ -30,6 +30,39 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
+ROOT = os.path.dirname(os.path.abspath(__file__))
+STEP_SOURCE = os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", "step.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_step_traffic.txt")
+
+
+def step_source_hash():
+    import hashlib
+    with open(STEP_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(M):
+    """HBM bytes per k_step launch at M tokens from the committed hardware-counter
+    summary (FETCH_SIZE and WRITE_SIZE, each from its own rocprofv3 --pmc run, scaled by
+    the factors a plain copy of known size gives), or None when there is no summary for
+    this M or the kernel source has changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha, scale, rows = None, {}, {}
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "source_sha256":
+            sha = f[1]
+        elif f[0] == "scale":
+            scale = dict(kv.split("=") for kv in f[1:])
+        elif f[0].startswith("M="):
+            rows[int(f[0][2:])] = dict(kv.split("=") for kv in f[1:])
+    if sha != step_source_hash() or M not in rows or not scale:
+        return None
+    r = rows[M]
+    return int(float(r["fetch_kib"]) * 1024 * float(scale["fetch"]) + float(r["write_kib"]) * 1024 * float(scale["write"]))
 
 
 def parse():
@@ -179,7 +212,7 @@ def main():
         # the step is one kernel launch: its average duration over the timed region
         roofline = {"bound": "hbm", "kernel": "k_step (moe_decode_step, M=%d)" % M0,
                     "achieved": round(head["hbm_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(head["hbm_frac"], 4), "traffic": None,
+                    "frac": round(head["hbm_frac"], 4), "traffic": measured_traffic(M0),
                     "bytes_per_launch": int(head["bytes_per_step"]),
                     "avg_launch_us": round(head["ms_per_step"] * 1e3, 2)}
     else:

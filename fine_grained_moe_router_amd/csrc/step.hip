@@ -490,26 +490,37 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
                 }
             } while (!pl.done(a, ok));
         }
-        uint64_t key[kEI];
+        // K rounds: the largest remaining ordered logit over the wave (DPP maximum),
+        // then the lowest expert id holding it (ballots in ascending id order)
+        uint32_t o[kEI];
         bool sel[kEI];
 #pragma unroll
         for (int i = 0; i < kEI; ++i) {
-            const int e = lane + 64 * i;
-            key[i] = e < E ? ((uint64_t)ordered(lgv[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+            o[i] = lane + 64 * i < E ? ordered(lgv[i]) : 0u;
             sel[i] = false;
         }
         float lmax = 0.0f;
         for (int k = 0; k < K; ++k) {
-            uint64_t best = key[0];
+            uint32_t v = o[0];
 #pragma unroll
-            for (int i = 1; i < kEI; ++i) best = key[i] > best ? key[i] : best;
-            const uint64_t W = wave_max_key(best);
-            if (k == 0) lmax = unordered((uint32_t)(W >> 32));
+            for (int i = 1; i < kEI; ++i) v = max(v, o[i]);
+            v = max(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
+            v = max(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
+            v = max(v, dppu<0x141>(v));   // row_half_mirror
+            v = max(v, dppu<0x140>(v));   // row_mirror
+            const uint32_t W = max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                                   max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+            if (k == 0) lmax = unordered(W);
+            bool found = false;
 #pragma unroll
             for (int i = 0; i < kEI; ++i) {
-                if (key[i] == W) {
-                    sel[i] = true;
-                    key[i] = 0ull;
+                const unsigned long long bm = __ballot(o[i] == W);
+                if (!found && bm) {
+                    found = true;
+                    if (lane == __ffsll((long long)bm) - 1) {
+                        sel[i] = true;
+                        o[i] = 0u;
+                    }
                 }
             }
         }
@@ -732,19 +743,23 @@ __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const Unit
         mm &= mm - 1u;
         float ag = 0.0f, au = 0.0f;
         const uint16_t *um = ul + (size_t)m * H + j * 8;
+        // the decode scale is opaque per token, so the decoded weights are not hoisted
+        // out of the token loop (holding them would cost 88 registers and occupancy)
+        float one = 1.0f;
+        asm volatile("" : "+v"(one));
 #pragma unroll
         for (int k = 0; k < kNC; ++k) {
             if (k < NC) {
                 const uint2 g = b.w[k], v = b.w[kNC + k];
                 const uint4 xv = *reinterpret_cast<const uint4 *>(um + k * 256);
-                ag = dot2(fp8x2_to_bf16<false>(g.x), as_bf2(xv.x), ag);
-                ag = dot2(fp8x2_to_bf16<true>(g.x), as_bf2(xv.y), ag);
-                ag = dot2(fp8x2_to_bf16<false>(g.y), as_bf2(xv.z), ag);
-                ag = dot2(fp8x2_to_bf16<true>(g.y), as_bf2(xv.w), ag);
-                au = dot2(fp8x2_to_bf16<false>(v.x), as_bf2(xv.x), au);
-                au = dot2(fp8x2_to_bf16<true>(v.x), as_bf2(xv.y), au);
-                au = dot2(fp8x2_to_bf16<false>(v.y), as_bf2(xv.z), au);
-                au = dot2(fp8x2_to_bf16<true>(v.y), as_bf2(xv.w), au);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, false), as_bf2(xv.x), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, true), as_bf2(xv.y), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, false), as_bf2(xv.z), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, true), as_bf2(xv.w), ag);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, false), as_bf2(xv.x), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, true), as_bf2(xv.y), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, false), as_bf2(xv.z), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, true), as_bf2(xv.w), au);
             }
         }
         const float gs = half_sum(ag);
@@ -818,13 +833,17 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
     for (int t = 0; t < ntok; ++t) {
         const int m = toks[0];
         float s0 = 0.0f, s1 = 0.0f;
+        int zero = 0;   // opaque per token: the decoded weights stay inside the loop
+        asm volatile("" : "+v"(zero));
 #pragma unroll
         for (int k = 0; k < kNC; ++k) {
             if (k < NCd) {
-                const f32x2 p0 = fp8x2_to_f32<false>(b.w[k].x), p1 = fp8x2_to_f32<true>(b.w[k].x);
-                const f32x2 p2 = fp8x2_to_f32<false>(b.w[k].y), p3 = fp8x2_to_f32<true>(b.w[k].y);
-                const f32x2 q0 = fp8x2_to_f32<false>(b.w[kNC + k].x), q1 = fp8x2_to_f32<true>(b.w[kNC + k].x);
-                const f32x2 q2 = fp8x2_to_f32<false>(b.w[kNC + k].y), q3 = fp8x2_to_f32<true>(b.w[kNC + k].y);
+                const uint32_t wx = b.w[k].x | zero, wy = b.w[k].y | zero;
+                const uint32_t vx = b.w[kNC + k].x | zero, vy = b.w[kNC + k].y | zero;
+                const f32x2 p0 = fp8x2_to_f32<false>(wx), p1 = fp8x2_to_f32<true>(wx);
+                const f32x2 p2 = fp8x2_to_f32<false>(wy), p3 = fp8x2_to_f32<true>(wy);
+                const f32x2 q0 = fp8x2_to_f32<false>(vx), q1 = fp8x2_to_f32<true>(vx);
+                const f32x2 q2 = fp8x2_to_f32<false>(vy), q3 = fp8x2_to_f32<true>(vy);
                 const int o = (t * segF + k * 64 + j * 8) / 4;
                 const float4 h0 = hs4[o], h1 = hs4[o + 1];
                 s0 = fmaf(p0.x, h0.x, s0); s0 = fmaf(p0.y, h0.y, s0);
