@@ -70,19 +70,20 @@ inline size_t lm_ws_bytes(int M, int V) {
 // ---------------------------------------------------------------- fused step
 
 constexpr int kMaxLayers = 64;
-constexpr int kStepMaxHidden = 3072;  // the fused step keeps 12 256-column chunks of a row per lane
-constexpr int kStepMaxWidth = 768;    // routed expert width: one 64-row down unit covers a whole row
+constexpr int kStepChunks = 11;       // the fused step's rows: 11 chunks (256 columns of H, 64 of a down row)
+constexpr int kStepMaxHidden = kStepChunks * 256;   // 2816: a row of H per lane group, zero-padded
+constexpr int kStepMaxWidth = kStepChunks * 64;     // 704: one 64-row down unit covers a whole routed row
 constexpr int kStepMaxSharedSeg = 8;  // column segments of the shared expert's down rows
 constexpr int kStepMaxGrid = 2048;    // persistent workgroups
 constexpr int kCtrStride = 16;        // ints between counters (64 bytes)
 constexpr unsigned kDefaultSpin = 1u << 18;   // about a quarter second of polling
 
 // Column segments of a down row of width F: the fewest that divide the F / 64 chunks
-// into at most 12 chunks each.
+// into at most kStepChunks chunks each.
 inline int step_nseg(int F) {
     if (F <= 0) return 0;
     const int c = F / 64;
-    for (int n = (c + 11) / 12; n < c; ++n)
+    for (int n = (c + kStepChunks - 1) / kStepChunks; n < c; ++n)
         if (c % n == 0) return n;
     return c;
 }

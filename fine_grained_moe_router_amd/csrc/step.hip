@@ -81,13 +81,22 @@ struct StepArgs {
 };
 
 constexpr int kWG = 256;
-constexpr int kNC = kStepMaxHidden / 256;       // 12: 256-column chunks of a row of H
-constexpr int kW = kStepMaxHidden / 2 / kWG;    // 6: residual words (2 x bf16) of a row per thread
+constexpr int kNC = kStepChunks;                // 256-column chunks of a row of H (router, lm_head)
+constexpr int kPc = 6;                          // 16-byte pieces of a unit row per lane
+constexpr int kUS = kPc * 32 * 16;              // 3072: LDS row stride of u (bf16); columns H.. hold zeros
+constexpr int kDS = kPc * 8 * 16;               // 768: LDS row stride of a down unit's staged h (fp32)
+constexpr int kW = (kUS / 2 + kWG - 1) / kWG;   // residual words (2 x bf16) of a row per thread
+static_assert(kUS >= kStepMaxHidden && kDS >= kStepMaxWidth, "unit rows must fit the padded LDS rows");
 
 // The phase functions are inlined into the kernel and read the kernel arguments on
 // demand through a pointer into the kernel-argument segment, made opaque to the
 // optimiser per layer so that argument fields are not held in registers across phases.
 typedef const __attribute__((address_space(4))) StepArgs *AP;
+// The weight-pointer table, read through the constant address space: it is written
+// before the launch and never during it, so its fields load through the scalar cache
+// and a use of them never waits on the vector loads in flight.
+typedef const __attribute__((address_space(4))) moe_layer_weights *WP;
+__device__ __forceinline__ WP layer_w(AP a, int l) { return (WP)(a->layers) + l; }
 
 __device__ __forceinline__ AP uniform(AP p) {
     const unsigned long long v = (unsigned long long)p;
@@ -97,6 +106,20 @@ __device__ __forceinline__ AP uniform(AP p) {
 }
 
 extern __shared__ __align__(16) char smem[];
+
+// Every access to device memory goes through the global address space: the pointers
+// here arrive as generic pointers (from the argument block and the weight table), and
+// generic (flat) accesses also count against the LDS wait counter, so an LDS wait would
+// otherwise wait for weight loads and hand-off stores still in flight.
+#define GAS __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ GAS T *glb(T *p) { return (GAS T *)p; }
+// A 16-byte load through the global address space.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16(const void *p) {
+    const u32x4 v = *(const GAS u32x4 *)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // The thread index, made opaque so that values derived from it are formed where a
 // phase needs them rather than hoisted out of the layer loop and kept live (in
@@ -110,16 +133,16 @@ __device__ __forceinline__ int ltid() {
 // -------------------------------------------------------- coherent hand-off access
 
 __device__ __forceinline__ void st32(void *p, uint32_t v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(glb(reinterpret_cast<uint32_t *>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st64(void *p, uint64_t v) {
-    __hip_atomic_store(reinterpret_cast<uint64_t *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(glb(reinterpret_cast<uint64_t *>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t ld32(const void *p) {
-    return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(glb(reinterpret_cast<const uint32_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t ld64(const void *p) {
-    return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(glb(reinterpret_cast<const uint64_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Hand-off words are read with these atomic loads: a plain load can hit a line that the
 // reading XCD's L2 still holds from before the write (the L2s of different XCDs are not
@@ -168,7 +191,7 @@ struct SlotLds {
 };
 
 __device__ __forceinline__ SlotLds &slots(AP a) { return *reinterpret_cast<SlotLds *>(smem + a->l_slot); }
-__device__ __forceinline__ uint16_t *ulds() { return reinterpret_cast<uint16_t *>(smem); }   // [M][H] bf16
+__device__ __forceinline__ uint16_t *ulds() { return reinterpret_cast<uint16_t *>(smem); }   // [M][kUS] bf16
 __device__ __forceinline__ char *scratch(AP a) { return smem + a->l_scr; }
 
 // ------------------------------------------------------------ polling
@@ -289,8 +312,8 @@ __device__ __forceinline__ int lanes_below(unsigned long long m) {
 
 // h_0 = bf16(x + noise_0) for the pair of columns (2 word, 2 word + 1) of token m
 __device__ __forceinline__ uint32_t h0_pair(AP a, int m, int word) {
-    const uint32_t xv = *reinterpret_cast<const uint32_t *>(a->x + (size_t)m * a->H + 2 * word);
-    const uint32_t nv = *reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * a->H + 2 * word);
+    const uint32_t xv = *glb(reinterpret_cast<const uint32_t *>(a->x + (size_t)m * a->H + 2 * word));
+    const uint32_t nv = *glb(reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * a->H + 2 * word));
     return pack2(f2bf(bf2f(xv & 0xffffu) + bf2f(nv & 0xffffu)), f2bf(bf2f(xv >> 16) + bf2f(nv >> 16)));
 }
 
@@ -298,12 +321,14 @@ __device__ __forceinline__ uint32_t h0_pair(AP a, int m, int word) {
 // LDS. h_0 comes from the inputs; h_l (l >= 1) from the residual words, polled until
 // current, four tokens at a time. Thread t owns words t, t+256, ... of every token and
 // the sums of squares are reduced in a fixed order, so every workgroup forms
-// bit-identical u. h is staged in the u area and rewritten in place.
+// bit-identical u. h is staged in the u area and rewritten in place; the columns from H
+// to the row stride are zeroed, so unit and router loops can run over whole padded
+// rows without bounds checks.
 constexpr int kNormTok = 4;
 template <int MT>
 __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint32_t tgt) {
     const int H = a->H, M = MT, tid = ltid(), hw = H / 2, lane = tid & 63, wave = tid >> 6;
-    uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][H/2] bf16 pairs
+    uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][kUS/2] bf16 pairs
     float ss[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) ss[m] = 0.0f;
@@ -319,8 +344,8 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
                 for (int k = 0; k < kW; ++k) {
                     const int m = m0 + mm, q = tid + k * kWG;
                     if (m < M && q < hw) {
-                        xv[mm][k] = *reinterpret_cast<const uint32_t *>(a->x + (size_t)m * H + 2 * q);
-                        nv[mm][k] = *reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * H + 2 * q);
+                        xv[mm][k] = *glb(reinterpret_cast<const uint32_t *>(a->x + (size_t)m * H + 2 * q));
+                        nv[mm][k] = *glb(reinterpret_cast<const uint32_t *>(a->noise + (size_t)m * H + 2 * q));
                     }
                 }
 #pragma unroll
@@ -364,7 +389,7 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
                     const float f0 = bf2f(hp[mm][k] & 0xffffu), f1 = bf2f(hp[mm][k] >> 16);
                     ss[m0 + mm] = fmaf(f0, f0, ss[m0 + mm]);
                     ss[m0 + mm] = fmaf(f1, f1, ss[m0 + mm]);
-                    uw[(size_t)m * hw + q] = hp[mm][k];
+                    uw[m * (kUS / 2) + q] = hp[mm][k];
                 }
             }
         }
@@ -386,11 +411,13 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
             for (int k = 0; k < kW; ++k) {
                 const int q = tid + k * kWG;
                 if (q < hw) {
-                    const uint32_t gv = *reinterpret_cast<const uint32_t *>(g + 2 * q);
-                    const uint32_t hv = uw[(size_t)m * hw + q];
+                    const uint32_t gv = *glb(reinterpret_cast<const uint32_t *>(g + 2 * q));
+                    const uint32_t hv = uw[m * (kUS / 2) + q];
                     const uint16_t u0 = f2bf(bf2f(hv & 0xffffu) * r * bf2f(gv & 0xffffu));
                     const uint16_t u1 = f2bf(bf2f(hv >> 16) * r * bf2f(gv >> 16));
-                    uw[(size_t)m * hw + q] = pack2(u0, u1);
+                    uw[m * (kUS / 2) + q] = pack2(u0, u1);
+                } else if (q < kUS / 2) {
+                    uw[m * (kUS / 2) + q] = 0u;
                 }
             }
         }
@@ -401,14 +428,15 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
 // ------------------------------------------------------------------ router
 
 // Router workgroup j's weights for layer l: experts 8j .. 8j+7, one half-wave (32
-// lanes) per expert, each lane 8 bf16 of every 256-column chunk of the expert's row.
+// lanes) per expert, each lane 8 bf16 of every 256-column chunk of the expert's row
+// (zeros past H).
 __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]) {
     const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
     const int e = min(8 * j + (tid >> 5), E - 1);
     const uint16_t *wr = a->rt + ((size_t)l * E + e) * H + (tid & 31) * 8;
 #pragma unroll
     for (int k = 0; k < kNC; ++k)
-        if (k < NC) wq[k] = *reinterpret_cast<const uint4 *>(wr + k * 256);
+        wq[k] = k < NC ? ld16(wr + k * 256) : make_uint4(0u, 0u, 0u, 0u);
 }
 
 // Router workgroup j, layer l: u_l, then the logits of experts 8j .. 8j+7 for every
@@ -416,7 +444,7 @@ __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]
 template <int MT>
 __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&wq)[kNC], uint32_t tgt) {
     const AP a = uniform(a0);
-    const int H = a->H, E = a->E, M = MT, NC = H / 256, tid = ltid(), lane32 = tid & 31;
+    const int H = a->H, E = a->E, M = MT, tid = ltid(), lane32 = tid & 31;
     const int e = 8 * j + (tid >> 5);
     const bool valid = e < E;
     norm_to_lds<MT>(a, l, a->gains + (size_t)l * H, tgt);
@@ -424,23 +452,25 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    int off = lane32 * 8;   // this lane's columns of the token's row of u
 #pragma unroll
-    for (int k = 0; k < kNC; ++k) {
-        if (k < NC) {
+    for (int m = 0; m < MT; ++m) {
+        // one token's row at a time: its kNC reads are issued together; the row offset
+        // depends on the previous token's sum, so the next token's reads are not hoisted
+        // into this one's registers
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                if (m < M) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(u + (size_t)m * H + k * 256 + lane32 * 8);
-                    acc[m] = dot2(as_bf2(wq[k].x), as_bf2(xv.x), acc[m]);
-                    acc[m] = dot2(as_bf2(wq[k].y), as_bf2(xv.y), acc[m]);
-                    acc[m] = dot2(as_bf2(wq[k].z), as_bf2(xv.z), acc[m]);
-                    acc[m] = dot2(as_bf2(wq[k].w), as_bf2(xv.w), acc[m]);
-                }
-            }
+        for (int k = 0; k < kNC; ++k) {
+            const uint4 xv = *reinterpret_cast<const uint4 *>(u + off + k * 256);
+            acc[m] = dot2(as_bf2(wq[k].x), as_bf2(xv.x), acc[m]);
+            acc[m] = dot2(as_bf2(wq[k].y), as_bf2(xv.y), acc[m]);
+            acc[m] = dot2(as_bf2(wq[k].z), as_bf2(xv.z), acc[m]);
+            acc[m] = dot2(as_bf2(wq[k].w), as_bf2(xv.w), acc[m]);
         }
+        off += kUS;
+        asm volatile("" : "+v"(off) : "v"(acc[m]));
     }
-    const float *bias = a->layers[l].router_bias;
-    const float bv = (bias && valid) ? bias[e] : 0.0f;
+    const float *bias = layer_w(a, l)->router_bias;
+    const float bv = (bias && valid) ? glb(bias)[e] : 0.0f;
     uint64_t *lg = logits(a, l);
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -541,8 +571,8 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
                 const float wv = ev[i] / z;
                 wt[m * E + e] = wv;
                 if (outputs) {
-                    if (a->topk_idx) a->topk_idx[((size_t)l * M + m) * K + pos] = e;
-                    if (a->topk_w) a->topk_w[((size_t)l * M + m) * K + pos] = wv;
+                    if (a->topk_idx) glb(a->topk_idx)[((size_t)l * M + m) * K + pos] = e;
+                    if (a->topk_w) glb(a->topk_w)[((size_t)l * M + m) * K + pos] = wv;
                 }
             }
             before += __popcll(bm);
@@ -608,11 +638,13 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
 
 // ----------------------------------------------------------------- units
 
-// A unit's weights: gate/up units hold the gate row's chunks in w[0..11] and the up
-// row's in w[12..23]; down units hold row c's chunks in w[0..11] and row c + 32's in
-// w[12..23]. sc holds the two rows' scales.
+// A unit's weights, 16-byte pieces (16 FP8 codes) per lane: gate/up units hold pieces
+// j, j + 32, ... of the gate row in w[0..kPc) and of the up row in w[kPc..2kPc) (32
+// lanes per row); down units hold pieces j, j + 8, ... of row c in w[0..kPc) and of row
+// c + 32 in w[kPc..2kPc) (8 lanes per row pair). Pieces past the row are zero. sc holds
+// the two rows' scales.
 struct UnitBuf {
-    uint2 w[2 * kNC];
+    uint4 w[2 * kPc];
     float sc[2];
 };
 
@@ -682,39 +714,40 @@ __device__ __forceinline__ UnitRef decode_unit(AP a, int q, const UnitList &L) {
 // expert's units can be loaded.
 __device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf &b, bool pre_route) {
     if (u.kind == kCMB) return;
-    const moe_layer_weights &w = a->layers[l];
+    const WP wp = layer_w(a, l);
     const SlotLds &S = slots(a);
-    const int e = pre_route ? a->E : S.se[u.s], tid = ltid(), H = a->H;
+    // the unit's expert is the same for the whole workgroup
+    const int e = __builtin_amdgcn_readfirstlane(pre_route ? a->E : S.se[u.s]), tid = ltid(), H = a->H;
     const bool shared = e == a->E;
+    // Pieces past the end of a row re-read the row's last piece: they meet the zero
+    // columns past the row in the LDS copy of u or h, and a single unconditional 16-byte
+    // load per piece keeps the loads free of per-lane branches.
     if (u.kind == kGU) {
-        const int NC = H / 256, j = tid & 31, row = u.row0 + (tid >> 5);
+        const int NP = H / 16, j = tid & 31, row = u.row0 + (tid >> 5);
         const size_t eoff = (size_t)e * a->D;
-        const uint8_t *gp = (shared ? (const uint8_t *)w.sh_gate_w : (const uint8_t *)w.gate_w + eoff * H) +
-                            (size_t)row * H + j * 8;
-        const uint8_t *vp = (shared ? (const uint8_t *)w.sh_up_w : (const uint8_t *)w.up_w + eoff * H) +
-                            (size_t)row * H + j * 8;
+        const uint4 *gp = reinterpret_cast<const uint4 *>(
+            (shared ? (const uint8_t *)wp->sh_gate_w : (const uint8_t *)wp->gate_w + eoff * H) + (size_t)row * H);
+        const uint4 *vp = reinterpret_cast<const uint4 *>(
+            (shared ? (const uint8_t *)wp->sh_up_w : (const uint8_t *)wp->up_w + eoff * H) + (size_t)row * H);
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
-            if (k < NC) b.w[k] = *reinterpret_cast<const uint2 *>(gp + k * 256);
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(gp + min(j + 32 * i, NP - 1));
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
-            if (k < NC) b.w[kNC + k] = *reinterpret_cast<const uint2 *>(vp + k * 256);
-        b.sc[0] = (shared ? w.sh_gate_s : w.gate_s + eoff)[row];
-        b.sc[1] = (shared ? w.sh_up_s : w.up_s + eoff)[row];
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(vp + min(j + 32 * i, NP - 1));
+        b.sc[0] = *glb((shared ? wp->sh_gate_s : wp->gate_s + eoff) + row);
+        b.sc[1] = *glb((shared ? wp->sh_up_s : wp->up_s + eoff) + row);
     } else {
-        const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NCd = segF / 64;
+        const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NP = segF / 16;
         const int j = tid & 7, c0 = u.cb * 64 + (tid >> 3);
-        const uint8_t *dp = (shared ? (const uint8_t *)w.sh_down_w : (const uint8_t *)w.down_w + (size_t)e * H * a->D) +
-                            (size_t)c0 * F + u.seg * segF + j * 8;
+        const uint8_t *dp = (shared ? (const uint8_t *)wp->sh_down_w : (const uint8_t *)wp->down_w + (size_t)e * H * a->D) +
+                            (size_t)c0 * F + u.seg * segF;
+        const uint4 *d0 = reinterpret_cast<const uint4 *>(dp), *d1 = reinterpret_cast<const uint4 *>(dp + (size_t)32 * F);
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
-            if (k < NCd) b.w[k] = *reinterpret_cast<const uint2 *>(dp + k * 64);
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(d0 + min(j + 8 * i, NP - 1));
 #pragma unroll
-        for (int k = 0; k < kNC; ++k)
-            if (k < NCd) b.w[kNC + k] = *reinterpret_cast<const uint2 *>(dp + (size_t)32 * F + k * 64);
-        const float *ds = shared ? w.sh_down_s : w.down_s + (size_t)e * H;
-        b.sc[0] = ds[c0];
-        b.sc[1] = ds[c0 + 32];
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(d1 + min(j + 8 * i, NP - 1));
+        const float *ds = shared ? wp->sh_down_s : wp->down_s + (size_t)e * H;
+        b.sc[0] = *glb(ds + c0);
+        b.sc[1] = *glb(ds + c0 + 32);
     }
 }
 
@@ -728,13 +761,13 @@ __device__ __forceinline__ void slot_tokens(unsigned mask, int (&toks)[MT]) {
 }
 
 // Gate/up unit: 8 rows of the slot's gate and up matrices; half-wave r computes row
-// row0 + r of both (32 lanes, 8 columns of every 256-column chunk per lane). Tokens are
-// taken one at a time in a loop (the FP8 codes are decoded again per token: one
+// row0 + r of both (32 lanes, 16 columns of every 512-column stretch per lane). Tokens
+// are taken one at a time in a loop (the FP8 codes are decoded again per token: one
 // instruction per pair) so that the code does not grow with the token count.
 template <int MT>
 __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
     const SlotLds &S = slots(a);
-    const int H = a->H, NC = H / 256, tid = ltid(), j = tid & 31, row = u.row0 + (tid >> 5);
+    const int tid = ltid(), j = tid & 31, row = u.row0 + (tid >> 5);
     const uint16_t *ul = ulds();
     unsigned mm = S.sm[u.s];
 #pragma unroll 1
@@ -742,25 +775,32 @@ __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const Unit
         const int m = __ffs(mm) - 1;
         mm &= mm - 1u;
         float ag = 0.0f, au = 0.0f;
-        const uint16_t *um = ul + (size_t)m * H + j * 8;
+        const uint16_t *um = ul + m * kUS + j * 16;
         // the decode scale is opaque per token, so the decoded weights are not hoisted
         // out of the token loop (holding them would cost 88 registers and occupancy)
         float one = 1.0f;
         asm volatile("" : "+v"(one));
 #pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-            if (k < NC) {
-                const uint2 g = b.w[k], v = b.w[kNC + k];
-                const uint4 xv = *reinterpret_cast<const uint4 *>(um + k * 256);
-                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, false), as_bf2(xv.x), ag);
-                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, true), as_bf2(xv.y), ag);
-                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, false), as_bf2(xv.z), ag);
-                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, true), as_bf2(xv.w), ag);
-                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, false), as_bf2(xv.x), au);
-                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, true), as_bf2(xv.y), au);
-                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, false), as_bf2(xv.z), au);
-                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, true), as_bf2(xv.w), au);
-            }
+        for (int i = 0; i < kPc; ++i) {
+            const uint4 g = b.w[i], v = b.w[kPc + i];
+            const uint4 x0 = *reinterpret_cast<const uint4 *>(um + i * 512);
+            const uint4 x1 = *reinterpret_cast<const uint4 *>(um + i * 512 + 8);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, false), as_bf2(x0.x), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, true), as_bf2(x0.y), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, false), as_bf2(x0.z), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, true), as_bf2(x0.w), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.z, one, false), as_bf2(x1.x), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.z, one, true), as_bf2(x1.y), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.w, one, false), as_bf2(x1.z), ag);
+            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.w, one, true), as_bf2(x1.w), ag);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, false), as_bf2(x0.x), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, true), as_bf2(x0.y), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, false), as_bf2(x0.z), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, true), as_bf2(x0.w), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, one, false), as_bf2(x1.x), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, one, true), as_bf2(x1.y), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, one, false), as_bf2(x1.z), au);
+            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, one, true), as_bf2(x1.w), au);
         }
         const float gs = half_sum(ag);
         const float us = half_sum(au);
@@ -773,19 +813,20 @@ constexpr int kStage = 8;    // h words per thread per staging round of a down u
 constexpr int kCmbChunk = 12;   // sub-slot words per poll of a combine unit
 
 // Down unit: rows c0 = 64 cb + (tid >> 3) and c0 + 32 of the slot's down matrix over
-// one column segment (8 lanes per row pair, 8 columns of every 64-column chunk per
+// one column segment (8 lanes per row pair, 16 columns of every 128-column stretch per
 // lane), for the slot's tokens, weighted by their combine weights.
 template <int MT>
 __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
     const SlotLds &S = slots(a);
     const int e = S.se[u.s], tid = ltid(), j = tid & 7;
     const bool shared = e == a->E;
-    const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NCd = segF / 64;
+    const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r);
     const unsigned mask = S.sm[u.s];
     const int ntok = __popc(mask);
     int toks[MT];
     slot_tokens<MT>(mask, toks);
-    // the slot's h for this segment, [ntok][segF] in LDS, polled until current
+    // the slot's h for this segment, [ntok][kDS] in LDS (zeros past segF), polled until
+    // current
     float *hs = reinterpret_cast<float *>(scratch(a));
     {
         const int np = ntok * segF;
@@ -822,7 +863,19 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
 #pragma unroll
             for (int k = 0; k < kStage; ++k) {
                 const int i = tid + (k0 + k) * kWG;
-                if (i < np) hs[i] = pv[k];
+                if (i < np) {
+                    int t = 0;
+#pragma unroll
+                    for (int tt = 1; tt < MT; ++tt) t += i >= tt * segF;
+                    hs[t * kDS + (i - t * segF)] = pv[k];
+                }
+            }
+        }
+        if (segF < kDS) {
+            const int pad = kDS - segF;
+            for (int i = tid; i < ntok * pad; i += kWG) {
+                const int t = i / pad;
+                hs[t * kDS + segF + (i - t * pad)] = 0.0f;
             }
         }
     }
@@ -836,24 +889,22 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
         int zero = 0;   // opaque per token: the decoded weights stay inside the loop
         asm volatile("" : "+v"(zero));
 #pragma unroll
-        for (int k = 0; k < kNC; ++k) {
-            if (k < NCd) {
-                const uint32_t wx = b.w[k].x | zero, wy = b.w[k].y | zero;
-                const uint32_t vx = b.w[kNC + k].x | zero, vy = b.w[kNC + k].y | zero;
-                const f32x2 p0 = fp8x2_to_f32<false>(wx), p1 = fp8x2_to_f32<true>(wx);
-                const f32x2 p2 = fp8x2_to_f32<false>(wy), p3 = fp8x2_to_f32<true>(wy);
-                const f32x2 q0 = fp8x2_to_f32<false>(vx), q1 = fp8x2_to_f32<true>(vx);
-                const f32x2 q2 = fp8x2_to_f32<false>(vy), q3 = fp8x2_to_f32<true>(vy);
-                const int o = (t * segF + k * 64 + j * 8) / 4;
-                const float4 h0 = hs4[o], h1 = hs4[o + 1];
-                s0 = fmaf(p0.x, h0.x, s0); s0 = fmaf(p0.y, h0.y, s0);
-                s0 = fmaf(p1.x, h0.z, s0); s0 = fmaf(p1.y, h0.w, s0);
-                s0 = fmaf(p2.x, h1.x, s0); s0 = fmaf(p2.y, h1.y, s0);
-                s0 = fmaf(p3.x, h1.z, s0); s0 = fmaf(p3.y, h1.w, s0);
-                s1 = fmaf(q0.x, h0.x, s1); s1 = fmaf(q0.y, h0.y, s1);
-                s1 = fmaf(q1.x, h0.z, s1); s1 = fmaf(q1.y, h0.w, s1);
-                s1 = fmaf(q2.x, h1.x, s1); s1 = fmaf(q2.y, h1.y, s1);
-                s1 = fmaf(q3.x, h1.z, s1); s1 = fmaf(q3.y, h1.w, s1);
+        for (int i = 0; i < kPc; ++i) {
+            // piece j + 8 i of both rows: columns 16 (j + 8 i) .. + 15 of the segment
+            const float4 *hp = hs4 + (t * kDS + i * 128 + j * 16) / 4;
+            const float4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
+            const uint32_t wv[4] = {b.w[i].x | zero, b.w[i].y | zero, b.w[i].z | zero, b.w[i].w | zero};
+            const uint32_t vv[4] = {b.w[kPc + i].x | zero, b.w[kPc + i].y | zero, b.w[kPc + i].z | zero,
+                                    b.w[kPc + i].w | zero};
+            const float4 hq[4] = {h0, h1, h2, h3};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x2 p0 = fp8x2_to_f32<false>(wv[q]), p1 = fp8x2_to_f32<true>(wv[q]);
+                const f32x2 q0 = fp8x2_to_f32<false>(vv[q]), q1 = fp8x2_to_f32<true>(vv[q]);
+                s0 = fmaf(p0.x, hq[q].x, s0); s0 = fmaf(p0.y, hq[q].y, s0);
+                s0 = fmaf(p1.x, hq[q].z, s0); s0 = fmaf(p1.y, hq[q].w, s0);
+                s1 = fmaf(q0.x, hq[q].x, s1); s1 = fmaf(q0.y, hq[q].y, s1);
+                s1 = fmaf(q1.x, hq[q].z, s1); s1 = fmaf(q1.y, hq[q].w, s1);
             }
         }
         float v0 = quad_sum(s0);
@@ -918,12 +969,12 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
         if (act && l == 0) hp = h0_pair(a, m, c / 2);
         const uint16_t y = f2bf(s);
         float hv = bf2f(odd ? hp >> 16 : hp & 0xffffu);
-        if (act && l + 1 < a->L) hv += bf2f(a->noise[((size_t)(l + 1) * M + m) * H + c]);
+        if (act && l + 1 < a->L) hv += bf2f(glb(a->noise)[((size_t)(l + 1) * M + m) * H + c]);
         const uint16_t hn = f2bf(hv + bf2f(y));
         // the pair partner's values (quad_perm [1,0,3,2])
         const uint32_t yo = dppu<0xB1>(y), ho = dppu<0xB1>(hn);
         if (act && !odd) {
-            if (a->y) *reinterpret_cast<uint32_t *>(a->y + (size_t)l * a->y_ls + (size_t)m * H + c) = pack2(y, (uint16_t)yo);
+            if (a->y) *glb(reinterpret_cast<uint32_t *>(a->y + (size_t)l * a->y_ls + (size_t)m * H + c)) = pack2(y, (uint16_t)yo);
             st64(hres(a, l + 1, m) + c / 2, tagged(pack2(hn, (uint16_t)ho), tgt));
         }
     }
@@ -931,16 +982,20 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
 
 template <int MT>
 __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
-    if (u.kind == kGU) run_gu<MT>(a, l, u, b, tgt);
-    else if (u.kind == kDN) run_dn<MT>(a, l, u, b, tgt);
-    else run_cmb<MT>(a, l, u.cb, tgt);
+    if (u.kind == kGU) {
+        run_gu<MT>(a, l, u, b, tgt);
+    } else if (u.kind == kDN) {
+        run_dn<MT>(a, l, u, b, tgt);
+    } else {
+        run_cmb<MT>(a, l, u.cb, tgt);
+    }
 }
 
 // Unit workgroup w (0 <= w < GU), layer l: u_l, the routing, then its units w, w + GU,
 // ..., two in flight (about 45 MB requested across the chip; a measured sweep of
-// scattered 45 KB reads on MI355X peaks at one to two units per workgroup and loses a
-// third of the bandwidth at three). A shared-expert unit's weights are requested
-// before the routing is known.
+// expert-shaped 45 KB reads on MI355X holds 6-6.7 TB/s at one or two units per
+// workgroup, and deeper prefetch loses bandwidth once the units carry compute). A
+// shared-expert unit's weights are requested before the routing is known.
 template <int MT>
 __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32_t tgt) {
     const AP a = uniform(a0);
@@ -987,14 +1042,14 @@ __device__ __forceinline__ void lm_load(AP a, int u0, int nst, int st, LmBuf &b)
         const size_t row = (size_t)unit * 64 + wave * 16 + (lane >> 4) * kLmRows;
         const uint8_t *p = a->lm_w + row * a->H + k * 256 + (lane & 15) * 16;
 #pragma unroll
-        for (int r = 0; r < kLmRows; ++r) b.q[r] = *reinterpret_cast<const uint4 *>(p + (size_t)r * a->H);
+        for (int r = 0; r < kLmRows; ++r) b.q[r] = ld16(p + (size_t)r * a->H);
     }
 }
 
 template <int MT>
 __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmBuf &b, LmAcc<MT> &A) {
     if (st >= nst) return;
-    const int tid = ltid(), H = a->H, NC = H / 256, M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
+    const int tid = ltid(), NC = a->H / 256, M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
     const int k = st % NC;
     const uint16_t *xl = ulds();
     bf16x2 wv[kLmRows][8];
@@ -1003,7 +1058,7 @@ __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmB
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         if (t < M) {
-            const uint4 *xs = reinterpret_cast<const uint4 *>(xl + (size_t)t * H + k * 256 + li * 16);
+            const uint4 *xs = reinterpret_cast<const uint4 *>(xl + t * kUS + k * 256 + li * 16);
             const uint4 x0 = xs[0], x1 = xs[1];
 #pragma unroll
             for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = dot16(wv[r], x0, x1, A.acc[r][t]);
@@ -1027,7 +1082,7 @@ __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmB
         }
         if (st + 1 < nst) {   // the next unit's scales
 #pragma unroll
-            for (int r = 0; r < kLmRows; ++r) A.sc[r] = a->lm_s[row + 64 + r];
+            for (int r = 0; r < kLmRows; ++r) A.sc[r] = glb(a->lm_s)[row + 64 + r];
         }
     }
 }
@@ -1054,13 +1109,16 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
     if (nst > 0) {
         const int row = u0 * 64 + wave * 16 + (lane >> 4) * kLmRows;
 #pragma unroll
-        for (int r = 0; r < kLmRows; ++r) A.sc[r] = a->lm_s[row + r];
+        for (int r = 0; r < kLmRows; ++r) A.sc[r] = glb(a->lm_s)[row + r];
     }
     norm_to_lds<MT>(a, a->L, a->gains + (size_t)a->L * H, tgt);
     if (w == 0 && a->x_final) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(ulds());
-        uint4 *dst = reinterpret_cast<uint4 *>(a->x_final);
-        for (int i = tid; i < M * H / 8; i += kWG) dst[i] = src[i];
+        const int r8 = H / 8;   // 16-byte pieces of a row
+        for (int i = tid; i < M * r8; i += kWG) {
+            const int m = i / r8, c = i - m * r8;
+            { const uint4 v = reinterpret_cast<const uint4 *>(ulds() + m * kUS)[c];
+              *(GAS u32x4 *)(a->x_final + (size_t)m * H + 8 * c) = u32x4{v.x, v.y, v.z, v.w}; }
+        }
     }
     for (int st = 0; st < nst; st += 3) {
         lm_step<MT>(a, u0, nst, st, b0, A);
@@ -1118,14 +1176,14 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
             unsigned long long key = wb[t];
             for (int q = 1; q < 4; ++q) key = wb[q * kMaxM + t] > key ? wb[q * kMaxM + t] : key;
             tok[t] = (int)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
-            a->token[t] = tok[t];
-            if (a->max_logit) a->max_logit[t] = unordered((uint32_t)(key >> 32));
+            glb(a->token)[t] = tok[t];
+            if (a->max_logit) glb(a->max_logit)[t] = unordered((uint32_t)(key >> 32));
         }
         const int gamma = M - 1;
         int n = 0;
-        while (n < gamma && a->draft[n] == tok[n]) ++n;
-        for (int t = 0; t < M; ++t) a->out_tokens[t] = t <= n ? tok[t] : -1;
-        *a->accepted = n;
+        while (n < gamma && glb(a->draft)[n] == tok[n]) ++n;
+        for (int t = 0; t < M; ++t) glb(a->out_tokens)[t] = t <= n ? tok[t] : -1;
+        *glb(a->accepted) = n;
         st32(flags(a) + a->f_epoch, tgt);   // every workgroup has read the epoch by now
     }
 }
@@ -1193,10 +1251,10 @@ int launch_mt(const StepArgs &a, size_t lds, int NR, void *stream) {
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-size_t step_lds_bytes(const moe_step_desc &d, const StepWs &W, int *l_scr, int *l_slot) {
-    const int H = d.layer.hidden, Mx = d.max_tokens, E = d.layer.num_experts;
-    const size_t u = ((size_t)Mx * H * 2 + 15) & ~(size_t)15;
-    size_t scr = (size_t)Mx * W.segFmax * 4;
+size_t step_lds_bytes(const moe_step_desc &d, int *l_scr, int *l_slot) {
+    const int Mx = d.max_tokens, E = d.layer.num_experts;
+    const size_t u = (size_t)Mx * kUS * 2;
+    size_t scr = (size_t)Mx * kDS * 4;
     scr = std::max(scr, (size_t)Mx * E * 4);
     scr = std::max(scr, (size_t)16 * kMaxM * 8);
     scr = (scr + 15) & ~(size_t)15;
@@ -1286,7 +1344,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.eps = d.eps;
     a.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpin;
 
-    const size_t lds = step_lds_bytes(d, W, &a.l_scr, &a.l_slot);
+    const size_t lds = step_lds_bytes(d, &a.l_scr, &a.l_slot);
     switch (M) {   // one kernel per token count: token loops are unrolled exactly
     case 1: return launch_mt<1>(a, lds, W.NR, stream);
     case 2: return launch_mt<2>(a, lds, W.NR, stream);

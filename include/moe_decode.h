@@ -193,14 +193,18 @@ int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_
  * rmsnorm(h; g) = bf16(h * rsqrt(mean(h^2) + eps) * g). (Attention is not part of
  * this step; the stacked workload adds noise in its place.)
  *
- * The step runs as one kernel of persistent workgroups that take work items in a
- * fixed order (per layer: router row blocks, gate/up row blocks, down row blocks;
- * then lm_head row blocks) and hand data to later items through device-memory
- * counters; every weight byte the step needs is read once.
+ * The step runs as one kernel of persistent workgroups. Per layer, router workgroups
+ * form the logits; every other workgroup selects the top K itself and takes its share
+ * of the layer's units (8-row gate/up blocks, 64-row down blocks, 64-row combine
+ * blocks) in a fixed order; then every workgroup streams a share of the lm_head.
+ * Data passes between workgroups in tagged device-memory words, each polled until its
+ * tag is the current step's. Every weight byte the step needs is read once. The shape
+ * must satisfy hidden <= 2816 and expert_width <= 704 (one 704-column down row per
+ * unit); wider layers are rejected with MOE_EINVAL.
  * ---------------------------------------------------------------------------- */
 
 typedef struct moe_step_desc {
-    moe_layer_desc layer;   /* shape of every layer (wtype MOE_W_FP8_E4M3; hidden <= 3072)   */
+    moe_layer_desc layer;   /* shape of every layer (wtype MOE_W_FP8_E4M3; hidden <= 2816)   */
     int num_layers;         /* L, 1..64                                                        */
     int vocab;              /* V, a multiple of 64, 64..2^30                                   */
     int max_tokens;         /* largest M the workspace serves, 1..8                            */

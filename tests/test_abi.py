@@ -191,8 +191,11 @@ def test_step_workspace_and_desc_validation():
                  ("eps", -1.0)):
         assert native.moe_decode_step_workspace(step_desc(**{k: v})) == 0, k
     wide = step_desc()
-    wide.layer.hidden = 4096                       # the fused step holds H <= 3072 per lane
+    wide.layer.hidden = 3072                       # the fused step takes H <= 2816
     assert native.moe_decode_step_workspace(wide) == 0
+    broad = step_desc()
+    broad.layer.expert_width = 768                 # and routed rows of at most 704 columns
+    assert native.moe_decode_step_workspace(broad) == 0
     assert L.moe_decode_step_workspace(None) == 0
 
 
