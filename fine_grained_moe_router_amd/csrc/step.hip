@@ -329,6 +329,13 @@ template <int MT>
 __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint32_t tgt) {
     const int H = a->H, M = MT, tid = ltid(), hw = H / 2, lane = tid & 63, wave = tid >> 6;
     uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][kUS/2] bf16 pairs
+    // the gains are requested first, so that they arrive while h is awaited
+    uint32_t gv[kW];
+#pragma unroll
+    for (int k = 0; k < kW; ++k) {
+        const int q = tid + k * kWG;
+        gv[k] = q < hw ? *glb(reinterpret_cast<const uint32_t *>(g + 2 * q)) : 0u;
+    }
     float ss[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) ss[m] = 0.0f;
@@ -403,23 +410,20 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
         }
     }
     __syncthreads();
+    // every word of the padded row is in range (kW * kWG == kUS / 2): the row's words
+    // are read together and the padding is written with a select, without branches
+    static_assert(kW * kWG == kUS / 2, "one pass of the normalisation covers the padded row");
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-            const float r = rsqrtf((S.red[0][m] + S.red[1][m] + S.red[2][m] + S.red[3][m]) / (float)H + a->eps);
+        const float r = rsqrtf((S.red[0][m] + S.red[1][m] + S.red[2][m] + S.red[3][m]) / (float)H + a->eps);
+        uint32_t hv[kW];
 #pragma unroll
-            for (int k = 0; k < kW; ++k) {
-                const int q = tid + k * kWG;
-                if (q < hw) {
-                    const uint32_t gv = *glb(reinterpret_cast<const uint32_t *>(g + 2 * q));
-                    const uint32_t hv = uw[m * (kUS / 2) + q];
-                    const uint16_t u0 = f2bf(bf2f(hv & 0xffffu) * r * bf2f(gv & 0xffffu));
-                    const uint16_t u1 = f2bf(bf2f(hv >> 16) * r * bf2f(gv >> 16));
-                    uw[m * (kUS / 2) + q] = pack2(u0, u1);
-                } else if (q < kUS / 2) {
-                    uw[m * (kUS / 2) + q] = 0u;
-                }
-            }
+        for (int k = 0; k < kW; ++k) hv[k] = uw[m * (kUS / 2) + tid + k * kWG];
+#pragma unroll
+        for (int k = 0; k < kW; ++k) {
+            const uint16_t u0 = f2bf(bf2f(hv[k] & 0xffffu) * r * bf2f(gv[k] & 0xffffu));
+            const uint16_t u1 = f2bf(bf2f(hv[k] >> 16) * r * bf2f(gv[k] >> 16));
+            uw[m * (kUS / 2) + tid + k * kWG] = tid + k * kWG < hw ? pack2(u0, u1) : 0u;
         }
     }
     __syncthreads();
@@ -444,9 +448,11 @@ __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]
 template <int MT>
 __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&wq)[kNC], uint32_t tgt) {
     const AP a = uniform(a0);
-    const int H = a->H, E = a->E, M = MT, tid = ltid(), lane32 = tid & 31;
+    const int H = a->H, E = a->E, tid = ltid(), lane32 = tid & 31;
     const int e = 8 * j + (tid >> 5);
     const bool valid = e < E;
+    const float *bias = layer_w(a, l)->router_bias;
+    const float bv = (bias && valid) ? glb(bias)[e] : 0.0f;   // requested before the norm's polls
     norm_to_lds<MT>(a, l, a->gains + (size_t)l * H, tgt);
     const uint16_t *u = ulds();
     float acc[MT];
@@ -454,30 +460,36 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
     int off = lane32 * 8;   // this lane's columns of the token's row of u
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        // one token's row at a time: its kNC reads are issued together; the row offset
-        // depends on the previous token's sum, so the next token's reads are not hoisted
-        // into this one's registers
+    for (int m = 0; m < MT; m += 2) {
+        // two tokens' rows at a time: their reads are issued together and their sums
+        // interleave; the row offset depends on the previous pair's sums, so the next
+        // pair's reads are not hoisted into this pair's registers
 #pragma unroll
         for (int k = 0; k < kNC; ++k) {
-            const uint4 xv = *reinterpret_cast<const uint4 *>(u + off + k * 256);
-            acc[m] = dot2(as_bf2(wq[k].x), as_bf2(xv.x), acc[m]);
-            acc[m] = dot2(as_bf2(wq[k].y), as_bf2(xv.y), acc[m]);
-            acc[m] = dot2(as_bf2(wq[k].z), as_bf2(xv.z), acc[m]);
-            acc[m] = dot2(as_bf2(wq[k].w), as_bf2(xv.w), acc[m]);
-        }
-        off += kUS;
-        asm volatile("" : "+v"(off) : "v"(acc[m]));
-    }
-    const float *bias = layer_w(a, l)->router_bias;
-    const float bv = (bias && valid) ? glb(bias)[e] : 0.0f;
-    uint64_t *lg = logits(a, l);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        if (m < M) {
-            const float v = half_sum(acc[m]);
-            if (lane32 == 16 && valid) st64(lg + (size_t)m * E + e, tagged(__float_as_uint(v + bv), tgt));
+            for (int mm = 0; mm < 2; ++mm) {
+                if (m + mm < MT) {
+                    const uint4 xv = *reinterpret_cast<const uint4 *>(u + off + mm * kUS + k * 256);
+                    acc[m + mm] = dot2(as_bf2(wq[k].x), as_bf2(xv.x), acc[m + mm]);
+                    acc[m + mm] = dot2(as_bf2(wq[k].y), as_bf2(xv.y), acc[m + mm]);
+                    acc[m + mm] = dot2(as_bf2(wq[k].z), as_bf2(xv.z), acc[m + mm]);
+                    acc[m + mm] = dot2(as_bf2(wq[k].w), as_bf2(xv.w), acc[m + mm]);
+                }
+            }
         }
+        off += 2 * kUS;
+        asm volatile("" : "+v"(off) : "v"(acc[m]), "v"(acc[m + 1 < MT ? m + 1 : m]));
+    }
+    // every logit is formed before the first store: stores count against the same
+    // in-order counter as loads, so a wait placed between two stores would also wait
+    // for the first store to complete
+    float v[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[m] = half_sum(acc[m]) + bv;
+    uint64_t *lg = logits(a, l);
+    if (lane32 == 16 && valid) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) st64(lg + (size_t)m * E + e, tagged(__float_as_uint(v[m]), tgt));
     }
 }
 
@@ -937,6 +949,8 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
     for (int p = 0; p * kWG < M * 64; ++p) {
         const int i = p * kWG + tid, m = i >> 6, c = cb * 64 + (i & 63);
         const bool act = m < M, odd = (i & 1) != 0;
+        // the noise is requested before the polls, so that it arrives while they wait
+        const uint16_t nz = act && l + 1 < a->L ? glb(a->noise)[((size_t)(l + 1) * M + m) * H + c] : (uint16_t)0;
         float s = 0.0f;
         uint32_t hp = 0;
         for (int k0 = 0; k0 < n; k0 += kCmbChunk) {
@@ -969,7 +983,7 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
         if (act && l == 0) hp = h0_pair(a, m, c / 2);
         const uint16_t y = f2bf(s);
         float hv = bf2f(odd ? hp >> 16 : hp & 0xffffu);
-        if (act && l + 1 < a->L) hv += bf2f(glb(a->noise)[((size_t)(l + 1) * M + m) * H + c]);
+        if (act && l + 1 < a->L) hv += bf2f(nz);
         const uint16_t hn = f2bf(hv + bf2f(y));
         // the pair partner's values (quad_perm [1,0,3,2])
         const uint32_t yo = dppu<0xB1>(y), ho = dppu<0xB1>(hn);
