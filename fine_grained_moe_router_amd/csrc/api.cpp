@@ -104,14 +104,12 @@ int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int
                      void *workspace, size_t workspace_bytes, void *stream) {
     CHECK(check_layer_desc(desc));
     if (!w || M < 1 || M > kMaxM) return MOE_EINVAL;
-    const bool fp8 = desc->wtype == MOE_W_FP8_E4M3;
     CHECK(check_weights(desc, w));
     CHECK(need(x));
     CHECK(need(y));
     if (((uintptr_t)topk_idx | (uintptr_t)topk_w) & 3u) return MOE_EALIGN;
     const LayerWs L = layer_ws(*desc, M);
     if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
-    if (!fp8) return MOE_EUNSUPPORTED;
     return launch_moe_layer(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, L, stream);
 }
 
@@ -175,7 +173,6 @@ int moe_decode_step_prepare(const moe_step_desc *desc, const moe_layer_weights *
     for (int l = 0; l < desc->num_layers; ++l) CHECK(check_weights(&desc->layer, &layers[l]));
     const StepWs W = step_ws(*desc);
     if (!ws_ok(workspace, workspace_bytes, W.total)) return MOE_EWORKSPACE;
-    if (desc->layer.wtype != MOE_W_FP8_E4M3) return MOE_EUNSUPPORTED;
     return step_prepare(W, desc->layer, layers, (char *)workspace);
 }
 
@@ -200,7 +197,6 @@ int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
     if ((y_layers && !aligned16(y_layers)) || (x_final && !aligned16(x_final))) return MOE_EALIGN;
     const StepWs W = step_ws(*desc);
     if (!ws_ok(workspace, workspace_bytes, W.total)) return MOE_EWORKSPACE;
-    if (desc->layer.wtype != MOE_W_FP8_E4M3) return MOE_EUNSUPPORTED;
     return launch_step(*desc, W, M, gains, lm_w, lm_s, x, noise, draft, token, max_logit,
                        accepted_len, out_tokens, y_layers, topk_idx, topk_w, x_final,
                        (char *)workspace, stream);

@@ -221,8 +221,10 @@ constexpr int kGateUpUnroll = 6;  // 16-byte chunks per lane in flight, per matr
 
 // Workgroup (row block, slot): 4 waves x 4 groups of 16 lanes; each group owns one
 // row j of gate and up; lane li reads bytes [256 i + 16 li, +16) of the row for
-// i = 0..H/256-1 (each load instruction reads 4 rows x 256 contiguous bytes).
-// h[slot][t][j] = gelu_tanh(s_g[j] (G_j . x_t)) * (s_u[j] (U_j . x_t)).
+// i = 0..(row bytes)/256-1 (each load instruction reads 4 rows x 256 contiguous bytes):
+// 16 columns per piece for FP8 codes, 8 for bf16 weights (BF).
+// h[slot][t][j] = gelu_tanh(s_g[j] (G_j . x_t)) * (s_u[j] (U_j . x_t)), scales 1 for bf16.
+template <bool BF>
 __global__ __launch_bounds__(256) void k_gateup(ExpertArgs a) {
     extern __shared__ uint4 xs[];  // [ntok][H/8]
     const int s = blockIdx.y;
@@ -247,13 +249,14 @@ __global__ __launch_bounds__(256) void k_gateup(ExpertArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, li = lane & 15;
     const int row = row0 + wave * 4 + g;
-    const size_t eoff = (size_t)e * a.D * H;
-    const uint8_t *gw = (shared ? a.sh_gate : a.gate + eoff) + (size_t)row * H + li * 16;
-    const uint8_t *uw = (shared ? a.sh_up : a.up + eoff) + (size_t)row * H + li * 16;
+    constexpr int EB = BF ? 2 : 1;   // bytes per weight
+    const size_t eoff = (size_t)e * a.D * H * EB;
+    const uint8_t *gw = (shared ? a.sh_gate : a.gate + eoff) + (size_t)row * H * EB + li * 16;
+    const uint8_t *uw = (shared ? a.sh_up : a.up + eoff) + (size_t)row * H * EB + li * 16;
     float accg[kMaxM], accu[kMaxM];
 #pragma unroll
     for (int t = 0; t < kMaxM; ++t) accg[t] = accu[t] = 0.0f;
-    const int NC = H / 256;
+    const int NC = H * EB / 256;
     for (int i0 = 0; i0 < NC; i0 += kGateUpUnroll) {
         uint4 qg[kGateUpUnroll], qu[kGateUpUnroll];
 #pragma unroll
@@ -266,23 +269,42 @@ __global__ __launch_bounds__(256) void k_gateup(ExpertArgs a) {
 #pragma unroll
         for (int k = 0; k < kGateUpUnroll; ++k) {
             if (i0 + k < NC) {
-                bf16x2 wg[8], wu[8];
-                decode16_bf16(qg[k], wg);
-                decode16_bf16(qu[k], wu);
-                const int xv = ((i0 + k) * 256 + li * 16) / 8;
+                if constexpr (BF) {
+                    // 8 bf16 weights: columns 128 i + 8 li .. + 7
+                    const int xv = ((i0 + k) * 128 + li * 8) / 8;
 #pragma unroll
-                for (int t = 0; t < kMaxM; ++t) {
-                    if (t < ntok) {
-                        const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
-                        accg[t] = dot16(wg, x0, x1, accg[t]);
-                        accu[t] = dot16(wu, x0, x1, accu[t]);
+                    for (int t = 0; t < kMaxM; ++t) {
+                        if (t < ntok) {
+                            const uint4 x0 = xs[t * hv + xv];
+                            accg[t] = dot2(as_bf2(qg[k].x), as_bf2(x0.x), accg[t]);
+                            accg[t] = dot2(as_bf2(qg[k].y), as_bf2(x0.y), accg[t]);
+                            accg[t] = dot2(as_bf2(qg[k].z), as_bf2(x0.z), accg[t]);
+                            accg[t] = dot2(as_bf2(qg[k].w), as_bf2(x0.w), accg[t]);
+                            accu[t] = dot2(as_bf2(qu[k].x), as_bf2(x0.x), accu[t]);
+                            accu[t] = dot2(as_bf2(qu[k].y), as_bf2(x0.y), accu[t]);
+                            accu[t] = dot2(as_bf2(qu[k].z), as_bf2(x0.z), accu[t]);
+                            accu[t] = dot2(as_bf2(qu[k].w), as_bf2(x0.w), accu[t]);
+                        }
+                    }
+                } else {
+                    bf16x2 wg[8], wu[8];
+                    decode16_bf16(qg[k], wg);
+                    decode16_bf16(qu[k], wu);
+                    const int xv = ((i0 + k) * 256 + li * 16) / 8;
+#pragma unroll
+                    for (int t = 0; t < kMaxM; ++t) {
+                        if (t < ntok) {
+                            const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
+                            accg[t] = dot16(wg, x0, x1, accg[t]);
+                            accu[t] = dot16(wu, x0, x1, accu[t]);
+                        }
                     }
                 }
             }
         }
     }
-    const float sg = (shared ? a.sh_gate_s : a.gate_s + (size_t)e * a.D)[row];
-    const float su = (shared ? a.sh_up_s : a.up_s + (size_t)e * a.D)[row];
+    const float sg = BF ? 1.0f : (shared ? a.sh_gate_s : a.gate_s + (size_t)e * a.D)[row];
+    const float su = BF ? 1.0f : (shared ? a.sh_up_s : a.up_s + (size_t)e * a.D)[row];
 #pragma unroll
     for (int t = 0; t < kMaxM; ++t) {
         if (t < ntok) {
@@ -301,8 +323,10 @@ constexpr int kDownUnroll = 6;
 constexpr int kDownLdsBytes = 64 * 1024;
 
 // Workgroup (row block, slot): wave w owns rows c0 + 16 w .. +16, 4 lanes per row;
-// lane q reads bytes [64 i + 16 q, +16) of the row (i = 0..F/64-1). h of the slot's
-// tokens is staged in LDS (fp32). ypart[slot][m][c] = w[slot][m] * s_d[c] (Dn_c . h).
+// lane q reads bytes [64 i + 16 q, +16) of the row (i = 0..(row bytes)/64-1): 16
+// columns per piece for FP8 codes, 8 for bf16 weights (BF). h of the slot's tokens is
+// staged in LDS (fp32). ypart[slot][m][c] = w[slot][m] * s_d[c] (Dn_c . h), s_d = 1 for bf16.
+template <bool BF>
 __global__ __launch_bounds__(256) void k_down(ExpertArgs a) {
     extern __shared__ float4 hs4[];  // [tp][F/4]
     const int s = blockIdx.y;
@@ -316,11 +340,12 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int q = lane & 3;
     const int c = blockIdx.x * kDownRows + wave * 16 + (lane >> 2);
-    const uint8_t *dw = (shared ? a.sh_down : a.down + (size_t)e * H * a.D) + (size_t)c * F + q * 16;
-    const float sd = (shared ? a.sh_down_s : a.down_s + (size_t)e * H)[c];
+    constexpr int EB = BF ? 2 : 1;   // bytes per weight
+    const uint8_t *dw = (shared ? a.sh_down : a.down + (size_t)e * H * a.D * EB) + (size_t)c * F * EB + q * 16;
+    const float sd = BF ? 1.0f : (shared ? a.sh_down_s : a.down_s + (size_t)e * H)[c];
     const int f4 = F / 4;
     const int tp = min(ntok, a.down_lds / (F * 4));
-    const int NI = F / 64;
+    const int NI = F * EB / 64;
     uint32_t mrem = mask;
     for (int t0 = 0; t0 < ntok; t0 += tp) {
         const int tn = min(tp, ntok - t0);
@@ -341,21 +366,27 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a) {
 #pragma unroll
             for (int k = 0; k < kDownUnroll; ++k) {
                 if (i0 + k < NI) {
-                    float wv[16];
+                    constexpr int NW = BF ? 8 : 16;   // weights in the piece
+                    float wv[NW];
                     const uint32_t qw[4] = {qd[k].x, qd[k].y, qd[k].z, qd[k].w};
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const f32x2 lo = fp8x2_to_f32<false>(qw[u]);
-                        const f32x2 hi = fp8x2_to_f32<true>(qw[u]);
-                        wv[4 * u + 0] = lo.x; wv[4 * u + 1] = lo.y;
-                        wv[4 * u + 2] = hi.x; wv[4 * u + 3] = hi.y;
+                        if constexpr (BF) {
+                            wv[2 * u + 0] = __uint_as_float(qw[u] << 16);
+                            wv[2 * u + 1] = __uint_as_float(qw[u] & 0xffff0000u);
+                        } else {
+                            const f32x2 lo = fp8x2_to_f32<false>(qw[u]);
+                            const f32x2 hi = fp8x2_to_f32<true>(qw[u]);
+                            wv[4 * u + 0] = lo.x; wv[4 * u + 1] = lo.y;
+                            wv[4 * u + 2] = hi.x; wv[4 * u + 3] = hi.y;
+                        }
                     }
-                    const int cv = ((i0 + k) * 64 + q * 16) / 4;
+                    const int cv = ((i0 + k) * (64 / EB) + q * NW) / 4;
 #pragma unroll
                     for (int t = 0; t < kMaxM; ++t) {
                         if (t < tn) {
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) {
+                            for (int u = 0; u < NW / 4; ++u) {
                                 const float4 hv = hs4[t * f4 + cv + u];
                                 acc[t] = fmaf(wv[4 * u + 0], hv.x, acc[t]);
                                 acc[t] = fmaf(wv[4 * u + 1], hv.y, acc[t]);
@@ -637,8 +668,13 @@ int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
                   reinterpret_cast<float *>(ws + L.h), reinterpret_cast<float *>(ws + L.ypart),
                   M, H, E, d.expert_width, d.shared_width, L.F,
                   min(M, kDownLdsBytes / (L.F * 4)) * L.F * 4};
-    hipLaunchKernelGGL(k_gateup, dim3(L.F / kGateUpRows, S_), dim3(256), (size_t)M * H * 2, S(stream), ea);
-    hipLaunchKernelGGL(k_down, dim3(H / kDownRows, S_), dim3(256), (size_t)ea.down_lds, S(stream), ea);
+    if (d.wtype == MOE_W_BF16) {
+        hipLaunchKernelGGL(k_gateup<true>, dim3(L.F / kGateUpRows, S_), dim3(256), (size_t)M * H * 2, S(stream), ea);
+        hipLaunchKernelGGL(k_down<true>, dim3(H / kDownRows, S_), dim3(256), (size_t)ea.down_lds, S(stream), ea);
+    } else {
+        hipLaunchKernelGGL(k_gateup<false>, dim3(L.F / kGateUpRows, S_), dim3(256), (size_t)M * H * 2, S(stream), ea);
+        hipLaunchKernelGGL(k_down<false>, dim3(H / kDownRows, S_), dim3(256), (size_t)ea.down_lds, S(stream), ea);
+    }
     CombineArgs ca{reinterpret_cast<const int32_t *>(ws + L.n_slots),
                    reinterpret_cast<const uint32_t *>(ws + L.slot_mask),
                    reinterpret_cast<const float *>(ws + L.ypart), y, M, H};

@@ -662,13 +662,27 @@ struct UnitBuf {
 
 enum { kGU = 0, kDN = 1, kCMB = 2 };
 
+// Unit geometry per expert weight type: FP8 codes (16 to a 16-byte piece) or bf16 weights
+// (8 to a piece). A bf16 unit has half the rows of an FP8 unit, so that both hold kPc
+// pieces of each of two rows per lane.
+template <bool BF>
+struct Geo {
+    static constexpr int EB = BF ? 2 : 1;      // bytes per weight
+    static constexpr int CP = 16 / EB;         // columns per piece
+    static constexpr int RG = BF ? 4 : 8;      // gate (and up) rows per gate/up unit
+    static constexpr int LG = kWG / RG;        // lanes per gate/up row
+    static constexpr int RD = BF ? 32 : 64;    // rows per down unit
+    static constexpr int LD = 2 * kWG / RD;    // lanes per down row pair
+    static_assert(LG * kPc * CP == kUS && LD * kPc * CP == kDS, "a unit row fills a padded LDS row");
+};
+
 struct UnitRef {
     int kind;
     int s;       // slot (gate/up, down)
-    int row0;    // gate/up: the first of its 8 rows
+    int row0;    // gate/up: the first of its rows
     int js;      // down: sub-slot
     int seg;     // down: column segment
-    int cb;      // down, combine: 64-row block
+    int cb;      // down: row block; combine: 64-row block
 };
 
 // The layer's unit list: the shared expert's gate/up units, its down units, the routed
@@ -679,39 +693,43 @@ struct UnitList {
     int nsub;                           // sub-slots
 };
 
+template <bool BF>
 __device__ __forceinline__ UnitList unit_list(AP a, int ns) {
+    using g = Geo<BF>;
     UnitList L;
-    const int has_sh = a->Ds > 0, nr = ns - has_sh;
-    L.sh_gu = has_sh ? a->Ds / 8 : 0;
-    L.sh_dn = L.sh_gu + (has_sh ? a->nseg_s * a->ND : 0);
-    L.r_gu = L.sh_dn + nr * (a->D / 8);
-    L.r_dn = L.r_gu + nr * a->nseg_r * a->ND;
+    const int has_sh = a->Ds > 0, nr = ns - has_sh, ndn = a->H / g::RD;
+    L.sh_gu = has_sh ? a->Ds / g::RG : 0;
+    L.sh_dn = L.sh_gu + (has_sh ? a->nseg_s * ndn : 0);
+    L.r_gu = L.sh_dn + nr * (a->D / g::RG);
+    L.r_dn = L.r_gu + nr * a->nseg_r * ndn;
     L.U = L.r_dn + a->ND;
     L.nsub = (has_sh ? a->nseg_s : 0) + nr * a->nseg_r;
     return L;
 }
 
+template <bool BF>
 __device__ __forceinline__ UnitRef decode_unit(AP a, int q, const UnitList &L) {
+    using g = Geo<BF>;
     UnitRef u;
-    const int has_sh = a->Ds > 0;
+    const int has_sh = a->Ds > 0, ndn = a->H / g::RD;
     u.s = u.row0 = u.js = u.seg = u.cb = 0;
     if (q < L.sh_gu) {
         u.kind = kGU;
-        u.row0 = 8 * q;
+        u.row0 = g::RG * q;
     } else if (q < L.sh_dn) {
         const int r = q - L.sh_gu;
         u.kind = kDN;
-        u.js = u.seg = r / a->ND;
-        u.cb = r % a->ND;
+        u.js = u.seg = r / ndn;
+        u.cb = r % ndn;
     } else if (q < L.r_gu) {
-        const int r = q - L.sh_dn, D8 = a->D / 8;
+        const int r = q - L.sh_dn, DG = a->D / g::RG;
         u.kind = kGU;
-        u.s = has_sh + r / D8;
-        u.row0 = 8 * (r % D8);
+        u.s = has_sh + r / DG;
+        u.row0 = g::RG * (r % DG);
     } else if (q < L.r_dn) {
-        const int r = q - L.r_gu, jr = r / a->ND;
+        const int r = q - L.r_gu, jr = r / ndn;
         u.kind = kDN;
-        u.cb = r % a->ND;
+        u.cb = r % ndn;
         u.js = (has_sh ? a->nseg_s : 0) + jr;
         u.s = has_sh + jr / a->nseg_r;
         u.seg = jr % a->nseg_r;
@@ -724,7 +742,9 @@ __device__ __forceinline__ UnitRef decode_unit(AP a, int q, const UnitList &L) {
 
 // Request a unit's weights. Before the routing is known (pre_route) only the shared
 // expert's units can be loaded.
+template <bool BF>
 __device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf &b, bool pre_route) {
+    using g = Geo<BF>;
     if (u.kind == kCMB) return;
     const WP wp = layer_w(a, l);
     const SlotLds &S = slots(a);
@@ -733,33 +753,35 @@ __device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf
     const bool shared = e == a->E;
     // Pieces past the end of a row re-read the row's last piece: they meet the zero
     // columns past the row in the LDS copy of u or h, and a single unconditional 16-byte
-    // load per piece keeps the loads free of per-lane branches.
+    // load per piece keeps the loads free of per-lane branches. bf16 weights carry no
+    // scales (1).
     if (u.kind == kGU) {
-        const int NP = H / 16, j = tid & 31, row = u.row0 + (tid >> 5);
+        const int NP = H / g::CP, j = tid % g::LG, row = u.row0 + tid / g::LG;
         const size_t eoff = (size_t)e * a->D;
         const uint4 *gp = reinterpret_cast<const uint4 *>(
-            (shared ? (const uint8_t *)wp->sh_gate_w : (const uint8_t *)wp->gate_w + eoff * H) + (size_t)row * H);
+            (shared ? (const uint8_t *)wp->sh_gate_w : (const uint8_t *)wp->gate_w + eoff * H * g::EB) + (size_t)row * H * g::EB);
         const uint4 *vp = reinterpret_cast<const uint4 *>(
-            (shared ? (const uint8_t *)wp->sh_up_w : (const uint8_t *)wp->up_w + eoff * H) + (size_t)row * H);
+            (shared ? (const uint8_t *)wp->sh_up_w : (const uint8_t *)wp->up_w + eoff * H * g::EB) + (size_t)row * H * g::EB);
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(gp + min(j + 32 * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(gp + min(j + g::LG * i, NP - 1));
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(vp + min(j + 32 * i, NP - 1));
-        b.sc[0] = *glb((shared ? wp->sh_gate_s : wp->gate_s + eoff) + row);
-        b.sc[1] = *glb((shared ? wp->sh_up_s : wp->up_s + eoff) + row);
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(vp + min(j + g::LG * i, NP - 1));
+        b.sc[0] = BF ? 1.0f : *glb((shared ? wp->sh_gate_s : wp->gate_s + eoff) + row);
+        b.sc[1] = BF ? 1.0f : *glb((shared ? wp->sh_up_s : wp->up_s + eoff) + row);
     } else {
-        const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NP = segF / 16;
-        const int j = tid & 7, c0 = u.cb * 64 + (tid >> 3);
-        const uint8_t *dp = (shared ? (const uint8_t *)wp->sh_down_w : (const uint8_t *)wp->down_w + (size_t)e * H * a->D) +
-                            (size_t)c0 * F + u.seg * segF;
-        const uint4 *d0 = reinterpret_cast<const uint4 *>(dp), *d1 = reinterpret_cast<const uint4 *>(dp + (size_t)32 * F);
+        const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r), NP = segF / g::CP;
+        const int j = tid % g::LD, c0 = u.cb * g::RD + tid / g::LD;
+        const uint8_t *dp = (shared ? (const uint8_t *)wp->sh_down_w : (const uint8_t *)wp->down_w + (size_t)e * H * a->D * g::EB) +
+                            ((size_t)c0 * F + u.seg * segF) * g::EB;
+        const uint4 *d0 = reinterpret_cast<const uint4 *>(dp);
+        const uint4 *d1 = reinterpret_cast<const uint4 *>(dp + (size_t)(g::RD / 2) * F * g::EB);
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(d0 + min(j + 8 * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(d0 + min(j + g::LD * i, NP - 1));
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(d1 + min(j + 8 * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(d1 + min(j + g::LD * i, NP - 1));
         const float *ds = shared ? wp->sh_down_s : wp->down_s + (size_t)e * H;
-        b.sc[0] = *glb(ds + c0);
-        b.sc[1] = *glb(ds + c0 + 32);
+        b.sc[0] = BF ? 1.0f : *glb(ds + c0);
+        b.sc[1] = BF ? 1.0f : *glb(ds + c0 + g::RD / 2);
     }
 }
 
@@ -772,14 +794,15 @@ __device__ __forceinline__ void slot_tokens(unsigned mask, int (&toks)[MT]) {
     }
 }
 
-// Gate/up unit: 8 rows of the slot's gate and up matrices; half-wave r computes row
-// row0 + r of both (32 lanes, 16 columns of every 512-column stretch per lane). Tokens
-// are taken one at a time in a loop (the FP8 codes are decoded again per token: one
+// Gate/up unit: RG rows of the slot's gate and up matrices; lane group r (LG lanes)
+// computes row row0 + r of both, CP columns of every LG * CP-column stretch per lane.
+// Tokens are taken one at a time in a loop (FP8 codes are decoded again per token: one
 // instruction per pair) so that the code does not grow with the token count.
-template <int MT>
+template <int MT, bool BF>
 __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
+    using g = Geo<BF>;
     const SlotLds &S = slots(a);
-    const int tid = ltid(), j = tid & 31, row = u.row0 + (tid >> 5);
+    const int tid = ltid(), j = tid % g::LG, row = u.row0 + tid / g::LG;
     const uint16_t *ul = ulds();
     unsigned mm = S.sm[u.s];
 #pragma unroll 1
@@ -787,36 +810,53 @@ __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const Unit
         const int m = __ffs(mm) - 1;
         mm &= mm - 1u;
         float ag = 0.0f, au = 0.0f;
-        const uint16_t *um = ul + m * kUS + j * 16;
-        // the decode scale is opaque per token, so the decoded weights are not hoisted
-        // out of the token loop (holding them would cost 88 registers and occupancy)
-        float one = 1.0f;
-        asm volatile("" : "+v"(one));
+        const uint16_t *um = ul + m * kUS + j * g::CP;
+        if constexpr (BF) {
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) {
-            const uint4 g = b.w[i], v = b.w[kPc + i];
-            const uint4 x0 = *reinterpret_cast<const uint4 *>(um + i * 512);
-            const uint4 x1 = *reinterpret_cast<const uint4 *>(um + i * 512 + 8);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, false), as_bf2(x0.x), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.x, one, true), as_bf2(x0.y), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, false), as_bf2(x0.z), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.y, one, true), as_bf2(x0.w), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.z, one, false), as_bf2(x1.x), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.z, one, true), as_bf2(x1.y), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.w, one, false), as_bf2(x1.z), ag);
-            ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(g.w, one, true), as_bf2(x1.w), ag);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, false), as_bf2(x0.x), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, one, true), as_bf2(x0.y), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, false), as_bf2(x0.z), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, one, true), as_bf2(x0.w), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, one, false), as_bf2(x1.x), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.z, one, true), as_bf2(x1.y), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, one, false), as_bf2(x1.z), au);
-            au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.w, one, true), as_bf2(x1.w), au);
+            for (int i = 0; i < kPc; ++i) {
+                const uint4 gw = b.w[i], vw = b.w[kPc + i];
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(um + i * g::LG * g::CP);
+                ag = dot2(as_bf2(gw.x), as_bf2(x0.x), ag);
+                ag = dot2(as_bf2(gw.y), as_bf2(x0.y), ag);
+                ag = dot2(as_bf2(gw.z), as_bf2(x0.z), ag);
+                ag = dot2(as_bf2(gw.w), as_bf2(x0.w), ag);
+                au = dot2(as_bf2(vw.x), as_bf2(x0.x), au);
+                au = dot2(as_bf2(vw.y), as_bf2(x0.y), au);
+                au = dot2(as_bf2(vw.z), as_bf2(x0.z), au);
+                au = dot2(as_bf2(vw.w), as_bf2(x0.w), au);
+            }
+        } else {
+            // the decode scale is opaque per token, so the decoded weights are not hoisted
+            // out of the token loop (holding them would cost 88 registers and occupancy)
+            float one = 1.0f;
+            asm volatile("" : "+v"(one));
+#pragma unroll
+            for (int i = 0; i < kPc; ++i) {
+                const uint4 gw = b.w[i], vw = b.w[kPc + i];
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(um + i * g::LG * g::CP);
+                const uint4 x1 = *reinterpret_cast<const uint4 *>(um + i * g::LG * g::CP + 8);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.x, one, false), as_bf2(x0.x), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.x, one, true), as_bf2(x0.y), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.y, one, false), as_bf2(x0.z), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.y, one, true), as_bf2(x0.w), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.z, one, false), as_bf2(x1.x), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.z, one, true), as_bf2(x1.y), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.w, one, false), as_bf2(x1.z), ag);
+                ag = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(gw.w, one, true), as_bf2(x1.w), ag);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.x, one, false), as_bf2(x0.x), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.x, one, true), as_bf2(x0.y), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.y, one, false), as_bf2(x0.z), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.y, one, true), as_bf2(x0.w), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.z, one, false), as_bf2(x1.x), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.z, one, true), as_bf2(x1.y), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.w, one, false), as_bf2(x1.z), au);
+                au = dot2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw.w, one, true), as_bf2(x1.w), au);
+            }
         }
-        const float gs = half_sum(ag);
-        const float us = half_sum(au);
-        if (j == 16)
+        // a row's sum: over its half-wave (valid in lanes 16..31 of it) or its wave
+        const float gs = BF ? wave_sum(ag) : half_sum(ag);
+        const float us = BF ? wave_sum(au) : half_sum(au);
+        if (j == (BF ? 0 : 16))
             st64(hact(a, l, u.s, m) + row, tagged(__float_as_uint(gelu_tanh(b.sc[0] * gs) * (b.sc[1] * us)), tgt));
     }
 }
@@ -824,13 +864,14 @@ __device__ __forceinline__ void run_gu(AP a, int l, const UnitRef &u, const Unit
 constexpr int kStage = 8;    // h words per thread per staging round of a down unit
 constexpr int kCmbChunk = 12;   // sub-slot words per poll of a combine unit
 
-// Down unit: rows c0 = 64 cb + (tid >> 3) and c0 + 32 of the slot's down matrix over
-// one column segment (8 lanes per row pair, 16 columns of every 128-column stretch per
-// lane), for the slot's tokens, weighted by their combine weights.
-template <int MT>
+// Down unit: rows c0 = RD cb + tid / LD and c0 + RD / 2 of the slot's down matrix over
+// one column segment (LD lanes per row pair, CP columns of every LD * CP-column stretch
+// per lane), for the slot's tokens, weighted by their combine weights.
+template <int MT, bool BF>
 __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
+    using g = Geo<BF>;
     const SlotLds &S = slots(a);
-    const int e = S.se[u.s], tid = ltid(), j = tid & 7;
+    const int e = S.se[u.s], tid = ltid(), j = tid % g::LD;
     const bool shared = e == a->E;
     const int F = shared ? a->Ds : a->D, segF = F / (shared ? a->nseg_s : a->nseg_r);
     const unsigned mask = S.sm[u.s];
@@ -893,7 +934,7 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
     }
     __syncthreads();
     const float4 *hs4 = reinterpret_cast<const float4 *>(hs);
-    const int c0 = u.cb * 64 + (tid >> 3);
+    const int c0 = u.cb * g::RD + tid / g::LD;
 #pragma unroll 1
     for (int t = 0; t < ntok; ++t) {
         const int m = toks[0];
@@ -902,32 +943,48 @@ __device__ __forceinline__ void run_dn(AP a, int l, const UnitRef &u, const Unit
         asm volatile("" : "+v"(zero));
 #pragma unroll
         for (int i = 0; i < kPc; ++i) {
-            // piece j + 8 i of both rows: columns 16 (j + 8 i) .. + 15 of the segment
-            const float4 *hp = hs4 + (t * kDS + i * 128 + j * 16) / 4;
-            const float4 h0 = hp[0], h1 = hp[1], h2 = hp[2], h3 = hp[3];
+            // piece j + LD i of both rows: columns CP (j + LD i) .. + CP - 1 of the segment
+            const float4 *hp = hs4 + (t * kDS + (j + g::LD * i) * g::CP) / 4;
             const uint32_t wv[4] = {b.w[i].x | zero, b.w[i].y | zero, b.w[i].z | zero, b.w[i].w | zero};
             const uint32_t vv[4] = {b.w[kPc + i].x | zero, b.w[kPc + i].y | zero, b.w[kPc + i].z | zero,
                                     b.w[kPc + i].w | zero};
-            const float4 hq[4] = {h0, h1, h2, h3};
+            if constexpr (BF) {
+                const float4 hq[2] = {hp[0], hp[1]};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x2 p0 = fp8x2_to_f32<false>(wv[q]), p1 = fp8x2_to_f32<true>(wv[q]);
-                const f32x2 q0 = fp8x2_to_f32<false>(vv[q]), q1 = fp8x2_to_f32<true>(vv[q]);
-                s0 = fmaf(p0.x, hq[q].x, s0); s0 = fmaf(p0.y, hq[q].y, s0);
-                s0 = fmaf(p1.x, hq[q].z, s0); s0 = fmaf(p1.y, hq[q].w, s0);
-                s1 = fmaf(q0.x, hq[q].x, s1); s1 = fmaf(q0.y, hq[q].y, s1);
-                s1 = fmaf(q1.x, hq[q].z, s1); s1 = fmaf(q1.y, hq[q].w, s1);
+                for (int q = 0; q < 4; ++q) {
+                    const float hx = q & 1 ? hq[q >> 1].z : hq[q >> 1].x, hy = q & 1 ? hq[q >> 1].w : hq[q >> 1].y;
+                    s0 = fmaf(__uint_as_float(wv[q] << 16), hx, s0);
+                    s0 = fmaf(__uint_as_float(wv[q] & 0xffff0000u), hy, s0);
+                    s1 = fmaf(__uint_as_float(vv[q] << 16), hx, s1);
+                    s1 = fmaf(__uint_as_float(vv[q] & 0xffff0000u), hy, s1);
+                }
+            } else {
+                const float4 hq[4] = {hp[0], hp[1], hp[2], hp[3]};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x2 p0 = fp8x2_to_f32<false>(wv[q]), p1 = fp8x2_to_f32<true>(wv[q]);
+                    const f32x2 q0 = fp8x2_to_f32<false>(vv[q]), q1 = fp8x2_to_f32<true>(vv[q]);
+                    s0 = fmaf(p0.x, hq[q].x, s0); s0 = fmaf(p0.y, hq[q].y, s0);
+                    s0 = fmaf(p1.x, hq[q].z, s0); s0 = fmaf(p1.y, hq[q].w, s0);
+                    s1 = fmaf(q0.x, hq[q].x, s1); s1 = fmaf(q0.y, hq[q].y, s1);
+                    s1 = fmaf(q1.x, hq[q].z, s1); s1 = fmaf(q1.y, hq[q].w, s1);
+                }
             }
         }
+        // sums over the LD lanes of the row pair (8: two quads; 16: a DPP row)
         float v0 = quad_sum(s0);
         v0 += dpp<0x141>(v0);   // row_half_mirror: the two quads of each 8-lane group
         float v1 = quad_sum(s1);
         v1 += dpp<0x141>(v1);
+        if constexpr (BF) {
+            v0 += dpp<0x140>(v0);   // row_mirror: the two halves of the 16-lane row
+            v1 += dpp<0x140>(v1);
+        }
         if (j == 0) {
             const float cw = S.sw[u.s][m];
             uint64_t *yp = ypart(a, l, u.js, m);
             st64(yp + c0, tagged(__float_as_uint(cw * (b.sc[0] * v0)), tgt));
-            st64(yp + c0 + 32, tagged(__float_as_uint(cw * (b.sc[1] * v1)), tgt));
+            st64(yp + c0 + g::RD / 2, tagged(__float_as_uint(cw * (b.sc[1] * v1)), tgt));
         }
         // the next token of the slot
 #pragma unroll
@@ -994,12 +1051,12 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
     }
 }
 
-template <int MT>
+template <int MT, bool BF>
 __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const UnitBuf &b, uint32_t tgt) {
     if (u.kind == kGU) {
-        run_gu<MT>(a, l, u, b, tgt);
+        run_gu<MT, BF>(a, l, u, b, tgt);
     } else if (u.kind == kDN) {
-        run_dn<MT>(a, l, u, b, tgt);
+        run_dn<MT, BF>(a, l, u, b, tgt);
     } else {
         run_cmb<MT>(a, l, u.cb, tgt);
     }
@@ -1010,25 +1067,25 @@ __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const Un
 // expert-shaped 45 KB reads on MI355X holds 6-6.7 TB/s at one or two units per
 // workgroup, and deeper prefetch loses bandwidth once the units carry compute). A
 // shared-expert unit's weights are requested before the routing is known.
-template <int MT>
+template <int MT, bool BF>
 __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32_t tgt) {
     const AP a = uniform(a0);
     norm_to_lds<MT>(a, l, a->gains + (size_t)l * a->H, tgt);
     // the shared expert's units sit at fixed places at the head of the list
-    const UnitList L0 = unit_list(a, a->Ds > 0 ? 1 : 0);
+    const UnitList L0 = unit_list<BF>(a, a->Ds > 0 ? 1 : 0);
     UnitBuf A, B;
     const bool early = w < L0.sh_dn;
-    if (early) load_unit(a, l, decode_unit(a, w, L0), A, true);
+    if (early) load_unit<BF>(a, l, decode_unit<BF>(a, w, L0), A, true);
     const int ns = route_phase<MT>(a, l, tgt, w == 0);
-    const UnitList L = unit_list(a, ns);
-    if (!early && w < L.U) load_unit(a, l, decode_unit(a, w, L), A, false);
-    if (w + GU < L.U) load_unit(a, l, decode_unit(a, w + GU, L), B, false);
+    const UnitList L = unit_list<BF>(a, ns);
+    if (!early && w < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w, L), A, false);
+    if (w + GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + GU, L), B, false);
     for (int i = w; i < L.U; i += 2 * GU) {
-        run_unit<MT>(a, l, decode_unit(a, i, L), A, tgt);
-        if (i + 2 * GU < L.U) load_unit(a, l, decode_unit(a, i + 2 * GU, L), A, false);
+        run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), A, tgt);
+        if (i + 2 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 2 * GU, L), A, false);
         if (i + GU < L.U) {
-            run_unit<MT>(a, l, decode_unit(a, i + GU, L), B, tgt);
-            if (i + 3 * GU < L.U) load_unit(a, l, decode_unit(a, i + 3 * GU, L), B, false);
+            run_unit<MT, BF>(a, l, decode_unit<BF>(a, i + GU, L), B, tgt);
+            if (i + 3 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 3 * GU, L), B, false);
         }
     }
 }
@@ -1207,7 +1264,7 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
 #ifndef MOE_STEP_MIN_BLOCKS
 #define MOE_STEP_MIN_BLOCKS 2
 #endif
-template <int MT>
+template <int MT, bool BF>
 __global__ __launch_bounds__(256, MOE_STEP_MIN_BLOCKS) void k_step(StepArgs args) {
     (void)args;
     const AP base = (AP)__builtin_amdgcn_kernarg_segment_ptr();
@@ -1232,7 +1289,7 @@ __global__ __launch_bounds__(256, MOE_STEP_MIN_BLOCKS) void k_step(StepArgs args
             AP a = base;
             asm volatile("" : "+s"(a));
             if (l >= a->L) break;
-            expert_phase<MT>(a, l, w, GU, tgt);
+            expert_phase<MT, BF>(a, l, w, GU, tgt);
         }
     }
     AP a = base;
@@ -1252,17 +1309,33 @@ inline hipStream_t Sm(void *p) { return reinterpret_cast<hipStream_t>(p); }
 
 // Every workgroup must be resident at once (units wait on other workgroups' units): the
 // grid is the occupancy of the step kernel for M tokens times the compute units.
-template <int MT>
+template <int MT, bool BF>
 int launch_mt(const StepArgs &a, size_t lds, int NR, void *stream) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<MT>, kWG, lds) != hipSuccess || per_cu < 1)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<MT, BF>, kWG, lds) != hipSuccess || per_cu < 1)
         return MOE_ELAUNCH;
     const int grid = std::min(cus * per_cu, kStepMaxGrid);
     if (grid <= NR) return MOE_ELAUNCH;   // the last NR workgroups only route
-    hipLaunchKernelGGL(k_step<MT>, dim3(grid), dim3(kWG), lds, Sm(stream), a);
+    hipLaunchKernelGGL((k_step<MT, BF>), dim3(grid), dim3(kWG), lds, Sm(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+// One kernel per token count (token loops are unrolled exactly) and expert weight type.
+template <bool BF>
+int launch_m(int M, const StepArgs &a, size_t lds, int NR, void *stream) {
+    switch (M) {
+    case 1: return launch_mt<1, BF>(a, lds, NR, stream);
+    case 2: return launch_mt<2, BF>(a, lds, NR, stream);
+    case 3: return launch_mt<3, BF>(a, lds, NR, stream);
+    case 4: return launch_mt<4, BF>(a, lds, NR, stream);
+    case 5: return launch_mt<5, BF>(a, lds, NR, stream);
+    case 6: return launch_mt<6, BF>(a, lds, NR, stream);
+    case 7: return launch_mt<7, BF>(a, lds, NR, stream);
+    case 8: return launch_mt<8, BF>(a, lds, NR, stream);
+    default: return MOE_EINVAL;
+    }
 }
 
 size_t step_lds_bytes(const moe_step_desc &d, int *l_scr, int *l_slot) {
@@ -1359,17 +1432,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpin;
 
     const size_t lds = step_lds_bytes(d, &a.l_scr, &a.l_slot);
-    switch (M) {   // one kernel per token count: token loops are unrolled exactly
-    case 1: return launch_mt<1>(a, lds, W.NR, stream);
-    case 2: return launch_mt<2>(a, lds, W.NR, stream);
-    case 3: return launch_mt<3>(a, lds, W.NR, stream);
-    case 4: return launch_mt<4>(a, lds, W.NR, stream);
-    case 5: return launch_mt<5>(a, lds, W.NR, stream);
-    case 6: return launch_mt<6>(a, lds, W.NR, stream);
-    case 7: return launch_mt<7>(a, lds, W.NR, stream);
-    case 8: return launch_mt<8>(a, lds, W.NR, stream);
-    default: return MOE_EINVAL;
-    }
+    return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, stream) : launch_m<false>(M, a, lds, W.NR, stream);
 }
 
 }  // namespace moe

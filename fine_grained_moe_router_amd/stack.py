@@ -79,7 +79,8 @@ class FusedDecodeStep:
         self.max_M = max_M
         self.layers = layers
         self.gains, self.lm_w, self.lm_s = gains, lm_w, lm_s
-        self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit)
+        expert_dtype = layers[0].get("expert_dtype", "fp8")
+        self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit, expert_dtype)
         self.ws_bytes = native.moe_decode_step_workspace(self.desc)
         if self.ws_bytes == 0:
             raise ValueError("unsupported shape for the fused decode step")

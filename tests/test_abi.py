@@ -122,13 +122,17 @@ def test_layer_workspace_validation():
     assert call_layer(M=5, ws=FAKE + 16) == native.MOE_EWORKSPACE     # not 256-byte aligned
 
 
-def test_bf16_experts_are_reported_unsupported_after_validation():
+def test_bf16_experts_pass_validation_without_scales():
     d = native.LayerDesc(2816, 128, 8, 704, 704, native.MOE_W_BF16)
     need = native.lib().moe_decode_layer_workspace(ctypes.byref(d), 1)
-    # bf16 weights need no scales: NULL scales pass validation
+    assert need > 0
+    # bf16 weights need no scales: with NULL scales the call gets past the weight checks
+    # and stops at the (deliberately short) workspace, before anything is launched
     w = fake_weights(gate_s=None, up_s=None, down_s=None, sh_gate_s=None, sh_up_s=None, sh_down_s=None)
-    st = call_layer(desc=d, weights=w, ws_bytes=need)
-    assert st in (native.MOE_EUNSUPPORTED,)
+    assert call_layer(desc=d, weights=w, ws_bytes=need - 1) == native.MOE_EWORKSPACE
+    # while FP8 weights without scales are rejected
+    d8 = native.LayerDesc(2816, 128, 8, 704, 704, native.MOE_W_FP8_E4M3)
+    assert call_layer(desc=d8, weights=w, ws_bytes=need) == native.MOE_EINVAL
 
 
 def test_lm_head_validation():

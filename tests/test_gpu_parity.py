@@ -26,12 +26,13 @@ def say(*a):
 class Layer:
     """Device weights of one layer plus a host copy for the oracle."""
 
-    def __init__(self, shape, layer=0, seed=0, device_gen="cpu", router_bias=None):
-        w = synth.layer_weights(shape, layer, device_gen, seed=seed, router_bias=router_bias)
+    def __init__(self, shape, layer=0, seed=0, device_gen="cpu", router_bias=None, expert_dtype="fp8"):
+        w = synth.layer_weights(shape, layer, device_gen, seed=seed, router_bias=router_bias,
+                                expert_dtype=expert_dtype)
         self.shape = shape
         self.dev = to_device(w, DEV)
         self.host = synth.weights_to_host(w)
-        self.desc = native.layer_desc(shape)
+        self.desc = native.layer_desc(shape, expert_dtype)
         self.lw = native.layer_weights(self.dev)
 
     def run(self, x_bits_dev, M):
@@ -113,6 +114,33 @@ def test_layer_with_zipf_router_bias():
     for M in (1, 8):
         x, r = unambiguous_layer_input(sh, M, L.host, 200)
         check_layer(L, x, r, "zipf M=%d" % M)
+
+
+BF16_SHAPES = {
+    "tiny": synth.TINY,
+    "tiny_wide_shared": synth.TINY.with_(shared_width=192),
+    "h2816": synth.TINY.with_(hidden=2816, experts=32, top_k=4, width=704, shared_width=704),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BF16_SHAPES))
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_layer_bf16_experts(name, M):
+    """bf16 expert weights (no scales): the same layer arithmetic with the weights used
+    as they are."""
+    sh = BF16_SHAPES[name]
+    say("bf16 experts %s M=%d" % (name, M))
+    L = Layer(sh, seed=6, expert_dtype="bf16")
+    x, r = unambiguous_layer_input(sh, M, L.host, 300 + M)
+    check_layer(L, x, r, "bf16 %s M=%d" % (name, M))
+
+
+def test_layer_bf16_experts_with_zipf_router_bias():
+    sh = synth.TINY.with_(experts=64, top_k=4, hidden=512)
+    L = Layer(sh, seed=7, router_bias=synth.zipf_router_bias(64), expert_dtype="bf16")
+    for M in (1, 8):
+        x, r = unambiguous_layer_input(sh, M, L.host, 400)
+        check_layer(L, x, r, "bf16 zipf M=%d" % M)
 
 
 def test_batch_consistency_identical_tokens_and_determinism():

@@ -21,8 +21,9 @@ def say(*a):
     print(*a, flush=True)
 
 
-def make(shape, seed=0):
-    layers = [synth.layer_weights(shape, l, "cpu", seed=seed, tag="fused") for l in range(shape.layers)]
+def make(shape, seed=0, expert_dtype="fp8", router_bias=None):
+    layers = [synth.layer_weights(shape, l, "cpu", seed=seed, tag="fused", expert_dtype=expert_dtype,
+                                  router_bias=router_bias) for l in range(shape.layers)]
     host = [synth.weights_to_host(w) for w in layers]
     gains = synth.rmsnorm_gains(shape, seed=seed)
     Q, s = synth.lm_head(shape, seed=seed)
@@ -41,8 +42,8 @@ def oracle_step(shape, host, gains, Q, s, M, step):
     raise RuntimeError("no unambiguous input")
 
 
-def run_and_check(shape, M, step, seed=0, what=""):
-    layers, host, gains, Q, s, dev = make(shape, seed)
+def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None):
+    layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias)
     x, noise, res = oracle_step(shape, host, gains, Q, s, M, step)
     drafts = synth.drafts(res["tok"], 0.7, shape.vocab, step)
     n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
@@ -93,6 +94,24 @@ FUSED_VARIANTS = {
 def test_fused_step_variants(name, M):
     say("fused variant %s M=%d" % (name, M))
     run_and_check(FUSED_VARIANTS[name], M, step=500 + M, seed=2, what=name)
+
+
+@pytest.mark.parametrize("name", ["tiny", "h2816"])
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_step_bf16_experts(name, M):
+    """bf16 expert weights: half the rows per unit, the same hand-offs."""
+    sh = synth.TINY.with_(layers=2) if name == "tiny" else FUSED_VARIANTS["h2816"]
+    say("fused bf16 %s M=%d" % (name, M))
+    run_and_check(sh, M, step=600 + M, seed=5, what="bf16 " + name, expert_dtype="bf16")
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_fused_step_zipf_router_bias_m8(dtype):
+    """The skewed-routing configuration in small: M=8 with a Zipf router bias."""
+    sh = synth.TINY.with_(experts=64, top_k=4, hidden=512, width=128, layers=2)
+    say("fused zipf M=8 %s" % dtype)
+    run_and_check(sh, 8, step=700, seed=6, what="zipf " + dtype, expert_dtype=dtype,
+                  router_bias=synth.zipf_router_bias(64))
 
 
 def test_fused_step_batch_consistency_and_determinism():
