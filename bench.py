@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes 5 times (a known "
                          "byte count for calibrating hardware traffic counters) and exit")
+    ap.add_argument("--zipf", action="store_true",
+                    help="the skewed-routing configuration instead: the stack at M=8 with a Zipf(1.1) "
+                         "router bias, once with FP8 and once with bf16 expert weights (its own JSON line)")
     ap.add_argument("--path", choices=("fused", "layers"), default="fused",
                     help="fused: one moe_decode_step launch per step; layers: per-layer entry points "
                          "captured in a HIP graph per step")
@@ -106,6 +109,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 5}), flush=True)
         return
+    if args.zipf:
+        return zipf_main(args)
     import synth
     from fine_grained_moe_router_amd import budget, native
     from fine_grained_moe_router_amd.stack import DecodeStack, FusedDecodeStep
@@ -127,84 +132,7 @@ def main():
     else:
         runner = DecodeStack(sh, layers, gains, Q, s, max_M=max(Ms))
 
-    results = {}
-    for M in Ms:
-        n = K + W
-        xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="bench_x") for i in range(n)]
-        noises = [synth.stack_noise(sh, M, i, device=dev, seed=args.seed) for i in range(n)]
-        g = torch.Generator().manual_seed(synth.seed_of(args.seed, "bench_drafts", M))
-        drafts = [torch.randint(0, sh.vocab, (max(M - 1, 1),), generator=g, dtype=torch.int32).to(dev)
-                  for _ in range(n)]
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        if args.path == "fused":
-            def launch(i, outputs=False):
-                runner.step(xs[i], noises[i], drafts[i], M, stream=stream, outputs=outputs)
-        else:
-            graphs = []
-            with torch.cuda.stream(stream):
-                runner.step(xs[0], noises[0], drafts[0], M)
-                torch.cuda.synchronize()
-                for i in range(n):
-                    gr = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(gr, stream=stream):
-                        runner.step(xs[i], noises[i], drafts[i], M)
-                    graphs.append(gr)
-            torch.cuda.synchronize()
-            log("M=%d: %d step graphs captured" % (M, n))
-
-            def launch(i, outputs=False):
-                graphs[i].replay()
-
-        with torch.cuda.stream(stream):
-            for i in range(W):
-                launch(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            w0 = time.perf_counter()
-            e0.record(stream)
-            for i in range(W, n):
-                launch(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - w0
-            ms_total = e0.elapsed_time(e1)
-
-            # per-step latency distribution and the routing each step took
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-            ev[0].record(stream)
-            for j, i in enumerate(range(W, n)):
-                launch(i)
-                ev[j + 1].record(stream)
-            torch.cuda.synchronize()
-            per_step = [ev[j].elapsed_time(ev[j + 1]) for j in range(K)]
-            uniq = []
-            for i in range(W, n):
-                launch(i, outputs=True)
-                torch.cuda.synchronize()
-                idx = (runner.topk_idx(M) if args.path == "fused" else runner.topk_idx[:, :M]).cpu().numpy()
-                uniq.append([len(np.unique(idx[l])) for l in range(sh.layers)])
-        if args.path == "fused":
-            st_code = runner.status()
-            if st_code != native.MOE_OK:
-                raise RuntimeError("fused step reported %s" % native.strerror(st_code))
-
-        bytes_steps = [budget.step_bytes(sh, u, M) for u in uniq]
-        ms = ms_total / K
-        bps = float(np.mean(bytes_steps))
-        results[M] = {
-            "steps_per_s": K / (ms_total / 1e3), "ms_per_step": ms, "wall_s": wall,
-            "p50_ms": float(np.percentile(per_step, 50)), "p99_ms": float(np.percentile(per_step, 99)),
-            "bytes_per_step": bps, "hbm_gbs": bps / (ms / 1e3) / 1e9,
-            "hbm_frac": bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "mean_unique_experts_per_layer": float(np.mean(uniq)),
-        }
-        log("M=%d: %.3f ms/step, %.1f steps/s, %.1f GB/s (%.1f%% of 8 TB/s), p50 %.3f p99 %.3f ms" % (
-            M, ms, results[M]["steps_per_s"], results[M]["hbm_gbs"], 100 * results[M]["hbm_frac"],
-            results[M]["p50_ms"], results[M]["p99_ms"]))
-        if args.path != "fused":
-            del graphs
-        torch.cuda.synchronize()
+    results = {M: measure(args, runner, sh, M) for M in Ms}
 
     M0 = Ms[0]
     head = results[M0]
@@ -272,6 +200,159 @@ def main():
                   for M, r in results.items()},
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
+    """Warm up, then time exactly args.steps steps of the runner at M tokens (HIP events
+    on the launch stream, bracketed by device synchronisations); then record each timed
+    step's routing to count the bytes it needed."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import budget, native
+    dev = "cuda"
+    K, W = args.steps, args.warmup
+    n = K + W
+    xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="bench_x") for i in range(n)]
+    noises = [synth.stack_noise(sh, M, i, device=dev, seed=args.seed) for i in range(n)]
+    g = torch.Generator().manual_seed(synth.seed_of(args.seed, "bench_drafts", M))
+    drafts = [torch.randint(0, sh.vocab, (max(M - 1, 1),), generator=g, dtype=torch.int32).to(dev)
+              for _ in range(n)]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    if args.path == "fused":
+        def launch(i, outputs=False):
+            runner.step(xs[i], noises[i], drafts[i], M, stream=stream, outputs=outputs)
+    else:
+        graphs = []
+        with torch.cuda.stream(stream):
+            runner.step(xs[0], noises[0], drafts[0], M)
+            torch.cuda.synchronize()
+            for i in range(n):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    runner.step(xs[i], noises[i], drafts[i], M)
+                graphs.append(gr)
+        torch.cuda.synchronize()
+        log("M=%d: %d step graphs captured" % (M, n))
+
+        def launch(i, outputs=False):
+            graphs[i].replay()
+
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            launch(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(W, n):
+            launch(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        ms_total = e0.elapsed_time(e1)
+
+        # per-step latency distribution and the routing each step took
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for j, i in enumerate(range(W, n)):
+            launch(i)
+            ev[j + 1].record(stream)
+        torch.cuda.synchronize()
+        per_step = [ev[j].elapsed_time(ev[j + 1]) for j in range(K)]
+        uniq = []
+        for i in range(W, n):
+            launch(i, outputs=True)
+            torch.cuda.synchronize()
+            idx = (runner.topk_idx(M) if args.path == "fused" else runner.topk_idx[:, :M]).cpu().numpy()
+            uniq.append([len(np.unique(idx[l])) for l in range(sh.layers)])
+    if args.path == "fused":
+        st_code = runner.status()
+        if st_code != native.MOE_OK:
+            raise RuntimeError("fused step reported %s" % native.strerror(st_code))
+
+    bytes_steps = [budget.step_bytes(sh, u, M, expert_dtype, bias) for u in uniq]
+    ms = ms_total / K
+    bps = float(np.mean(bytes_steps))
+    r = {
+        "steps_per_s": K / (ms_total / 1e3), "ms_per_step": ms, "wall_s": wall,
+        "p50_ms": float(np.percentile(per_step, 50)), "p99_ms": float(np.percentile(per_step, 99)),
+        "bytes_per_step": bps, "hbm_gbs": bps / (ms / 1e3) / 1e9,
+        "hbm_frac": bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+        "mean_unique_experts_per_layer": float(np.mean(uniq)),
+    }
+    log("M=%d: %.3f ms/step, %.1f steps/s, %.1f GB/s (%.1f%% of 8 TB/s), p50 %.3f p99 %.3f ms" % (
+        M, ms, r["steps_per_s"], r["hbm_gbs"], 100 * r["hbm_frac"], r["p50_ms"], r["p99_ms"]))
+    if args.path != "fused":
+        del graphs
+    torch.cuda.synchronize()
+    return r
+
+
+def zipf_main(args):
+    """The skewed-routing configuration: the 30-layer stack at M=8 tokens per step with a
+    router bias b_e = -1.1 ln(rank_e) (Zipf(1.1) expert popularity), run twice on the
+    fused step: FP8 expert weights (5,964,288 B per expert) and bf16 expert weights
+    (11,894,784 B per expert, no scales). Reports steps/s, bytes/step and the realised
+    union size per layer for each; one JSON line."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import native
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    M = 8
+    sh = synth.GEMMA4_26B_A4B.with_(layers=args.layers)
+    bias = synth.zipf_router_bias(sh.experts, seed=args.seed)
+    gains = synth.rmsnorm_gains(sh, dev, seed=args.seed)
+    Q, s = synth.lm_head(sh, dev, seed=args.seed)
+    per = {}
+    for dt in ("fp8", "bf16"):
+        t0 = time.time()
+        layers = [synth.layer_weights(sh, l, dev, seed=args.seed, tag="stack", expert_dtype=dt, router_bias=bias)
+                  for l in range(sh.layers)]
+        torch.cuda.synchronize()
+        log("%s experts generated in %.1fs (%.2f GB resident)" % (dt, time.time() - t0,
+                                                                 torch.cuda.memory_allocated() / 1e9))
+        runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=M)
+        r = measure(args, runner, sh, M, dt, bias=True)
+        per[dt] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        del runner, layers
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = per["fp8"]
+    line = {
+        "metric": "decode steps/s + bytes/step, 26B-A4B MoE stack with Zipf(1.1)-skewed routing, M=8, "
+                  "FP8 and bf16 experts",
+        "value": round(head["steps_per_s"], 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 (value) and bf16 (per_dtype) expert weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,.) weights, FP8 E4M3FN or bf16 experts, N(0,1) inputs, Zipf router bias)",
+        "config": {"workload": "Gemma-4-26B-A4B-shaped MoE stack, 30 layers, router bias -1.1 ln(rank), "
+                               "M=8 tokens/step, + tied 262144x2816 FP8 lm_head + argmax + greedy accept",
+                   "path": "fused", "M": M, "layers": sh.layers, "hidden": sh.hidden,
+                   "experts": sh.experts, "top_k": sh.top_k, "expert_width": sh.width,
+                   "vocab": sh.vocab},
+        "bytes_per_step": int(head["bytes_per_step"]),
+        "hbm_gbs": round(head["hbm_gbs"], 1),
+        "hbm_frac": round(head["hbm_frac"], 4),
+        "per_dtype": per,
+        "roofline": {"bound": "hbm", "kernel": "k_step (moe_decode_step, M=8, FP8 experts)",
+                     "achieved": round(head["hbm_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["hbm_frac"], 4), "traffic": None,
+                     "bytes_per_launch": int(head["bytes_per_step"]),
+                     "avg_launch_us": round(head["ms_per_step"] * 1e3, 2)},
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
