@@ -79,6 +79,13 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MB",
                     help="only run a plain device-to-device copy of MB megabytes 5 times (a known "
                          "byte count for calibrating hardware traffic counters) and exit")
+    ap.add_argument("--layer", action="store_true",
+                    help="the one-layer configurations instead, through the per-layer entry points: "
+                         "a Gemma-shaped MoE layer at M=1, and at M=5 followed by the lm_head, argmax "
+                         "and acceptance; --steps fresh inputs each (its own JSON line)")
+    ap.add_argument("--copies", type=int, default=8,
+                    help="--layer: weight copies rotated step by step, so that an expert's reuse "
+                         "distance exceeds the Infinity Cache")
     ap.add_argument("--zipf", action="store_true",
                     help="the skewed-routing configuration instead: the stack at M=8 with a Zipf(1.1) "
                          "router bias, once with FP8 and once with bf16 expert weights (its own JSON line)")
@@ -111,6 +118,8 @@ def main():
         return
     if args.zipf:
         return zipf_main(args)
+    if args.layer:
+        return layer_main(args)
     import synth
     from fine_grained_moe_router_amd import budget, native
     from fine_grained_moe_router_amd.stack import DecodeStack, FusedDecodeStep
@@ -289,6 +298,112 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
         del graphs
     torch.cuda.synchronize()
     return r
+
+
+def layer_main(args):
+    """The one-layer configurations, through the boundary's per-layer entry points:
+    (a) one Gemma-4-26B-A4B-shaped MoE layer at M=1 (moe_decode_layer), and (b) the same
+    layer at M=5 followed by lm_head_argmax and spec_accept (the verify step). Each step
+    takes a fresh seeded input; the layer's weights rotate over args.copies copies (8 x
+    0.77 GB) and the lm_head over 2, so no step finds its weights in the 256 MB Infinity
+    Cache. The timed steps are captured into HIP graphs of 100 steps each (a step is a
+    few launches), replayed back to back on one stream and timed with HIP events."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import budget, native
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    sh = synth.GEMMA4_26B_A4B.with_(layers=1)
+    R, K, W = args.copies, args.steps, args.warmup
+    desc = native.layer_desc(sh)
+    copies = [synth.layer_weights(sh, 0, dev, seed=args.seed + c, tag="layer") for c in range(R)]
+    lws = [native.layer_weights(w) for w in copies]
+    lms = [synth.lm_head(sh, dev, seed=args.seed + c) for c in range(2)]
+    torch.cuda.synchronize()
+    log("layer copies: %d x %.2f GB, lm_head copies: 2 (%.2f GB resident)" % (
+        R, budget.expert_bytes(sh.hidden, sh.width) * sh.experts / 1e9, torch.cuda.memory_allocated() / 1e9))
+    out = {}
+    for M, with_lm in ((1, False), (5, True)):
+        n = K + W
+        xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="layer_x") for i in range(n)]
+        wsb = native.moe_decode_layer_workspace(desc, M)
+        ws = native.workspace(wsb)
+        lwsb = native.lm_head_argmax_workspace(M, sh.hidden, sh.vocab)
+        lws_ = native.workspace(lwsb)
+        y = torch.empty(M, sh.hidden, dtype=torch.bfloat16, device=dev)
+        idx = torch.empty(n, M, sh.top_k, dtype=torch.int32, device=dev)
+        wts = torch.empty(M, sh.top_k, dtype=torch.float32, device=dev)
+        tok = torch.empty(M, dtype=torch.int32, device=dev)
+        acc = torch.empty(4, dtype=torch.int32, device=dev)
+        outt = torch.empty(M, dtype=torch.int32, device=dev)
+        g = torch.Generator().manual_seed(synth.seed_of(args.seed, "layer_drafts", M))
+        drafts = torch.randint(0, sh.vocab, (n, max(M - 1, 1)), generator=g, dtype=torch.int32).to(dev)
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+
+        def launch(i):
+            native.moe_decode_layer(desc, lws[i % R], M, xs[i], y, idx[i], wts, ws, wsb, stream)
+            if with_lm:
+                Q, s = lms[i % 2]
+                native.lm_head_argmax(M, sh.hidden, sh.vocab, y, Q, s, tok, None, lws_, lwsb, stream)
+                native.spec_accept(M - 1, drafts[i], tok, acc, outt, stream)
+
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                launch(i)
+            torch.cuda.synchronize()
+            graphs = []
+            for c0 in range(W, n, 100):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    for i in range(c0, min(n, c0 + 100)):
+                        launch(i)
+                graphs.append(gr)
+            torch.cuda.synchronize()
+            graphs[0].replay()   # warm replay
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for gr in graphs:
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / K
+        del graphs
+        ih = idx[W:].cpu().numpy()
+        uniq = [len(np.unique(ih[j])) for j in range(K)]
+        bps = float(np.mean([budget.layer_bytes(sh, u, M) for u in uniq]))
+        if with_lm:
+            bps += budget.lm_head_bytes(sh.vocab, sh.hidden) + 16 * M
+        name = "layer_m1" if not with_lm else "verify_m5_lm_head"
+        out[name] = {"us_per_step": round(ms * 1e3, 2), "steps_per_s": round(1e3 / ms, 1),
+                     "bytes_per_step": int(bps), "hbm_gbs": round(bps / (ms / 1e3) / 1e9, 1),
+                     "hbm_frac": round(bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mean_unique_experts": round(float(np.mean(uniq)), 2)}
+        log("%s: %.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s), %.2f MB/step, union %.2f" % (
+            name, ms * 1e3, out[name]["hbm_gbs"], 100 * out[name]["hbm_frac"], bps / 1e6, np.mean(uniq)))
+    head = out["layer_m1"]
+    line = {
+        "metric": "per-step latency + achieved HBM GB/s, one 26B-A4B MoE layer (M=1) and its verify step "
+                  "with lm_head (M=5)",
+        "value": head["steps_per_s"], "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(head["us_per_step"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,.) weights quantised to FP8 E4M3FN, N(0,1) inputs), %d layer copies "
+                "and 2 lm_head copies rotated" % R,
+        "config": {"workload": "one Gemma-4-26B-A4B-shaped MoE layer (router 2816x128, top-8 of 128 + shared, "
+                               "width 704, FP8) at M=1; at M=5 + tied 262144x2816 FP8 lm_head + argmax + "
+                               "greedy accept", "path": "layers", "hidden": sh.hidden, "experts": sh.experts,
+                   "top_k": sh.top_k, "expert_width": sh.width, "vocab": sh.vocab},
+        "per_config": out,
+        "roofline": {"bound": "hbm", "kernel": "moe_decode_layer (5 launches, M=1)",
+                     "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": None, "bytes_per_launch": head["bytes_per_step"],
+                     "avg_launch_us": head["us_per_step"]},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def zipf_main(args):
