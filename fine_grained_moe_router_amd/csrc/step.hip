@@ -1079,6 +1079,25 @@ __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32
     const int ns = route_phase<MT>(a, l, tgt, w == 0);
     const UnitList L = unit_list<BF>(a, ns);
     if (!early && w < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w, L), A, false);
+    if constexpr (MT == 1) {
+        // One token: every workgroup's first unit is requested alone and runs as soon as
+        // its weights are in. Requesting the second unit as well would hold the first
+        // unit's compute until the second's loads have been accepted, which takes as long
+        // as the whole layer's weight burst.
+        if (w >= L.U) return;
+        run_unit<MT, BF>(a, l, decode_unit<BF>(a, w, L), A, tgt);
+        if (w + GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + GU, L), B, false);
+        if (w + 2 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + 2 * GU, L), A, false);
+        for (int i = w + GU; i < L.U; i += 2 * GU) {
+            run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), B, tgt);
+            if (i + 2 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 2 * GU, L), B, false);
+            if (i + GU < L.U) {
+                run_unit<MT, BF>(a, l, decode_unit<BF>(a, i + GU, L), A, tgt);
+                if (i + 3 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 3 * GU, L), A, false);
+            }
+        }
+        return;
+    }
     if (w + GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + GU, L), B, false);
     for (int i = w; i < L.U; i += 2 * GU) {
         run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), A, tgt);
