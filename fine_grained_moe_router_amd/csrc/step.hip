@@ -19,7 +19,7 @@
 //  units    the layer's work is a list: 8-row gate/up units (gate and up rows of one
 //           slot), 64-row down units (one slot, one row block), then 64-row combine
 //           units. Unit i belongs to workgroup i mod G, which keeps two of its units'
-//           weights in flight. A gate/up unit writes h = gelu_tanh(gate) * up for the
+//           weights in flight (one, with one token). A gate/up unit writes h = gelu_tanh(gate) * up for the
 //           slot's tokens; a down unit reads the slot's h, multiplies and writes its
 //           weighted partial sums; a combine unit sums a row block's sub-slots in a
 //           fixed order into y_l, adds the residual and the next layer's noise and
@@ -1063,7 +1063,8 @@ __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const Un
 }
 
 // Unit workgroup w (0 <= w < GU), layer l: u_l, the routing, then its units w, w + GU,
-// ..., two in flight (about 45 MB requested across the chip; a measured sweep of
+// ..., two in flight with several tokens and one with one token (about 45 MB requested
+// across the chip with two; a measured sweep of
 // expert-shaped 45 KB reads on MI355X holds 6-6.7 TB/s at one or two units per
 // workgroup, and deeper prefetch loses bandwidth once the units carry compute). A
 // shared-expert unit's weights are requested before the routing is known.
@@ -1073,31 +1074,25 @@ __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32
     norm_to_lds<MT>(a, l, a->gains + (size_t)l * a->H, tgt);
     // the shared expert's units sit at fixed places at the head of the list
     const UnitList L0 = unit_list<BF>(a, a->Ds > 0 ? 1 : 0);
-    UnitBuf A, B;
+    UnitBuf A;
     const bool early = w < L0.sh_dn;
     if (early) load_unit<BF>(a, l, decode_unit<BF>(a, w, L0), A, true);
     const int ns = route_phase<MT>(a, l, tgt, w == 0);
     const UnitList L = unit_list<BF>(a, ns);
     if (!early && w < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w, L), A, false);
     if constexpr (MT == 1) {
-        // One token: every workgroup's first unit is requested alone and runs as soon as
-        // its weights are in. Requesting the second unit as well would hold the first
-        // unit's compute until the second's loads have been accepted, which takes as long
-        // as the whole layer's weight burst.
-        if (w >= L.U) return;
-        run_unit<MT, BF>(a, l, decode_unit<BF>(a, w, L), A, tgt);
-        if (w + GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + GU, L), B, false);
-        if (w + 2 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + 2 * GU, L), A, false);
-        for (int i = w + GU; i < L.U; i += 2 * GU) {
-            run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), B, tgt);
-            if (i + 2 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 2 * GU, L), B, false);
-            if (i + GU < L.U) {
-                run_unit<MT, BF>(a, l, decode_unit<BF>(a, i + GU, L), A, tgt);
-                if (i + 3 * GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, i + 3 * GU, L), A, false);
-            }
+        // One token: one unit in flight per workgroup, requested as soon as the routing
+        // is known (or the unit before it is done) and computed as soon as its weights
+        // are in. A second unit in flight would hold the first unit's compute until the
+        // second's loads had been accepted, which takes as long as the layer's weight
+        // burst.
+        for (int i = w; i < L.U; i += GU) {
+            if (i != w) load_unit<BF>(a, l, decode_unit<BF>(a, i, L), A, false);
+            run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), A, tgt);
         }
         return;
     }
+    UnitBuf B;
     if (w + GU < L.U) load_unit<BF>(a, l, decode_unit<BF>(a, w + GU, L), B, false);
     for (int i = w; i < L.U; i += 2 * GU) {
         run_unit<MT, BF>(a, l, decode_unit<BF>(a, i, L), A, tgt);
@@ -1142,16 +1137,28 @@ __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmB
     const int tid = ltid(), NC = a->H / 256, M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
     const int k = st % NC;
     const uint16_t *xl = ulds();
-    bf16x2 wv[kLmRows][8];
+    if constexpr (MT == 1) {
+        // one token: each row is decoded just before its dot product (fewer live registers)
+        const uint4 *xs = reinterpret_cast<const uint4 *>(xl + k * 256 + li * 16);
+        const uint4 x0 = xs[0], x1 = xs[1];
 #pragma unroll
-    for (int r = 0; r < kLmRows; ++r) decode16_bf16(b.q[r], wv[r]);
+        for (int r = 0; r < kLmRows; ++r) {
+            bf16x2 wv[8];
+            decode16_bf16(b.q[r], wv);
+            A.acc[r][0] = dot16(wv, x0, x1, A.acc[r][0]);
+        }
+    } else {
+        bf16x2 wv[kLmRows][8];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        if (t < M) {
-            const uint4 *xs = reinterpret_cast<const uint4 *>(xl + t * kUS + k * 256 + li * 16);
-            const uint4 x0 = xs[0], x1 = xs[1];
+        for (int r = 0; r < kLmRows; ++r) decode16_bf16(b.q[r], wv[r]);
 #pragma unroll
-            for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = dot16(wv[r], x0, x1, A.acc[r][t]);
+        for (int t = 0; t < MT; ++t) {
+            if (t < M) {
+                const uint4 *xs = reinterpret_cast<const uint4 *>(xl + t * kUS + k * 256 + li * 16);
+                const uint4 x0 = xs[0], x1 = xs[1];
+#pragma unroll
+                for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = dot16(wv[r], x0, x1, A.acc[r][t]);
+            }
         }
     }
     if (k == NC - 1) {
@@ -1280,11 +1287,19 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
 
 // ------------------------------------------------------------------- kernel
 
-#ifndef MOE_STEP_MIN_BLOCKS
-#define MOE_STEP_MIN_BLOCKS 2
-#endif
+// Workgroups per compute unit: the register budget the kernel is compiled for, and the
+// most the grid uses. The verify batches run two (two units in flight per workgroup).
+// One token keeps one unit in flight and runs two workgroups per compute unit, compiled
+// for a budget of three: every workgroup forms u_l and routes for itself, polling the
+// residual rows and logits meanwhile, and on the Gemma-shaped stack fewer such
+// workgroups measured faster (0.81 ms per step at two, 0.84 at three, 1.07 at five,
+// 0.90 at one).
+template <int MT>
+constexpr int step_min_blocks() { return MT == 1 ? 3 : 2; }
+template <int MT>
+constexpr int step_max_blocks() { return MT == 1 ? 2 : 64; }
 template <int MT, bool BF>
-__global__ __launch_bounds__(256, MOE_STEP_MIN_BLOCKS) void k_step(StepArgs args) {
+__global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs args) {
     (void)args;
     const AP base = (AP)__builtin_amdgcn_kernarg_segment_ptr();
     const int w = blockIdx.x, G = gridDim.x, GU = G - base->NR;
@@ -1335,7 +1350,7 @@ int launch_mt(const StepArgs &a, size_t lds, int NR, void *stream) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<MT, BF>, kWG, lds) != hipSuccess || per_cu < 1)
         return MOE_ELAUNCH;
-    const int grid = std::min(cus * per_cu, kStepMaxGrid);
+    const int grid = std::min(cus * std::min(per_cu, step_max_blocks<MT>()), kStepMaxGrid);
     if (grid <= NR) return MOE_ELAUNCH;   // the last NR workgroups only route
     hipLaunchKernelGGL((k_step<MT, BF>), dim3(grid), dim3(kWG), lds, Sm(stream), a);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
@@ -1357,11 +1372,14 @@ int launch_m(int M, const StepArgs &a, size_t lds, int NR, void *stream) {
     }
 }
 
-size_t step_lds_bytes(const moe_step_desc &d, int *l_scr, int *l_slot) {
-    const int Mx = d.max_tokens, E = d.layer.num_experts;
-    const size_t u = (size_t)Mx * kUS * 2;
-    size_t scr = (size_t)Mx * kDS * 4;
-    scr = std::max(scr, (size_t)Mx * E * 4);
+// LDS of a launch for M tokens (every LDS array is indexed by the call's tokens, so a
+// call with fewer tokens than the descriptor's maximum takes less LDS and can run more
+// workgroups per compute unit).
+size_t step_lds_bytes(const moe_step_desc &d, int M, int *l_scr, int *l_slot) {
+    const int E = d.layer.num_experts;
+    const size_t u = (size_t)M * kUS * 2;
+    size_t scr = (size_t)M * kDS * 4;
+    scr = std::max(scr, (size_t)M * E * 4);
     scr = std::max(scr, (size_t)16 * kMaxM * 8);
     scr = (scr + 15) & ~(size_t)15;
     *l_scr = (int)u;
@@ -1450,7 +1468,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.eps = d.eps;
     a.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpin;
 
-    const size_t lds = step_lds_bytes(d, &a.l_scr, &a.l_slot);
+    const size_t lds = step_lds_bytes(d, M, &a.l_scr, &a.l_slot);
     return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, stream) : launch_m<false>(M, a, lds, W.NR, stream);
 }
 
