@@ -497,7 +497,8 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
 
 constexpr int kEI = kMaxExperts / 64;   // experts per lane in the top-K selection
 
-// Every workgroup, layer l: route. Wave w selects the top K of tokens w, w+4: each lane
+// Every workgroup, layer l: route. Wave w selects the top K of tokens w and w+4 (in the
+// same rounds): each lane
 // holds the (ordered logit, inverted id) keys of experts lane, lane+64, ..., and K
 // rounds of a wave-wide maximum take the largest remaining key (ties to the lower id).
 // The selected experts' softmax weights are renormalised over the K (the full softmax
@@ -511,107 +512,149 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
     SlotLds &S = slots(a);
     float *wt = reinterpret_cast<float *>(scratch(a));   // [M][E] weight of expert e for token m
     const uint64_t *src = logits(a, l);
-    for (int m = wave; m < M; m += 4) {
-        float lgv[kEI];
+    // Wave w selects token w and, with more than four tokens, token w + 4 in the same
+    // rounds: a round is a chain of dependent cross-lane steps, so two tokens' chains
+    // interleaved take about as long as one.
+    constexpr int NT = MT > 4 ? 2 : 1;
+    if (wave < M) {   // waves without a token skip the selection
+        float lgv[NT][kEI];
         {
             Poll pl;
             bool ok;
             do {
-                uint64_t v[kEI];
-#pragma unroll
-                for (int i = 0; i < kEI; ++i)
-                    if (lane + 64 * i < E) v[i] = ld64(src + (size_t)m * E + lane + 64 * i);
+                uint64_t v[NT][kEI];
+    #pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int m = wave + 4 * t;
+    #pragma unroll
+                    for (int i = 0; i < kEI; ++i)
+                        if (m < M && lane + 64 * i < E) v[t][i] = ld64(src + (size_t)m * E + lane + 64 * i);
+                }
                 ok = true;
-#pragma unroll
-                for (int i = 0; i < kEI; ++i) {
-                    lgv[i] = 0.0f;
-                    if (lane + 64 * i < E) {
-                        lgv[i] = __uint_as_float((uint32_t)v[i]);
-                        ok = ok && current(v[i], tgt);
+    #pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const int m = wave + 4 * t;
+    #pragma unroll
+                    for (int i = 0; i < kEI; ++i) {
+                        lgv[t][i] = 0.0f;
+                        if (m < M && lane + 64 * i < E) {
+                            lgv[t][i] = __uint_as_float((uint32_t)v[t][i]);
+                            ok = ok && current(v[t][i], tgt);
+                        }
                     }
                 }
             } while (!pl.done(a, ok));
         }
-        // K rounds: the largest remaining ordered logit over the wave (DPP maximum),
-        // then the lowest expert id holding it (ballots in ascending id order)
-        uint32_t o[kEI];
-        bool sel[kEI];
-#pragma unroll
-        for (int i = 0; i < kEI; ++i) {
-            o[i] = lane + 64 * i < E ? ordered(lgv[i]) : 0u;
-            sel[i] = false;
-        }
-        float lmax = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            uint32_t v = o[0];
-#pragma unroll
-            for (int i = 1; i < kEI; ++i) v = max(v, o[i]);
-            v = max(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
-            v = max(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
-            v = max(v, dppu<0x141>(v));   // row_half_mirror
-            v = max(v, dppu<0x140>(v));   // row_mirror
-            const uint32_t W = max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
-                                   max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
-            if (k == 0) lmax = unordered(W);
-            bool found = false;
-#pragma unroll
+        // K rounds: the largest remaining ordered logit over the wave (DPP maximum), then the
+        // lowest expert id holding it (ballots in ascending id order)
+        uint32_t o[NT][kEI];
+        bool sel[NT][kEI];
+    #pragma unroll
+        for (int t = 0; t < NT; ++t)
+    #pragma unroll
             for (int i = 0; i < kEI; ++i) {
-                const unsigned long long bm = __ballot(o[i] == W);
-                if (!found && bm) {
-                    found = true;
-                    if (lane == __ffsll((long long)bm) - 1) {
-                        sel[i] = true;
-                        o[i] = 0u;
+                o[t][i] = wave + 4 * t < M && lane + 64 * i < E ? ordered(lgv[t][i]) : 0u;
+                sel[t][i] = false;
+            }
+        float lmax[NT];
+        for (int k = 0; k < K; ++k) {
+            uint32_t v[NT], W[NT];
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                v[t] = o[t][0];
+    #pragma unroll
+                for (int i = 1; i < kEI; ++i) v[t] = max(v[t], o[t][i]);
+            }
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0xB1>(v[t]));    // quad_perm [1,0,3,2]
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x4E>(v[t]));    // quad_perm [2,3,0,1]
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x141>(v[t]));   // row_half_mirror
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x140>(v[t]));   // row_mirror
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                W[t] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 0), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 16)),
+                           max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 32), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 48)));
+                if (k == 0) lmax[t] = unordered(W[t]);
+            }
+    #pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                bool found = false;
+    #pragma unroll
+                for (int i = 0; i < kEI; ++i) {
+                    const unsigned long long bm = __ballot(o[t][i] == W[t]);
+                    if (!found && bm) {
+                        found = true;
+                        if (lane == __ffsll((long long)bm) - 1) {
+                            sel[t][i] = true;
+                            o[t][i] = 0u;
+                        }
                     }
                 }
             }
         }
-        float ev[kEI], zl = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kEI; ++i) {
-            ev[i] = sel[i] ? expf(lgv[i] - lmax) : 0.0f;
-            zl += ev[i];
-        }
-        const float z = wave_sum(zl);
-        int before = 0;
-#pragma unroll
-        for (int i = 0; i < kEI; ++i) {
-            const unsigned long long bm = __ballot(sel[i]);
-            if (lane == 0) S.bal[m][i] = bm;
-            if (sel[i]) {
-                const int e = lane + 64 * i, pos = before + lanes_below(bm);
-                const float wv = ev[i] / z;
-                wt[m * E + e] = wv;
-                if (outputs) {
-                    if (a->topk_idx) glb(a->topk_idx)[((size_t)l * M + m) * K + pos] = e;
-                    if (a->topk_w) glb(a->topk_w)[((size_t)l * M + m) * K + pos] = wv;
-                }
+    #pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int m = wave + 4 * t;
+            if (m >= M) break;
+            float ev[kEI], zl = 0.0f;
+    #pragma unroll
+            for (int i = 0; i < kEI; ++i) {
+                ev[i] = sel[t][i] ? expf(lgv[t][i] - lmax[t]) : 0.0f;
+                zl += ev[i];
             }
-            before += __popcll(bm);
+            const float z = wave_sum(zl);
+            int before = 0;
+    #pragma unroll
+            for (int i = 0; i < kEI; ++i) {
+                const unsigned long long bm = __ballot(sel[t][i]);
+                if (lane == 0) S.bal[m][i] = bm;
+                if (sel[t][i]) {
+                    const int e = lane + 64 * i, pos = before + lanes_below(bm);
+                    const float wv = ev[i] / z;
+                    wt[m * E + e] = wv;
+                    if (outputs) {
+                        if (a->topk_idx) glb(a->topk_idx)[((size_t)l * M + m) * K + pos] = e;
+                        if (a->topk_w) glb(a->topk_w)[((size_t)l * M + m) * K + pos] = wv;
+                    }
+                }
+                before += __popcll(bm);
+            }
         }
     }
     __syncthreads();
     const int has_sh = a->Ds > 0, nsh = has_sh ? a->nseg_s : 0, nsr = a->nseg_r;
-    // union of the selections; register arrays are only indexed by constants
-    unsigned long long U[kEI];
+    // union of the selections, and for expert tid = lane + 64 * wave its selection mask
+    // word and the number of experts each token selected below its word; every mask word
+    // is read once, all together (register arrays are only indexed by constants)
+    unsigned long long U[kEI], Bw[MT];
+    int pre[MT];
 #pragma unroll
-    for (int i = 0; i < kEI; ++i) {
-        U[i] = 0ull;
+    for (int i = 0; i < kEI; ++i) U[i] = 0ull;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
-            if (m < M) U[i] |= S.bal[m][i];
+    for (int m = 0; m < MT; ++m) {
+        Bw[m] = 0ull;
+        pre[m] = 0;
+#pragma unroll
+        for (int i = 0; i < kEI; ++i) {
+            const unsigned long long b = S.bal[m][i];
+            U[i] |= b;
+            pre[m] += i < wave ? __popcll(b) : 0;
+            Bw[m] = i == wave ? b : Bw[m];
+        }
     }
     int ns = has_sh;
 #pragma unroll
     for (int i = 0; i < kEI; ++i) ns += __popcll(U[i]);
     if (tid < E) {
-        // expert tid = lane + 64 * wave
-        unsigned long long Bw[MT];
         unsigned um = 0;
+        float wm[MT];
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-            Bw[m] = m < M ? S.bal[m][wave] : 0ull;
             um |= (unsigned)((Bw[m] >> lane) & 1ull) << m;
+            wm[m] = wt[m * E + tid];
         }
         if (um) {
             int slot = has_sh;
@@ -626,11 +669,11 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
             S.sm[slot] = um;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                S.sw[slot][m] = ((um >> m) & 1u) ? wt[m * E + tid] : 0.0f;
-                if ((um >> m) & 1u) {
+                const bool on = (um >> m) & 1u;
+                S.sw[slot][m] = on ? wm[m] : 0.0f;
+                if (on) {
                     // expert tid's place in token m's list (ascending id)
-                    int pos = lanes_below(Bw[m]);
-                    for (int q = 0; q < wave; ++q) pos += __popcll(S.bal[m][q]);
+                    const int pos = pre[m] + lanes_below(Bw[m]);
                     for (int sg = 0; sg < nsr; ++sg) S.tsub[m][nsh + pos * nsr + sg] = nsh + (slot - has_sh) * nsr + sg;
                 }
             }
