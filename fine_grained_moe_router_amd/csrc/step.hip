@@ -197,9 +197,10 @@ __device__ __forceinline__ char *scratch(AP a) { return smem + a->l_scr; }
 // ------------------------------------------------------------ polling
 
 // A wave's polling loop: done() is true once every lane's words are current (or the
-// spin limit is reached, which raises the error flag); otherwise it sleeps briefly and
-// the loop reloads.
-struct Poll {
+// spin limit is reached, which raises the error flag); otherwise it sleeps SLEEP x 64
+// cycles and the loop reloads.
+template <int SLEEP>
+struct PollS {
     unsigned spins = 0;
     __device__ __forceinline__ bool done(AP a, bool ok) {
         if (__all(ok)) return true;
@@ -207,10 +208,11 @@ struct Poll {
             if ((ltid() & 63) == 0) st32(ctr(a, kErrCtr), 1u);
             return true;
         }
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(SLEEP);
         return false;
     }
 };
+typedef PollS<1> Poll;
 
 // Wait until all n flags hold a value >= tgt (wrap-safe); wave 0 polls.
 __device__ __forceinline__ void wait_flags(AP a, const uint32_t *f, int n, uint32_t tgt) {
@@ -325,7 +327,7 @@ __device__ __forceinline__ uint32_t h0_pair(AP a, int m, int word) {
 // to the row stride are zeroed, so unit and router loops can run over whole padded
 // rows without bounds checks.
 constexpr int kNormTok = 4;
-template <int MT>
+template <int MT, int SLEEP = 1>
 __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint32_t tgt) {
     const int H = a->H, M = MT, tid = ltid(), hw = H / 2, lane = tid & 63, wave = tid >> 6;
     uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][kUS/2] bf16 pairs
@@ -362,7 +364,7 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
                     hp[mm][k] = pack2(f2bf(bf2f(xv[mm][k] & 0xffffu) + bf2f(nv[mm][k] & 0xffffu)),
                                       f2bf(bf2f(xv[mm][k] >> 16) + bf2f(nv[mm][k] >> 16)));
         } else {
-            Poll pl;
+            PollS<SLEEP> pl;
             bool ok;
             do {
                 uint64_t v[kNormTok][kW];
@@ -1114,7 +1116,10 @@ __device__ __forceinline__ void run_unit(AP a, int l, const UnitRef &u, const Un
 template <int MT, bool BF>
 __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32_t tgt) {
     const AP a = uniform(a0);
-    norm_to_lds<MT>(a, l, a->gains + (size_t)l * a->H, tgt);
+    // the residual rows are polled with long sleeps in between: a unit workgroup needs u_l
+    // only after the logits, which come a hop and a router GEMV after the rows, and every
+    // unit workgroup polls meanwhile (64 measured faster than 1 at one and five tokens)
+    norm_to_lds<MT, 64>(a, l, a->gains + (size_t)l * a->H, tgt);
     // the shared expert's units sit at fixed places at the head of the list
     const UnitList L0 = unit_list<BF>(a, a->Ds > 0 ? 1 : 0);
     UnitBuf A;
