@@ -114,6 +114,40 @@ def test_fused_step_zipf_router_bias_m8(dtype):
                   router_bias=synth.zipf_router_bias(64))
 
 
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_step_routing_ties_go_to_lower_id(M):
+    """Exact ties among the router logits: with zero router weights and a bias that gives
+    six experts the same largest logit, every token of every layer selects the K lowest
+    ids of the six, each with weight exactly 1/K (at M=5 and M=8 a wave selects two
+    tokens in the same rounds), and the layer outputs match the oracle's, which breaks
+    ties the same way."""
+    sh = synth.TINY.with_(experts=64, top_k=4, hidden=512, width=128, layers=2)
+    tied = [3, 7, 9, 12, 40, 50]
+    bias = torch.zeros(64, dtype=torch.float32)
+    bias[tied] = 1.0
+    layers, host, gains, Q, s, dev = make(sh, seed=9, router_bias=bias)
+    for w, hw in zip(dev, host):
+        w["router_w"] = torch.zeros_like(w["router_w"])
+        hw["router_w"] = np.zeros_like(hw["router_w"])
+    x = synth.hidden_inputs(sh, M, 0, 0)
+    noise = synth.stack_noise(sh, M, 0, 0)
+    res = oracle.stack_step(synth.bits16(x), host, synth.bits16(noise), synth.bits16(gains),
+                            synth.bytes8(Q), synth.f32(s), sh.top_k)
+    say("fused routing ties M=%d" % M)
+    fs = FusedDecodeStep(sh, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8)
+    dd = torch.zeros(M - 1, dtype=torch.int32, device=DEV) if M > 1 else None
+    fs.step(x.to(DEV), noise.to(DEV), dd, M)
+    torch.cuda.synchronize()
+    assert fs.status() == native.MOE_OK
+    want = np.array(tied[:sh.top_k])
+    idx, wts, y = fs.topk_idx(M).cpu().numpy(), fs.topk_w(M).cpu().numpy(), fs.y(M)
+    assert (idx == want).all(), idx
+    assert (wts == np.float32(1.0 / sh.top_k)).all(), wts
+    for l in range(sh.layers):
+        assert (res["layers"][l]["idx"] == want).all()
+        check_bf16_output(synth.bits16(y[l]), res["layers"][l]["y"], None, "ties y layer %d" % l)
+
+
 def test_fused_step_batch_consistency_and_determinism():
     sh = synth.TINY.with_(experts=64, top_k=4, hidden=512, width=128, layers=3)
     layers, host, gains, Q, s, dev = make(sh, seed=3)
