@@ -525,18 +525,18 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
             bool ok;
             do {
                 uint64_t v[NT][kEI];
-    #pragma unroll
+#pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const int m = wave + 4 * t;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < kEI; ++i)
                         if (m < M && lane + 64 * i < E) v[t][i] = ld64(src + (size_t)m * E + lane + 64 * i);
                 }
                 ok = true;
-    #pragma unroll
+#pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const int m = wave + 4 * t;
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < kEI; ++i) {
                         lgv[t][i] = 0.0f;
                         if (m < M && lane + 64 * i < E) {
@@ -550,70 +550,77 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
         // K rounds: the largest remaining ordered logit over the wave (DPP maximum), then the
         // lowest expert id holding it (ballots in ascending id order)
         uint32_t o[NT][kEI];
-        bool sel[NT][kEI];
-    #pragma unroll
-        for (int t = 0; t < NT; ++t)
-    #pragma unroll
-            for (int i = 0; i < kEI; ++i) {
-                o[t][i] = wave + 4 * t < M && lane + 64 * i < E ? ordered(lgv[t][i]) : 0u;
-                sel[t][i] = false;
-            }
+        unsigned sel[NT];   // bit i: this lane's expert lane + 64 i is selected
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            sel[t] = 0u;
+#pragma unroll
+            for (int i = 0; i < kEI; ++i) o[t][i] = wave + 4 * t < M && lane + 64 * i < E ? ordered(lgv[t][i]) : 0u;
+        }
         float lmax[NT];
         for (int k = 0; k < K; ++k) {
             uint32_t v[NT], W[NT];
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) {
                 v[t] = o[t][0];
-    #pragma unroll
+#pragma unroll
                 for (int i = 1; i < kEI; ++i) v[t] = max(v[t], o[t][i]);
             }
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0xB1>(v[t]));    // quad_perm [1,0,3,2]
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x4E>(v[t]));    // quad_perm [2,3,0,1]
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x141>(v[t]));   // row_half_mirror
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x140>(v[t]));   // row_mirror
-    #pragma unroll
+#pragma unroll
             for (int t = 0; t < NT; ++t) {
                 W[t] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 0), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 16)),
                            max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 32), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 48)));
                 if (k == 0) lmax[t] = unordered(W[t]);
             }
-    #pragma unroll
+            // the lowest id holding the maximum: the first word with a lane equal to it, and
+            // that word's lowest such lane, chosen with wave-uniform selects (no branches)
+#pragma unroll
             for (int t = 0; t < NT; ++t) {
-                bool found = false;
-    #pragma unroll
+                unsigned long long bm[kEI];
+#pragma unroll
+                for (int i = 0; i < kEI; ++i) bm[i] = __ballot(o[t][i] == W[t]);
+                int wsel = kEI - 1;
+                unsigned long long bw = bm[kEI - 1];
+#pragma unroll
+                for (int i = kEI - 2; i >= 0; --i) {
+                    wsel = bm[i] ? i : wsel;
+                    bw = bm[i] ? bm[i] : bw;
+                }
+                const int lsel = __ffsll((long long)bw) - 1;
+#pragma unroll
                 for (int i = 0; i < kEI; ++i) {
-                    const unsigned long long bm = __ballot(o[t][i] == W[t]);
-                    if (!found && bm) {
-                        found = true;
-                        if (lane == __ffsll((long long)bm) - 1) {
-                            sel[t][i] = true;
-                            o[t][i] = 0u;
-                        }
-                    }
+                    const bool take = i == wsel && lane == lsel;
+                    o[t][i] = take ? 0u : o[t][i];
+                    sel[t] |= take ? 1u << i : 0u;
                 }
             }
         }
-    #pragma unroll
+#pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int m = wave + 4 * t;
             if (m >= M) break;
             float ev[kEI], zl = 0.0f;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < kEI; ++i) {
-                ev[i] = sel[t][i] ? expf(lgv[t][i] - lmax[t]) : 0.0f;
+                ev[i] = (sel[t] >> i) & 1u ? expf(lgv[t][i] - lmax[t]) : 0.0f;
                 zl += ev[i];
             }
             const float z = wave_sum(zl);
             int before = 0;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < kEI; ++i) {
-                const unsigned long long bm = __ballot(sel[t][i]);
+                const bool si = (sel[t] >> i) & 1u;
+                const unsigned long long bm = __ballot(si);
                 if (lane == 0) S.bal[m][i] = bm;
-                if (sel[t][i]) {
+                if (si) {
                     const int e = lane + 64 * i, pos = before + lanes_below(bm);
                     const float wv = ev[i] / z;
                     wt[m * E + e] = wv;
