@@ -98,15 +98,35 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
         const int m = wave;
         float l[4];
         bool taken[4];
+        // the logits: each expert's row-block partials summed in block order; the
+        // partials are requested kChunk blocks at a time for all of the lane's experts,
+        // so that a batch costs one memory latency
+        constexpr int kChunk = 11;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            l[i] = 0.0f;
+            taken[i] = false;
+        }
+        for (int b0 = 0; b0 < a.NB; b0 += kChunk) {
+            float t[4][kChunk];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j) {
+                    const int e = lane + 64 * i, b = b0 + j;
+                    t[i][j] = e < E && b < a.NB ? a.partial[((size_t)b * M + m) * E + e] : 0.0f;
+                }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kChunk; ++j)
+                    if (b0 + j < a.NB) l[i] += t[i][j];
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = lane + 64 * i;
-            taken[i] = false;
             if (e < E) {
-                float s = 0.0f;
-                for (int b = 0; b < a.NB; ++b) s += a.partial[((size_t)b * M + m) * E + e];
-                if (a.bias) s += a.bias[e];
-                l[i] = s;
+                if (a.bias) l[i] += a.bias[e];
             } else {
                 l[i] = -INFINITY;
             }
@@ -552,34 +572,56 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 }
 
 __global__ __launch_bounds__(256) void k_argmax_final(LmArgs a) {
-    __shared__ float rv[256];
-    __shared__ int ri[256];
-    for (int t = 0; t < a.M; ++t) {
-        float v = -INFINITY;
-        int i = 0x7fffffff;
-        for (int k = threadIdx.x; k < a.nwg; k += 256) {
-            const float kv = a.best_v[k * a.M + t];
-            const int ki = a.best_i[k * a.M + t];
-            if (better(kv, ki, v, i)) {
-                v = kv;
-                i = ki;
+    // every token's best (logit, row) over the workgroups' keys; all keys are requested up
+    // front, then one tree reduction serves every token
+    constexpr int kPer = (kLmMaxWG + 255) / 256;
+    __shared__ float rv[kMaxM][256];
+    __shared__ int ri[kMaxM][256];
+    const int M = a.M, tid = threadIdx.x;
+    float v[kMaxM];
+    int i[kMaxM];
+    float kv[kPer][kMaxM];
+    int ki[kPer][kMaxM];
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+        const int k = tid + 256 * q;
+#pragma unroll
+        for (int t = 0; t < kMaxM; ++t) {
+            const bool ok = k < a.nwg && t < M;
+            kv[q][t] = ok ? a.best_v[k * M + t] : -INFINITY;
+            ki[q][t] = ok ? a.best_i[k * M + t] : 0x7fffffff;
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxM; ++t) {
+        v[t] = -INFINITY;
+        i[t] = 0x7fffffff;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            if (better(kv[q][t], ki[q][t], v[t], i[t])) {
+                v[t] = kv[q][t];
+                i[t] = ki[q][t];
             }
         }
-        rv[threadIdx.x] = v;
-        ri[threadIdx.x] = i;
-        __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (threadIdx.x < off && better(rv[threadIdx.x + off], ri[threadIdx.x + off], rv[threadIdx.x], ri[threadIdx.x])) {
-                rv[threadIdx.x] = rv[threadIdx.x + off];
-                ri[threadIdx.x] = ri[threadIdx.x + off];
+        rv[t][tid] = v[t];
+        ri[t][tid] = i[t];
+    }
+    __syncthreads();
+    for (int off = 128; off >= 1; off >>= 1) {
+        if (tid < off) {
+#pragma unroll
+            for (int t = 0; t < kMaxM; ++t) {
+                if (t < M && better(rv[t][tid + off], ri[t][tid + off], rv[t][tid], ri[t][tid])) {
+                    rv[t][tid] = rv[t][tid + off];
+                    ri[t][tid] = ri[t][tid + off];
+                }
             }
-            __syncthreads();
-        }
-        if (threadIdx.x == 0) {
-            a.token[t] = ri[0];
-            if (a.max_logit) a.max_logit[t] = rv[0];
         }
         __syncthreads();
+    }
+    if (tid < M) {
+        a.token[tid] = ri[tid][0];
+        if (a.max_logit) a.max_logit[tid] = rv[tid][0];
     }
 }
 
