@@ -1,5 +1,6 @@
 // device_common.h -- gfx950 device helpers shared by the kernels: FP8 and bf16
-// conversions, packed bf16 dot products, and fixed-order DPP reductions.
+// conversions, packed bf16 dot products, fixed-order DPP reductions and the top-K
+// selection rounds.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -79,6 +80,94 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<0x141>(v);  // row_half_mirror: combines the two quads of each half row
     v += dpp<0x140>(v);  // row_mirror: combines the two half rows
     return v;
+}
+
+// ------------------------------------------------------------ cross-lane helpers
+
+// Order-preserving map of a float onto uint32 (larger float -> larger integer).
+__device__ __forceinline__ uint32_t ordered(float v) {
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float unordered(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__device__ __forceinline__ float readlane(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over the 64 lanes in a fixed order; the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int lanes_below(unsigned long long m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+}
+
+// Top-K selection by one wave for NT tokens at once. o[t][i] holds the order-preserving
+// key of expert lane + 64 i of token t (0 where there is no expert). K rounds each take
+// the largest remaining key over the wave (a DPP maximum and four lane reads) and select
+// the lowest expert id holding it (the first 64-expert word with a lane equal to it, and
+// that word's lowest such lane, picked with wave-uniform selects). On return bit i of
+// sel[t] marks expert lane + 64 i as selected for token t, and wmax[t] is the first
+// round's key (the token's largest). A round is a chain of dependent cross-lane steps, so
+// the NT tokens' rounds are interleaved.
+template <int NT, int NE>
+__device__ __forceinline__ void topk_rounds(uint32_t (&o)[NT][NE], int K, int lane, unsigned (&sel)[NT],
+                                            uint32_t (&wmax)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sel[t] = 0u;
+    for (int k = 0; k < K; ++k) {
+        uint32_t v[NT], W[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            v[t] = o[t][0];
+#pragma unroll
+            for (int i = 1; i < NE; ++i) v[t] = max(v[t], o[t][i]);
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0xB1>(v[t]));    // quad_perm [1,0,3,2]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x4E>(v[t]));    // quad_perm [2,3,0,1]
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x141>(v[t]));   // row_half_mirror
+#pragma unroll
+        for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x140>(v[t]));   // row_mirror
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            W[t] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 0), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 16)),
+                       max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 32), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 48)));
+            if (k == 0) wmax[t] = W[t];
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            unsigned long long bm[NE];
+#pragma unroll
+            for (int i = 0; i < NE; ++i) bm[i] = __ballot(o[t][i] == W[t]);
+            int wsel = NE - 1;
+            unsigned long long bw = bm[NE - 1];
+#pragma unroll
+            for (int i = NE - 2; i >= 0; --i) {
+                wsel = bm[i] ? i : wsel;
+                bw = bm[i] ? bm[i] : bw;
+            }
+            const int lsel = __ffsll((long long)bw) - 1;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) {
+                const bool take = i == wsel && lane == lsel;
+                o[t][i] = take ? 0u : o[t][i];
+                sel[t] |= take ? 1u << i : 0u;
+            }
+        }
+    }
 }
 
 __device__ __forceinline__ float gelu_tanh(float z) {

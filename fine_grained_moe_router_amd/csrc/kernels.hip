@@ -87,26 +87,22 @@ struct TopkArgs {
 // (id E) is appended last with weight 1 for every token.
 __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
     __shared__ float wsel[kMaxM][kMaxExperts];
-    __shared__ int sel_e[kMaxM][kMaxTopK];
-    __shared__ float sel_l[kMaxM][kMaxTopK];
+    __shared__ unsigned long long bal_m[kMaxM][4];   // bit e % 64 of word e / 64: token m selected e
     __shared__ int wave_cnt[4];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int E = a.E, K = a.K, M = a.M;
     for (int i = tid; i < kMaxM * kMaxExperts; i += 512) (&wsel[0][0])[i] = 0.0f;
+    if (tid < kMaxM * 4) (&bal_m[0][0])[tid] = 0ull;
     __syncthreads();
     if (wave < M) {
         const int m = wave;
         float l[4];
-        bool taken[4];
         // the logits: each expert's row-block partials summed in block order; the
         // partials are requested kChunk blocks at a time for all of the lane's experts,
         // so that a batch costs one memory latency
-        constexpr int kChunk = 11;
+        constexpr int kChunk = 22;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            l[i] = 0.0f;
-            taken[i] = false;
-        }
+        for (int i = 0; i < 4; ++i) l[i] = 0.0f;
         for (int b0 = 0; b0 < a.NB; b0 += kChunk) {
             float t[4][kChunk];
 #pragma unroll
@@ -131,69 +127,45 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
                 l[i] = -INFINITY;
             }
         }
-        for (int k = 0; k < K; ++k) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
+        // K rounds of a wave-wide maximum over order-preserving keys, ties to the lower id;
+        // the selected experts' softmax weights renormalised over the K (the full softmax
+        // denominator cancels), the denominator summed over the wave in a fixed order
+        uint32_t o[1][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = lane + 64 * i;
-                if (e < E && !taken[i] && (l[i] > bv || (l[i] == bv && e < bi))) {
-                    bv = l[i];
-                    bi = e;
-                }
-            }
+        for (int i = 0; i < 4; ++i) o[0][i] = lane + 64 * i < E ? ordered(l[i]) : 0u;
+        unsigned sel[1];
+        uint32_t wmax[1];
+        topk_rounds<1, 4>(o, K, lane, sel, wmax);
+        const float lmax = unordered(wmax[0]);
+        float ev[4], zl = 0.0f;
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane + 64 * i == bi) taken[i] = true;
-            if (lane == 0) {
-                sel_e[m][k] = bi;
-                sel_l[m][k] = bv;
-            }
+        for (int i = 0; i < 4; ++i) {
+            ev[i] = (sel[0] >> i) & 1u ? expf(l[i] - lmax) : 0.0f;
+            zl += ev[i];
         }
-        if (lane == 0) {
-            // renormalised softmax over the selected logits (the full-softmax
-            // denominator cancels); sel_l[m][0] is the largest logit
-            const float lmax = sel_l[m][0];
-            float z = 0.0f;
-            for (int k = 0; k < K; ++k) z += expf(sel_l[m][k] - lmax);
-            // ascending expert id (insertion sort of K <= 16 entries)
-            for (int k = 1; k < K; ++k) {
-                const int ek = sel_e[m][k];
-                const float lk = sel_l[m][k];
-                int j = k - 1;
-                while (j >= 0 && sel_e[m][j] > ek) {
-                    sel_e[m][j + 1] = sel_e[m][j];
-                    sel_l[m][j + 1] = sel_l[m][j];
-                    --j;
-                }
-                sel_e[m][j + 1] = ek;
-                sel_l[m][j + 1] = lk;
+        const float z = wave_sum(zl);
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool si = (sel[0] >> i) & 1u;
+            const unsigned long long bm = __ballot(si);
+            if (lane == 0) bal_m[m][i] = bm;
+            if (si) {
+                // outputs in ascending expert id
+                const int e = lane + 64 * i, pos = before + lanes_below(bm);
+                const float wk = ev[i] / z;
+                wsel[m][e] = wk;
+                if (a.topk_idx) a.topk_idx[m * K + pos] = e;
+                if (a.topk_w) a.topk_w[m * K + pos] = wk;
             }
-            for (int k = 0; k < K; ++k) {
-                const float wk = expf(sel_l[m][k] - lmax) / z;
-                wsel[m][sel_e[m][k]] = wk;
-                if (a.topk_idx) a.topk_idx[m * K + k] = sel_e[m][k];
-                if (a.topk_w) a.topk_w[m * K + k] = wk;
-            }
+            before += __popcll(bm);
         }
     }
     __syncthreads();
     // union over tokens, slots in ascending expert id
     uint32_t mask = 0;
-    if (tid < 256 && tid < E) {
-        for (int m = 0; m < M; ++m)
-            for (int k = 0; k < K; ++k)
-                if (sel_e[m][k] == tid) mask |= 1u << m;
-    }
+    if (tid < 256 && tid < E)
+        for (int m = 0; m < M; ++m) mask |= (unsigned)((bal_m[m][wave] >> lane) & 1ull) << m;
     const unsigned long long bal = __ballot(mask != 0);
     if (tid < 256 && lane == 0) wave_cnt[wave] = __popcll(bal);
     __syncthreads();

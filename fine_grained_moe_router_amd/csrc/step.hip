@@ -250,37 +250,11 @@ __device__ __forceinline__ void publish(uint32_t *f, uint32_t tgt) {
 
 // ------------------------------------------------------------ cross-lane helpers
 
-// Order-preserving map of a float onto uint32 (larger float -> larger integer).
-__device__ __forceinline__ uint32_t ordered(float v) {
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float unordered(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-
-// Cross-lane reductions use DPP and readlane only (no LDS round trips).
-
-__device__ __forceinline__ float readlane(float v, int lane) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// Sum over the 64 lanes in a fixed order; the result is wave-uniform.
-__device__ __forceinline__ float wave_sum(float v) {
-    v = row16_sum(v);
-    return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
-}
-
 // Sum over each half-wave (32 lanes); valid in lanes 16..31 and 48..63.
 __device__ __forceinline__ float half_sum(float v) {
     v = row16_sum(v);
     // row_bcast:15 into rows 1 and 3 only: lane 15 of the row below
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dppu(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
 __device__ __forceinline__ void kmax_step(uint32_t &hi, uint32_t &lo, uint32_t oh, uint32_t ol) {
@@ -306,9 +280,6 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
     return best;
 }
 
-__device__ __forceinline__ int lanes_below(unsigned long long m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
-}
 
 // ------------------------------------------------------------ norm
 
@@ -552,57 +523,14 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
         uint32_t o[NT][kEI];
         unsigned sel[NT];   // bit i: this lane's expert lane + 64 i is selected
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            sel[t] = 0u;
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < kEI; ++i) o[t][i] = wave + 4 * t < M && lane + 64 * i < E ? ordered(lgv[t][i]) : 0u;
-        }
+        uint32_t wmax[NT];
+        topk_rounds<NT, kEI>(o, K, lane, sel, wmax);
         float lmax[NT];
-        for (int k = 0; k < K; ++k) {
-            uint32_t v[NT], W[NT];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                v[t] = o[t][0];
-#pragma unroll
-                for (int i = 1; i < kEI; ++i) v[t] = max(v[t], o[t][i]);
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0xB1>(v[t]));    // quad_perm [1,0,3,2]
-#pragma unroll
-            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x4E>(v[t]));    // quad_perm [2,3,0,1]
-#pragma unroll
-            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x141>(v[t]));   // row_half_mirror
-#pragma unroll
-            for (int t = 0; t < NT; ++t) v[t] = max(v[t], dppu<0x140>(v[t]));   // row_mirror
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                W[t] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 0), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 16)),
-                           max((uint32_t)__builtin_amdgcn_readlane((int)v[t], 32), (uint32_t)__builtin_amdgcn_readlane((int)v[t], 48)));
-                if (k == 0) lmax[t] = unordered(W[t]);
-            }
-            // the lowest id holding the maximum: the first word with a lane equal to it, and
-            // that word's lowest such lane, chosen with wave-uniform selects (no branches)
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                unsigned long long bm[kEI];
-#pragma unroll
-                for (int i = 0; i < kEI; ++i) bm[i] = __ballot(o[t][i] == W[t]);
-                int wsel = kEI - 1;
-                unsigned long long bw = bm[kEI - 1];
-#pragma unroll
-                for (int i = kEI - 2; i >= 0; --i) {
-                    wsel = bm[i] ? i : wsel;
-                    bw = bm[i] ? bm[i] : bw;
-                }
-                const int lsel = __ffsll((long long)bw) - 1;
-#pragma unroll
-                for (int i = 0; i < kEI; ++i) {
-                    const bool take = i == wsel && lane == lsel;
-                    o[t][i] = take ? 0u : o[t][i];
-                    sel[t] |= take ? 1u << i : 0u;
-                }
-            }
-        }
+        for (int t = 0; t < NT; ++t) lmax[t] = unordered(wmax[t]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int m = wave + 4 * t;
