@@ -31,14 +31,20 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 ROOT = os.path.dirname(os.path.abspath(__file__))
-STEP_SOURCE = os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", "step.hip")
+# the sources the fused step kernel is compiled from
+STEP_SOURCES = [os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", f)
+                for f in ("step.hip", "device_common.h", "internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_step_traffic.txt")
 
 
 def step_source_hash():
+    """sha256 over the fused step kernel's sources, in a fixed order."""
     import hashlib
-    with open(STEP_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in STEP_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(M):
