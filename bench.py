@@ -183,6 +183,11 @@ def main():
                     "bytes_per_launch": lm_bytes, "avg_launch_us": round(lm_ms * 1e3, 2)}
         log("lm_head alone: %.1f us, %.1f GB/s" % (lm_ms * 1e3, lm_gbs))
 
+    probe = read_probe()
+    log("HBM read probe: %.1f GB/s over %.1f GiB (%.1f%% of 8 TB/s)" % (
+        probe["read_gbs"], probe["bytes"] / 2 ** 30, 100 * probe["read_gbs"] / HBM_PEAK_GBS))
+    roofline["frac_of_probe"] = round(roofline["achieved"] / probe["read_gbs"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, sh, layers, gains, Q, s, Ms[0])
@@ -214,9 +219,36 @@ def main():
         "per_M": {str(M): {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                   for M, r in results.items()},
         "roofline": roofline,
+        "hbm_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def read_probe(nbytes=4 << 30, reps=10):
+    """The practical HBM ceiling beside the nominal peak: the library's streaming-read
+    probe (moe_hbm_read_probe) over nbytes of device memory, HIP-event-timed on its stream."""
+    import torch
+    from fine_grained_moe_router_amd import native
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(native.PROBE_GRID, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            native.moe_hbm_read_probe(src, nbytes, sink, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            native.moe_hbm_read_probe(src, nbytes, sink, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    del src, sink
+    torch.cuda.empty_cache()
+    return {"kernel": "moe_hbm_read_probe", "bytes": nbytes, "avg_launch_us": round(us, 2),
+            "read_gbs": round(nbytes / (us / 1e6) / 1e9, 1)}
 
 
 def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):

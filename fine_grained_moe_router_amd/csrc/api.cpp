@@ -217,4 +217,11 @@ int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_
     return launch_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream);
 }
 
+int moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    if (bytes == 0 || bytes % 16) return MOE_EINVAL;
+    CHECK(need(src));
+    CHECK(need(sink));
+    return launch_read_probe(src, bytes, sink, stream);
+}
+
 }  // extern "C"

@@ -158,5 +158,6 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
 int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weights *layers, char *ws);
 int step_status(const StepWs &W, char *ws);
 int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream);
+int launch_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 }  // namespace moe

@@ -723,12 +723,50 @@ int launch_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *a0, c
     return launched();
 }
 
+// --------------------------------------------------------- HBM read probe
+
+// Thread t of the grid reads 16-byte pieces t, t + T, t + 2T, ... (T threads in all),
+// kProbeDepth in flight at a time, and XORs their words; each workgroup leaves the XOR of
+// its threads' words in sink[w].
+constexpr int kProbeDepth = 8;
+__global__ __launch_bounds__(256) void k_read_probe(const uint4 *__restrict__ src, size_t n, uint32_t *sink) {
+    __shared__ uint32_t red[256];
+    const size_t T = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kProbeDepth - 1) * T < n; i += kProbeDepth * T) {
+        uint4 p[kProbeDepth];
+#pragma unroll
+        for (int k = 0; k < kProbeDepth; ++k) p[k] = src[i + k * T];
+#pragma unroll
+        for (int k = 0; k < kProbeDepth; ++k) acc ^= p[k].x ^ p[k].y ^ p[k].z ^ p[k].w;
+    }
+    for (; i < n; i += T) {
+        const uint4 p0 = src[i];
+        acc ^= p0.x ^ p0.y ^ p0.z ^ p0.w;
+    }
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t x = 0;
+        for (int j = 0; j < 256; ++j) x ^= red[j];
+        sink[blockIdx.x] = x;
+    }
+}
+
 int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream) {
     (void)hipGetLastError();
     const int threads = n / 4;
     hipLaunchKernelGGL(k_fp8_decode, dim3((threads + 255) / 256), dim3(256), 0, S(stream), n,
                        reinterpret_cast<const uint32_t *>(codes), reinterpret_cast<float4 *>(via_bf16),
                        reinterpret_cast<float4 *>(via_f32));
+    return launched();
+}
+
+int launch_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(k_read_probe, dim3(MOE_PROBE_GRID), dim3(256), 0, S(stream),
+                       reinterpret_cast<const uint4 *>(src), bytes / 16, sink);
     return launched();
 }
 

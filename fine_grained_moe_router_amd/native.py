@@ -23,7 +23,7 @@ MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "lm_head_argmax_workspace",
            "lm_head_argmax", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
-           "moe_strerror")
+           "moe_hbm_read_probe", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.moe_add_rmsnorm.argtypes = [I, I, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P]
         L.moe_fp8_decode.restype = I
         L.moe_fp8_decode.argtypes = [I, _P, _P, _P, _P]
+        L.moe_hbm_read_probe.restype = I
+        L.moe_hbm_read_probe.argtypes = [_P, S, _P, _P]
         L.moe_decode_step_workspace.restype = S
         L.moe_decode_step_workspace.argtypes = [ctypes.POINTER(StepDesc)]
         L.moe_decode_step_prepare.restype = I
@@ -163,6 +165,14 @@ def moe_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream=None):
     st = lib().moe_fp8_decode(int(n), _ptr(codes), _ptr(out_via_bf16), _ptr(out_via_f32),
                               _stream(stream))
     _check("moe_fp8_decode", st)
+
+
+PROBE_GRID = 4096   # MOE_PROBE_GRID: words of the read probe's sink
+
+
+def moe_hbm_read_probe(src, nbytes, sink, stream=None):
+    st = lib().moe_hbm_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream))
+    _check("moe_hbm_read_probe", st)
 
 
 def step_desc(shape, max_tokens: int, eps: float = 1e-6, spin_limit: int = 0,

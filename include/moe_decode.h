@@ -180,6 +180,17 @@ int moe_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *add0,
 int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,
                    void *stream);
 
+/*
+ * Diagnostic: the streaming-read rate a kernel of this library gets from HBM, the
+ * practical ceiling to set beside the nominal 8 TB/s. Reads `bytes` bytes from src once,
+ * with 16-byte loads spread over MOE_PROBE_GRID workgroups of 256 threads, and folds them
+ * into one word per workgroup (sink[w] = XOR of the 32-bit words workgroup w read), so
+ * that the loads are kept. bytes a positive multiple of 16; src and sink 16-byte aligned;
+ * sink holds MOE_PROBE_GRID words. Asynchronous on `stream`.
+ */
+#define MOE_PROBE_GRID 4096
+int moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
 /* ------------------------------------------------------------------------------
  * The whole stacked decode step in one launch.
  *

@@ -177,6 +177,15 @@ def test_fp8_decode_validation():
     assert L.moe_fp8_decode(256, FAKE, FAKE + 4, FAKE, None) == native.MOE_EALIGN
 
 
+def test_hbm_read_probe_validation():
+    L = native.lib()
+    assert L.moe_hbm_read_probe(FAKE, 0, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_hbm_read_probe(FAKE, 24, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_hbm_read_probe(None, 4096, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_hbm_read_probe(FAKE + 8, 4096, FAKE, None) == native.MOE_EALIGN
+    assert L.moe_hbm_read_probe(FAKE, 4096, FAKE + 4, None) == native.MOE_EALIGN
+
+
 # ------------------------------------------------------------------ fused step
 
 def step_desc(**over):

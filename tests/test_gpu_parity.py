@@ -304,3 +304,20 @@ def test_add_rmsnorm(H, M):
         native.moe_add_rmsnorm(M, H, hd2, a0.to(DEV), a1.to(DEV) if with_a1 else None, g.to(DEV), 1e-6, hd2, u2)
         torch.cuda.synchronize()
         assert (synth.bits16(hd2) == hb).all() and (synth.bits16(u2) == ub).all()
+
+
+def test_hbm_read_probe_reads_every_byte_once():
+    """The read probe's sink words XOR to the XOR of every 32-bit word of the buffer (each
+    16-byte piece is read exactly once), including a tail that is not a multiple of the
+    grid's stride."""
+    g = torch.Generator().manual_seed(11)
+    for nbytes in (16, 4096 * 256 * 16 * 4 + 48, 3 << 20):
+        data = torch.randint(0, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+        src = data.to(DEV)
+        sink = torch.zeros(native.PROBE_GRID, dtype=torch.int32, device=DEV)
+        native.moe_hbm_read_probe(src, nbytes, sink)
+        torch.cuda.synchronize()
+        want = np.bitwise_xor.reduce(data.numpy().view(np.uint32))
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, nbytes
+
