@@ -19,11 +19,11 @@
 //  units    the layer's work is a list: 8-row gate/up units (gate and up rows of one
 //           slot), 64-row down units (one slot, one row block), then 64-row combine
 //           units. Unit i belongs to workgroup i mod G, which keeps two of its units'
-//           weights in flight (one, with one token). A gate/up unit writes h = gelu_tanh(gate) * up for the
-//           slot's tokens; a down unit reads the slot's h, multiplies and writes its
-//           weighted partial sums; a combine unit sums a row block's sub-slots in a
-//           fixed order into y_l, adds the residual and the next layer's noise and
-//           writes the next residual rows.
+//           weights in flight (one, with one token). A gate/up unit writes
+//           h = gelu_tanh(gate) * up for the slot's tokens; a down unit reads the
+//           slot's h, multiplies and writes its weighted partial sums; a combine unit
+//           sums a row block's sub-slots in a fixed order into y_l, adds the residual
+//           and the next layer's noise and writes the next residual rows.
 //  lm_head  every workgroup forms x_f itself, streams an equal share of the
 //           vocabulary rows with three steps in flight, and leaves its per-token best
 //           (ordered logit, inverted row) key; workgroup 0 reduces the keys, writes
