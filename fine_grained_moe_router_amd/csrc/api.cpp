@@ -70,6 +70,7 @@ int check_step_desc(const moe_step_desc *d) {
     if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
     if (d->max_tokens < 1 || d->max_tokens > kMaxM) return MOE_EINVAL;
     if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    if (d->flags & ~MOE_STEP_COOPERATIVE) return MOE_EINVAL;
     return MOE_OK;
 }
 

@@ -22,8 +22,9 @@
 //           weights in flight (one, with one token). A gate/up unit writes
 //           h = gelu_tanh(gate) * up for the slot's tokens; a down unit reads the
 //           slot's h, multiplies and writes its weighted partial sums; a combine unit
-//           sums a row block's sub-slots in a fixed order into y_l, adds the residual
-//           and the next layer's noise and writes the next residual rows.
+//           sums a row block's sub-slots into y_l (each token's routed experts in
+//           ascending id, then the shared expert's column segments), adds the
+//           residual and the next layer's noise and writes the next residual rows.
 //  lm_head  every workgroup forms x_f itself, streams an equal share of the
 //           vocabulary rows with three steps in flight, and leaves its per-token best
 //           (ordered logit, inverted row) key; workgroup 0 reduces the keys, writes
@@ -199,6 +200,9 @@ __device__ __forceinline__ char *scratch(AP a) { return smem + a->l_scr; }
 // A wave's polling loop: done() is true once every lane's words are current (or the
 // spin limit is reached, which raises the error flag); otherwise it sleeps SLEEP x 64
 // cycles and the loop reloads.
+// Once any wait of the step has given up, every other wait gives up within 256 polls
+// (it checks the error flag that often), so a step whose workgroups cannot all make
+// progress ends after about one spin limit rather than one per wait.
 template <int SLEEP>
 struct PollS {
     unsigned spins = 0;
@@ -208,6 +212,7 @@ struct PollS {
             if ((ltid() & 63) == 0) st32(ctr(a, kErrCtr), 1u);
             return true;
         }
+        if ((spins & 255u) == 0u && __builtin_amdgcn_readfirstlane(ld32(ctr(a, kErrCtr))) != 0u) return true;
         __builtin_amdgcn_s_sleep(SLEEP);
         return false;
     }
@@ -609,15 +614,16 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
                 const bool on = (um >> m) & 1u;
                 S.sw[slot][m] = on ? wm[m] : 0.0f;
                 if (on) {
-                    // expert tid's place in token m's list (ascending id)
+                    // expert tid's place in token m's list (ascending id); the shared
+                    // expert's segments follow the K routed experts
                     const int pos = pre[m] + lanes_below(Bw[m]);
-                    for (int sg = 0; sg < nsr; ++sg) S.tsub[m][nsh + pos * nsr + sg] = nsh + (slot - has_sh) * nsr + sg;
+                    for (int sg = 0; sg < nsr; ++sg) S.tsub[m][pos * nsr + sg] = nsh + (slot - has_sh) * nsr + sg;
                 }
             }
         }
     }
     if (tid < M) {
-        for (int sg = 0; sg < nsh; ++sg) S.tsub[tid][sg] = sg;
+        for (int sg = 0; sg < nsh; ++sg) S.tsub[tid][K * nsr + sg] = sg;
         if (has_sh) S.sw[0][tid] = 1.0f;
     }
     if (tid == 0 && has_sh) {
@@ -1325,32 +1331,51 @@ __global__ void k_router_transpose(const uint16_t *__restrict__ src, uint16_t *_
 inline hipStream_t Sm(void *p) { return reinterpret_cast<hipStream_t>(p); }
 
 // Every workgroup must be resident at once (units wait on other workgroups' units): the
-// grid is the occupancy of the step kernel for M tokens times the compute units.
+// grid is the occupancy of the step kernel for M tokens times the compute units. With
+// `coop` and outside stream capture the step is launched cooperatively, so the runtime
+// starts it only with every workgroup resident and refuses a grid that cannot be
+// (MOE_EUNSUPPORTED); it costs about 27 us per step on MI355X. A plain launch (and every
+// captured step) relies on the caller not running other work on the device meanwhile;
+// the bounded waits end a step that could not make progress (MOE_ETIMEOUT from
+// moe_decode_step_status).
 template <int MT, bool BF>
-int launch_mt(const StepArgs &a, size_t lds, int NR, void *stream) {
+int launch_mt(const StepArgs &a, size_t lds, int NR, bool coop, void *stream) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_step<MT, BF>, kWG, lds) != hipSuccess || per_cu < 1)
         return MOE_ELAUNCH;
     const int grid = std::min(cus * std::min(per_cu, step_max_blocks<MT>()), kStepMaxGrid);
-    if (grid <= NR) return MOE_ELAUNCH;   // the last NR workgroups only route
-    hipLaunchKernelGGL((k_step<MT, BF>), dim3(grid), dim3(kWG), lds, Sm(stream), a);
-    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+    if (grid <= NR) return MOE_EUNSUPPORTED;   // the last NR workgroups only route
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(Sm(stream), &cap) != hipSuccess) return MOE_ELAUNCH;
+    if (!coop || cap != hipStreamCaptureStatusNone) {
+        hipLaunchKernelGGL((k_step<MT, BF>), dim3(grid), dim3(kWG), lds, Sm(stream), a);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+    }
+    StepArgs arg = a;
+    void *params[] = {&arg};
+    const hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&k_step<MT, BF>), dim3(grid),
+                                                    dim3(kWG), params, (unsigned)lds, Sm(stream));
+    if (e == hipErrorCooperativeLaunchTooLarge) {
+        (void)hipGetLastError();
+        return MOE_EUNSUPPORTED;
+    }
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
 // One kernel per token count (token loops are unrolled exactly) and expert weight type.
 template <bool BF>
-int launch_m(int M, const StepArgs &a, size_t lds, int NR, void *stream) {
+int launch_m(int M, const StepArgs &a, size_t lds, int NR, bool coop, void *stream) {
     switch (M) {
-    case 1: return launch_mt<1, BF>(a, lds, NR, stream);
-    case 2: return launch_mt<2, BF>(a, lds, NR, stream);
-    case 3: return launch_mt<3, BF>(a, lds, NR, stream);
-    case 4: return launch_mt<4, BF>(a, lds, NR, stream);
-    case 5: return launch_mt<5, BF>(a, lds, NR, stream);
-    case 6: return launch_mt<6, BF>(a, lds, NR, stream);
-    case 7: return launch_mt<7, BF>(a, lds, NR, stream);
-    case 8: return launch_mt<8, BF>(a, lds, NR, stream);
+    case 1: return launch_mt<1, BF>(a, lds, NR, coop, stream);
+    case 2: return launch_mt<2, BF>(a, lds, NR, coop, stream);
+    case 3: return launch_mt<3, BF>(a, lds, NR, coop, stream);
+    case 4: return launch_mt<4, BF>(a, lds, NR, coop, stream);
+    case 5: return launch_mt<5, BF>(a, lds, NR, coop, stream);
+    case 6: return launch_mt<6, BF>(a, lds, NR, coop, stream);
+    case 7: return launch_mt<7, BF>(a, lds, NR, coop, stream);
+    case 8: return launch_mt<8, BF>(a, lds, NR, coop, stream);
     default: return MOE_EINVAL;
     }
 }
@@ -1386,13 +1411,17 @@ int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weig
     return hipDeviceSynchronize() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
+// After a wait has given up, hand-off words of that step (or of a workgroup that started
+// after the epoch moved on) may carry the next step's tag. The flag, the epoch and every
+// hand-off word are therefore cleared (the weight table and the re-laid-out router
+// weights are kept), so the next step starts from tag 1 with nothing current.
 int step_status(const StepWs &W, char *ws) {
     int err = 0;
     char *flag = ws + W.ctr + sizeof(int) * kCtrStride * kErrCtr;
     if (hipMemcpy(&err, flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ELAUNCH;
     if (!err) return MOE_OK;
-    const int zero = 0;
-    if (hipMemcpy(flag, &zero, sizeof(int), hipMemcpyHostToDevice) != hipSuccess) return MOE_ELAUNCH;
+    if (hipMemset(ws + W.ctr, 0, W.total - W.ctr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return MOE_ELAUNCH;
     return MOE_ETIMEOUT;
 }
 
@@ -1452,7 +1481,9 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.spin_limit = d.spin_limit ? d.spin_limit : kDefaultSpin;
 
     const size_t lds = step_lds_bytes(d, M, &a.l_scr, &a.l_slot);
-    return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, stream) : launch_m<false>(M, a, lds, W.NR, stream);
+    const bool coop = (d.flags & MOE_STEP_COOPERATIVE) != 0;
+    return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, coop, stream)
+                                  : launch_m<false>(M, a, lds, W.NR, coop, stream);
 }
 
 }  // namespace moe

@@ -48,7 +48,11 @@ class LayerWeights(ctypes.Structure):
 
 class StepDesc(ctypes.Structure):
     _fields_ = [("layer", LayerDesc), ("num_layers", ctypes.c_int), ("vocab", ctypes.c_int),
-                ("max_tokens", ctypes.c_int), ("eps", ctypes.c_float), ("spin_limit", ctypes.c_uint)]
+                ("max_tokens", ctypes.c_int), ("eps", ctypes.c_float), ("spin_limit", ctypes.c_uint),
+                ("flags", ctypes.c_uint)]
+
+
+MOE_STEP_COOPERATIVE = 1
 
 
 def lib() -> ctypes.CDLL:
@@ -176,8 +180,9 @@ def moe_hbm_read_probe(src, nbytes, sink, stream=None):
 
 
 def step_desc(shape, max_tokens: int, eps: float = 1e-6, spin_limit: int = 0,
-              expert_dtype: str = "fp8") -> StepDesc:
-    return StepDesc(layer_desc(shape, expert_dtype), shape.layers, shape.vocab, max_tokens, eps, spin_limit)
+              expert_dtype: str = "fp8", cooperative: bool = False) -> StepDesc:
+    return StepDesc(layer_desc(shape, expert_dtype), shape.layers, shape.vocab, max_tokens, eps, spin_limit,
+                    MOE_STEP_COOPERATIVE if cooperative else 0)
 
 
 def moe_decode_step_workspace(desc: StepDesc) -> int:

@@ -73,14 +73,15 @@ class FusedDecodeStep:
     moe_decode_step (one persistent kernel per step)."""
 
     def __init__(self, shape, layers, gains, lm_w, lm_s, max_M: int, eps: float = 1e-6,
-                 spin_limit: int = 0, device="cuda"):
+                 spin_limit: int = 0, device="cuda", cooperative: bool = False):
         self.shape = shape
         self.L = len(layers)
         self.max_M = max_M
         self.layers = layers
         self.gains, self.lm_w, self.lm_s = gains, lm_w, lm_s
         expert_dtype = layers[0].get("expert_dtype", "fp8")
-        self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit, expert_dtype)
+        self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit, expert_dtype,
+                                     cooperative)
         self.ws_bytes = native.moe_decode_step_workspace(self.desc)
         if self.ws_bytes == 0:
             raise ValueError("unsupported shape for the fused decode step")

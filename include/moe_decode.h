@@ -106,7 +106,13 @@ size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M);
 
 /*
  * One MoE layer for M tokens (1 <= M <= 8; the batch-1 decode step is M = 1, the
- * speculative verify step with gamma drafts is M = gamma + 1).
+ * speculative verify step with gamma drafts is M = gamma + 1). Page "LLM decoding":
+ * "The exact architecture, and why it rules out 4-bit" (top 8 of 128 routed experts
+ * plus one always-on shared expert, expert width 704, hidden 2816); "Where the
+ * 7.36 GB goes" (a gate, an up and a down matrix per expert, and the router);
+ * "Lever 1: fewer bytes (FP8 weights)" (8-bit weights, arithmetic in a wider type).
+ * The gating (softmax over all experts, keep K, renormalise), the GELU-tanh gate and
+ * the tie rule are readings the page leaves open.
  *   logits[m][e] = sum_c x[m][c] * router_w[c][e] (+ router_bias[e])
  *   S_m          = the K experts with the largest logits (equal logits: lower id)
  *   w[m][e]      = softmax(logits[m])[e] / sum_{j in S_m} softmax(logits[m])[j]
@@ -209,9 +215,24 @@ int moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stre
  * of the layer's units (8-row gate/up blocks, 64-row down blocks, 64-row combine
  * blocks) in a fixed order; then every workgroup streams a share of the lm_head.
  * Data passes between workgroups in tagged device-memory words, each polled until its
- * tag is the current step's. Every weight byte the step needs is read once. The shape
- * must satisfy hidden <= 2816 and expert_width <= 704 (one 704-column down row per
- * unit); wider layers are rejected with MOE_EINVAL.
+ * tag is the current step's. Every weight byte the step needs is read once. y_l[m] is
+ * summed as in moe_decode_layer: token m's routed experts in ascending id, then the
+ * shared expert (whose down rows are split into column segments when it is wider
+ * than 704, each segment a separate term, in order). The shape must satisfy
+ * hidden <= 2816 and expert_width <= 704 (one 704-column down row per unit); wider
+ * layers are rejected with MOE_EINVAL.
+ *
+ * Co-residency: every workgroup of the step waits on other workgroups, so all of them
+ * must be resident at once. The grid is sized to the kernel's occupancy on the device
+ * (a grid that cannot fit returns MOE_EUNSUPPORTED). With MOE_STEP_COOPERATIVE in
+ * flags, and outside stream capture, the step is launched cooperatively: the runtime
+ * starts it only with every workgroup resident (about 27 us more per step on MI355X,
+ * for callers that share the device with other work). Otherwise, and always inside
+ * capture, it is a plain launch that relies on nothing else occupying the device. In
+ * every case each device-side wait is bounded (spin_limit polls) and, once one gives
+ * up, the others give up within a few hundred polls: a step that cannot make progress
+ * ends quickly, its results invalid and the timeout recorded for
+ * moe_decode_step_status; it never hangs and never reports wrong results as valid.
  * ---------------------------------------------------------------------------- */
 
 typedef struct moe_step_desc {
@@ -222,7 +243,10 @@ typedef struct moe_step_desc {
     float eps;              /* RMSNorm epsilon, >= 0                                           */
     unsigned spin_limit;    /* polls of a device-side wait before it gives up and flags a
                                timeout (0: a default of about a quarter second)                    */
+    unsigned flags;         /* MOE_STEP_* bits                                                 */
 } moe_step_desc;
+
+#define MOE_STEP_COOPERATIVE 1u   /* launch cooperatively outside stream capture (see above) */
 
 /* Bytes of workspace for moe_decode_step (0 if desc is invalid). */
 size_t moe_decode_step_workspace(const moe_step_desc *desc);
@@ -257,8 +281,10 @@ int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
 
 /*
  * Synchronous: MOE_OK, or MOE_ETIMEOUT if a device-side wait of a step run on this
- * workspace since the last call gave up (its results are then invalid). Clears the
- * flag. Call after the stream has been synchronised.
+ * workspace since the last call gave up (its results, and those of later steps up to
+ * this call, are then invalid). After a timeout it clears the flag and every hand-off
+ * word of the workspace (the prepared weight table stays), so the next step runs
+ * normally. Call after the stream has been synchronised, with no step in flight.
  */
 int moe_decode_step_status(const moe_step_desc *desc, void *workspace);
 

@@ -201,8 +201,9 @@ def test_step_workspace_and_desc_validation():
     d = step_desc()
     assert native.moe_decode_step_workspace(d) > 0
     for k, v in (("num_layers", 0), ("num_layers", 65), ("vocab", 100), ("max_tokens", 9), ("max_tokens", 0),
-                 ("eps", -1.0)):
+                 ("eps", -1.0), ("flags", 2), ("flags", 0x80000001)):
         assert native.moe_decode_step_workspace(step_desc(**{k: v})) == 0, k
+    assert native.moe_decode_step_workspace(step_desc(flags=native.MOE_STEP_COOPERATIVE)) > 0
     wide = step_desc()
     wide.layer.hidden = 3072                       # the fused step takes H <= 2816
     assert native.moe_decode_step_workspace(wide) == 0

@@ -186,7 +186,11 @@ def test_verify_batch_equals_sequential_steps(stack):
 def test_fused_step_each_layer_on_oracle_inputs(stack, oracle_steps, M):
     """The fused kernel run as a one-layer step on every layer's weights, with the
     oracle's residual h_l as its input (noise 0, gains g_l and g_L): the layer's
-    expert ids and y_l must match the oracle's."""
+    expert ids and y_l must match the oracle's, and so must the tokens of the full
+    262,144-row lm_head on that one-layer step's final norm (the oracle's own x_f =
+    rmsnorm(h_l + y_l; g_L)), wherever the oracle's top-2 logit margin is at least
+    1e-3. Each such step streams 8 lm_head units per workgroup, so the unit-to-unit
+    scale prefetch of the lm_head phase is exercised."""
     from fine_grained_moe_router_amd.stack import FusedDecodeStep
     sh, st, host, gains_h, Qh, sh_ = stack
     x, noise, drafts, res = oracle_steps[M]
@@ -194,6 +198,7 @@ def test_fused_step_each_layer_on_oracle_inputs(stack, oracle_steps, M):
     zero = torch.zeros(1, M, sh.hidden, dtype=torch.bfloat16, device=DEV)
     d = torch.zeros(max(M - 1, 1), dtype=torch.int32, device=DEV)
     worst = 0.0
+    checked = 0
     for l in range(sh.layers):
         r = res["layers"][l]
         g2 = torch.stack([st.gains[l], st.gains[sh.layers]]).contiguous()
@@ -204,8 +209,78 @@ def test_fused_step_each_layer_on_oracle_inputs(stack, oracle_steps, M):
         assert (fs.topk_idx(M)[0].cpu().numpy() == r["idx"]).all(), "layer %d expert ids" % l
         err, _ = check_bf16_output(synth.bits16(fs.y(M)[0]), r["y"], None, "fused y layer %d" % l)
         worst = max(worst, err)
+        # the oracle's one-layer step from the same h_l: x_f from its own y_l, then lm_head
+        _, xf = oracle.add_rmsnorm(r["h"], r["y_bf16"], None, gains_h[sh.layers])
+        tok, ml, gap = oracle.lm_head_argmax(xf, Qh, sh_)
+        got = fs.tok[:M].cpu().numpy()
+        sure = gap >= 1e-3
+        assert (got[sure] == tok[sure]).all(), "layer %d one-layer tokens %s vs %s" % (l, got, tok)
+        np.testing.assert_allclose(fs.max_logit[:M].cpu().numpy()[sure], ml[sure], rtol=2e-3, atol=1e-4)
+        checked += int(sure.sum())
         del fs
-    say("M=%d fused, layer by layer: all 30 layers match; worst y rel-L2 %.3g" % (M, worst))
+    say("M=%d fused, layer by layer: all 30 layers match; worst y rel-L2 %.3g; %d one-layer tokens checked" % (
+        M, worst, checked))
+    assert checked >= sh.layers * M // 2
+
+
+def _two_layer_case(stack, M, step, bias=None):
+    """The first two Gemma-shaped layers of the stack (optionally with a router bias),
+    gains g_0, g_1 and the final gain, and a step input resampled until every decision
+    of the oracle's two-layer step has a margin of at least 1e-3."""
+    sh, st, host, gains_h, Qh, sh_ = stack
+    two = sh.with_(layers=2)
+    dev_layers = [dict(w) for w in st.layers[:2]]
+    host_layers = [dict(w) for w in host[:2]]
+    if bias is not None:
+        for w in dev_layers:
+            w["router_b"] = bias.to(DEV)
+        for w in host_layers:
+            w["router_b"] = bias.numpy()
+    g3_h = np.ascontiguousarray(gains_h[[0, 1, sh.layers]])
+    g3 = torch.stack([st.gains[0], st.gains[1], st.gains[sh.layers]]).contiguous()
+    for sub in range(40):
+        x = synth.hidden_inputs(two, M, step, sub)
+        noise = synth.stack_noise(two, M, step, sub)
+        res = oracle.stack_step(synth.bits16(x), host_layers, synth.bits16(noise), g3_h, Qh, sh_, sh.top_k)
+        if stack_decisions_unambiguous(res):
+            return two, dev_layers, g3, x, noise, res
+        say("M=%d sub %d: ambiguous decision, resampling" % (M, sub))
+    raise RuntimeError("no unambiguous two-layer input")
+
+
+@pytest.mark.parametrize("M,zipf", [(1, False), (5, False), (8, False), (8, True)])
+def test_fused_step_two_gemma_layers_end_to_end(stack, M, zipf):
+    """The fused step at the full Gemma-4-26B-A4B shape (H 2816, 128 experts, top 8,
+    width 704, the 262,144-row lm_head, up to 65 expert slots per layer at M=8), two
+    layers chained on the device, against the oracle's two-layer step end to end:
+    expert ids, routing weights and y of both layers, x_final, the tokens, the best
+    logits and the accepted length."""
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+    sh, st, host, gains_h, Qh, sh_ = stack
+    bias = synth.zipf_router_bias(sh.experts) if zipf else None
+    two, dev_layers, g3, x, noise, res = _two_layer_case(stack, M, 950 + M + 10 * zipf, bias)
+    drafts = synth.drafts(res["tok"], 0.7, sh.vocab, 950 + M)
+    n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
+    say("fused two Gemma layers M=%d zipf=%s" % (M, zipf))
+    fs = FusedDecodeStep(two, dev_layers, g3, st.lm_w, st.lm_s, max_M=8)
+    dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV) if M > 1 else None
+    fs.step(x.to(DEV), noise.to(DEV), dd, M)
+    torch.cuda.synchronize()
+    assert fs.status() == native.MOE_OK
+    idx = fs.topk_idx(M).cpu().numpy()
+    for l in range(2):
+        r = res["layers"][l]
+        assert (idx[l] == r["idx"]).all(), "layer %d expert ids" % l
+        np.testing.assert_allclose(fs.topk_w(M)[l].cpu().numpy(), r["w"], rtol=2e-3, atol=1e-5)
+        check_bf16_output(synth.bits16(fs.y(M)[l]), r["y"], None, "y layer %d" % l)
+    xf = synth.bits16(fs.x_final[:M])
+    assert rel_l2(bf16_f64(xf), bf16_f64(res["x_final"])) <= 2e-3
+    assert (xf == res["x_final"]).mean() > 0.95
+    assert (fs.tok[:M].cpu().numpy() == res["tok"]).all()
+    np.testing.assert_allclose(fs.max_logit[:M].cpu().numpy(), res["max_logit"], rtol=2e-3, atol=1e-4)
+    assert int(fs.accepted[0]) == n_ref and (fs.out_tokens[:M].cpu().numpy() == out_ref).all()
+    slots = [len(np.unique(idx[l])) + 1 for l in range(2)]
+    say("M=%d zipf=%s: two layers, tokens and acceptance match; expert slots per layer %s" % (M, zipf, slots))
 
 
 @pytest.mark.parametrize("M", [1, 5])

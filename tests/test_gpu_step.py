@@ -42,12 +42,12 @@ def oracle_step(shape, host, gains, Q, s, M, step):
     raise RuntimeError("no unambiguous input")
 
 
-def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None):
+def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None, cooperative=False):
     layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias)
     x, noise, res = oracle_step(shape, host, gains, Q, s, M, step)
     drafts = synth.drafts(res["tok"], 0.7, shape.vocab, step)
     n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
-    fs = FusedDecodeStep(shape, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8)
+    fs = FusedDecodeStep(shape, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8, cooperative=cooperative)
     dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV) if M > 1 else None
     fs.step(x.to(DEV), noise.to(DEV), dd, M)
     torch.cuda.synchronize()
@@ -78,6 +78,14 @@ def test_fused_step_tiny(L, M):
     run_and_check(synth.TINY.with_(layers=L), M, step=10 * L + M, what="L=%d M=%d" % (L, M))
 
 
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_step_cooperative_launch(M):
+    """The opt-in cooperative launch (every workgroup resident before any starts) gives
+    the same results as the oracle."""
+    say("fused cooperative M=%d" % M)
+    run_and_check(synth.TINY.with_(layers=2), M, step=30 + M, what="coop M=%d" % M, cooperative=True)
+
+
 FUSED_VARIANTS = {
     "no_shared": synth.TINY.with_(shared_width=0, layers=2),
     "wide_shared": synth.TINY.with_(shared_width=192, layers=2),
@@ -86,6 +94,9 @@ FUSED_VARIANTS = {
     "e48_k6": synth.TINY.with_(experts=48, top_k=6, layers=2),
     "h2816": synth.TINY.with_(hidden=2816, experts=32, top_k=4, width=704, shared_width=704, vocab=8192,
                               layers=2),
+    # the page's 2112-wide always-on MLP as the shared expert: three 704-column down segments
+    "h2816_sh2112": synth.TINY.with_(hidden=2816, experts=32, top_k=4, width=704, shared_width=2112,
+                                     vocab=8192, layers=2),
 }
 
 
@@ -194,3 +205,35 @@ def test_fused_step_graph_capture_replays():
         assert torch.equal(fs.y(5), ref[0]) and torch.equal(fs.tok[:5], ref[1]), rep
         _ = torch.ones(512, device=DEV).sum().item()
     assert fs.status() == native.MOE_OK
+
+
+def test_fused_step_timeout_then_recovers():
+    """A spin limit of one poll makes the step's own bounded waits give up (no wait is
+    satisfied on its first poll): every workgroup still exits, the status reports the
+    timeout, and the next step on the same workspace with the default limit matches
+    the oracle."""
+    sh = synth.TINY.with_(layers=2)
+    M = 5
+    layers, host, gains, Q, s, dev = make(sh, seed=11)
+    x, noise, res = oracle_step(sh, host, gains, Q, s, M, step=800)
+    drafts = synth.drafts(res["tok"], 0.7, sh.vocab, 800)
+    n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
+    fs = FusedDecodeStep(sh, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8, spin_limit=1)
+    dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV)
+    say("fused step with spin limit 1")
+    fs.step(x.to(DEV), noise.to(DEV), dd, M)
+    torch.cuda.synchronize()
+    assert fs.status() == native.MOE_ETIMEOUT
+    assert fs.status() == native.MOE_OK          # cleared
+    fs.desc.spin_limit = 0
+    say("fused step with the default spin limit")
+    for rep in range(2):
+        fs.step(x.to(DEV), noise.to(DEV), dd, M)
+        torch.cuda.synchronize()
+        assert fs.status() == native.MOE_OK
+        idx, y = fs.topk_idx(M).cpu().numpy(), fs.y(M)
+        for l in range(sh.layers):
+            assert (idx[l] == res["layers"][l]["idx"]).all(), (rep, l)
+            check_bf16_output(synth.bits16(y[l]), res["layers"][l]["y"], None, "y layer %d" % l)
+        assert (fs.tok[:M].cpu().numpy() == res["tok"]).all()
+        assert int(fs.accepted[0]) == n_ref and (fs.out_tokens[:M].cpu().numpy() == out_ref).all()

@@ -413,26 +413,145 @@ def test_add_rmsnorm_vs_torch():
 
 
 # --------------------------------------------------------- stack wiring
+#
+# The stacked step is pinned against an independent numpy evaluation: bf16
+# round-to-nearest-even written from the format (np.round is half-to-even), the
+# dense numpy layer above, a numpy RMSNorm and a dense numpy lm_head. None of it
+# calls the oracle, so a wiring mistake in oracle.stack_step (noise added after the
+# norm, a gain applied to the wrong layer, noise after the last layer, a dropped
+# residual term) makes the two disagree.
 
-def test_stack_step_wiring_matches_manual_composition():
-    shape = synth.TINY.with_(layers=2)
-    layers = [synth.weights_to_host(synth.layer_weights(shape, l, "cpu", seed=1)) for l in range(2)]
-    x = synth.bits16(synth.hidden_inputs(shape, 2, step=0))
-    noise = synth.bits16(synth.stack_noise(shape, 2, step=0))
-    gains = synth.bits16(synth.rmsnorm_gains(shape))
-    Q, s = synth.lm_head(shape)
-    Q, s = synth.bytes8(Q), synth.f32(s)
-    out = oracle.stack_step(x, layers, noise, gains, Q, s, shape.top_k,
-                            draft=np.array([1], np.int32))
-    h0, u0 = oracle.add_rmsnorm(x, noise[0], None, gains[0])
-    y0 = oracle.moe_layer(u0, layers[0], shape.top_k)["y_bf16"]
-    h1, u1 = oracle.add_rmsnorm(h0, noise[1], y0, gains[1])
-    y1 = oracle.moe_layer(u1, layers[1], shape.top_k)["y_bf16"]
-    h2, xf = oracle.add_rmsnorm(h1, y1, None, gains[2])
-    tok, _, _ = oracle.lm_head_argmax(xf, Q, s)
-    assert (out["layers"][1]["u"] == u1).all() and (out["x_final"] == xf).all()
+def bf16_rne_np(v):
+    """Nearest bf16 (ties to even) of fp64 values, as uint16 bit patterns (normal and
+    subnormal range; no overflow handling needed here)."""
+    v = np.asarray(v, np.float64)
+    _, e = np.frexp(v)                      # |v| = f 2^e, f in [0.5, 1)
+    ex = np.maximum(e - 1, -126)            # unbiased exponent, clamped to the subnormal range
+    q = np.ldexp(1.0, ex - 7)               # spacing of bf16 values near v
+    r = np.round(v / q) * q                 # exact: v / q scales by a power of two
+    r = np.where(v == 0, v, r)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def rmsnorm_np(h_bits, g_bits, eps):
+    h = bf16_np(h_bits)
+    ms = np.array([math.fsum(row * row) for row in h]) / h.shape[1]
+    r = 1.0 / np.sqrt(ms + eps)
+    return bf16_rne_np(h * r[:, None] * bf16_np(g_bits)[None, :])
+
+
+def stack_numpy(x, layers, noise, gains, Q, s, K, eps=1e-6):
+    """The stacked step: h_0 = bf16(x + noise_0), u_l = rmsnorm(h_l; g_l),
+    y_l = layer_l(u_l), h_{l+1} = bf16(h_l + noise_{l+1} + y_l) (no noise after the last
+    layer), x_f = rmsnorm(h_L; g_L), tok = argmax lm_head(x_f)."""
+    L = len(layers)
+    h = bf16_rne_np(bf16_np(x) + bf16_np(noise[0]))
+    per = []
+    for l in range(L):
+        u = rmsnorm_np(h, gains[l], eps)
+        sel, _, y, _ = dense_layer_numpy(u, layers[l], K)
+        yb = bf16_rne_np(y)
+        per.append({"h": h, "u": u, "idx": sel, "y": y, "y_bf16": yb})
+        nxt = bf16_np(h) + bf16_np(yb)
+        if l + 1 < L:
+            nxt = nxt + bf16_np(noise[l + 1])
+        h = bf16_rne_np(nxt)
+    xf = rmsnorm_np(h, gains[L], eps)
+    logits = (FP8_TABLE[Q] @ bf16_np(xf).T).T * s.astype(np.float64)[None, :]
+    return per, h, xf, np.argmax(logits, axis=1), logits
+
+
+def _stack_inputs(shape, M, seed):
+    layers = [synth.weights_to_host(synth.layer_weights(shape, l, "cpu", seed=seed)) for l in range(shape.layers)]
+    gains = synth.bits16(synth.rmsnorm_gains(shape, seed=seed))
+    Q, s = synth.lm_head(shape, seed=seed)
+    return layers, gains, synth.bytes8(Q), synth.f32(s)
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_stack_step_matches_independent_numpy_stack(M):
+    shape = synth.TINY.with_(layers=3)
+    layers, gains, Q, s = _stack_inputs(shape, M, seed=1)
+    x = synth.bits16(synth.hidden_inputs(shape, M, step=0))
+    noise = synth.bits16(synth.stack_noise(shape, M, step=0))
+    out = oracle.stack_step(x, layers, noise, gains, Q, s, shape.top_k)
+    per, h_last, xf, tok, logits = stack_numpy(x, layers, noise, gains, Q, s, shape.top_k)
+    for l in range(shape.layers):
+        o, r = out["layers"][l], per[l]
+        assert (o["gap"] > 1e-9).all()
+        assert (o["h"] == r["h"]).all(), "residual entering layer %d" % l
+        assert (o["u"] == r["u"]).all(), "normalised input of layer %d" % l
+        assert (o["idx"] == r["idx"]).all(), "routing of layer %d" % l
+        np.testing.assert_allclose(o["y"], r["y"], rtol=1e-12, atol=1e-15)
+        assert (o["y_bf16"] == r["y_bf16"]).all(), "y of layer %d" % l
+    assert (out["h_final"] == h_last).all()
+    assert (out["x_final"] == xf).all()
     assert (out["tok"] == tok).all()
-    assert out["accepted"] == (1 if tok[0] == 1 else 0)
+    np.testing.assert_allclose(out["max_logit"], logits.max(axis=1), rtol=1e-12)
+
+
+def _zero_experts(w):
+    w = dict(w)
+    for k in ("gate_s", "sh_gate_s"):
+        w[k] = np.zeros_like(w[k])
+    return w
+
+
+def test_stack_step_zero_experts_closed_form():
+    """Zero gate scales make every expert output exactly 0 (gelu(0) = 0), so the
+    residual stream is the running bf16 sum of x and the noises, x_final its RMSNorm
+    with the last gain, and the tokens the argmax of the dense lm_head of x_final."""
+    shape = synth.TINY.with_(layers=3)
+    M = 4
+    layers, gains, Q, s = _stack_inputs(shape, M, seed=2)
+    layers = [_zero_experts(w) for w in layers]
+    x = synth.bits16(synth.hidden_inputs(shape, M, step=3))
+    noise = synth.bits16(synth.stack_noise(shape, M, step=3))
+    out = oracle.stack_step(x, layers, noise, gains, Q, s, shape.top_k)
+    h = bf16_np(x)
+    for l in range(shape.layers):
+        h = bf16_np(bf16_rne_np(h + bf16_np(noise[l])))
+        assert (out["layers"][l]["y_bf16"] == 0).all()
+        assert (out["layers"][l]["h"] == bf16_rne_np(h)).all(), l
+        assert (out["layers"][l]["u"] == rmsnorm_np(bf16_rne_np(h), gains[l], 1e-6)).all(), l
+    assert (out["h_final"] == bf16_rne_np(h)).all()
+    xf = rmsnorm_np(bf16_rne_np(h), gains[shape.layers], 1e-6)
+    assert (out["x_final"] == xf).all()
+    logits = (FP8_TABLE[Q] @ bf16_np(xf).T).T * s.astype(np.float64)[None, :]
+    assert (out["tok"] == np.argmax(logits, axis=1)).all()
+
+
+def test_stack_step_noise_and_gain_indices():
+    """x = 0, noise_l = 2^l everywhere, zero experts, eps = 0: layer l sees the
+    constant residual 2^(l+1) - 1, its normalised input is exactly its own gain g_l,
+    the final residual is 7 (no noise after the last layer) and x_final is g_L."""
+    shape = synth.TINY.with_(layers=3)
+    M, H = 2, shape.hidden
+    layers, gains, Q, s = _stack_inputs(shape, M, seed=3)
+    layers = [_zero_experts(w) for w in layers]
+    x = np.zeros((M, H), np.uint16)
+    noise = np.stack([np.full((M, H), bf16_rne_np(2.0 ** l), np.uint16) for l in range(shape.layers)])
+    out = oracle.stack_step(x, layers, noise, gains, Q, s, shape.top_k, eps=0.0)
+    for l in range(shape.layers):
+        assert (bf16_np(out["layers"][l]["h"]) == 2.0 ** (l + 1) - 1).all(), l
+        assert (out["layers"][l]["u"] == gains[l][None, :]).all(), l
+    assert (bf16_np(out["h_final"]) == 7.0).all()
+    assert (out["x_final"] == gains[shape.layers][None, :]).all()
+
+
+def test_stack_numpy_pin_detects_planted_wiring_mistakes():
+    """The numpy stack tells apart the wirings a plausible mistake would give."""
+    shape = synth.TINY.with_(layers=2)
+    layers, gains, Q, s = _stack_inputs(shape, 2, seed=4)
+    x = synth.bits16(synth.hidden_inputs(shape, 2, step=5))
+    noise = synth.bits16(synth.stack_noise(shape, 2, step=5))
+    good = oracle.stack_step(x, layers, noise, gains, Q, s, shape.top_k)
+    swapped = oracle.stack_step(x, layers, noise, gains[[1, 0, 2]], Q, s, shape.top_k)
+    assert not (swapped["layers"][0]["u"] == good["layers"][0]["u"]).all()
+    per, h_last, xf, _, _ = stack_numpy(x, layers, noise, gains, Q, s, shape.top_k)
+    assert (good["x_final"] == xf).all()
+    extra = bf16_rne_np(bf16_np(h_last) + bf16_np(noise[-1]))     # noise after the last layer
+    assert not (extra == h_last).all()
 
 
 # ------------------------------------------------------------ byte budget
