@@ -137,6 +137,20 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     return launch_lm_head(M, H, V, x, w, w_s, token, max_logit, (char *)workspace, stream);
 }
 
+int lm_head_argmax_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
+                           int32_t *token, float *max_logit, void *stream) {
+    if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||
+        V > (1 << 30))
+        return MOE_EINVAL;
+    CHECK(need(x));
+    CHECK(need(w));
+    CHECK(need(w_s));
+    CHECK(need(token));
+    if (max_logit && !aligned16(max_logit)) return MOE_EALIGN;
+    if (lm_ws_bytes(M, V) > kLmNoallocScratch) return MOE_EWORKSPACE;   // beyond the static scratch
+    return launch_lm_head_noalloc(M, H, V, x, w, w_s, token, max_logit, stream);
+}
+
 int spec_accept(int num_draft, const int32_t *draft, const int32_t *target,
                 int32_t *accepted_len, int32_t *out_tokens, void *stream) {
     if (num_draft < 0 || num_draft > kMaxM - 1) return MOE_EINVAL;

@@ -67,6 +67,10 @@ inline size_t lm_ws_bytes(int M, int V) {
            align256((size_t)lm_grid(V) * M * sizeof(int32_t));
 }
 
+// Static scratch of lm_head_argmax_noalloc: the workspace of the largest call (M = 8,
+// the full lm_head grid), 128 KiB.
+constexpr size_t kLmNoallocScratch = 2 * (size_t)kLmMaxWG * kMaxM * 4;
+
 // ---------------------------------------------------------------- fused step
 
 constexpr int kMaxLayers = 64;
@@ -146,6 +150,8 @@ int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
                      char *ws, const LayerWs &L, void *stream);
 int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                    int32_t *token, float *max_logit, char *ws, void *stream);
+int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
+                           int32_t *token, float *max_logit, void *stream);
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,
                        int32_t *accepted_len, int32_t *out_tokens, void *stream);
 int launch_add_rmsnorm(int M, int H, const uint16_t *h_in, const uint16_t *a0, const uint16_t *a1,

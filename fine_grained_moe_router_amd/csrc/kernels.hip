@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -706,6 +708,39 @@ int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     hipLaunchKernelGGL(k_lmhead, dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, S(stream), a);
     return launched();
+}
+
+// ------------------------------------------------ lm_head without allocation
+
+// The scratch of lm_head_argmax_noalloc: the per-workgroup best logits and rows that
+// k_lmhead leaves for k_argmax_final, in a file-scope device array instead of a caller
+// workspace. Each device the library runs on holds its own copy until the process ends.
+// Host code never passes the array's name to a kernel (on the host it only stands in for
+// the symbol): its device address is looked up once per device with hipGetSymbolAddress
+// and kept below.
+static __device__ __align__(256) char g_lm_scratch[kLmNoallocScratch];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of g_lm_scratch, per device (set once)
+}  // namespace
+
+int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
+                           int32_t *token, float *max_logit, void *stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_lm_scratch)) != hipSuccess || !p) return MOE_ELAUNCH;
+            g_scratch_ptr[dev] = p;
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    return launch_lm_head(M, H, V, x, w, s, token, max_logit, static_cast<char *>(ptr), stream);
 }
 
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,

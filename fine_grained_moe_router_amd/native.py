@@ -21,7 +21,7 @@ MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "lm_head_argmax_workspace",
-           "lm_head_argmax", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
+           "lm_head_argmax", "lm_head_argmax_noalloc", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
            "moe_hbm_read_probe", "moe_strerror")
 
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.lm_head_argmax_workspace.argtypes = [I, I, I]
         L.lm_head_argmax.restype = I
         L.lm_head_argmax.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P, S, _P]
+        L.lm_head_argmax_noalloc.restype = I
+        L.lm_head_argmax_noalloc.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P]
         L.spec_accept.restype = I
         L.spec_accept.argtypes = [I, _P, _P, _P, _P, _P]
         L.moe_add_rmsnorm.restype = I
@@ -151,6 +153,12 @@ def lm_head_argmax(M, H, V, x, w, w_s, token, max_logit, workspace, workspace_by
     st = lib().lm_head_argmax(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), _ptr(token),
                               _ptr(max_logit), _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("lm_head_argmax", st)
+
+
+def lm_head_argmax_noalloc(M, H, V, x, w, w_s, token, max_logit, stream=None):
+    st = lib().lm_head_argmax_noalloc(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), _ptr(token),
+                                      _ptr(max_logit), _stream(stream))
+    _check("lm_head_argmax_noalloc", st)
 
 
 def spec_accept(num_draft, draft, target, accepted_len, out_tokens, stream=None):

@@ -151,6 +151,23 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
                    void *stream);
 
 /*
+ * lm_head_argmax for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the scratch held in a static device array of the library instead of a
+ * caller workspace. Arguments as lm_head_argmax (without the workspace).
+ *   - The static scratch is 128 KiB per device, enough for every valid M and V; a call
+ *     needing more returns MOE_EWORKSPACE. Each device keeps its copy until the process
+ *     ends; its address is looked up on the first call on that device (with that device
+ *     current), which is the only call that touches the HIP runtime beyond launching.
+ *   - Allocates nothing (no hipMalloc, no allocating library routine).
+ *   - Every call on a device shares that device's scratch, which keeps the last call's
+ *     contents (every value read is written first by the same call): calls that
+ *     overlap on one device, on different streams or from different threads, race.
+ */
+int lm_head_argmax_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w,
+                           const float *w_s, int32_t *token, float *max_logit, void *stream);
+
+/*
  * Greedy speculative acceptance (page "LLM decoding", "Lever 2: fewer passes" and
  * "What we learned": a drafted token is kept only if it is the token the target
  * itself produces, so the output equals ordinary greedy decoding).

@@ -149,6 +149,16 @@ def test_lm_head_validation():
     assert f(wsb=ws - 1) == native.MOE_EWORKSPACE and f(ws=None) == native.MOE_EWORKSPACE
 
 
+def test_lm_head_noalloc_validation():
+    L = native.lib()
+    assert L.lm_head_argmax_noalloc(0, 2816, 262144, FAKE, FAKE, FAKE, FAKE, None, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_noalloc(9, 2816, 262144, FAKE, FAKE, FAKE, FAKE, None, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_noalloc(1, 2816, 100, FAKE, FAKE, FAKE, FAKE, None, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_noalloc(1, 2816, 4096, None, FAKE, FAKE, FAKE, None, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_noalloc(1, 2816, 4096, FAKE + 2, FAKE, FAKE, FAKE, None, None) == native.MOE_EALIGN
+    assert L.lm_head_argmax_noalloc(1, 2816, 4096, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == native.MOE_EALIGN
+
+
 def test_spec_accept_validation():
     L = native.lib()
     assert L.spec_accept(-1, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
