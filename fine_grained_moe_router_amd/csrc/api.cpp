@@ -97,7 +97,7 @@ const char *moe_strerror(int status) {
 
 size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M) {
     if (check_layer_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
-    return layer_ws(*desc, max_M).total;
+    return layer_fits_step(*desc) ? layer_step_ws(*desc, max_M).total : layer_ws(*desc, max_M).total;
 }
 
 int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
@@ -109,9 +109,20 @@ int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int
     CHECK(need(x));
     CHECK(need(y));
     if (((uintptr_t)topk_idx | (uintptr_t)topk_w) & 3u) return MOE_EALIGN;
+    if (layer_fits_step(*desc)) {
+        if (!ws_ok(workspace, workspace_bytes, layer_step_ws(*desc, M).total)) return MOE_EWORKSPACE;
+        return launch_layer_step(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, stream);
+    }
     const LayerWs L = layer_ws(*desc, M);
     if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
     return launch_moe_layer(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, L, stream);
+}
+
+int moe_decode_layer_status(const moe_layer_desc *desc, void *workspace) {
+    CHECK(check_layer_desc(desc));
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MOE_EWORKSPACE;
+    if (!layer_fits_step(*desc)) return MOE_OK;   // the per-layer kernels have no device-side waits
+    return step_status(layer_step_ws(*desc, 1), (char *)workspace);
 }
 
 size_t lm_head_argmax_workspace(int max_M, int H, int V) {

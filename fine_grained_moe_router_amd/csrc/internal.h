@@ -108,7 +108,10 @@ struct StepWs {
     int f_lm, f_epoch, nflags;
 };
 
-inline StepWs step_ws(const moe_step_desc &d) {
+// prepared: the fused step's layout (weight table and re-laid-out router weights first);
+// otherwise moe_decode_layer's (neither region; the error flag and the flags come first, at
+// offsets that do not depend on the token count).
+inline StepWs step_ws(const moe_step_desc &d, bool prepared = true) {
     StepWs W{};
     const moe_layer_desc &ld = d.layer;
     const int H = ld.hidden, E = ld.num_experts, L = d.num_layers, Mx = d.max_tokens;
@@ -130,8 +133,8 @@ inline StepWs step_ws(const moe_step_desc &d) {
     W.nflags = W.f_epoch + 16;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
-    W.table = take(sizeof(moe_layer_weights) * (size_t)L);
-    W.rt = take(2 * (size_t)L * E * H);
+    W.table = take(prepared ? sizeof(moe_layer_weights) * (size_t)L : 0);
+    W.rt = take(prepared ? 2 * (size_t)L * E * H : 0);
     W.ctr = take(sizeof(int) * (size_t)kCtrStride);
     W.flags = take(4 * (size_t)W.nflags);
     W.logits = take(8 * (size_t)L * Mx * E);
@@ -142,6 +145,25 @@ inline StepWs step_ws(const moe_step_desc &d) {
     W.total = o;
     return W;
 }
+
+// moe_decode_layer runs on the fused step's kernel (one layer, no lm_head) when the layer
+// fits its unit geometry; wider layers take the separate per-layer kernels.
+inline bool layer_fits_step(const moe_layer_desc &d) {
+    return d.hidden <= kStepMaxHidden && d.expert_width <= kStepMaxWidth &&
+           step_nseg(d.shared_width) <= kStepMaxSharedSeg;
+}
+
+inline moe_step_desc layer_step_desc(const moe_layer_desc &d, int M) {
+    moe_step_desc s{};
+    s.layer = d;
+    s.num_layers = 1;
+    s.vocab = 64;
+    s.max_tokens = M;
+    return s;
+}
+
+// Layout of moe_decode_layer's workspace on the fused kernel, for M tokens.
+inline StepWs layer_step_ws(const moe_layer_desc &d, int M) { return step_ws(layer_step_desc(d, M), false); }
 
 // Launchers (kernels.hip, step.hip). Arguments were validated by api.cpp. Each returns
 // MOE_OK or MOE_ELAUNCH.
@@ -161,6 +183,8 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
                 const int32_t *draft, int32_t *token, float *max_logit, int32_t *accepted_len,
                 int32_t *out_tokens, uint16_t *y_layers, int32_t *topk_idx, float *topk_w,
                 uint16_t *x_final, char *ws, void *stream);
+int launch_layer_step(const moe_layer_desc &d, const moe_layer_weights &w, int M, const uint16_t *x, uint16_t *y,
+                      int32_t *topk_idx, float *topk_w, char *ws, void *stream);
 int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weights *layers, char *ws);
 int step_status(const StepWs &W, char *ws);
 int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream);

@@ -79,6 +79,8 @@ struct StepArgs {
     int M, Mx, H, E, K, D, Ds, L, V, Sx, NR, ND, NSUBx, Fmax, nseg_r, nseg_s, NLU;
     float eps;
     unsigned spin_limit;
+    int layer_mode;                    // 1: one MoE layer from x (already normalised) to y (moe_decode_layer)
+    moe_layer_weights lw;              // layer mode: the layer's weights (router as given, [H][E])
 };
 
 constexpr int kWG = 256;
@@ -97,7 +99,7 @@ typedef const __attribute__((address_space(4))) StepArgs *AP;
 // before the launch and never during it, so its fields load through the scalar cache
 // and a use of them never waits on the vector loads in flight.
 typedef const __attribute__((address_space(4))) moe_layer_weights *WP;
-__device__ __forceinline__ WP layer_w(AP a, int l) { return (WP)(a->layers) + l; }
+__device__ __forceinline__ WP layer_w(AP a, int l) { return a->layer_mode ? &a->lw : (WP)(a->layers) + l; }
 
 __device__ __forceinline__ AP uniform(AP p) {
     const unsigned long long v = (unsigned long long)p;
@@ -407,6 +409,35 @@ __device__ __forceinline__ void norm_to_lds(AP a, int l, const uint16_t *g, uint
     __syncthreads();
 }
 
+// Layer mode: the layer input x (already normalised) into the u area as it is, zeros
+// past H, in place of the norm.
+template <int MT>
+__device__ __forceinline__ void x_to_lds(AP a) {
+    const int H = a->H, hw = H / 2, tid = ltid();
+    uint32_t *uw = reinterpret_cast<uint32_t *>(ulds());   // [M][kUS/2] bf16 pairs
+    uint32_t v[MT][kW];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int k = 0; k < kW; ++k) {
+            const int q = tid + k * kWG;
+            v[m][k] = q < hw ? *glb(reinterpret_cast<const uint32_t *>(a->x + (size_t)m * H + 2 * q)) : 0u;
+        }
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int k = 0; k < kW; ++k) uw[m * (kUS / 2) + tid + k * kWG] = v[m][k];
+    __syncthreads();
+}
+
+template <int MT, int SLEEP = 1>
+__device__ __forceinline__ void layer_input(AP a, int l, uint32_t tgt) {
+    if (a->layer_mode)
+        x_to_lds<MT>(a);
+    else
+        norm_to_lds<MT, SLEEP>(a, l, a->gains + (size_t)l * a->H, tgt);
+}
+
 // ------------------------------------------------------------------ router
 
 // Router workgroup j's weights for layer l: experts 8j .. 8j+7, one half-wave (32
@@ -421,6 +452,23 @@ __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]
         wq[k] = k < NC ? ld16(wr + k * 256) : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Layer mode: the same per-lane pieces gathered from the router weights as given, [H][E]
+// (element (c, e) at c * E + e): piece k of expert e holds columns k * 256 + 8 lane + 0..7,
+// eight 2-byte loads at a stride of one row. The arithmetic that follows is the fused
+// step's, so both give the same logits for the same u.
+__device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
+    const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
+    const int e = min(8 * j + (tid >> 5), E - 1);
+    const uint16_t *base = layer_w(a, 0)->router_w + e + (size_t)(tid & 31) * 8 * E;
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+        uint32_t v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = k < NC ? *glb(base + ((size_t)k * 256 + i) * E) : 0u;
+        wq[k] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+    }
+}
+
 // Router workgroup j, layer l: u_l, then the logits of experts 8j .. 8j+7 for every
 // token (weights already in wq).
 template <int MT>
@@ -431,7 +479,7 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
     const bool valid = e < E;
     const float *bias = layer_w(a, l)->router_bias;
     const float bv = (bias && valid) ? glb(bias)[e] : 0.0f;   // requested before the norm's polls
-    norm_to_lds<MT>(a, l, a->gains + (size_t)l * H, tgt);
+    layer_input<MT>(a, l, tgt);
     const uint16_t *u = ulds();
     float acc[MT];
 #pragma unroll
@@ -1023,7 +1071,7 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
             } while (!pl.done(a, ok));
             s = sc;
         }
-        if (act && l == 0) hp = h0_pair(a, m, c / 2);
+        if (act && l == 0 && !a->layer_mode) hp = h0_pair(a, m, c / 2);
         const uint16_t y = f2bf(s);
         float hv = bf2f(odd ? hp >> 16 : hp & 0xffffu);
         if (act && l + 1 < a->L) hv += bf2f(nz);
@@ -1032,7 +1080,7 @@ __device__ __forceinline__ void run_cmb(AP a, int l, int cb, uint32_t tgt) {
         const uint32_t yo = dppu<0xB1>(y), ho = dppu<0xB1>(hn);
         if (act && !odd) {
             if (a->y) *glb(reinterpret_cast<uint32_t *>(a->y + (size_t)l * a->y_ls + (size_t)m * H + c)) = pack2(y, (uint16_t)yo);
-            st64(hres(a, l + 1, m) + c / 2, tagged(pack2(hn, (uint16_t)ho), tgt));
+            if (!a->layer_mode) st64(hres(a, l + 1, m) + c / 2, tagged(pack2(hn, (uint16_t)ho), tgt));
         }
     }
 }
@@ -1060,7 +1108,7 @@ __device__ __forceinline__ void expert_phase(AP a0, int l, int w, int GU, uint32
     // the residual rows are polled with long sleeps in between: a unit workgroup needs u_l
     // only after the logits, which come a hop and a router GEMV after the rows, and every
     // unit workgroup polls meanwhile (64 measured faster than 1 at one and five tokens)
-    norm_to_lds<MT, 64>(a, l, a->gains + (size_t)l * a->H, tgt);
+    layer_input<MT, 64>(a, l, tgt);
     // the shared expert's units sit at fixed places at the head of the list
     const UnitList L0 = unit_list<BF>(a, a->Ds > 0 ? 1 : 0);
     UnitBuf A;
@@ -1274,6 +1322,16 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
     }
 }
 
+// Layer mode, the end of the call: every workgroup signals; workgroup 0 waits for all of
+// them (so that every workgroup has read the epoch) and advances the epoch.
+__device__ __forceinline__ void layer_end(AP a0, int w, int G, uint32_t tgt) {
+    const AP a = uniform(a0);
+    publish(flags(a) + a->f_lm + w, tgt);
+    if (w != 0) return;
+    wait_flags(a, flags(a) + a->f_lm, G, tgt);
+    if (ltid() == 0) st32(flags(a) + a->f_epoch, tgt);
+}
+
 // ------------------------------------------------------------------- kernel
 
 // Workgroups per compute unit: the register budget the kernel is compiled for, and the
@@ -1297,7 +1355,10 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
         // router workgroup: each layer's weights are requested as soon as the previous
         // layer's logits are out
         uint4 wq[kNC];
-        router_load(base, 0, w - GU, wq);
+        if (base->layer_mode)
+            router_load_hxe(base, w - GU, wq);
+        else
+            router_load(base, 0, w - GU, wq);
         for (int l = 0;; ++l) {
             AP a = base;
             asm volatile("" : "+s"(a));
@@ -1317,7 +1378,10 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
     }
     AP a = base;
     asm volatile("" : "+s"(a));
-    lm_phase<MT>(a, w, G, tgt);
+    if (a->layer_mode)
+        layer_end(a, w, G, tgt);
+    else
+        lm_phase<MT>(a, w, G, tgt);
 }
 
 // Router weights [H][E] -> [E][H] (once, at prepare time).
@@ -1411,18 +1475,70 @@ int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weig
     return hipDeviceSynchronize() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// After a wait has given up, hand-off words of that step (or of a workgroup that started
-// after the epoch moved on) may carry the next step's tag. The flag, the epoch and every
-// hand-off word are therefore cleared (the weight table and the re-laid-out router
-// weights are kept), so the next step starts from tag 1 with nothing current.
+// After a wait has given up, a workgroup that started after workgroup 0 advanced the
+// epoch may have written hand-off words with the next step's tag (epoch + 1). The epoch
+// is therefore advanced by two more, so that every word in the workspace is older than
+// the next step's tag, and the flag is cleared. No step may be in flight.
 int step_status(const StepWs &W, char *ws) {
     int err = 0;
     char *flag = ws + W.ctr + sizeof(int) * kCtrStride * kErrCtr;
     if (hipMemcpy(&err, flag, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ELAUNCH;
     if (!err) return MOE_OK;
-    if (hipMemset(ws + W.ctr, 0, W.total - W.ctr) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    uint32_t epoch = 0;
+    char *ep = ws + W.flags + sizeof(uint32_t) * (size_t)W.f_epoch;
+    if (hipMemcpy(&epoch, ep, sizeof epoch, hipMemcpyDeviceToHost) != hipSuccess) return MOE_ELAUNCH;
+    epoch += 2u;
+    const int zero = 0;
+    if (hipMemcpy(ep, &epoch, sizeof epoch, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(flag, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
         return MOE_ELAUNCH;
     return MOE_ETIMEOUT;
+}
+
+int launch_layer_step(const moe_layer_desc &ld, const moe_layer_weights &w, int M, const uint16_t *x, uint16_t *y,
+                      int32_t *topk_idx, float *topk_w, char *ws, void *stream) {
+    (void)hipGetLastError();
+    const moe_step_desc d = layer_step_desc(ld, M);
+    const StepWs W = step_ws(d, false);
+    StepArgs a{};
+    a.layer_mode = 1;
+    a.lw = w;
+    a.x = x;
+    a.y = y;
+    a.y_ls = (size_t)M * ld.hidden;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_w;
+    a.ws = ws;
+    a.o_ctr = W.ctr;
+    a.o_flags = W.flags;
+    a.o_logits = W.logits;
+    a.o_hres = W.hres;
+    a.o_hact = W.hact;
+    a.o_ypart = W.ypart;
+    a.o_lmbest = W.lmbest;
+    a.f_lm = W.f_lm;
+    a.f_epoch = W.f_epoch;
+    a.M = M;
+    a.Mx = W.Mx;
+    a.H = ld.hidden;
+    a.E = ld.num_experts;
+    a.K = ld.top_k;
+    a.D = ld.expert_width;
+    a.Ds = ld.shared_width;
+    a.L = 1;
+    a.V = 0;
+    a.Sx = W.Sx;
+    a.NR = W.NR;
+    a.ND = W.ND;
+    a.NSUBx = W.NSUBx;
+    a.Fmax = W.F;
+    a.nseg_r = W.nseg_r;
+    a.nseg_s = W.nseg_s;
+    a.NLU = 0;
+    a.spin_limit = kDefaultSpin;
+    const size_t lds = step_lds_bytes(d, M, &a.l_scr, &a.l_slot);
+    return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, false, stream)
+                                  : launch_m<false>(M, a, lds, W.NR, false, stream);
 }
 
 int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *gains,

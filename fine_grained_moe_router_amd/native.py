@@ -20,7 +20,7 @@ MOE_ETIMEOUT = -6
 MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
-EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "lm_head_argmax_workspace",
+EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
            "lm_head_argmax", "lm_head_argmax_noalloc", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
            "moe_hbm_read_probe", "moe_strerror")
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_layer.restype = I
         L.moe_decode_layer.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(LayerWeights), I,
                                        _P, _P, _P, _P, _P, S, _P]
+        L.moe_decode_layer_status.restype = I
+        L.moe_decode_layer_status.argtypes = [ctypes.POINTER(LayerDesc), _P]
         L.lm_head_argmax_workspace.restype = S
         L.lm_head_argmax_workspace.argtypes = [I, I, I]
         L.lm_head_argmax.restype = I
@@ -143,6 +145,11 @@ def moe_decode_layer(desc: LayerDesc, weights: LayerWeights, M: int, x, y, topk_
                                 _ptr(topk_idx), _ptr(topk_w), _ptr(workspace), int(workspace_bytes),
                                 _stream(stream))
     _check("moe_decode_layer", st)
+
+
+def moe_decode_layer_status(desc: LayerDesc, workspace) -> int:
+    """MOE_OK or MOE_ETIMEOUT (synchronous; clears the flag)."""
+    return lib().moe_decode_layer_status(ctypes.byref(desc), _ptr(workspace))
 
 
 def lm_head_argmax_workspace(max_M: int, H: int, V: int) -> int:

@@ -105,6 +105,16 @@ typedef struct moe_layer_weights {
 size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M);
 
 /*
+ * Synchronous: MOE_OK, or MOE_ETIMEOUT if a device-side wait of a moe_decode_layer call
+ * on this workspace gave up since the last call (its results are then invalid); the
+ * flag is cleared and the workspace made ready for the next call, as with
+ * moe_decode_step_status. Call after the stream has been synchronised, with no call in
+ * flight. Layers that take the separate per-layer kernels (see moe_decode_layer) have
+ * no device-side waits and always return MOE_OK.
+ */
+int moe_decode_layer_status(const moe_layer_desc *desc, void *workspace);
+
+/*
  * One MoE layer for M tokens (1 <= M <= 8; the batch-1 decode step is M = 1, the
  * speculative verify step with gamma drafts is M = gamma + 1). Page "LLM decoding":
  * "The exact architecture, and why it rules out 4-bit" (top 8 of 128 routed experts
@@ -127,7 +137,16 @@ size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M);
  *   y          bf16 [M][H], the MoE branch output (the residual is NOT added)
  *   topk_idx   int32 [M][K], S_m in ascending expert id, or NULL (4-byte aligned)
  *   topk_w     fp32 [M][K], the weights aligned with topk_idx, or NULL (4-byte aligned)
- *   workspace  at least moe_decode_layer_workspace(desc, M) bytes, 256-byte aligned
+ *   workspace  at least moe_decode_layer_workspace(desc, M) bytes, 256-byte aligned,
+ *              zero-filled before its first use and then left to the library (it keeps
+ *              a step counter and tagged hand-off words between calls)
+ * Layers with hidden <= 2816, expert_width <= 704 and a shared expert of at most eight
+ * 704-column segments (the Gemma-4-26B-A4B layer among them) run as one launch of the
+ * fused step's persistent kernel (see moe_decode_step: the same routing, units and
+ * combine, so y is bit-identical to that step's layer output for the same input, and
+ * the same co-residency requirement and bounded waits; see moe_decode_layer_status).
+ * Wider layers run as five dependent kernels (router partials, top-K and union,
+ * gate/up, down, combine) with no device-side waits.
  */
 int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int M,
                      const uint16_t *x, uint16_t *y, int32_t *topk_idx, float *topk_w,
@@ -299,9 +318,9 @@ int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
 /*
  * Synchronous: MOE_OK, or MOE_ETIMEOUT if a device-side wait of a step run on this
  * workspace since the last call gave up (its results, and those of later steps up to
- * this call, are then invalid). After a timeout it clears the flag and every hand-off
- * word of the workspace (the prepared weight table stays), so the next step runs
- * normally. Call after the stream has been synchronised, with no step in flight.
+ * this call, are then invalid). After a timeout it clears the flag and moves the
+ * workspace's step counter past every tag a hand-off word can hold, so the next step
+ * runs normally. Call after the stream has been synchronised, with no step in flight.
  */
 int moe_decode_step_status(const moe_step_desc *desc, void *workspace);
 

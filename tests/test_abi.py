@@ -115,6 +115,13 @@ def test_layer_pointer_validation():
                               1 << 30, None) == native.MOE_EINVAL
 
 
+def test_layer_status_validation():
+    L = native.lib()
+    assert L.moe_decode_layer_status(None, FAKE) == native.MOE_EINVAL
+    assert L.moe_decode_layer_status(ctypes.byref(GEMMA), None) == native.MOE_EWORKSPACE
+    assert L.moe_decode_layer_status(ctypes.byref(GEMMA), FAKE + 16) == native.MOE_EWORKSPACE
+
+
 def test_layer_workspace_validation():
     need = native.lib().moe_decode_layer_workspace(ctypes.byref(GEMMA), 5)
     assert call_layer(M=5, ws_bytes=need - 1) == native.MOE_EWORKSPACE

@@ -44,6 +44,7 @@ class Layer:
         wts = torch.zeros(M, sh.top_k, dtype=torch.float32, device=DEV)
         native.moe_decode_layer(self.desc, self.lw, M, x_bits_dev, y, idx, wts, ws, wsb)
         torch.cuda.synchronize()
+        assert native.moe_decode_layer_status(self.desc, ws) == native.MOE_OK
         return synth.bits16(y), idx.cpu().numpy(), wts.cpu().numpy()
 
 
@@ -95,6 +96,9 @@ VARIANTS = {
     "e128_k16": synth.TINY.with_(experts=128, top_k=16, hidden=768),
     "e48": synth.TINY.with_(experts=48, top_k=6),
     "wide_d": synth.TINY.with_(hidden=1024, width=320, shared_width=128),
+    # beyond the fused kernel's unit geometry (H > 2816, D > 704): the separate per-layer kernels
+    "beyond_fused_h": synth.TINY.with_(hidden=3072, experts=16, top_k=2, width=64, shared_width=64),
+    "beyond_fused_d": synth.TINY.with_(hidden=512, width=768, shared_width=128),
 }
 
 
@@ -193,6 +197,47 @@ def test_gemma_layer_shared_2112(gemma_layer):
     for M in (1, 8):
         x, r = unambiguous_layer_input(sh, M, L.host, 300 + M)
         check_layer(L, x, r, "shared2112 M=%d" % M)
+
+
+def _unit_rms_inputs(shape, M, seed):
+    """bf16 +-1 vectors: with unit gains and eps 0 their RMSNorm is themselves."""
+    g = torch.Generator().manual_seed(seed)
+    sign = torch.randint(0, 2, (M, shape.hidden), generator=g) * 2 - 1
+    return sign.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("where", ["tiny", "gemma"])
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_layer_entry_point_is_bit_identical_to_the_fused_step_layer(gemma_layer, where, M):
+    """moe_decode_layer and the fused step's layer share the routing, the units and the
+    combine: on the same normalised input they give the same expert ids and weights and
+    the same y bit for bit. The fused step normalises its input itself; with +-1 inputs,
+    unit gains and eps 0 that norm returns the input unchanged, so both see the same u."""
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+    if where == "gemma":
+        layer = gemma_layer
+    else:
+        layer = Layer(synth.TINY, seed=12)
+    sh = layer.shape.with_(layers=1)
+    x = _unit_rms_inputs(sh, M, 77 + M)
+    xd = x.to(DEV)
+    y_l, i_l, w_l = layer.run(xd, M)
+    gains = torch.ones(2, sh.hidden, dtype=torch.bfloat16, device=DEV)
+    Q, s = synth.lm_head(sh.with_(vocab=4096), DEV, seed=1)
+    fs = FusedDecodeStep(sh.with_(vocab=4096), [layer.dev], gains, Q, s, max_M=8, eps=0.0)
+    noise = torch.zeros(1, M, sh.hidden, dtype=torch.bfloat16, device=DEV)
+    d = torch.zeros(max(M - 1, 1), dtype=torch.int32, device=DEV)
+    fs.step(xd, noise, d if M > 1 else None, M)
+    torch.cuda.synchronize()
+    assert fs.status() == native.MOE_OK
+    assert (fs.topk_idx(M)[0].cpu().numpy() == i_l).all()
+    assert (fs.topk_w(M)[0].cpu().numpy().view(np.uint32) == w_l.view(np.uint32)).all()
+    assert (synth.bits16(fs.y(M)[0]) == y_l).all(), "%s M=%d: y differs between the two entry points" % (where, M)
+    # and both against the oracle, where its routing margins allow a one-to-one comparison
+    r = oracle.moe_layer(synth.bits16(x), layer.host, sh.top_k)
+    if (r["gap"] >= TAU).all():
+        assert (i_l == r["idx"]).all()
+        check_bf16_output(y_l, r["y"], None, "%s M=%d" % (where, M))
 
 
 # ----------------------------------------------------------------- lm_head
