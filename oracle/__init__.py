@@ -67,6 +67,15 @@ def lib():
             L.oracle_spec_accept.argtypes = [I, P, P, P]
             L.oracle_add_rmsnorm.restype = None
             L.oracle_add_rmsnorm.argtypes = [I, I, P, P, P, P, ctypes.c_double, P, P]
+            L.oracle_philox4x32_10.restype = None
+            L.oracle_philox4x32_10.argtypes = [P, P, P]
+            L.oracle_sample_uniform.restype = ctypes.c_double
+            L.oracle_sample_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint64, I, I]
+            L.oracle_lm_head_logits.restype = None
+            L.oracle_lm_head_logits.argtypes = [I, I, I, P, P, P, P]
+            L.oracle_spec_sample.restype = I
+            L.oracle_spec_sample.argtypes = [I, I, P, ctypes.c_double, P, P, P, ctypes.c_uint64,
+                                             ctypes.c_uint64, P, P, P]
             L.oracle_num_threads.restype = I
             L.oracle_num_threads.argtypes = []
             _lib = L
@@ -189,6 +198,49 @@ def spec_accept(draft, target):
     out = np.empty(gamma + 1, np.int32)
     n = lib().oracle_spec_accept(gamma, _p(draft), _p(target), _p(out))
     return n, out
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 of a 4-word counter under a 2-word key -> 4 uint32 words."""
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def sample_uniform(seed: int, step: int, row: int, v: int) -> float:
+    return lib().oracle_sample_uniform(int(seed), int(step), int(row), int(v))
+
+
+def lm_head_logits(x, Q, s):
+    """x uint16 [M][H], Q uint8 [V][H], s f32 [V] -> fp64 logits [M][V]."""
+    x = _c(x, np.uint16)
+    Q = _c(Q, np.uint8)
+    s = _c(s, np.float32)
+    M, H = x.shape
+    V = Q.shape[0]
+    out = np.empty((M, V), np.float64)
+    lib().oracle_lm_head_logits(M, H, V, _p(x), _p(Q), _p(s), _p(out))
+    return out
+
+
+def spec_sample(logits, T, draft, q, u_acc, seed, step):
+    """Stochastic speculative acceptance over target logits [M][V] (fp64) at temperature T:
+    draft int32 [M-1], q f32 [M-1][V] (the drafter's distributions), u_acc f32 [M-1].
+    Returns (n, out int32 [M], acc_margin f64 [M-1], samp_margin)."""
+    logits = _c(logits, np.float64)
+    M, V = logits.shape
+    g = M - 1
+    draft = _c(draft, np.int32) if g > 0 else np.zeros(1, np.int32)
+    q = _c(q, np.float32) if g > 0 else np.zeros((1, V), np.float32)
+    u = _c(u_acc, np.float32) if g > 0 else np.zeros(1, np.float32)
+    out = np.empty(M, np.int32)
+    am = np.empty(max(g, 1), np.float64)
+    sm = np.empty(1, np.float64)
+    n = lib().oracle_spec_sample(M, V, _p(logits), float(T), _p(draft), _p(q), _p(u), int(seed), int(step),
+                                 _p(out), _p(am), _p(sm))
+    return n, out, am[:g], float(sm[0])
 
 
 def add_rmsnorm(h, a0, a1, g, eps=1e-6):

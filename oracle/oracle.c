@@ -374,6 +374,155 @@ int oracle_spec_accept(int gamma, const int32_t *draft, const int32_t *target, i
     return n;
 }
 
+/* --------------------------------------------- stochastic speculative acceptance */
+
+/*
+ * Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3" (SC 2011): ten rounds of two 32x32->64
+ * multiplications on a 4-word counter, with a 2-word key bumped by the Weyl constants
+ * between rounds. out = Philox(ctr, key).
+ */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    const uint64_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    const uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+    uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = M0 * (uint64_t)c0, p1 = M1 * (uint64_t)c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0, n1 = lo1, n2 = hi0 ^ c3 ^ k1, n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+        k0 += W0;
+        k1 += W1;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The uniform draw for vocabulary entry v of target row `row` in decode step `step`
+ * under `seed`: Philox4x32-10 with key (seed low, seed high) on the counter
+ * (v / 4, row, step low, step high), word v % 4, mapped to (x + 1/2) / 2^32, so in (0, 1). */
+double oracle_sample_uniform(uint64_t seed, uint64_t step, int row, int v)
+{
+    const uint32_t ctr[4] = {(uint32_t)v >> 2, (uint32_t)row, (uint32_t)step, (uint32_t)(step >> 32)};
+    const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t out[4];
+    oracle_philox4x32_10(ctr, key, out);
+    return ((double)out[v & 3] + 0.5) / 4294967296.0;
+}
+
+/* Full logits of the tied lm_head: out[m][v] = s[v] * sum_c Q[v][c] x[m][c] (fp64). */
+void oracle_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *Q, const float *s,
+                           double *out)
+{
+    fp8_tab_init();
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xm = x + (size_t)m * H;
+        int v;
+#pragma omp parallel for schedule(static)
+        for (v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += fp8(Q[(size_t)v * H + c]) * oracle_bf16(xm[c]);
+            out[(size_t)m * V + v] = (double)s[v] * acc;
+        }
+    }
+}
+
+/*
+ * Stochastic speculative acceptance ([LLMD] "What we learned, and where this goes": a
+ * drafted token is kept only if it passes the exact distribution the target would have
+ * sampled from, and a rejected one falls back to a real model step, so the output is
+ * distributed as ordinary decoding; the temperature-0.7 column of "The ladder, every
+ * rung"). The page does not spell the procedure out; the standard speculative sampling
+ * rule is taken:
+ *   p_i = softmax(logits[i] / T) for target rows i = 0..gamma (row i: the token after
+ *         the prefix and d_1..d_i); q_i = q + (i - 1) V, the drafter's distribution that
+ *         proposed d_i (i = 1..gamma)
+ *   d_i is accepted iff u_i * q_i(d_i) < p_{i-1}(d_i) (probability min(1, p/q));
+ *         ids outside [0, V) are rejected; n = the number of leading accepted drafts
+ *   the last token is drawn from r = max(0, p_n - q_{n+1}) if n < gamma (the residual),
+ *         else from r = p_gamma (the bonus token), by the Gumbel-max rule:
+ *         t = argmax over {v : r_v > 0} of log r_v - log(-log U_v), U_v =
+ *         oracle_sample_uniform(seed, step, n, v); equal values: lower v. (If r is zero
+ *         everywhere, p_n is used.)
+ *   out = d_1 .. d_n, t, then -1; returns n.
+ * Margins of the decisions (for parity against a float32 implementation), fp64:
+ *   acc_margin[i-1] = |log(u_i q_i(d_i)) - log p_{i-1}(d_i)| for the decided drafts
+ *   (INFINITY where it was not reached or the id is out of range);
+ *   *samp_margin = best minus second-best perturbed value, less a bound on how far a
+ *   float32 evaluation can move each of the two (cancellation in p - q:
+ *   2^-20 (p_v + q_v) / r_v + 1e-5 per value).
+ */
+int oracle_spec_sample(int M, int V, const double *logits, double T, const int32_t *draft,
+                       const float *q, const float *u_acc, uint64_t seed, uint64_t step,
+                       int32_t *out, double *acc_margin, double *samp_margin)
+{
+    const int gamma = M - 1;
+    double *logz = malloc(sizeof(double) * (size_t)M);
+    for (int i = 0; i < M; ++i) {
+        const double *l = logits + (size_t)i * V;
+        double mx = -INFINITY;
+        for (int v = 0; v < V; ++v)
+            if (l[v] / T > mx) mx = l[v] / T;
+        double z = 0.0;
+        for (int v = 0; v < V; ++v)
+            z += exp(l[v] / T - mx);
+        logz[i] = mx + log(z);
+    }
+    for (int i = 0; i < gamma; ++i)
+        acc_margin[i] = INFINITY;
+    int n = 0;
+    while (n < gamma) {
+        const int d = draft[n];
+        if (d < 0 || d >= V)
+            break;
+        const double lp = logits[(size_t)n * V + d] / T - logz[n];
+        const double qd = (double)q[(size_t)n * V + d];
+        const double lq = log((double)u_acc[n] * qd);
+        acc_margin[n] = fabs(lq - lp);
+        if (!(lq < lp))
+            break;
+        ++n;
+    }
+    const double *l = logits + (size_t)n * V;
+    const float *qr = n < gamma ? q + (size_t)n * V : NULL;
+    int any = 0;
+    if (qr)
+        for (int v = 0; v < V && !any; ++v)
+            any = exp(l[v] / T - logz[n]) > (double)qr[v];
+    if (!any)
+        qr = NULL;
+    double best = -INFINITY, second = -INFINITY, best_err = 0.0, second_err = 0.0;
+    int tb = -1;
+    for (int v = 0; v < V; ++v) {
+        const double p = exp(l[v] / T - logz[n]);
+        const double qv = qr ? (double)qr[v] : 0.0;
+        const double r = p - qv;
+        if (!(r > 0.0))
+            continue;
+        const double g = -log(-log(oracle_sample_uniform(seed, step, n, v)));
+        const double val = log(r) + g;
+        const double err = ldexp(p + qv, -20) / r + 1e-5;
+        if (val > best) {
+            second = best;
+            second_err = best_err;
+            best = val;
+            best_err = err;
+            tb = v;
+        } else if (val > second) {
+            second = val;
+            second_err = err;
+        }
+    }
+    *samp_margin = second == -INFINITY ? INFINITY : (best - second) - best_err - second_err;
+    for (int i = 0; i < M; ++i)
+        out[i] = i < n ? draft[i] : (i == n ? tb : -1);
+    free(logz);
+    return n;
+}
+
 /* ----------------------------------------------------------- residual norm */
 
 /*
