@@ -148,6 +148,38 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     return launch_lm_head(M, H, V, x, w, w_s, token, max_logit, (char *)workspace, stream);
 }
 
+size_t lm_head_spec_sample_workspace(int max_M, int H, int V) {
+    if (max_M < 1 || max_M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||
+        V > kSampleMaxVocab)
+        return 0;
+    return sample_ws(max_M, V).total;
+}
+
+int lm_head_spec_sample(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
+                        float temperature, const int32_t *draft, const float *q, const float *u_accept,
+                        uint64_t seed, uint64_t step, int32_t *accepted_len, int32_t *out_tokens,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||
+        V > kSampleMaxVocab || !(temperature > 0.0f) || !(temperature < 1e30f))
+        return MOE_EINVAL;
+    CHECK(need(x));
+    CHECK(need(w));
+    CHECK(need(w_s));
+    if (M > 1) {
+        CHECK(need(q));
+        if (!draft || !u_accept) return MOE_EINVAL;
+    }
+    if (!accepted_len || !out_tokens) return MOE_EINVAL;
+    if (((uintptr_t)draft | (uintptr_t)u_accept | (uintptr_t)accepted_len | (uintptr_t)out_tokens) & 3u)
+        return MOE_EALIGN;
+    const SampleWs L = sample_ws(M, V);
+    if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
+    const float inv_t = 1.0f / temperature;
+    CHECK(launch_lm_head_logits(M, H, V, x, w, w_s, inv_t, L, (char *)workspace, stream));
+    return launch_spec_sample(M, V, inv_t, draft, q, u_accept, seed, step, accepted_len, out_tokens, L,
+                              (char *)workspace, stream);
+}
+
 int lm_head_argmax_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
                            int32_t *token, float *max_logit, void *stream) {
     if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||

@@ -67,6 +67,33 @@ inline size_t lm_ws_bytes(int M, int V) {
            align256((size_t)lm_grid(V) * M * sizeof(int32_t));
 }
 
+// Workspace of lm_head_spec_sample for M tokens over V rows: the lm_head's per-workgroup
+// bests (unused by the sampler, kept by the shared kernel), every logit, the per-workgroup
+// softmax states, the accepted count and the per-row log normalisers, the sampling
+// workgroups' argmax keys.
+constexpr int kSampleTok = 1024;   // vocabulary entries per sampling workgroup (4 per thread)
+struct SampleWs {
+    size_t best_v, best_i, logits, smax, ssum, acc, keys, total;
+    int nwg, nsg;
+};
+inline SampleWs sample_ws(int M, int V) {
+    SampleWs W{};
+    W.nwg = lm_grid(V);
+    W.nsg = (V + kSampleTok - 1) / kSampleTok;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+    W.best_v = take(4 * (size_t)W.nwg * M);
+    W.best_i = take(4 * (size_t)W.nwg * M);
+    W.logits = take(4 * (size_t)M * V);
+    W.smax = take(4 * (size_t)W.nwg * M);
+    W.ssum = take(4 * (size_t)W.nwg * M);
+    W.acc = take(4 * (size_t)(1 + kMaxM));       // int n, then float logZ[M]
+    W.keys = take(8 * 2 * (size_t)W.nsg);        // per sampling workgroup: residual key, target key
+    W.total = o;
+    return W;
+}
+constexpr int kSampleMaxVocab = 1 << 24;
+
 // Static scratch of lm_head_argmax_noalloc: the workspace of the largest call (M = 8,
 // the full lm_head grid), 128 KiB.
 constexpr size_t kLmNoallocScratch = 2 * (size_t)kLmMaxWG * kMaxM * 4;
@@ -172,6 +199,11 @@ int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
                      char *ws, const LayerWs &L, void *stream);
 int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                    int32_t *token, float *max_logit, char *ws, void *stream);
+int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s, float inv_t,
+                          const SampleWs &L, char *ws, void *stream);
+int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const float *q, const float *u_acc,
+                       uint64_t seed, uint64_t step, int32_t *accepted_len, int32_t *out_tokens,
+                       const SampleWs &L, char *ws, void *stream);
 int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                            int32_t *token, float *max_logit, void *stream);
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,

@@ -437,6 +437,12 @@ struct LmArgs {
     int32_t *token;
     float *max_logit;
     int M, H, V, nwg;
+    // with logits (the sampling path): every logit, and per workgroup and token the
+    // running maximum of logit / T and the sum of exp(logit / T - maximum)
+    float *logits;      // [M][V]
+    float *smax;        // [grid][M]
+    float *ssum;        // [grid][M]
+    float inv_t;        // 1 / temperature
 };
 
 constexpr int kLmRowsPerLane = 4;
@@ -450,6 +456,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // blk*64 + 16 w + 4 g + r (r = 0..3) and reads the same 16-byte column chunk of all
 // four, so each bf16 activation chunk read from LDS serves 4 rows. Row sums go
 // through the 16-lane DPP reduction; each group keeps its running best per token.
+template <bool LOGITS>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     extern __shared__ uint4 xs[];  // [M][H/8]; reused at the end for the per-group bests
     const int H = a.H, hv = H / 8, M = a.M;
@@ -460,10 +467,13 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     const int g = lane >> 4, li = lane & 15;
     float bv[kMaxM];
     int bi[kMaxM];
+    float smx[kMaxM], ssm[kMaxM];   // online softmax state (LOGITS only)
 #pragma unroll
     for (int t = 0; t < kMaxM; ++t) {
         bv[t] = -INFINITY;
         bi[t] = 0x7fffffff;
+        smx[t] = -INFINITY;
+        ssm[t] = 0.0f;
     }
     const int NC = H / 256;
     const int nblk = a.V / kLmRowsPerWG;
@@ -513,6 +523,16 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
                         bv[t] = lg;
                         bi[t] = v;
                     }
+                    if constexpr (LOGITS) {
+                        if (li == 0) a.logits[(size_t)t * a.V + v] = lg;
+                        const float z = lg * a.inv_t;
+                        if (z > smx[t]) {
+                            ssm[t] = ssm[t] * __expf(smx[t] - z) + 1.0f;
+                            smx[t] = z;
+                        } else {
+                            ssm[t] += __expf(z - smx[t]);
+                        }
+                    }
                 }
             }
         }
@@ -542,6 +562,32 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
             }
         a.best_v[blockIdx.x * M + t] = v;
         a.best_i[blockIdx.x * M + t] = i;
+    }
+    if constexpr (LOGITS) {
+        // the 16 groups' softmax states per token: maximum, then the rescaled sum
+        __syncthreads();
+        float *gm = reinterpret_cast<float *>(xs);
+        float *gs = gm + 16 * M;
+        if (li == 0) {
+#pragma unroll
+            for (int t = 0; t < kMaxM; ++t) {
+                if (t < M) {
+                    gm[(wave * 4 + g) * M + t] = smx[t];
+                    gs[(wave * 4 + g) * M + t] = ssm[t];
+                }
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < M) {
+            const int t = threadIdx.x;
+            float mx = gm[t];
+            for (int k = 1; k < 16; ++k) mx = fmaxf(mx, gm[k * M + t]);
+            float sm = 0.0f;
+            for (int k = 0; k < 16; ++k)
+                if (gm[k * M + t] > -INFINITY) sm += gs[k * M + t] * __expf(gm[k * M + t] - mx);
+            a.smax[blockIdx.x * M + t] = mx;
+            a.ssum[blockIdx.x * M + t] = sm;
+        }
     }
 }
 
@@ -705,8 +751,21 @@ int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     LmArgs a{x, w, s, reinterpret_cast<float *>(ws),
              reinterpret_cast<int32_t *>(ws + align256((size_t)nwg * M * sizeof(float))),
              token, max_logit, M, H, V, nwg};
-    hipLaunchKernelGGL(k_lmhead, dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
+    hipLaunchKernelGGL(k_lmhead<false>, dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, S(stream), a);
+    return launched();
+}
+
+int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s, float inv_t,
+                          const SampleWs &L, char *ws, void *stream) {
+    (void)hipGetLastError();
+    LmArgs a{x, w, s, reinterpret_cast<float *>(ws + L.best_v), reinterpret_cast<int32_t *>(ws + L.best_i),
+             nullptr, nullptr, M, H, V, L.nwg};
+    a.logits = reinterpret_cast<float *>(ws + L.logits);
+    a.smax = reinterpret_cast<float *>(ws + L.smax);
+    a.ssum = reinterpret_cast<float *>(ws + L.ssum);
+    a.inv_t = inv_t;
+    hipLaunchKernelGGL(k_lmhead<true>, dim3(L.nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     return launched();
 }
 

@@ -21,7 +21,8 @@ MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
-           "lm_head_argmax", "lm_head_argmax_noalloc", "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
+           "lm_head_argmax", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
+           "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
            "moe_hbm_read_probe", "moe_strerror")
 
@@ -74,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.lm_head_argmax_workspace.argtypes = [I, I, I]
         L.lm_head_argmax.restype = I
         L.lm_head_argmax.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P, S, _P]
+        L.lm_head_spec_sample_workspace.restype = S
+        L.lm_head_spec_sample_workspace.argtypes = [I, I, I]
+        L.lm_head_spec_sample.restype = I
+        L.lm_head_spec_sample.argtypes = [I, I, I, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_uint64,
+                                          ctypes.c_uint64, _P, _P, _P, S, _P]
         L.lm_head_argmax_noalloc.restype = I
         L.lm_head_argmax_noalloc.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P]
         L.spec_accept.restype = I
@@ -160,6 +166,18 @@ def lm_head_argmax(M, H, V, x, w, w_s, token, max_logit, workspace, workspace_by
     st = lib().lm_head_argmax(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), _ptr(token),
                               _ptr(max_logit), _ptr(workspace), int(workspace_bytes), _stream(stream))
     _check("lm_head_argmax", st)
+
+
+def lm_head_spec_sample_workspace(max_M: int, H: int, V: int) -> int:
+    return lib().lm_head_spec_sample_workspace(int(max_M), int(H), int(V))
+
+
+def lm_head_spec_sample(M, H, V, x, w, w_s, temperature, draft, q, u_accept, seed, step, accepted_len, out_tokens,
+                        workspace, workspace_bytes, stream=None):
+    st = lib().lm_head_spec_sample(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), float(temperature),
+                                   _ptr(draft), _ptr(q), _ptr(u_accept), int(seed), int(step), _ptr(accepted_len),
+                                   _ptr(out_tokens), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("lm_head_spec_sample", st)
 
 
 def lm_head_argmax_noalloc(M, H, V, x, w, w_s, token, max_logit, stream=None):

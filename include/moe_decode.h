@@ -169,6 +169,42 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
                    int32_t *token, float *max_logit, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* Bytes of workspace lm_head_spec_sample needs (0 for invalid sizes). */
+size_t lm_head_spec_sample_workspace(int max_M, int H, int V);
+
+/*
+ * The verify step's lm_head with stochastic speculative acceptance at temperature T > 0
+ * (page "LLM decoding", "What we learned, and where this goes": a drafted token is kept
+ * only if it passes the exact distribution the target would have sampled from, so the
+ * output is distributed as ordinary decoding; the temperature-0.7 column of the table
+ * "The ladder, every rung"). The page does not spell out the procedure; the standard
+ * speculative sampling rule is taken:
+ *   logit[i][v] = w_s[v] * sum_c decode(w[v][c]) * x[i][c]     (as lm_head_argmax)
+ *   p_i         = softmax(logit[i] / T), rows i = 0..gamma (gamma = M - 1)
+ *   d_i (i = 1..gamma) is accepted iff u_accept[i-1] * q[i-1][d_i] < p_{i-1}(d_i),
+ *                 i.e. with probability min(1, p/q); ids outside [0, V) are rejected;
+ *                 n = the number of leading accepted drafts
+ *   the last token t is drawn from r = max(0, p_n - q[n]) when n < gamma (the residual;
+ *                 p_n itself if r is zero everywhere), else from r = p_gamma (the bonus),
+ *                 by the Gumbel-max rule t = argmax_{v: r_v > 0} log r_v - log(-log U_v)
+ *                 (equal values: lower v), with U_v = (W + 1/2) / 2^32 where W is word
+ *                 v % 4 of Philox4x32-10 (Salmon et al., SC 2011) on the counter
+ *                 (v / 4, n, step low, step high) under the key (seed low, seed high)
+ *   accepted_len = n; out_tokens = d_1 .. d_n, t, then -1.
+ * Given the same uniforms the result is a deterministic function of the inputs.
+ *   M 1..8; H a multiple of 256 up to 4096; V a multiple of 64, 64..2^24; temperature > 0
+ *   x bf16 [M][H]; w FP8 codes [V][H]; w_s fp32 [V]
+ *   draft int32 [M-1]; q fp32 [M-1][V] (q[i-1] is the drafter's distribution that proposed
+ *   d_i); u_accept fp32 [M-1] in [0, 1); draft, q and u_accept may be NULL when M == 1
+ *   accepted_len int32 [1]; out_tokens int32 [M]
+ *   workspace >= lm_head_spec_sample_workspace(M, H, V) bytes, 256-byte aligned
+ */
+int lm_head_spec_sample(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *w_s,
+                        float temperature, const int32_t *draft, const float *q,
+                        const float *u_accept, uint64_t seed, uint64_t step,
+                        int32_t *accepted_len, int32_t *out_tokens, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /*
  * lm_head_argmax for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same kernels and

@@ -166,6 +166,26 @@ def test_lm_head_noalloc_validation():
     assert L.lm_head_argmax_noalloc(1, 2816, 4096, FAKE, FAKE, FAKE, FAKE, FAKE + 4, None) == native.MOE_EALIGN
 
 
+def test_spec_sample_validation():
+    L = native.lib()
+    assert native.lm_head_spec_sample_workspace(5, 2816, 262144) > 0
+    assert native.lm_head_spec_sample_workspace(5, 2816, (1 << 24) + 64) == 0
+    assert native.lm_head_spec_sample_workspace(9, 2816, 4096) == 0
+    ws = native.lm_head_spec_sample_workspace(5, 2816, 4096)
+    args = lambda **o: [o.get(k, v) for k, v in (
+        ("M", 5), ("H", 2816), ("V", 4096), ("x", FAKE), ("w", FAKE), ("s", FAKE), ("T", 0.7), ("d", FAKE),
+        ("q", FAKE), ("u", FAKE), ("seed", 1), ("step", 2), ("n", FAKE), ("out", FAKE), ("ws", FAKE),
+        ("wsb", ws), ("stream", None))]
+    assert L.lm_head_spec_sample(*args(T=0.0)) == native.MOE_EINVAL
+    assert L.lm_head_spec_sample(*args(T=-1.0)) == native.MOE_EINVAL
+    assert L.lm_head_spec_sample(*args(M=0)) == native.MOE_EINVAL
+    assert L.lm_head_spec_sample(*args(d=None)) == native.MOE_EINVAL
+    assert L.lm_head_spec_sample(*args(q=None)) == native.MOE_EINVAL
+    assert L.lm_head_spec_sample(*args(q=FAKE + 4)) == native.MOE_EALIGN
+    assert L.lm_head_spec_sample(*args(out=FAKE + 2)) == native.MOE_EALIGN
+    assert L.lm_head_spec_sample(*args(wsb=ws - 1)) == native.MOE_EWORKSPACE
+
+
 def test_spec_accept_validation():
     L = native.lib()
     assert L.spec_accept(-1, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL
