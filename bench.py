@@ -11,11 +11,19 @@ acceptance of M-1 draft tokens. M=1 is plain decoding, M=5 the verify step of
 speculative decoding with 4 drafts.
 
 Weights (23.8 GB of FP8 experts and lm_head, every expert at its own address) and
-all step inputs are seeded synthetic data resident in HBM before timing. Each
-step is captured once in a HIP graph; W warm-up steps are replayed, then exactly K
-steps are timed with HIP events on the replay stream, bracketed by
-device synchronisations. Bytes per step are the algorithmic bytes of the routing
-the GPU actually took (each selected expert counted once per step).
+all step inputs are seeded synthetic data resident in HBM before timing. The default
+path launches the single-kernel step (moe_decode_step) directly, one launch per step
+(--path layers captures the per-layer entry points of each step in a HIP graph). W
+warm-up steps run, then exactly K steps are timed with HIP events on the launch
+stream, bracketed by device synchronisations, as five contiguous blocks: `value` is K
+over the whole timed span, and the median of the five blocks' rates is reported
+beside it. Bytes per step are the algorithmic bytes of the routing the GPU actually
+took (each selected expert counted once per step).
+
+Other configurations, each its own JSON line: --layer (one Gemma-shaped layer at M=1
+and its M=5 verify step through the per-layer entry points), --zipf (the stack at M=8
+with Zipf-skewed routing, FP8 and bf16 experts), --sample (the M=5 verify step's
+lm_head with stochastic acceptance at temperature 0.7).
 
 Prints ONE JSON line.
 """
@@ -95,6 +103,9 @@ def parse():
     ap.add_argument("--zipf", action="store_true",
                     help="the skewed-routing configuration instead: the stack at M=8 with a Zipf(1.1) "
                          "router bias, once with FP8 and once with bf16 expert weights (its own JSON line)")
+    ap.add_argument("--sample", action="store_true",
+                    help="the verify step's lm_head with stochastic acceptance instead (lm_head_spec_sample, "
+                         "M=5, temperature 0.7, 2 rotated lm_head copies; its own JSON line)")
     ap.add_argument("--path", choices=("fused", "layers"), default="fused",
                     help="fused: one moe_decode_step launch per step; layers: per-layer entry points "
                          "captured in a HIP graph per step")
@@ -124,6 +135,8 @@ def main():
         return
     if args.zipf:
         return zipf_main(args)
+    if args.sample:
+        return sample_main(args)
     if args.layer:
         return layer_main(args)
     import synth
@@ -291,15 +304,20 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
         for i in range(W):
             launch(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # exactly K steps, timed as five contiguous blocks (events between blocks do not
+        # stall the stream): the whole span gives the rate, the blocks its spread
+        bounds = [W + (K * b) // 5 for b in range(6)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         w0 = time.perf_counter()
-        e0.record(stream)
-        for i in range(W, n):
-            launch(i)
-        e1.record(stream)
+        evs[0].record(stream)
+        for b in range(5):
+            for i in range(bounds[b], bounds[b + 1]):
+                launch(i)
+            evs[b + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        ms_total = e0.elapsed_time(e1)
+        ms_total = evs[0].elapsed_time(evs[5])
+        block_ms = [evs[b].elapsed_time(evs[b + 1]) / max(1, bounds[b + 1] - bounds[b]) for b in range(5)]
 
         # per-step latency distribution and the routing each step took
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
@@ -325,6 +343,7 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
     bps = float(np.mean(bytes_steps))
     r = {
         "steps_per_s": K / (ms_total / 1e3), "ms_per_step": ms, "wall_s": wall,
+        "median_block_ms_per_step": float(np.median(block_ms)), "block_ms_per_step": [round(b, 4) for b in block_ms],
         "p50_ms": float(np.percentile(per_step, 50)), "p99_ms": float(np.percentile(per_step, 99)),
         "bytes_per_step": bps, "hbm_gbs": bps / (ms / 1e3) / 1e9,
         "hbm_frac": bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -510,6 +529,89 @@ def zipf_main(args):
     print(json.dumps(line), flush=True)
 
 
+def sample_main(args):
+    """The verify step's lm_head with stochastic speculative acceptance (lm_head_spec_sample):
+    M=5 rows of the Gemma-shaped tied lm_head (262,144 x 2816 FP8) at temperature 0.7, four
+    drafts with synthetic drafter distributions q (softmax of seeded N(0,1) logits at the same
+    temperature), seeded accept uniforms. The lm_head rotates over 2 copies so that no step
+    finds it in the Infinity Cache. Steps are captured into HIP graphs of 100 and replayed."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import budget, native
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    sh = synth.GEMMA4_26B_A4B
+    M, T, K, W = 5, 0.7, args.steps, args.warmup
+    H, V, g = sh.hidden, sh.vocab, M - 1
+    lms = [synth.lm_head(sh, dev, seed=args.seed + c) for c in range(2)]
+    n = K + W
+    xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="sample_x") for i in range(n)]
+    gen = torch.Generator(device=dev).manual_seed(synth.seed_of(args.seed, "sample_q"))
+    qs = [torch.softmax(torch.randn(g, V, generator=gen, device=dev) / T, dim=1).contiguous() for _ in range(4)]
+    ds = [torch.multinomial(q, 1, generator=gen).view(-1).to(torch.int32).contiguous() for q in qs]
+    us = [torch.rand(g, generator=gen, device=dev) for _ in range(n)]
+    wsb = native.lm_head_spec_sample_workspace(M, H, V)
+    ws = native.workspace(wsb)
+    acc = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = torch.zeros(M, dtype=torch.int32, device=dev)
+    accs = torch.zeros(n, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def launch(i):
+        Q, s = lms[i % 2]
+        native.lm_head_spec_sample(M, H, V, xs[i], Q, s, T, ds[i % 4], qs[i % 4], us[i], 12345, i, accs[i:i + 1],
+                                   out, ws, wsb, stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            launch(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for c0 in range(W, n, 100):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for i in range(c0, min(n, c0 + 100)):
+                    launch(i)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    mean_acc = float(accs[W:].float().mean())
+    # algorithmic bytes: the lm_head, the M input rows, the drafter row the draw reads (V fp32)
+    # and the drafted ids' probabilities and uniforms; the logits' round trip through memory
+    # (M x V fp32 written, one row read back) is this implementation's, not the method's
+    bps = budget.lm_head_bytes(V, H) + M * H * 2 + V * 4 + g * 12 + 4 * M
+    gbs = bps / (ms / 1e3) / 1e9
+    log("sample M=5: %.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s), mean accepted %.2f" % (
+        ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS, mean_acc))
+    line = {
+        "metric": "verify-step lm_head + stochastic speculative acceptance (temperature 0.7), steps/s and HBM GB/s",
+        "value": round(1e3 / ms, 2), "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 weights x bf16 activations, fp32 accumulate and softmax",
+        "data": "synthetic (seeded FP8 lm_head, N(0,1) inputs, drafter distributions softmax(N(0,1)/T)), "
+                "2 lm_head copies rotated",
+        "config": {"workload": "tied 262144x2816 FP8 lm_head over M=5 verify rows + temperature-0.7 softmax + "
+                               "accept min(1,p/q) + residual/bonus draw (Gumbel-max, Philox4x32-10)",
+                   "M": M, "hidden": H, "vocab": V, "temperature": T},
+        "bytes_per_step": int(bps), "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mean_accepted": round(mean_acc, 3),
+        "roofline": {"bound": "hbm", "kernel": "lm_head_spec_sample (k_lmhead<true> + 3 sampling kernels, M=5)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": int(bps),
+                     "avg_launch_us": round(ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(args, sh, layers, gains, Q, s, M):
     """The oracle (plain fp64 C, OpenMP over output rows) on a bounded sample of the
     same workload: the first cpu_layers layers for cpu_steps step inputs, plus the
@@ -538,12 +640,44 @@ def cpu_baseline(args, sh, layers, gains, Q, s, M):
         oracle.lm_head_argmax(u, Qh, sh_)
         t_lm += time.perf_counter() - t
     per_step = (t_layers / args.cpu_layers * sh.layers + t_lm) / args.cpu_steps
-    log("oracle: %.2f s per full step (sample %.1f s)" % (per_step, t_layers + t_lm))
-    return {"value": round(1.0 / per_step, 5), "unit": "steps/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    threads = oracle.num_threads()
+    log("oracle: %.2f s per full step on %d threads (sample %.1f s)" % (per_step, threads, t_layers + t_lm))
+    # the same oracle on one thread, over a smaller sample (2 layers + the lm_head, 2 steps)
+    oracle.set_num_threads(1)
+    t1_layers = t1_lm = 0.0
+    for i in range(2):
+        x = synth.bits16(synth.hidden_inputs(sh, M, i, tag="bench_x"))
+        noise = synth.bits16(synth.stack_noise(sh, M, i))
+        t = time.perf_counter()
+        h, y = x, None
+        for l in range(2):
+            h, u = oracle.add_rmsnorm(h, noise[l], y, gh[l])
+            y = oracle.moe_layer(u, host[l], sh.top_k)["y_bf16"]
+        t1_layers += time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.lm_head_argmax(u, Qh, sh_)
+        t1_lm += time.perf_counter() - t
+    oracle.set_num_threads(threads)
+    per_step_1 = (t1_layers / 2 * sh.layers + t1_lm) / 2
+    log("oracle: %.2f s per full step on 1 thread" % per_step_1)
+    return {"value": round(1.0 / per_step, 5), "unit": "steps/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "single_thread": {"value": round(1.0 / per_step_1, 6), "unit": "steps/s", "cores": 1,
+                              "sample": "M=%d, 2 step inputs x (layers 0-1 + the full lm_head), scaled to 30 "
+                                        "layers; %.1f s of CPU time" % (M, t1_layers + t1_lm)},
             "sample": "M=%d, %d step inputs x (layers 0-%d of the 30-layer stack + the full 262144-row "
                       "lm_head), scaled to 30 layers; %.1f s of CPU time" % (
                           M, args.cpu_steps, args.cpu_layers - 1, t_layers + t_lm)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -175,7 +175,7 @@ int lm_head_spec_sample(int M, int H, int V, const uint16_t *x, const uint8_t *w
     const SampleWs L = sample_ws(M, V);
     if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
     const float inv_t = 1.0f / temperature;
-    CHECK(launch_lm_head_logits(M, H, V, x, w, w_s, inv_t, L, (char *)workspace, stream));
+    CHECK(launch_lm_head_logits(M, H, V, x, w, w_s, L, (char *)workspace, stream));
     return launch_spec_sample(M, V, inv_t, draft, q, u_accept, seed, step, accepted_len, out_tokens, L,
                               (char *)workspace, stream);
 }

@@ -68,12 +68,13 @@ inline size_t lm_ws_bytes(int M, int V) {
 }
 
 // Workspace of lm_head_spec_sample for M tokens over V rows: the lm_head's per-workgroup
-// bests (unused by the sampler, kept by the shared kernel), every logit, the per-workgroup
-// softmax states, the accepted count and the per-row log normalisers, the sampling
-// workgroups' argmax keys.
+// bests (unused by the sampler, kept by the shared kernel), every logit, the per-chunk
+// softmax states (maximum of logit / T and the sum of exp(logit / T - maximum) per
+// 1024-entry chunk and row), the accepted count and the per-row log normalisers, the
+// sampling workgroups' argmax keys.
 constexpr int kSampleTok = 1024;   // vocabulary entries per sampling workgroup (4 per thread)
 struct SampleWs {
-    size_t best_v, best_i, logits, smax, ssum, acc, keys, total;
+    size_t best_v, best_i, logits, stats, acc, keys, total;
     int nwg, nsg;
 };
 inline SampleWs sample_ws(int M, int V) {
@@ -85,8 +86,7 @@ inline SampleWs sample_ws(int M, int V) {
     W.best_v = take(4 * (size_t)W.nwg * M);
     W.best_i = take(4 * (size_t)W.nwg * M);
     W.logits = take(4 * (size_t)M * V);
-    W.smax = take(4 * (size_t)W.nwg * M);
-    W.ssum = take(4 * (size_t)W.nwg * M);
+    W.stats = take(8 * (size_t)W.nsg * M);       // float2 [nsg][M]
     W.acc = take(4 * (size_t)(1 + kMaxM));       // int n, then float logZ[M]
     W.keys = take(8 * 2 * (size_t)W.nsg);        // per sampling workgroup: residual key, target key
     W.total = o;
@@ -199,7 +199,7 @@ int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
                      char *ws, const LayerWs &L, void *stream);
 int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                    int32_t *token, float *max_logit, char *ws, void *stream);
-int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s, float inv_t,
+int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                           const SampleWs &L, char *ws, void *stream);
 int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const float *q, const float *u_acc,
                        uint64_t seed, uint64_t step, int32_t *accepted_len, int32_t *out_tokens,

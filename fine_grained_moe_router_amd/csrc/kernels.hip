@@ -437,12 +437,7 @@ struct LmArgs {
     int32_t *token;
     float *max_logit;
     int M, H, V, nwg;
-    // with logits (the sampling path): every logit, and per workgroup and token the
-    // running maximum of logit / T and the sum of exp(logit / T - maximum)
-    float *logits;      // [M][V]
-    float *smax;        // [grid][M]
-    float *ssum;        // [grid][M]
-    float inv_t;        // 1 / temperature
+    float *logits;      // with logits (the sampling path): every logit, [M][V]
 };
 
 constexpr int kLmRowsPerLane = 4;
@@ -467,13 +462,10 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     const int g = lane >> 4, li = lane & 15;
     float bv[kMaxM];
     int bi[kMaxM];
-    float smx[kMaxM], ssm[kMaxM];   // online softmax state (LOGITS only)
 #pragma unroll
     for (int t = 0; t < kMaxM; ++t) {
         bv[t] = -INFINITY;
         bi[t] = 0x7fffffff;
-        smx[t] = -INFINITY;
-        ssm[t] = 0.0f;
     }
     const int NC = H / 256;
     const int nblk = a.V / kLmRowsPerWG;
@@ -511,28 +503,26 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
                 }
             }
         }
+        float sc[kLmRowsPerLane];
 #pragma unroll
-        for (int r = 0; r < kLmRowsPerLane; ++r) {
-            const int v = rbase + r;
-            const float sc = a.s[v];
+        for (int r = 0; r < kLmRowsPerLane; ++r) sc[r] = a.s[rbase + r];
 #pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
-                if (t < M) {
-                    const float lg = sc * row16_sum(acc[r][t]);
-                    if (better(lg, v, bv[t], bi[t])) {
-                        bv[t] = lg;
-                        bi[t] = v;
+        for (int t = 0; t < kMaxM; ++t) {
+            if (t < M) {
+                float lg[kLmRowsPerLane];
+#pragma unroll
+                for (int r = 0; r < kLmRowsPerLane; ++r) {
+                    lg[r] = sc[r] * row16_sum(acc[r][t]);
+                    if (better(lg[r], rbase + r, bv[t], bi[t])) {
+                        bv[t] = lg[r];
+                        bi[t] = rbase + r;
                     }
-                    if constexpr (LOGITS) {
-                        if (li == 0) a.logits[(size_t)t * a.V + v] = lg;
-                        const float z = lg * a.inv_t;
-                        if (z > smx[t]) {
-                            ssm[t] = ssm[t] * __expf(smx[t] - z) + 1.0f;
-                            smx[t] = z;
-                        } else {
-                            ssm[t] += __expf(z - smx[t]);
-                        }
-                    }
+                }
+                if constexpr (LOGITS) {
+                    // every lane of the group holds the group's 4 logits of token t: lane
+                    // r < 4 stores row rbase + r, 16 contiguous bytes per group and token
+                    const float sel = li == 0 ? lg[0] : li == 1 ? lg[1] : li == 2 ? lg[2] : lg[3];
+                    if (li < kLmRowsPerLane) a.logits[(size_t)t * a.V + rbase + li] = sel;
                 }
             }
         }
@@ -562,32 +552,6 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
             }
         a.best_v[blockIdx.x * M + t] = v;
         a.best_i[blockIdx.x * M + t] = i;
-    }
-    if constexpr (LOGITS) {
-        // the 16 groups' softmax states per token: maximum, then the rescaled sum
-        __syncthreads();
-        float *gm = reinterpret_cast<float *>(xs);
-        float *gs = gm + 16 * M;
-        if (li == 0) {
-#pragma unroll
-            for (int t = 0; t < kMaxM; ++t) {
-                if (t < M) {
-                    gm[(wave * 4 + g) * M + t] = smx[t];
-                    gs[(wave * 4 + g) * M + t] = ssm[t];
-                }
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < M) {
-            const int t = threadIdx.x;
-            float mx = gm[t];
-            for (int k = 1; k < 16; ++k) mx = fmaxf(mx, gm[k * M + t]);
-            float sm = 0.0f;
-            for (int k = 0; k < 16; ++k)
-                if (gm[k * M + t] > -INFINITY) sm += gs[k * M + t] * __expf(gm[k * M + t] - mx);
-            a.smax[blockIdx.x * M + t] = mx;
-            a.ssum[blockIdx.x * M + t] = sm;
-        }
     }
 }
 
@@ -756,15 +720,11 @@ int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     return launched();
 }
 
-int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s, float inv_t,
+int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                           const SampleWs &L, char *ws, void *stream) {
     (void)hipGetLastError();
     LmArgs a{x, w, s, reinterpret_cast<float *>(ws + L.best_v), reinterpret_cast<int32_t *>(ws + L.best_i),
-             nullptr, nullptr, M, H, V, L.nwg};
-    a.logits = reinterpret_cast<float *>(ws + L.logits);
-    a.smax = reinterpret_cast<float *>(ws + L.smax);
-    a.ssum = reinterpret_cast<float *>(ws + L.ssum);
-    a.inv_t = inv_t;
+             nullptr, nullptr, M, H, V, L.nwg, reinterpret_cast<float *>(ws + L.logits)};
     hipLaunchKernelGGL(k_lmhead<true>, dim3(L.nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     return launched();
 }

@@ -12,7 +12,9 @@
 // seed: a parallel argmax over the vocabulary instead of a prefix scan, and a decision
 // whose margin (the gap between the two largest perturbed values) is of order one.
 //
-// Kernels, after k_lmhead<true> has written every logit and per-workgroup softmax state:
+// Kernels, after k_lmhead<true> has written every logit:
+//   k_sample_stats   V / 1024 workgroups: per 1024-entry chunk and row, the maximum of
+//                    logit / T and the sum of exp(logit / T - maximum)
 //   k_sample_accept  one workgroup: log normalisers of all rows, the accept tests -> n
 //   k_sample_draw    V / 1024 workgroups, 4 entries per thread (one Philox call): the
 //                    residual (or bonus) candidates' perturbed values -> per-workgroup keys
@@ -30,8 +32,7 @@ using namespace dev;
 
 struct SampleArgs {
     const float *logits;    // [M][V]
-    const float *smax;      // [nwg][M]
-    const float *ssum;      // [nwg][M]
+    float2 *stats;          // [nsg][M]: (maximum, sum) per chunk and row
     const int32_t *draft;   // [gamma]
     const float *q;         // [gamma][V]
     const float *u_acc;     // [gamma]
@@ -75,32 +76,74 @@ __device__ __forceinline__ unsigned long long key_of(float val, int v) {
     return ((unsigned long long)ordered(val) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)v);
 }
 
-// log normaliser of every row from the lm_head workgroups' states, then the accept tests
-__global__ __launch_bounds__(256) void k_sample_accept(SampleArgs a) {
-    __shared__ float rm[256], rs[256];
-    __shared__ float logz[kMaxM];
-    const int tid = threadIdx.x, M = a.M;
-    for (int m = 0; m < M; ++m) {
-        float mx = -INFINITY;
-        for (int i = tid; i < a.nwg; i += 256) mx = fmaxf(mx, a.smax[(size_t)i * M + m]);
-        rm[tid] = mx;
-        __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (tid < off) rm[tid] = fmaxf(rm[tid], rm[tid + off]);
-            __syncthreads();
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Chunk b (entries 1024 b ..): per row, the maximum of logit / T over the chunk and the
+// sum of exp(logit / T - maximum); thread t holds entries 1024 b + 4 t .. + 3.
+__global__ __launch_bounds__(256) void k_sample_stats(SampleArgs a) {
+    __shared__ float wm[4][kMaxM], ws[4][kMaxM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, M = a.M;
+    const int v0 = (blockIdx.x * 256 + tid) * 4;
+    float4 l4[kMaxM];
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m)
+        if (m < M) l4[m] = v0 < a.V ? *reinterpret_cast<const float4 *>(a.logits + (size_t)m * a.V + v0)
+                                    : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m) {
+        if (m < M) {
+            const float z = wave_max_f(fmaxf(fmaxf(l4[m].x, l4[m].y), fmaxf(l4[m].z, l4[m].w)) * a.inv_t);
+            if (lane == 0) wm[wave][m] = z;
         }
-        const float gmx = rm[0];
-        float sm = 0.0f;
-        for (int i = tid; i < a.nwg; i += 256) sm += a.ssum[(size_t)i * M + m] * __expf(a.smax[(size_t)i * M + m] - gmx);
-        rs[tid] = sm;
-        __syncthreads();
-        for (int off = 128; off >= 1; off >>= 1) {
-            if (tid < off) rs[tid] += rs[tid + off];
-            __syncthreads();
-        }
-        if (tid == 0) logz[m] = gmx + logf(rs[0]);
-        __syncthreads();
     }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < kMaxM; ++m) {
+        if (m < M) {
+            const float mx = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
+            float e = 0.0f;
+            if (v0 < a.V)
+                e = (__expf(l4[m].x * a.inv_t - mx) + __expf(l4[m].y * a.inv_t - mx)) +
+                    (__expf(l4[m].z * a.inv_t - mx) + __expf(l4[m].w * a.inv_t - mx));
+            e = wave_sum_f(e);
+            if (lane == 0) ws[wave][m] = e;
+        }
+    }
+    __syncthreads();
+    if (tid < M) {
+        const int m = tid;
+        const float mx = fmaxf(fmaxf(wm[0][m], wm[1][m]), fmaxf(wm[2][m], wm[3][m]));
+        a.stats[(size_t)blockIdx.x * M + m] = make_float2(mx, (ws[0][m] + ws[1][m]) + (ws[2][m] + ws[3][m]));
+    }
+}
+
+// log normaliser of every row from the chunks' states (wave w combines rows w and w + 4),
+// then the accept tests
+__global__ __launch_bounds__(256) void k_sample_accept(SampleArgs a) {
+    __shared__ float logz[kMaxM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, M = a.M;
+    for (int m = wave; m < M; m += 4) {
+        float mx = -INFINITY;
+        for (int i = lane; i < a.nsg; i += 64) mx = fmaxf(mx, a.stats[(size_t)i * M + m].x);
+        mx = wave_max_f(mx);
+        float sm = 0.0f;
+        for (int i = lane; i < a.nsg; i += 64) {
+            const float2 st = a.stats[(size_t)i * M + m];
+            sm += st.y * __expf(st.x - mx);
+        }
+        sm = wave_sum_f(sm);
+        if (lane == 0) logz[m] = mx + logf(sm);
+    }
+    __syncthreads();
     if (tid == 0) {
         const int gamma = M - 1;
         int n = 0;
@@ -208,8 +251,7 @@ int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const fl
     (void)hipGetLastError();
     SampleArgs a{};
     a.logits = reinterpret_cast<const float *>(ws + L.logits);
-    a.smax = reinterpret_cast<const float *>(ws + L.smax);
-    a.ssum = reinterpret_cast<const float *>(ws + L.ssum);
+    a.stats = reinterpret_cast<float2 *>(ws + L.stats);
     a.draft = draft;
     a.q = q;
     a.u_acc = u_acc;
@@ -224,6 +266,7 @@ int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const fl
     a.V = V;
     a.nwg = L.nwg;
     a.nsg = L.nsg;
+    hipLaunchKernelGGL(k_sample_stats, dim3(L.nsg), dim3(256), 0, S(stream), a);
     hipLaunchKernelGGL(k_sample_accept, dim3(1), dim3(256), 0, S(stream), a);
     hipLaunchKernelGGL(k_sample_draw, dim3(L.nsg), dim3(256), 0, S(stream), a);
     hipLaunchKernelGGL(k_sample_final, dim3(1), dim3(256), 0, S(stream), a);

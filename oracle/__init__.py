@@ -78,6 +78,8 @@ def lib():
                                              ctypes.c_uint64, P, P, P]
             L.oracle_num_threads.restype = I
             L.oracle_num_threads.argtypes = []
+            L.oracle_set_num_threads.restype = None
+            L.oracle_set_num_threads.argtypes = [I]
             _lib = L
     return _lib
 
@@ -92,6 +94,10 @@ def _c(a, dtype):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
 
 
 def fp8_e4m3(code: int) -> float:

@@ -562,3 +562,13 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads the parallel loops above use from now on (for timing the oracle). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
+}
