@@ -170,6 +170,62 @@ __device__ __forceinline__ void topk_rounds(uint32_t (&o)[NT][NE], int K, int la
     }
 }
 
+// Top-K selection by one wave for NT tokens at once, by bisection on the key value; same
+// contract as topk_rounds. For each token, 32 steps from the top bit find T, the K-th
+// largest key (the largest value with at least K keys at or above it): each step counts
+// the keys at or above a trial value with one ballot and popcount per 64-expert word, all
+// wave-uniform scalar work, and the NT tokens' chains are interleaved. Then every key
+// above T is selected, and of the keys equal to T the lowest ids, as many as K still
+// needs (the ids of word i are lane + 64 i, so the lowest ids are the lowest set bits of
+// the lowest words). wmax[t] is the token's largest key (a DPP maximum).
+template <int NT, int NE>
+__device__ __forceinline__ void topk_bisect(const uint32_t (&o)[NT][NE], int K, int lane, unsigned (&sel)[NT],
+                                            uint32_t (&wmax)[NT]) {
+    uint32_t T[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) T[t] = 0u;
+#pragma unroll 4
+    for (int b = 31; b >= 0; --b) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint32_t trial = T[t] | (1u << b);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < NE; ++i) cnt += __popcll(__ballot(o[t][i] >= trial));
+            T[t] = cnt >= K ? trial : T[t];
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        int gt = 0;
+        unsigned long long eq[NE];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            gt += __popcll(__ballot(o[t][i] > T[t]));
+            eq[i] = __ballot(o[t][i] == T[t]);
+        }
+        const int need = K - gt;   // keys equal to T still to take (at least one)
+        unsigned s = 0u;
+        int before = 0;
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const bool take = o[t][i] > T[t] || (((eq[i] >> lane) & 1ull) && before + lanes_below(eq[i]) < need);
+            s |= take ? 1u << i : 0u;
+            before += __popcll(eq[i]);
+        }
+        sel[t] = s;
+        uint32_t v = o[t][0];
+#pragma unroll
+        for (int i = 1; i < NE; ++i) v = max(v, o[t][i]);
+        v = max(v, dppu<0xB1>(v));    // quad_perm [1,0,3,2]
+        v = max(v, dppu<0x4E>(v));    // quad_perm [2,3,0,1]
+        v = max(v, dppu<0x141>(v));   // row_half_mirror
+        v = max(v, dppu<0x140>(v));   // row_mirror
+        wmax[t] = max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16)),
+                      max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48)));
+    }
+}
+
 __device__ __forceinline__ float gelu_tanh(float z) {
     const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
     return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));

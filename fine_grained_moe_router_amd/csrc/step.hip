@@ -12,9 +12,9 @@
 //           normalised input u_l as soon as the previous layer's residual rows are
 //           in, and writes its experts' logits for all tokens.
 //  route    every workgroup reads the E x M logits and selects the top K per token
-//           itself (one wave per token, K rounds of a wave-wide maximum, ties to the
-//           lower id), so nothing stands between the logits and the expert weight
-//           loads. The union of selected experts becomes the slot list: the shared
+//           itself (one wave per token: the K-th largest logit by a 32-step bisection
+//           of ballots and popcounts, ties to the lower id), so nothing stands between
+//           the logits and the expert weight loads. The union of selected experts becomes the slot list: the shared
 //           expert first, then the routed experts in ascending id.
 //  units    the layer's work is a list: 8-row gate/up units (gate and up rows of one
 //           slot), 64-row down units (one slot, one row block), then 64-row combine
@@ -571,8 +571,7 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
                 }
             } while (!pl.done(a, ok));
         }
-        // K rounds: the largest remaining ordered logit over the wave (DPP maximum), then the
-        // lowest expert id holding it (ballots in ascending id order)
+        // the K largest ordered logits over the wave (ties: lower id), by bisection on the value
         uint32_t o[NT][kEI];
         unsigned sel[NT];   // bit i: this lane's expert lane + 64 i is selected
 #pragma unroll
@@ -580,7 +579,17 @@ __device__ __forceinline__ int route_phase(AP a0, int l, uint32_t tgt, bool outp
 #pragma unroll
             for (int i = 0; i < kEI; ++i) o[t][i] = wave + 4 * t < M && lane + 64 * i < E ? ordered(lgv[t][i]) : 0u;
         uint32_t wmax[NT];
-        topk_rounds<NT, kEI>(o, K, lane, sel, wmax);
+        if (E <= 128) {   // two 64-expert words suffice: the bisection counts only those
+            uint32_t o2[NT][2];
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                o2[t][0] = o[t][0];
+                o2[t][1] = o[t][1];
+            }
+            topk_bisect<NT, 2>(o2, K, lane, sel, wmax);
+        } else {
+            topk_bisect<NT, kEI>(o, K, lane, sel, wmax);
+        }
         float lmax[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) lmax[t] = unordered(wmax[t]);
