@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--sample", action="store_true",
                     help="the verify step's lm_head with stochastic acceptance instead (lm_head_spec_sample, "
                          "M=5, temperature 0.7, 2 rotated lm_head copies; its own JSON line)")
+    ap.add_argument("--ladder", action="store_true",
+                    help="the precision ladder instead: the stack at M=1 and M=5 for FP8/bf16 experts x FP8/bf16 "
+                         "lm_head, with tokens/s modelled from the acceptance rate (its own JSON line)")
     ap.add_argument("--path", choices=("fused", "layers"), default="fused",
                     help="fused: one moe_decode_step launch per step; layers: per-layer entry points "
                          "captured in a HIP graph per step")
@@ -137,6 +140,8 @@ def main():
         return zipf_main(args)
     if args.sample:
         return sample_main(args)
+    if args.ladder:
+        return ladder_main(args)
     if args.layer:
         return layer_main(args)
     import synth
@@ -264,7 +269,7 @@ def read_probe(nbytes=4 << 30, reps=10):
             "read_gbs": round(nbytes / (us / 1e6) / 1e9, 1)}
 
 
-def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
+def measure(args, runner, sh, M, expert_dtype="fp8", bias=False, lm_dtype="fp8"):
     """Warm up, then time exactly args.steps steps of the runner at M tokens (HIP events
     on the launch stream, bracketed by device synchronisations); then record each timed
     step's routing to count the bytes it needed."""
@@ -338,7 +343,7 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False):
         if st_code != native.MOE_OK:
             raise RuntimeError("fused step reported %s" % native.strerror(st_code))
 
-    bytes_steps = [budget.step_bytes(sh, u, M, expert_dtype, bias) for u in uniq]
+    bytes_steps = [budget.step_bytes(sh, u, M, expert_dtype, bias, lm_dtype) for u in uniq]
     ms = ms_total / K
     bps = float(np.mean(bytes_steps))
     r = {
@@ -608,6 +613,79 @@ def sample_main(args):
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": int(bps),
                      "avg_launch_us": round(ms * 1e3, 2)},
         "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def expected_emitted(alpha, gamma):
+    """Tokens emitted per verify step when each draft is accepted with probability alpha
+    (prefix acceptance, then the bonus or correction token): sum_{j=0..gamma} alpha^j."""
+    return sum(alpha ** j for j in range(gamma + 1))
+
+
+def ladder_main(args):
+    """The precision ladder (page "LLM decoding", "Lever 1: fewer bytes" and the table "The
+    ladder, every rung"): the 30-layer stack on the fused step at M=1 (plain decoding) and M=5
+    (the verify step with 4 drafts), for FP8 or bf16 expert weights (routed and shared) and
+    an FP8 or bf16 lm_head; the router is bf16 in every rung. Per rung: bytes/step and
+    steps/s at both M, and tokens/s = steps/s(M=1) for plain decoding and steps/s(M=5) x
+    E[n+1] for speculative decoding at the page's acceptance rates (E[n+1] = sum_j alpha^j,
+    j = 0..4). The drafter's own cost is not in these figures."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import native
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    sh = synth.GEMMA4_26B_A4B.with_(layers=args.layers)
+    gains = synth.rmsnorm_gains(sh, dev, seed=args.seed)
+    lm = {"fp8": synth.lm_head(sh, dev, seed=args.seed), "bf16": (synth.lm_head_bf16(sh, dev, seed=args.seed), None)}
+    rungs = {}
+    for edt in ("bf16", "fp8"):
+        t0 = time.time()
+        layers = [synth.layer_weights(sh, l, dev, seed=args.seed, tag="stack", expert_dtype=edt)
+                  for l in range(sh.layers)]
+        torch.cuda.synchronize()
+        log("%s experts generated in %.1fs (%.2f GB resident)" % (edt, time.time() - t0,
+                                                                 torch.cuda.memory_allocated() / 1e9))
+        for ldt in ("bf16", "fp8"):
+            Q, s = lm[ldt]
+            runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=5)
+            r = {}
+            for M in (1, 5):
+                m = measure(args, runner, sh, M, edt, lm_dtype=ldt)
+                r["M%d" % M] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()
+                                if k in ("steps_per_s", "ms_per_step", "bytes_per_step", "hbm_gbs", "hbm_frac",
+                                         "median_block_ms_per_step")}
+            r["tokens_per_s_plain"] = round(r["M1"]["steps_per_s"], 1)
+            for alpha in (0.87, 0.90):
+                r["tokens_per_s_spec_alpha%.2f" % alpha] = round(r["M5"]["steps_per_s"] * expected_emitted(alpha, 4), 1)
+            name = "experts_%s+lm_head_%s" % (edt, ldt)
+            rungs[name] = r
+            log("%s: M=1 %.3f ms, M=5 %.3f ms, plain %.0f tok/s, spec(0.87) %.0f tok/s" % (
+                name, r["M1"]["ms_per_step"], r["M5"]["ms_per_step"], r["tokens_per_s_plain"],
+                r["tokens_per_s_spec_alpha0.87"]))
+            del runner
+            torch.cuda.synchronize()
+        del layers
+        torch.cuda.empty_cache()
+    top, base = rungs["experts_fp8+lm_head_fp8"], rungs["experts_bf16+lm_head_bf16"]
+    line = {
+        "metric": "precision ladder: decode steps/s and modelled tokens/s, 26B-A4B MoE stack, FP8/bf16 experts x "
+                  "FP8/bf16 lm_head, M=1 and M=5",
+        "value": top["tokens_per_s_plain"], "unit": "tokens/s (FP8 rung, plain decoding)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": top["M1"]["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 or bf16 weights (per rung) x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded N(0,.) weights; FP8 rungs quantise the same draws the bf16 rungs round)",
+        "config": {"workload": "Gemma-4-26B-A4B-shaped MoE stack, 30 layers + tied lm_head + argmax + accept, "
+                               "fused step, M=1 and M=5", "layers": sh.layers, "hidden": sh.hidden,
+                   "experts": sh.experts, "top_k": sh.top_k, "expert_width": sh.width, "vocab": sh.vocab},
+        "rungs": rungs,
+        "fp8_over_bf16_plain": round(top["tokens_per_s_plain"] / base["tokens_per_s_plain"], 3),
+        "fp8_spec_over_bf16_plain_alpha0.87": round(top["tokens_per_s_spec_alpha0.87"] / base["tokens_per_s_plain"], 3),
+        "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 

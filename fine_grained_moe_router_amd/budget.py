@@ -49,15 +49,16 @@ def layer_bytes(shape, unique_routed: int, M: int, expert_dtype: str = "fp8",
 
 
 def step_bytes(shape, unique_routed_per_layer, M: int, expert_dtype: str = "fp8",
-               bias: bool = False) -> int:
+               bias: bool = False, lm_dtype: str = "fp8") -> int:
     """Whole stacked step: every layer (with its residual norm), the final norm, the
-    lm_head, and the argmax / acceptance outputs (negligible, counted as 16 B/token)."""
+    lm_head (FP8 codes and row scales, or bf16), and the argmax / acceptance outputs
+    (negligible, counted as 16 B/token)."""
     b = 0
     for u in unique_routed_per_layer:
         b += layer_bytes(shape, int(u), M, expert_dtype, bias, norm=True)
     H = shape.hidden
     b += 3 * M * H * 2 + H * 2            # final residual add + norm
-    b += lm_head_bytes(shape.vocab, H)
+    b += lm_head_bytes(shape.vocab, H) if lm_dtype == "fp8" else 2 * shape.vocab * H
     b += 16 * M
     return b
 

@@ -70,7 +70,7 @@ int check_step_desc(const moe_step_desc *d) {
     if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
     if (d->max_tokens < 1 || d->max_tokens > kMaxM) return MOE_EINVAL;
     if (!(d->eps >= 0.0f)) return MOE_EINVAL;
-    if (d->flags & ~MOE_STEP_COOPERATIVE) return MOE_EINVAL;
+    if (d->flags & ~(MOE_STEP_COOPERATIVE | MOE_STEP_LM_BF16)) return MOE_EINVAL;
     return MOE_OK;
 }
 
@@ -146,6 +146,20 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lm_ws_bytes(M, V))
         return MOE_EWORKSPACE;
     return launch_lm_head(M, H, V, x, w, w_s, token, max_logit, (char *)workspace, stream);
+}
+
+int lm_head_argmax_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *w, int32_t *token,
+                        float *max_logit, void *workspace, size_t workspace_bytes, void *stream) {
+    if (M < 1 || M > kMaxM || H < 256 || H > kMaxHidden || H % 256 || V < 64 || V % 64 ||
+        V > (1 << 30))
+        return MOE_EINVAL;
+    CHECK(need(x));
+    CHECK(need(w));
+    CHECK(need(token));
+    if (max_logit && !aligned16(max_logit)) return MOE_EALIGN;
+    if (!workspace || ((uintptr_t)workspace & 255u) || workspace_bytes < lm_ws_bytes(M, V))
+        return MOE_EWORKSPACE;
+    return launch_lm_head_bf16(M, H, V, x, w, token, max_logit, (char *)workspace, stream);
 }
 
 size_t lm_head_spec_sample_workspace(int max_M, int H, int V) {
@@ -244,7 +258,7 @@ int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
     if (M < 1 || M > desc->max_tokens) return MOE_EINVAL;
     CHECK(need(gains));
     CHECK(need(lm_w));
-    CHECK(need(lm_s));
+    if (!(desc->flags & MOE_STEP_LM_BF16)) CHECK(need(lm_s));
     CHECK(need(x));
     CHECK(need(noise));
     if (M > 1 && !draft) return MOE_EINVAL;

@@ -204,6 +204,8 @@ int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t 
 int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const float *q, const float *u_acc,
                        uint64_t seed, uint64_t step, int32_t *accepted_len, int32_t *out_tokens,
                        const SampleWs &L, char *ws, void *stream);
+int launch_lm_head_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *w, int32_t *token, float *max_logit,
+                        char *ws, void *stream);
 int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                            int32_t *token, float *max_logit, void *stream);
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,

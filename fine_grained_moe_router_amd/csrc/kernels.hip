@@ -451,7 +451,9 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // blk*64 + 16 w + 4 g + r (r = 0..3) and reads the same 16-byte column chunk of all
 // four, so each bf16 activation chunk read from LDS serves 4 rows. Row sums go
 // through the 16-lane DPP reduction; each group keeps its running best per token.
-template <bool LOGITS>
+// WBF: bf16 weights ([V][H] bf16, no scales): a 16-byte piece holds 8 columns, so a
+// 16-lane chunk of a row covers 128 columns instead of 256 and a row has twice the chunks.
+template <bool LOGITS, bool WBF>
 __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
     extern __shared__ uint4 xs[];  // [M][H/8]; reused at the end for the per-group bests
     const int H = a.H, hv = H / 8, M = a.M;
@@ -467,11 +469,13 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
         bv[t] = -INFINITY;
         bi[t] = 0x7fffffff;
     }
-    const int NC = H / 256;
+    constexpr int EB = WBF ? 2 : 1;          // bytes per weight
+    constexpr int CPC = 256 / EB;            // columns per 16-lane chunk of a row
+    const int NC = H / CPC;
     const int nblk = a.V / kLmRowsPerWG;
     for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
         const int rbase = blk * kLmRowsPerWG + wave * 16 + g * 4;
-        const uint8_t *wr = a.w + (size_t)rbase * H + li * 16;
+        const uint8_t *wr = a.w + (size_t)rbase * H * EB + li * 16;
         float acc[kLmRowsPerLane][kMaxM];
 #pragma unroll
         for (int r = 0; r < kLmRowsPerLane; ++r)
@@ -484,20 +488,38 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 #pragma unroll
                 for (int r = 0; r < kLmRowsPerLane; ++r)
                     if (i0 + k < NC)
-                        q[k][r] = *reinterpret_cast<const uint4 *>(wr + (size_t)r * H + (size_t)(i0 + k) * 256);
+                        q[k][r] = *reinterpret_cast<const uint4 *>(wr + (size_t)r * H * EB + (size_t)(i0 + k) * 256);
 #pragma unroll
             for (int k = 0; k < kLmUnroll; ++k) {
                 if (i0 + k < NC) {
-                    bf16x2 wv[kLmRowsPerLane][8];
+                    if constexpr (WBF) {
+                        const int xv = ((i0 + k) * CPC + li * 8) / 8;
 #pragma unroll
-                    for (int r = 0; r < kLmRowsPerLane; ++r) decode16_bf16(q[k][r], wv[r]);
-                    const int xv = ((i0 + k) * 256 + li * 16) / 8;
+                        for (int t = 0; t < kMaxM; ++t) {
+                            if (t < M) {
+                                const uint4 x0 = xs[t * hv + xv];
 #pragma unroll
-                    for (int t = 0; t < kMaxM; ++t) {
-                        if (t < M) {
-                            const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
+                                for (int r = 0; r < kLmRowsPerLane; ++r) {
+                                    float v = acc[r][t];
+                                    v = dot2(as_bf2(q[k][r].x), as_bf2(x0.x), v);
+                                    v = dot2(as_bf2(q[k][r].y), as_bf2(x0.y), v);
+                                    v = dot2(as_bf2(q[k][r].z), as_bf2(x0.z), v);
+                                    acc[r][t] = dot2(as_bf2(q[k][r].w), as_bf2(x0.w), v);
+                                }
+                            }
+                        }
+                    } else {
+                        bf16x2 wv[kLmRowsPerLane][8];
 #pragma unroll
-                            for (int r = 0; r < kLmRowsPerLane; ++r) acc[r][t] = dot16(wv[r], x0, x1, acc[r][t]);
+                        for (int r = 0; r < kLmRowsPerLane; ++r) decode16_bf16(q[k][r], wv[r]);
+                        const int xv = ((i0 + k) * CPC + li * 16) / 8;
+#pragma unroll
+                        for (int t = 0; t < kMaxM; ++t) {
+                            if (t < M) {
+                                const uint4 x0 = xs[t * hv + xv], x1 = xs[t * hv + xv + 1];
+#pragma unroll
+                                for (int r = 0; r < kLmRowsPerLane; ++r) acc[r][t] = dot16(wv[r], x0, x1, acc[r][t]);
+                            }
                         }
                     }
                 }
@@ -505,7 +527,7 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
         }
         float sc[kLmRowsPerLane];
 #pragma unroll
-        for (int r = 0; r < kLmRowsPerLane; ++r) sc[r] = a.s[rbase + r];
+        for (int r = 0; r < kLmRowsPerLane; ++r) sc[r] = WBF ? 1.0f : a.s[rbase + r];
 #pragma unroll
         for (int t = 0; t < kMaxM; ++t) {
             if (t < M) {
@@ -715,7 +737,19 @@ int launch_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
     LmArgs a{x, w, s, reinterpret_cast<float *>(ws),
              reinterpret_cast<int32_t *>(ws + align256((size_t)nwg * M * sizeof(float))),
              token, max_logit, M, H, V, nwg};
-    hipLaunchKernelGGL(k_lmhead<false>, dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
+    hipLaunchKernelGGL((k_lmhead<false, false>), dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
+    hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, S(stream), a);
+    return launched();
+}
+
+int launch_lm_head_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *w, int32_t *token, float *max_logit,
+                        char *ws, void *stream) {
+    (void)hipGetLastError();
+    const int nwg = lm_grid(V);
+    LmArgs a{x, reinterpret_cast<const uint8_t *>(w), nullptr, reinterpret_cast<float *>(ws),
+             reinterpret_cast<int32_t *>(ws + align256((size_t)nwg * M * sizeof(float))),
+             token, max_logit, M, H, V, nwg};
+    hipLaunchKernelGGL((k_lmhead<false, true>), dim3(nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     hipLaunchKernelGGL(k_argmax_final, dim3(1), dim3(256), 0, S(stream), a);
     return launched();
 }
@@ -725,7 +759,7 @@ int launch_lm_head_logits(int M, int H, int V, const uint16_t *x, const uint8_t 
     (void)hipGetLastError();
     LmArgs a{x, w, s, reinterpret_cast<float *>(ws + L.best_v), reinterpret_cast<int32_t *>(ws + L.best_i),
              nullptr, nullptr, M, H, V, L.nwg, reinterpret_cast<float *>(ws + L.logits)};
-    hipLaunchKernelGGL(k_lmhead<true>, dim3(L.nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
+    hipLaunchKernelGGL((k_lmhead<true, false>), dim3(L.nwg), dim3(256), (size_t)M * H * 2, S(stream), a);
     return launched();
 }
 

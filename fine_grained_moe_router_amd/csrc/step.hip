@@ -80,6 +80,7 @@ struct StepArgs {
     float eps;
     unsigned spin_limit;
     int layer_mode;                    // 1: one MoE layer from x (already normalised) to y (moe_decode_layer)
+    int lm_bf;                         // 1: lm_w holds bf16 weights without scales
     moe_layer_weights lw;              // layer mode: the layer's weights (router as given, [H][E])
 };
 
@@ -1165,25 +1166,47 @@ struct LmAcc {
     unsigned long long best[MT];
 };
 
+// Chunks per row of the lm_head: 16 lanes x 16 bytes, 256 FP8 columns or 128 bf16 columns
+// (LBF: bf16 weights without scales).
+template <bool LBF>
+__device__ __forceinline__ int lm_chunks(AP a) { return LBF ? a->H / 128 : a->H / 256; }
+
 // step st of this workgroup's row stream: 64-row unit u0 + st / NC, chunk st % NC
+template <bool LBF>
 __device__ __forceinline__ void lm_load(AP a, int u0, int nst, int st, LmBuf &b) {
     if (st < nst) {
-        const int t = ltid(), NC = a->H / 256, lane = t & 63, wave = t >> 6;
+        const int t = ltid(), NC = lm_chunks<LBF>(a), lane = t & 63, wave = t >> 6, EB = LBF ? 2 : 1;
         const int unit = u0 + st / NC, k = st % NC;
         const size_t row = (size_t)unit * 64 + wave * 16 + (lane >> 4) * kLmRows;
-        const uint8_t *p = a->lm_w + row * a->H + k * 256 + (lane & 15) * 16;
+        const uint8_t *p = a->lm_w + row * a->H * EB + k * 256 + (lane & 15) * 16;
 #pragma unroll
-        for (int r = 0; r < kLmRows; ++r) b.q[r] = ld16(p + (size_t)r * a->H);
+        for (int r = 0; r < kLmRows; ++r) b.q[r] = ld16(p + (size_t)r * a->H * EB);
     }
 }
 
-template <int MT>
+template <int MT, bool LBF>
 __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmBuf &b, LmAcc<MT> &A) {
     if (st >= nst) return;
-    const int tid = ltid(), NC = a->H / 256, M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
+    const int tid = ltid(), NC = lm_chunks<LBF>(a), M = MT, lane = tid & 63, wave = tid >> 6, li = lane & 15;
     const int k = st % NC;
     const uint16_t *xl = ulds();
-    if constexpr (MT == 1) {
+    if constexpr (LBF) {
+        // bf16 weights: 8 columns per lane, one 16-byte activation piece per token
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            if (t < M) {
+                const uint4 x0 = *reinterpret_cast<const uint4 *>(xl + t * kUS + k * 128 + li * 8);
+#pragma unroll
+                for (int r = 0; r < kLmRows; ++r) {
+                    float v = A.acc[r][t];
+                    v = dot2(as_bf2(b.q[r].x), as_bf2(x0.x), v);
+                    v = dot2(as_bf2(b.q[r].y), as_bf2(x0.y), v);
+                    v = dot2(as_bf2(b.q[r].z), as_bf2(x0.z), v);
+                    A.acc[r][t] = dot2(as_bf2(b.q[r].w), as_bf2(x0.w), v);
+                }
+            }
+        }
+    } else if constexpr (MT == 1) {
         // one token: each row is decoded just before its dot product (fewer live registers)
         const uint4 *xs = reinterpret_cast<const uint4 *>(xl + k * 256 + li * 16);
         const uint4 x0 = xs[0], x1 = xs[1];
@@ -1223,23 +1246,23 @@ __device__ __forceinline__ void lm_step(AP a, int u0, int nst, int st, const LmB
                 A.acc[r][t] = 0.0f;
             }
         }
-        if (st + 1 < nst) {   // the next unit's scales
+        if (st + 1 < nst && !LBF) {   // the next unit's scales
 #pragma unroll
             for (int r = 0; r < kLmRows; ++r) A.sc[r] = glb(a->lm_s)[row + 64 + r];
         }
     }
 }
 
-template <int MT>
+template <int MT, bool LBF>
 __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
     const AP a = uniform(a0);
-    const int H = a->H, M = MT, NC = H / 256, tid = ltid(), lane = tid & 63, wave = tid >> 6;
+    const int H = a->H, M = MT, NC = lm_chunks<LBF>(a), tid = ltid(), lane = tid & 63, wave = tid >> 6;
     const int u0 = (int)((long long)w * a->NLU / G), u1 = (int)((long long)(w + 1) * a->NLU / G);
     const int nst = (u1 - u0) * NC;
     LmBuf b0, b1, b2;
-    lm_load(a, u0, nst, 0, b0);
-    lm_load(a, u0, nst, 1, b1);
-    lm_load(a, u0, nst, 2, b2);
+    lm_load<LBF>(a, u0, nst, 0, b0);
+    lm_load<LBF>(a, u0, nst, 1, b1);
+    lm_load<LBF>(a, u0, nst, 2, b2);
     LmAcc<MT> A;
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
@@ -1248,8 +1271,8 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
         for (int r = 0; r < kLmRows; ++r) A.acc[r][t] = 0.0f;
     }
 #pragma unroll
-    for (int r = 0; r < kLmRows; ++r) A.sc[r] = 0.0f;
-    if (nst > 0) {
+    for (int r = 0; r < kLmRows; ++r) A.sc[r] = LBF ? 1.0f : 0.0f;
+    if (nst > 0 && !LBF) {
         const int row = u0 * 64 + wave * 16 + (lane >> 4) * kLmRows;
 #pragma unroll
         for (int r = 0; r < kLmRows; ++r) A.sc[r] = glb(a->lm_s)[row + r];
@@ -1264,12 +1287,12 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
         }
     }
     for (int st = 0; st < nst; st += 3) {
-        lm_step<MT>(a, u0, nst, st, b0, A);
-        lm_load(a, u0, nst, st + 3, b0);
-        lm_step<MT>(a, u0, nst, st + 1, b1, A);
-        lm_load(a, u0, nst, st + 4, b1);
-        lm_step<MT>(a, u0, nst, st + 2, b2, A);
-        lm_load(a, u0, nst, st + 5, b2);
+        lm_step<MT, LBF>(a, u0, nst, st, b0, A);
+        lm_load<LBF>(a, u0, nst, st + 3, b0);
+        lm_step<MT, LBF>(a, u0, nst, st + 1, b1, A);
+        lm_load<LBF>(a, u0, nst, st + 4, b1);
+        lm_step<MT, LBF>(a, u0, nst, st + 2, b2, A);
+        lm_load<LBF>(a, u0, nst, st + 5, b2);
     }
     // the workgroup's best per token: 16 lane groups, then one key per token
     unsigned long long *gb = reinterpret_cast<unsigned long long *>(scratch(a));   // [16][MT]
@@ -1389,8 +1412,10 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
     asm volatile("" : "+s"(a));
     if (a->layer_mode)
         layer_end(a, w, G, tgt);
+    else if (a->lm_bf)   // the lm_head's weight type picks one of two versions of the phase
+        lm_phase<MT, true>(a, w, G, tgt);
     else
-        lm_phase<MT>(a, w, G, tgt);
+        lm_phase<MT, false>(a, w, G, tgt);
 }
 
 // Router weights [H][E] -> [E][H] (once, at prepare time).
@@ -1565,6 +1590,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.noise = noise;
     a.lm_w = lm_w;
     a.lm_s = lm_s;
+    a.lm_bf = (d.flags & MOE_STEP_LM_BF16) ? 1 : 0;
     a.draft = draft;
     a.token = token;
     a.max_logit = max_logit;

@@ -21,7 +21,7 @@ MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
-           "lm_head_argmax", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
+           "lm_head_argmax", "lm_head_argmax_bf16", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
            "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
            "moe_hbm_read_probe", "moe_strerror")
@@ -54,6 +54,7 @@ class StepDesc(ctypes.Structure):
 
 
 MOE_STEP_COOPERATIVE = 1
+MOE_STEP_LM_BF16 = 2
 
 
 def lib() -> ctypes.CDLL:
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.lm_head_spec_sample.restype = I
         L.lm_head_spec_sample.argtypes = [I, I, I, _P, _P, _P, ctypes.c_float, _P, _P, _P, ctypes.c_uint64,
                                           ctypes.c_uint64, _P, _P, _P, S, _P]
+        L.lm_head_argmax_bf16.restype = I
+        L.lm_head_argmax_bf16.argtypes = [I, I, I, _P, _P, _P, _P, _P, S, _P]
         L.lm_head_argmax_noalloc.restype = I
         L.lm_head_argmax_noalloc.argtypes = [I, I, I, _P, _P, _P, _P, _P, _P]
         L.spec_accept.restype = I
@@ -180,6 +183,12 @@ def lm_head_spec_sample(M, H, V, x, w, w_s, temperature, draft, q, u_accept, see
     _check("lm_head_spec_sample", st)
 
 
+def lm_head_argmax_bf16(M, H, V, x, w, token, max_logit, workspace, workspace_bytes, stream=None):
+    st = lib().lm_head_argmax_bf16(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(token), _ptr(max_logit),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("lm_head_argmax_bf16", st)
+
+
 def lm_head_argmax_noalloc(M, H, V, x, w, w_s, token, max_logit, stream=None):
     st = lib().lm_head_argmax_noalloc(int(M), int(H), int(V), _ptr(x), _ptr(w), _ptr(w_s), _ptr(token),
                                       _ptr(max_logit), _stream(stream))
@@ -213,9 +222,9 @@ def moe_hbm_read_probe(src, nbytes, sink, stream=None):
 
 
 def step_desc(shape, max_tokens: int, eps: float = 1e-6, spin_limit: int = 0,
-              expert_dtype: str = "fp8", cooperative: bool = False) -> StepDesc:
+              expert_dtype: str = "fp8", cooperative: bool = False, lm_bf16: bool = False) -> StepDesc:
     return StepDesc(layer_desc(shape, expert_dtype), shape.layers, shape.vocab, max_tokens, eps, spin_limit,
-                    MOE_STEP_COOPERATIVE if cooperative else 0)
+                    (MOE_STEP_COOPERATIVE if cooperative else 0) | (MOE_STEP_LM_BF16 if lm_bf16 else 0))
 
 
 def moe_decode_step_workspace(desc: StepDesc) -> int:

@@ -80,8 +80,9 @@ class FusedDecodeStep:
         self.layers = layers
         self.gains, self.lm_w, self.lm_s = gains, lm_w, lm_s
         expert_dtype = layers[0].get("expert_dtype", "fp8")
+        self.lm_bf16 = lm_w.dtype == torch.bfloat16      # the BF16 rung: [V][H] bf16, no scales
         self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit, expert_dtype,
-                                     cooperative)
+                                     cooperative, self.lm_bf16)
         self.ws_bytes = native.moe_decode_step_workspace(self.desc)
         if self.ws_bytes == 0:
             raise ValueError("unsupported shape for the fused decode step")

@@ -169,6 +169,14 @@ int lm_head_argmax(int M, int H, int V, const uint16_t *x, const uint8_t *w, con
                    int32_t *token, float *max_logit, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/*
+ * lm_head_argmax with bf16 weights (the precision ladder's BF16 rung; page "LLM decoding",
+ * "Lever 1: fewer bytes" and "The ladder, every rung"): logit[m][v] = sum_c w[v][c] x[m][c],
+ * no scales; otherwise as lm_head_argmax (same workspace size). w bf16 [V][H].
+ */
+int lm_head_argmax_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *w, int32_t *token,
+                        float *max_logit, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Bytes of workspace lm_head_spec_sample needs (0 for invalid sizes). */
 size_t lm_head_spec_sample_workspace(int max_M, int H, int V);
 
@@ -319,6 +327,8 @@ typedef struct moe_step_desc {
 } moe_step_desc;
 
 #define MOE_STEP_COOPERATIVE 1u   /* launch cooperatively outside stream capture (see above) */
+#define MOE_STEP_LM_BF16 2u       /* lm_w holds bf16 [V][H] weights without scales (lm_s unused,
+                                     may be NULL): the precision ladder's BF16 lm_head */
 
 /* Bytes of workspace for moe_decode_step (0 if desc is invalid). */
 size_t moe_decode_step_workspace(const moe_step_desc *desc);
@@ -335,7 +345,8 @@ int moe_decode_step_prepare(const moe_step_desc *desc, const moe_layer_weights *
 /*
  * One stacked decode step for M tokens (1 <= M <= desc->max_tokens), asynchronous on
  * `stream` and capturable. Concurrent steps must use distinct workspaces.
- *   gains      bf16 [L+1][H]            lm_w FP8 [V][H], lm_s fp32 [V]
+ *   gains      bf16 [L+1][H]            lm_w FP8 [V][H], lm_s fp32 [V] (MOE_STEP_LM_BF16: lm_w
+ *                                       bf16 [V][H], lm_s unused)
  *   x          bf16 [M][H]              noise bf16 [L][M][H]
  *   draft      int32 [M-1] (NULL when M == 1)
  *   token      int32 [M]; max_logit fp32 [M] or NULL; accepted_len int32 [1];

@@ -61,6 +61,8 @@ def lib():
             L.oracle_moe_layer.argtypes = [I] * 7 + [P] * 21
             L.oracle_lm_head.restype = None
             L.oracle_lm_head.argtypes = [I, I, I, P, P, P, P, P, P]
+            L.oracle_lm_head_bf16.restype = None
+            L.oracle_lm_head_bf16.argtypes = [I, I, I, P, P, P, P, P]
             L.oracle_lm_head_rows.restype = None
             L.oracle_lm_head_rows.argtypes = [I, I, I, P, P, P, P, P]
             L.oracle_spec_accept.restype = I
@@ -184,6 +186,19 @@ def lm_head_argmax(x, Q, s):
     return tok, ml, gap
 
 
+def lm_head_argmax_bf16(x, W):
+    """x uint16 [M][H], W uint16 (bf16 bits) [V][H] -> (tok int32 [M], max_logit f64 [M], gap f64 [M])."""
+    x = _c(x, np.uint16)
+    W = _c(W, np.uint16)
+    M, H = x.shape
+    V = W.shape[0]
+    tok = np.empty(M, np.int32)
+    ml = np.empty(M, np.float64)
+    gap = np.empty(M, np.float64)
+    lib().oracle_lm_head_bf16(M, H, V, _p(x), _p(W), _p(tok), _p(ml), _p(gap))
+    return tok, ml, gap
+
+
 def lm_head_rows(x, Q, s, rows):
     """Logits of the given vocab rows only: f64 [M][len(rows)]."""
     x = _c(x, np.uint16)
@@ -262,7 +277,7 @@ def add_rmsnorm(h, a0, a1, g, eps=1e-6):
     return ho, uo
 
 
-def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None):
+def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None, lm_bf16=False):
     """One decode step through a stack of MoE layers, then lm_head, argmax, acceptance.
 
     Wiring (the pages omit attention; the stacked workload replaces it by a residual
@@ -272,6 +287,7 @@ def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None):
         h, x_f = add_rmsnorm(h, y_{L-1}, None, g_L)
         tok = argmax(lm_head(x_f)); (n, out) = spec_accept(draft, tok)
     layers: a list of host weight dicts (or a callable l -> dict, to fetch lazily).
+    lm_bf16: lm_w holds bf16 bits [V][H] (no scales; lm_s ignored) instead of FP8 codes.
     Returns per-layer u, routing, gaps and y, plus the final tokens and gaps.
     """
     L = len(noise)
@@ -288,7 +304,7 @@ def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None):
         y_prev = r["y_bf16"]
     h_last = h
     h, xf = add_rmsnorm(h, y_prev, None, gains[L], eps)
-    tok, ml, gap = lm_head_argmax(xf, lm_w, lm_s)
+    tok, ml, gap = lm_head_argmax_bf16(xf, lm_w) if lm_bf16 else lm_head_argmax(xf, lm_w, lm_s)
     out = {"layers": per, "h_last": h_last, "x_final": xf, "h_final": h, "tok": tok,
            "max_logit": ml, "lm_gap": gap}
     if draft is not None:

@@ -337,6 +337,42 @@ void oracle_lm_head(int M, int H, int V, const uint16_t *x, const uint8_t *Q,
     free(lg);
 }
 
+/*
+ * The tied lm_head with bf16 weights (the precision ladder's BF16 rung, [LLMD] "Lever 1:
+ * fewer bytes" and the table "The ladder, every rung": the same projection before FP8
+ * quantisation), no scales:
+ *   logit[m][v] = sum_c W[v][c] x[m][c]           W row-major [V][H] bf16
+ *   tok[m] = argmax_v logit[m][v], ties: lower v; max_logit, gap as oracle_lm_head.
+ */
+void oracle_lm_head_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *W, int32_t *tok,
+                         double *max_logit, double *gap)
+{
+    double *lg = malloc(sizeof(double) * (size_t)V);
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *xm = x + (size_t)m * H;
+        int v;
+#pragma omp parallel for schedule(static)
+        for (v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += oracle_bf16(W[(size_t)v * H + c]) * oracle_bf16(xm[c]);
+            lg[v] = acc;
+        }
+        int best = 0;
+        for (int vv = 1; vv < V; ++vv)
+            if (lg[vv] > lg[best])
+                best = vv;
+        double second = -INFINITY;
+        for (int vv = 0; vv < V; ++vv)
+            if (vv != best && lg[vv] > second)
+                second = lg[vv];
+        tok[m] = best;
+        max_logit[m] = lg[best];
+        gap[m] = V > 1 ? lg[best] - second : INFINITY;
+    }
+    free(lg);
+}
+
 /* Logits of selected rows only: out[m][r] = s[rows[r]] * sum_c Q[rows[r]][c] x[m][c]. */
 void oracle_lm_head_rows(int M, int H, int nrows, const int32_t *rows, const uint16_t *x,
                          const uint8_t *Q, const float *s, double *out)

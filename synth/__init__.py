@@ -159,6 +159,18 @@ def lm_head(shape: Shape, device="cpu", seed: int = 0, tag: str = "lm_head"):
     return _fp8_matrix((shape.vocab, shape.hidden), LM_HEAD_STD, device, seed, tag)
 
 
+def lm_head_bf16(shape: Shape, device="cpu", seed: int = 0, tag: str = "lm_head") -> torch.Tensor:
+    """Tied lm_head [V][H] in bf16: the same N(0, 0.02) draws as lm_head(), rounded once to
+    bf16 instead of quantised (the precision ladder's BF16 rung)."""
+    V, H = shape.vocab, shape.hidden
+    out = torch.empty((V, H), dtype=torch.bfloat16, device=device)
+    per = max(1, (1 << 27) // H)
+    for i0 in range(0, V, per):
+        i1 = min(V, i0 + per)
+        out[i0:i1] = normal((i1 - i0, H), LM_HEAD_STD, device, seed, tag, i0).to(torch.bfloat16)
+    return out
+
+
 def hidden_inputs(shape: Shape, M: int, step: int, sub: int = 0, device="cpu",
                   seed: int = 0, tag: str = "x") -> torch.Tensor:
     """M fresh bf16 hidden vectors N(0, 1) for one decode step (sub: resample index)."""

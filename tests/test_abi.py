@@ -156,6 +156,15 @@ def test_lm_head_validation():
     assert f(wsb=ws - 1) == native.MOE_EWORKSPACE and f(ws=None) == native.MOE_EWORKSPACE
 
 
+def test_lm_head_bf16_validation():
+    L = native.lib()
+    ws = native.lm_head_argmax_workspace(5, 2816, 4096)
+    assert L.lm_head_argmax_bf16(0, 2816, 4096, FAKE, FAKE, FAKE, None, FAKE, ws, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_bf16(5, 2816, 4096, FAKE, None, FAKE, None, FAKE, ws, None) == native.MOE_EINVAL
+    assert L.lm_head_argmax_bf16(5, 2816, 4096, FAKE, FAKE + 8, FAKE, None, FAKE, ws, None) == native.MOE_EALIGN
+    assert L.lm_head_argmax_bf16(5, 2816, 4096, FAKE, FAKE, FAKE, None, FAKE, ws - 1, None) == native.MOE_EWORKSPACE
+
+
 def test_lm_head_noalloc_validation():
     L = native.lib()
     assert L.lm_head_argmax_noalloc(0, 2816, 262144, FAKE, FAKE, FAKE, FAKE, None, None) == native.MOE_EINVAL
@@ -238,9 +247,10 @@ def test_step_workspace_and_desc_validation():
     d = step_desc()
     assert native.moe_decode_step_workspace(d) > 0
     for k, v in (("num_layers", 0), ("num_layers", 65), ("vocab", 100), ("max_tokens", 9), ("max_tokens", 0),
-                 ("eps", -1.0), ("flags", 2), ("flags", 0x80000001)):
+                 ("eps", -1.0), ("flags", 4), ("flags", 0x80000001)):
         assert native.moe_decode_step_workspace(step_desc(**{k: v})) == 0, k
-    assert native.moe_decode_step_workspace(step_desc(flags=native.MOE_STEP_COOPERATIVE)) > 0
+    for f in (native.MOE_STEP_COOPERATIVE, native.MOE_STEP_LM_BF16, native.MOE_STEP_COOPERATIVE | native.MOE_STEP_LM_BF16):
+        assert native.moe_decode_step_workspace(step_desc(flags=f)) > 0
     wide = step_desc()
     wide.layer.hidden = 3072                       # the fused step takes H <= 2816
     assert native.moe_decode_step_workspace(wide) == 0

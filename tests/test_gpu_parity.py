@@ -301,6 +301,28 @@ def test_lm_head_full_size(gemma_lm_head, M):
 
 # -------------------------------------------------------------- acceptance
 
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("M", [1, 5])
+def test_lm_head_bf16(M, full):
+    """The precision ladder's BF16 lm_head rung: bf16 weights, no scales."""
+    sh = synth.GEMMA4_26B_A4B if full else synth.TINY
+    W = synth.lm_head_bf16(sh, DEV if full else "cpu", seed=4)
+    Wh = synth.bits16(W)
+    for sub in range(50):
+        x = synth.hidden_inputs(sh, M, 60, sub, tag="lmbf")
+        tok, ml, gap = oracle.lm_head_argmax_bf16(synth.bits16(x), Wh)
+        if (gap >= TAU).all():
+            break
+    wsb = native.lm_head_argmax_workspace(M, sh.hidden, sh.vocab)
+    ws = native.workspace(wsb)
+    t = torch.empty(M, dtype=torch.int32, device=DEV)
+    mlg = torch.empty(M, dtype=torch.float32, device=DEV)
+    native.lm_head_argmax_bf16(M, sh.hidden, sh.vocab, x.to(DEV), W.to(DEV), t, mlg, ws, wsb)
+    torch.cuda.synchronize()
+    assert (t.cpu().numpy() == tok).all()
+    np.testing.assert_allclose(mlg.cpu().numpy(), ml, rtol=1e-5, atol=1e-6)
+
+
 def test_spec_accept_all_patterns():
     rng = np.random.default_rng(0)
     for gamma in range(8):

@@ -21,33 +21,40 @@ def say(*a):
     print(*a, flush=True)
 
 
-def make(shape, seed=0, expert_dtype="fp8", router_bias=None):
+def make(shape, seed=0, expert_dtype="fp8", router_bias=None, lm_bf16=False):
     layers = [synth.layer_weights(shape, l, "cpu", seed=seed, tag="fused", expert_dtype=expert_dtype,
                                   router_bias=router_bias) for l in range(shape.layers)]
     host = [synth.weights_to_host(w) for w in layers]
     gains = synth.rmsnorm_gains(shape, seed=seed)
-    Q, s = synth.lm_head(shape, seed=seed)
+    if lm_bf16:   # the BF16 lm_head rung: bf16 weights, no scales (s stays None)
+        Q, s = synth.lm_head_bf16(shape, seed=seed), None
+    else:
+        Q, s = synth.lm_head(shape, seed=seed)
     dev = [to_device(w) for w in layers]
     return layers, host, gains, Q, s, dev
 
 
 def oracle_step(shape, host, gains, Q, s, M, step):
+    lm_bf16 = Q.dtype == torch.bfloat16
     for sub in range(60):
         x = synth.hidden_inputs(shape, M, step, sub)
         noise = synth.stack_noise(shape, M, step, sub)
         res = oracle.stack_step(synth.bits16(x), host, synth.bits16(noise), synth.bits16(gains),
-                                synth.bytes8(Q), synth.f32(s), shape.top_k)
+                                synth.bits16(Q) if lm_bf16 else synth.bytes8(Q), None if lm_bf16 else synth.f32(s),
+                                shape.top_k, lm_bf16=lm_bf16)
         if stack_decisions_unambiguous(res):
             return x, noise, res
     raise RuntimeError("no unambiguous input")
 
 
-def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None, cooperative=False):
-    layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias)
+def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None, cooperative=False,
+                  lm_bf16=False):
+    layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias, lm_bf16)
     x, noise, res = oracle_step(shape, host, gains, Q, s, M, step)
     drafts = synth.drafts(res["tok"], 0.7, shape.vocab, step)
     n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
-    fs = FusedDecodeStep(shape, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8, cooperative=cooperative)
+    fs = FusedDecodeStep(shape, dev, gains.to(DEV), Q.to(DEV), None if s is None else s.to(DEV), max_M=8,
+                         cooperative=cooperative)
     dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV) if M > 1 else None
     fs.step(x.to(DEV), noise.to(DEV), dd, M)
     torch.cuda.synchronize()
@@ -76,6 +83,15 @@ def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bi
 def test_fused_step_tiny(L, M):
     say("fused tiny L=%d M=%d" % (L, M))
     run_and_check(synth.TINY.with_(layers=L), M, step=10 * L + M, what="L=%d M=%d" % (L, M))
+
+
+@pytest.mark.parametrize("experts", ["fp8", "bf16"])
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_step_bf16_lm_head(M, experts):
+    """The precision ladder's BF16 rungs: a bf16 lm_head (no scales), with FP8 or bf16 experts."""
+    say("fused bf16 lm_head M=%d experts %s" % (M, experts))
+    run_and_check(FUSED_VARIANTS["h2816"], M, step=70 + M, seed=8, what="bf16 lm_head M=%d" % M,
+                  expert_dtype=experts, lm_bf16=True)
 
 
 @pytest.mark.parametrize("M", [1, 5, 8])

@@ -582,3 +582,27 @@ def test_fp8_expert_and_lm_head_bytes():
     assert budget.lm_head_bytes(sh.vocab, sh.hidden) == 739_246_080
     assert abs(budget.expected_unique(128, 8, 5) - 35.30) < 0.01
     assert abs(budget.expected_unique(128, 8, 8) - 51.62) < 0.01
+
+
+# --------------------------------------------------- bf16 lm_head (ladder rung)
+
+def test_lm_head_bf16_vs_numpy_and_planted_winner():
+    sh = synth.TINY
+    W = synth.bits16(synth.lm_head_bf16(sh, seed=3))
+    x = synth.bits16(synth.hidden_inputs(sh, 3, 0))
+    tok, ml, gap = oracle.lm_head_argmax_bf16(x, W)
+    lg = bf16_np(x) @ bf16_np(W).T                      # independent dense evaluation
+    assert (tok == lg.argmax(axis=1)).all()
+    np.testing.assert_allclose(ml, lg.max(axis=1), rtol=1e-12)
+    srt = np.sort(lg, axis=1)
+    np.testing.assert_allclose(gap, srt[:, -1] - srt[:, -2], rtol=1e-9, atol=1e-12)
+    # a planted winner: x equal to row 1234 scaled up, and a duplicate row resolves to the lower id
+    W2 = W.copy()
+    W2[3000] = W2[1234]
+    xp = W2[1234:1235].copy()
+    tok2, _, _ = oracle.lm_head_argmax_bf16(xp, W2)
+    assert tok2[0] == 1234
+    # the bf16 draws are the FP8 rung's draws before quantisation
+    Q, s = synth.lm_head(sh, seed=3)
+    deq = FP8_TABLE[synth.bytes8(Q)] * synth.f32(s)[:, None].astype(np.float64)
+    assert np.abs(deq - bf16_np(W)).max() < 0.1 * np.abs(bf16_np(W)).max()
