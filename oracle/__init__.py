@@ -78,6 +78,12 @@ def lib():
             L.oracle_spec_sample.restype = I
             L.oracle_spec_sample.argtypes = [I, I, P, ctypes.c_double, P, P, P, ctypes.c_uint64,
                                              ctypes.c_uint64, P, P, P]
+            L.oracle_gemv_fp8.restype = None
+            L.oracle_gemv_fp8.argtypes = [I, I, P, P, P, P]
+            L.oracle_dense_mlp.restype = None
+            L.oracle_dense_mlp.argtypes = [I, I, P, P, P, P, P, P, P, P]
+            L.oracle_bf16_round_n.restype = None
+            L.oracle_bf16_round_n.argtypes = [I, P, P]
             L.oracle_num_threads.restype = I
             L.oracle_num_threads.argtypes = []
             L.oracle_set_num_threads.restype = None
@@ -262,6 +268,86 @@ def spec_sample(logits, T, draft, q, u_acc, seed, step):
     n = lib().oracle_spec_sample(M, V, _p(logits), float(T), _p(draft), _p(q), _p(u), int(seed), int(step),
                                  _p(out), _p(am), _p(sm))
     return n, out, am[:g], float(sm[0])
+
+
+def gemv_fp8(Q, s, x):
+    """Q uint8 [N][K] FP8, s f32 [N], x uint16 bf16 [K] -> fp64 [N]."""
+    Q = _c(Q, np.uint8)
+    s = _c(s, np.float32)
+    x = _c(x, np.uint16)
+    N, K = Q.shape
+    out = np.empty(N, np.float64)
+    lib().oracle_gemv_fp8(N, K, _p(Q), _p(s), _p(x), _p(out))
+    return out
+
+
+def dense_mlp(u, G, U, Dn, sg, su, sd):
+    """u uint16 [H]; G, U uint8 [F][H]; Dn uint8 [H][F]; scales f32 -> fp64 [H]."""
+    u = _c(u, np.uint16)
+    G, U, Dn = _c(G, np.uint8), _c(U, np.uint8), _c(Dn, np.uint8)
+    sg, su, sd = _c(sg, np.float32), _c(su, np.float32), _c(sd, np.float32)
+    F, H = G.shape
+    out = np.empty(H, np.float64)
+    lib().oracle_dense_mlp(H, F, _p(u), _p(G), _p(U), _p(Dn), _p(sg), _p(su), _p(sd), _p(out))
+    return out
+
+
+def bf16_round_n(v):
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_bf16_round_n(v.size, _p(v), _p(out))
+    return out
+
+
+def draft_step(tok0, hidden0, head, target_Q, target_s, gamma, eps=1e-6):
+    """The MTP drafter's step, gamma drafts in sequence (page "LLM decoding", "The one-line
+    shape bug that disabled the model's own drafter": the head's pre_projection takes 5632 =
+    2 x 2816 inputs, the target's 2816-wide embedding of the token and a 2816-wide hidden
+    state, down to its 1024-wide width; the head has its own 1024-wide embedding table;
+    "Lever 2": a 430M head proposes the tokens the target then verifies). The rest of the
+    head is not on the page; the reading taken (the body sized so the head holds about 430M
+    parameters) is, per draft i = 1..gamma from the previous token t and hidden g:
+        e   = bf16(s_t * dec(Q_target[t]))                 the target's (tied) embedding row
+        z   = bf16(pre_proj([e | g]))                      5632 -> 1024
+        for each block b: u = rmsnorm(z; g_b), z = bf16(z + mlp_b(u))      width 1024
+        zf  = rmsnorm(z; g_final)
+        d_i = argmax_v table(zf)[v]                        the head's own 262144 x 1024 table
+        g   = bf16(post_proj(zf))                          1024 -> 2816, the next draft's hidden
+    head: dict of numpy arrays (FP8 codes uint8, scales f32, gains bf16 uint16):
+        pre_w [1024][5632], pre_s; blocks: list of dict(gain, gate_w, gate_s, up_w, up_s,
+        down_w, down_s); final_gain; table_w [V][1024], table_s; post_w [2816][1024], post_s.
+    Returns dict(drafts int32 [gamma], gaps f64 [gamma] (the argmax margins), z [gamma][1024],
+    g [gamma][2816])."""
+    t = int(tok0)
+    g = np.ascontiguousarray(hidden0, np.uint16)
+    H = g.shape[0]
+    drafts, gaps, zs, gs = [], [], [], []
+    dec = _fp8_values()
+    for i in range(gamma):
+        e = bf16_round_n(float(target_s[t]) * dec[target_Q[t]])
+        x = np.concatenate([e, g])
+        z = bf16_round_n(gemv_fp8(head["pre_w"], head["pre_s"], x))
+        for b in head["blocks"]:
+            _, u = add_rmsnorm(z[None, :], np.zeros_like(z)[None, :], None, b["gain"], eps)
+            y = dense_mlp(u[0], b["gate_w"], b["up_w"], b["down_w"], b["gate_s"], b["up_s"], b["down_s"])
+            z = bf16_round_n(_bf16_values(z) + y)
+        _, zf = add_rmsnorm(z[None, :], np.zeros_like(z)[None, :], None, head["final_gain"], eps)
+        tok, _, gap = lm_head_argmax(zf, head["table_w"], head["table_s"])
+        t = int(tok[0])
+        g = bf16_round_n(gemv_fp8(head["post_w"], head["post_s"], zf[0]))
+        drafts.append(t)
+        gaps.append(float(gap[0]))
+        zs.append(z)
+        gs.append(g)
+    return {"drafts": np.array(drafts, np.int32), "gaps": np.array(gaps), "z": np.array(zs), "g": np.array(gs)}
+
+
+def _fp8_values():
+    return np.array([fp8_e4m3(c) for c in range(256)], np.float64)
+
+
+def _bf16_values(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def add_rmsnorm(h, a0, a1, g, eps=1e-6):

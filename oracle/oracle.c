@@ -410,6 +410,43 @@ int oracle_spec_accept(int gamma, const int32_t *draft, const int32_t *target, i
     return n;
 }
 
+/* ------------------------------------------------------------ drafter step */
+
+/*
+ * A dense FP8 matrix-vector product with per-row scales (the drafter's projections):
+ *   out[n] = s[n] * sum_c Q[n][c] x[c]        Q row-major [N][K] FP8, x bf16 [K]
+ */
+void oracle_gemv_fp8(int N, int K, const uint8_t *Q, const float *s, const uint16_t *x, double *out)
+{
+    int n;
+    fp8_tab_init();
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int c = 0; c < K; ++c)
+            acc += fp8(Q[(size_t)n * K + c]) * oracle_bf16(x[c]);
+        out[n] = (double)s[n] * acc;
+    }
+}
+
+/* A dense GELU-gated MLP on one bf16 vector (the drafter's blocks): the expert routine
+ * above with FP8 weights, o = down(gelu_tanh(gate u) * (up u)), fp64. */
+void oracle_dense_mlp(int H, int F, const uint16_t *u, const uint8_t *G, const uint8_t *U, const uint8_t *Dn,
+                      const float *sg, const float *su, const float *sd, double *o)
+{
+    double *hbuf = malloc(sizeof(double) * (size_t)F);
+    fp8_tab_init();
+    expert_apply(H, F, 0, u, G, U, Dn, sg, su, sd, hbuf, o);
+    free(hbuf);
+}
+
+/* Round n doubles to bf16 (oracle_bf16_round element by element). */
+void oracle_bf16_round_n(int n, const double *v, uint16_t *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = oracle_bf16_round(v[i]);
+}
+
 /* --------------------------------------------- stochastic speculative acceptance */
 
 /*

@@ -171,6 +171,55 @@ def lm_head_bf16(shape: Shape, device="cpu", seed: int = 0, tag: str = "lm_head"
     return out
 
 
+@dataclasses.dataclass(frozen=True)
+class DraftShape:
+    """The MTP drafter head (page 'LLM decoding', "The one-line shape bug that disabled the
+    model's own drafter": a 5632 = 2 x 2816 -> 1024 pre_projection and a 1024-wide own
+    embedding table; "Lever 2": a 430M head). The body's depth and width are a reading: 12
+    GELU-gated MLP blocks of width 4096, so the head holds about 430M parameters."""
+    hidden: int = 2816      # the target's width (embedding and hidden state)
+    width: int = 1024       # the head's width
+    ffn: int = 4096         # the blocks' inner width
+    blocks: int = 12
+    vocab: int = 262144
+
+    def params(self) -> int:
+        D, F, H, V = self.width, self.ffn, self.hidden, self.vocab
+        return D * 2 * H + self.blocks * 3 * D * F + V * D + H * D
+
+
+MTP_HEAD = DraftShape()
+TINY_HEAD = DraftShape(hidden=256, width=128, ffn=256, blocks=2, vocab=1024)
+
+
+def draft_head(shape: DraftShape, device="cpu", seed: int = 0, tag: str = "mtp") -> dict:
+    """The drafter head's weights: FP8 codes with per-row fp32 scales (N(0, 0.02) draws
+    quantised like the experts) and bf16 RMSNorm gains N(1, 0.1) ([blocks + 1][width], the
+    last the final norm's). Block matrices are stacked: gate_w, up_w [blocks][ffn][width],
+    down_w [blocks][width][ffn]."""
+    D, F, H, V, B = shape.width, shape.ffn, shape.hidden, shape.vocab, shape.blocks
+    out = {}
+    out["pre_w"], out["pre_s"] = _fp8_matrix((D, 2 * H), EXPERT_STD, device, seed, tag, "pre")
+    out["gate_w"], out["gate_s"] = _fp8_matrix((B, F, D), EXPERT_STD, device, seed, tag, "gate")
+    out["up_w"], out["up_s"] = _fp8_matrix((B, F, D), EXPERT_STD, device, seed, tag, "up")
+    out["down_w"], out["down_s"] = _fp8_matrix((B, D, F), EXPERT_STD, device, seed, tag, "down")
+    out["table_w"], out["table_s"] = _fp8_matrix((V, D), LM_HEAD_STD, device, seed, tag, "table")
+    out["post_w"], out["post_s"] = _fp8_matrix((H, D), EXPERT_STD, device, seed, tag, "post")
+    out["gains"] = normal((B + 1, D), GAIN_STD, device, seed, tag, "gain", mean=GAIN_MEAN).to(torch.bfloat16)
+    return out
+
+
+def draft_head_to_host(w: dict, shape: DraftShape) -> dict:
+    """The layout oracle.draft_step takes: numpy arrays, blocks as a list of dicts."""
+    h = {k: (bytes8(v) if v.dtype == torch.uint8 else (bits16(v) if v.dtype == torch.bfloat16 else f32(v)))
+         for k, v in w.items()}
+    blocks = [{"gain": h["gains"][b], "gate_w": h["gate_w"][b], "gate_s": h["gate_s"][b], "up_w": h["up_w"][b],
+               "up_s": h["up_s"][b], "down_w": h["down_w"][b], "down_s": h["down_s"][b]}
+              for b in range(shape.blocks)]
+    return {"pre_w": h["pre_w"], "pre_s": h["pre_s"], "blocks": blocks, "final_gain": h["gains"][shape.blocks],
+            "table_w": h["table_w"], "table_s": h["table_s"], "post_w": h["post_w"], "post_s": h["post_s"]}
+
+
 def hidden_inputs(shape: Shape, M: int, step: int, sub: int = 0, device="cpu",
                   seed: int = 0, tag: str = "x") -> torch.Tensor:
     """M fresh bf16 hidden vectors N(0, 1) for one decode step (sub: resample index)."""
