@@ -280,6 +280,51 @@ int moe_decode_step_status(const moe_step_desc *desc, void *workspace) {
     return step_status(step_ws(*desc), (char *)workspace);
 }
 
+static int check_draft_desc(const moe_draft_desc *d) {
+    if (!d) return MOE_EINVAL;
+    if (d->hidden < 256 || d->hidden > kMaxHidden || d->hidden % 256) return MOE_EINVAL;
+    if (d->width < 256 || d->width > 4096 || d->width % 256) return MOE_EINVAL;
+    if (d->ffn < 256 || d->ffn > 16384 || d->ffn % 256) return MOE_EINVAL;
+    if (d->blocks < 0 || d->blocks > 64) return MOE_EINVAL;
+    if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
+    if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+size_t moe_draft_step_workspace(const moe_draft_desc *desc) {
+    if (check_draft_desc(desc) != MOE_OK) return 0;
+    return draft_ws(*desc).total;
+}
+
+int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int gamma, const int32_t *tok0,
+                   const uint16_t *hidden0, const uint8_t *emb_w, const float *emb_s, int32_t *drafts,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    CHECK(check_draft_desc(desc));
+    if (!w || gamma < 1 || gamma > kMaxM - 1) return MOE_EINVAL;
+    CHECK(need(w->pre_w));
+    CHECK(need(w->pre_s));
+    if (desc->blocks > 0) {
+        CHECK(need(w->gate_w));
+        CHECK(need(w->gate_s));
+        CHECK(need(w->up_w));
+        CHECK(need(w->up_s));
+        CHECK(need(w->down_w));
+        CHECK(need(w->down_s));
+    }
+    CHECK(need(w->gains));
+    CHECK(need(w->table_w));
+    CHECK(need(w->table_s));
+    CHECK(need(w->post_w));
+    CHECK(need(w->post_s));
+    CHECK(need(hidden0));
+    CHECK(need(emb_w));
+    CHECK(need(emb_s));
+    if (!tok0 || !drafts) return MOE_EINVAL;
+    if (((uintptr_t)tok0 | (uintptr_t)drafts) & 3u) return MOE_EALIGN;
+    if (!ws_ok(workspace, workspace_bytes, draft_ws(*desc).total)) return MOE_EWORKSPACE;
+    return launch_draft_step(*desc, *w, gamma, tok0, hidden0, emb_w, emb_s, drafts, (char *)workspace, stream);
+}
+
 int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,
                    void *stream) {
     if (n < 4 || n > (1 << 20) || n % 4) return MOE_EINVAL;

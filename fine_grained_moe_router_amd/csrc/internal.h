@@ -94,6 +94,25 @@ inline SampleWs sample_ws(int M, int V) {
 }
 constexpr int kSampleMaxVocab = 1 << 24;
 
+// Workspace of moe_draft_step: the concatenated input, the head's vector and its norm,
+// the next hidden state, the blocks' inner vector, the argmax's per-workgroup bests.
+struct DraftWs {
+    size_t x, z, zf, g, h, lm, total;
+};
+inline DraftWs draft_ws(const moe_draft_desc &d) {
+    DraftWs W{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+    W.x = take(2 * 2 * (size_t)d.hidden);
+    W.z = take(2 * (size_t)d.width);
+    W.zf = take(2 * (size_t)d.width);
+    W.g = take(2 * (size_t)d.hidden);
+    W.h = take(4 * (size_t)d.ffn);
+    W.lm = take(lm_ws_bytes(1, d.vocab));
+    W.total = o;
+    return W;
+}
+
 // Static scratch of lm_head_argmax_noalloc: the workspace of the largest call (M = 8,
 // the full lm_head grid), 128 KiB.
 constexpr size_t kLmNoallocScratch = 2 * (size_t)kLmMaxWG * kMaxM * 4;
@@ -206,6 +225,9 @@ int launch_spec_sample(int M, int V, float inv_t, const int32_t *draft, const fl
                        const SampleWs &L, char *ws, void *stream);
 int launch_lm_head_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *w, int32_t *token, float *max_logit,
                         char *ws, void *stream);
+int launch_draft_step(const moe_draft_desc &d, const moe_draft_weights &w, int gamma, const int32_t *tok0,
+                      const uint16_t *hidden0, const uint8_t *emb_w, const float *emb_s, int32_t *drafts,
+                      char *ws, void *stream);
 int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                            int32_t *token, float *max_logit, void *stream);
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,

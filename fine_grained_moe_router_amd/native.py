@@ -24,7 +24,7 @@ EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_s
            "lm_head_argmax", "lm_head_argmax_bf16", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
            "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
-           "moe_hbm_read_probe", "moe_strerror")
+           "moe_hbm_read_probe", "moe_draft_step_workspace", "moe_draft_step", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -55,6 +55,16 @@ class StepDesc(ctypes.Structure):
 
 MOE_STEP_COOPERATIVE = 1
 MOE_STEP_LM_BF16 = 2
+
+
+class DraftDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int), ("width", ctypes.c_int), ("ffn", ctypes.c_int), ("blocks", ctypes.c_int),
+                ("vocab", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
+class DraftWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("pre_w", "pre_s", "gate_w", "gate_s", "up_w", "up_s", "down_w", "down_s", "gains",
+                                  "table_w", "table_s", "post_w", "post_s")]
 
 
 def lib() -> ctypes.CDLL:
@@ -101,6 +111,11 @@ def lib() -> ctypes.CDLL:
         L.moe_decode_step.argtypes = [ctypes.POINTER(StepDesc), I] + [_P] * 14 + [_P, S, _P]
         L.moe_decode_step_status.restype = I
         L.moe_decode_step_status.argtypes = [ctypes.POINTER(StepDesc), _P]
+        L.moe_draft_step_workspace.restype = S
+        L.moe_draft_step_workspace.argtypes = [ctypes.POINTER(DraftDesc)]
+        L.moe_draft_step.restype = I
+        L.moe_draft_step.argtypes = [ctypes.POINTER(DraftDesc), ctypes.POINTER(DraftWeights), I, _P, _P, _P, _P, _P,
+                                     _P, S, _P]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_strerror.argtypes = [I]
         _lib = L
@@ -256,3 +271,25 @@ def moe_decode_step_status(desc: StepDesc, workspace) -> int:
 def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     """A zeroed device buffer of nbytes (torch allocations are 256-byte aligned)."""
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def draft_desc(shape, eps: float = 1e-6) -> DraftDesc:
+    return DraftDesc(shape.hidden, shape.width, shape.ffn, shape.blocks, shape.vocab, eps)
+
+
+def draft_weights(w: dict) -> DraftWeights:
+    """DraftWeights from a dict of device tensors (keys as synth.draft_head)."""
+    return DraftWeights(*[_ptr(w[k]) for k in ("pre_w", "pre_s", "gate_w", "gate_s", "up_w", "up_s", "down_w",
+                                                "down_s", "gains", "table_w", "table_s", "post_w", "post_s")])
+
+
+def moe_draft_step_workspace(desc: DraftDesc) -> int:
+    return lib().moe_draft_step_workspace(ctypes.byref(desc))
+
+
+def moe_draft_step(desc: DraftDesc, weights: DraftWeights, gamma, tok0, hidden0, emb_w, emb_s, drafts, workspace,
+                   workspace_bytes, stream=None):
+    st = lib().moe_draft_step(ctypes.byref(desc), ctypes.byref(weights), int(gamma), _ptr(tok0), _ptr(hidden0),
+                              _ptr(emb_w), _ptr(emb_s), _ptr(drafts), _ptr(workspace), int(workspace_bytes),
+                              _stream(stream))
+    _check("moe_draft_step", st)

@@ -371,6 +371,58 @@ int moe_decode_step(const moe_step_desc *desc, int M, const uint16_t *gains,
  */
 int moe_decode_step_status(const moe_step_desc *desc, void *workspace);
 
+/* ------------------------------------------------------------------------------
+ * The MTP drafter's step (page "LLM decoding", "The one-line shape bug that disabled the
+ * model's own drafter": a pre_projection from 5632 = 2 x 2816 inputs, the target's
+ * embedding of the token and a hidden state, down to the head's 1024-wide width, and the
+ * head's own 1024-wide embedding table; "Lever 2: fewer passes": a 430M head proposes the
+ * tokens the target verifies). The head's body is not on the page; the reading taken is a
+ * stack of dense GELU-gated blocks at the head's width (pre-RMSNorm, residual), a final
+ * RMSNorm, the head's own table for the draft's argmax, and a post-projection back to the
+ * target's width for the next draft's hidden state. Per draft i = 1..gamma, from the
+ * previous token t (t_0 = *tok0) and hidden state g (g_0 = hidden0):
+ *   e   = bf16(emb_s[t] * decode(emb_w[t]))                 (the product exact, one rounding)
+ *   z   = bf16(pre_w [e | g])                                [width] from [2 hidden]
+ *   for b < blocks: u = rmsnorm(z; gains[b]), z = bf16(z + down_b(gelu_tanh(gate_b u) * up_b u))
+ *   zf  = rmsnorm(z; gains[blocks]);  drafts[i-1] = argmax_v table_s[v] (table_w[v] . zf)
+ *   g   = bf16(post_w zf)                                    [hidden], for the next draft
+ * Every matrix is FP8 E4M3FN with per-row fp32 scales applied after the dot product; the
+ * argmax breaks ties to the lower id. The drafted tokens stay on the device (each draft
+ * reads the previous one from `drafts`), so the call is asynchronous and capturable.
+ * ---------------------------------------------------------------------------- */
+typedef struct moe_draft_desc {
+    int hidden;   /* the target's width (2816): a multiple of 256, at most 4096            */
+    int width;    /* the head's width (1024): a multiple of 256, at most 4096               */
+    int ffn;      /* the blocks' inner width: a multiple of 256, at most 16384              */
+    int blocks;   /* 0..64                                                                  */
+    int vocab;    /* a multiple of 64, 64..2^30                                             */
+    float eps;    /* RMSNorm epsilon, >= 0                                                  */
+} moe_draft_desc;
+
+typedef struct moe_draft_weights {     /* device pointers, 16-byte aligned                  */
+    const uint8_t *pre_w;   const float *pre_s;    /* [width][2 hidden], [width]            */
+    const uint8_t *gate_w;  const float *gate_s;   /* [blocks][ffn][width], [blocks][ffn]   */
+    const uint8_t *up_w;    const float *up_s;     /* [blocks][ffn][width], [blocks][ffn]   */
+    const uint8_t *down_w;  const float *down_s;   /* [blocks][width][ffn], [blocks][width] */
+    const uint16_t *gains;                         /* bf16 [blocks + 1][width]              */
+    const uint8_t *table_w; const float *table_s;  /* [vocab][width], [vocab]               */
+    const uint8_t *post_w;  const float *post_s;   /* [hidden][width], [hidden]             */
+} moe_draft_weights;
+
+/* Bytes of workspace moe_draft_step needs (0 if desc is invalid). */
+size_t moe_draft_step_workspace(const moe_draft_desc *desc);
+
+/*
+ * gamma drafts (1..7) of the head above. tok0 int32 [1] and hidden0 bf16 [hidden] are
+ * device arrays (the target's last token and its hidden state); emb_w FP8 [vocab][hidden]
+ * with emb_s fp32 [vocab] is the target's tied embedding table (the lm_head); drafts
+ * int32 [gamma]. Asynchronous on `stream`, one short chain of launches per draft.
+ */
+int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int gamma,
+                   const int32_t *tok0, const uint16_t *hidden0, const uint8_t *emb_w,
+                   const float *emb_s, int32_t *drafts, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
 /* A static string describing a moe_status value. */
 const char *moe_strerror(int status);
 

@@ -189,7 +189,7 @@ class DraftShape:
 
 
 MTP_HEAD = DraftShape()
-TINY_HEAD = DraftShape(hidden=256, width=128, ffn=256, blocks=2, vocab=1024)
+TINY_HEAD = DraftShape(hidden=256, width=256, ffn=512, blocks=2, vocab=1024)
 
 
 def draft_head(shape: DraftShape, device="cpu", seed: int = 0, tag: str = "mtp") -> dict:

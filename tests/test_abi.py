@@ -195,6 +195,30 @@ def test_spec_sample_validation():
     assert L.lm_head_spec_sample(*args(wsb=ws - 1)) == native.MOE_EWORKSPACE
 
 
+def test_draft_step_validation():
+    import synth
+    L = native.lib()
+    good = native.draft_desc(synth.MTP_HEAD)
+    wsb = native.moe_draft_step_workspace(good)
+    assert wsb > 0
+    for k, v in (("hidden", 100), ("width", 128), ("ffn", 0), ("blocks", 65), ("vocab", 100), ("eps", -1.0)):
+        d = native.draft_desc(synth.MTP_HEAD)
+        setattr(d, k, v)
+        assert native.moe_draft_step_workspace(d) == 0, k
+    w = native.DraftWeights(*([FAKE] * 13))
+    args = lambda **o: [o.get(k, v) for k, v in (
+        ("d", ctypes.byref(good)), ("w", ctypes.byref(w)), ("g", 4), ("t", FAKE), ("h", FAKE), ("e", FAKE),
+        ("s", FAKE), ("out", FAKE), ("ws", FAKE), ("wsb", wsb), ("st", None))]
+    assert L.moe_draft_step(*args(g=0)) == native.MOE_EINVAL
+    assert L.moe_draft_step(*args(g=8)) == native.MOE_EINVAL
+    assert L.moe_draft_step(*args(t=None)) == native.MOE_EINVAL
+    assert L.moe_draft_step(*args(h=FAKE + 2)) == native.MOE_EALIGN
+    assert L.moe_draft_step(*args(out=FAKE + 2)) == native.MOE_EALIGN
+    assert L.moe_draft_step(*args(wsb=wsb - 1)) == native.MOE_EWORKSPACE
+    wbad = native.DraftWeights(*([FAKE] * 12 + [None]))
+    assert L.moe_draft_step(*args(w=ctypes.byref(wbad))) == native.MOE_EINVAL
+
+
 def test_spec_accept_validation():
     L = native.lib()
     assert L.spec_accept(-1, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL

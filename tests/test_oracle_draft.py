@@ -41,7 +41,7 @@ def test_gemv_and_mlp_vs_numpy():
     w = synth.draft_head(synth.TINY_HEAD, seed=1)
     h = synth.draft_head_to_host(w, synth.TINY_HEAD)
     b = h["blocks"][0]
-    u = rne(rng.normal(size=128))
+    u = rne(rng.normal(size=256))
     G = FP8[b["gate_w"]] * b["gate_s"][:, None]
     U = FP8[b["up_w"]] * b["up_s"][:, None]
     Dn = FP8[b["down_w"]] * b["down_s"][:, None]
