@@ -106,6 +106,9 @@ def parse():
     ap.add_argument("--sample", action="store_true",
                     help="the verify step's lm_head with stochastic acceptance instead (lm_head_spec_sample, "
                          "M=5, temperature 0.7, 2 rotated lm_head copies; its own JSON line)")
+    ap.add_argument("--draft", action="store_true",
+                    help="the MTP drafter step instead (moe_draft_step, 4 drafts of the 430M head), timed beside the "
+                         "fused verify step, with the drafter tax and modelled tokens/s (its own JSON line)")
     ap.add_argument("--ladder", action="store_true",
                     help="the precision ladder instead: the stack at M=1 and M=5 for FP8/bf16 experts x FP8/bf16 "
                          "lm_head, with tokens/s modelled from the acceptance rate (its own JSON line)")
@@ -142,6 +145,8 @@ def main():
         return sample_main(args)
     if args.ladder:
         return ladder_main(args)
+    if args.draft:
+        return draft_main(args)
     if args.layer:
         return layer_main(args)
     import synth
@@ -612,6 +617,104 @@ def sample_main(args):
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": int(bps),
                      "avg_launch_us": round(ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def draft_bytes(hs) -> int:
+    """Weight bytes one draft reads: the FP8 matrices with their row scales, the gains and the
+    target embedding row (the head's 262,144-row table dominates)."""
+    D, F, H, V, B = hs.width, hs.ffn, hs.hidden, hs.vocab, hs.blocks
+    return ((D * 2 * H + 4 * D) + B * (3 * D * F + 4 * (2 * F + D)) + (B + 1) * D * 2 + (V * D + 4 * V) +
+            (H * D + 4 * H) + (H + 4))
+
+
+def draft_main(args):
+    """The MTP drafter's step (moe_draft_step): gamma = 4 drafts of the 430M head, each chained on
+    the previous one on the device, graph-captured in groups of 10 steps; timed beside the fused
+    verify step (M = 5) and plain decoding (M = 1) of the 30-layer stack in the same process.
+    Reports the drafter tax (drafter time / verify time) and tokens/s = E[n+1] / (t_verify +
+    t_draft) at acceptance rates from the page (39 % on random prompts, 87 % and 94 % on
+    coherent text)."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import native
+    from fine_grained_moe_router_amd.stack import FusedDecodeStep
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    hs, gamma, K, W = synth.MTP_HEAD, 4, args.steps, args.warmup
+    sh = synth.GEMMA4_26B_A4B.with_(layers=args.layers)
+    head = synth.draft_head(hs, dev, seed=args.seed)
+    Q, s = synth.lm_head(sh, dev, seed=args.seed)
+    desc = native.draft_desc(hs)
+    dw = native.draft_weights(head)
+    wsb = native.moe_draft_step_workspace(desc)
+    ws = native.workspace(wsb)
+    n = K + W
+    g0 = [synth.hidden_inputs(sh, 1, i, device=dev, seed=args.seed, tag="draft_g")[0].contiguous() for i in range(n)]
+    t0 = torch.randint(0, sh.vocab, (n, 1), generator=torch.Generator().manual_seed(args.seed),
+                       dtype=torch.int32).to(dev)
+    drafts = torch.zeros(n, gamma, dtype=torch.int32, device=dev)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+
+    def launch(i):
+        native.moe_draft_step(desc, dw, gamma, t0[i], g0[i], Q, s, drafts[i], ws, wsb, stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(W):
+            launch(i)
+        torch.cuda.synchronize()
+        graphs = []
+        for c0 in range(W, n, 10):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=stream):
+                for i in range(c0, min(n, c0 + 10)):
+                    launch(i)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for gr in graphs:
+            gr.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms_draft = e0.elapsed_time(e1) / K
+    del graphs
+    bpd = draft_bytes(hs)
+    gbs = gamma * bpd / (ms_draft / 1e3) / 1e9
+    log("drafter step (%d drafts): %.1f us (%.1f us per draft), %.1f GB/s over %.1f MB per draft" % (
+        gamma, ms_draft * 1e3, ms_draft * 1e3 / gamma, gbs, bpd / 1e6))
+    layers = [synth.layer_weights(sh, l, dev, seed=args.seed, tag="stack") for l in range(sh.layers)]
+    gains = synth.rmsnorm_gains(sh, dev, seed=args.seed)
+    runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=5)
+    ver = {M: measure(args, runner, sh, M) for M in (1, 5)}
+    t1, t5 = ver[1]["ms_per_step"], ver[5]["ms_per_step"]
+    model = {}
+    for alpha in (0.39, 0.87, 0.94):
+        e = expected_emitted(alpha, gamma)
+        model["alpha%.2f" % alpha] = {"emitted_per_step": round(e, 3), "tokens_per_s": round(e / ((t5 + ms_draft) / 1e3), 1),
+                                      "tokens_per_s_without_drafter": round(e / (t5 / 1e3), 1)}
+    line = {
+        "metric": "MTP drafter step (4 drafts of a 430M head) and the drafter tax beside the verify step",
+        "value": round(1e3 / ms_draft, 2), "unit": "drafter steps/s (4 drafts each)", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_draft, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 weights x bf16 activations, fp32 accumulate",
+        "data": "synthetic (seeded FP8 head: pre_projection 5632->1024, 12 GELU-gated blocks 1024->4096->1024, "
+                "own 262144x1024 table, post-projection 1024->2816)",
+        "config": {"workload": "MTP drafter, 4 chained drafts per step (embedding row + pre_projection + 12 blocks + "
+                               "norm + 262144-row argmax + post-projection each)", "hidden": hs.hidden,
+                   "width": hs.width, "ffn": hs.ffn, "blocks": hs.blocks, "vocab": hs.vocab, "params": hs.params()},
+        "us_per_draft": round(ms_draft * 1e3 / gamma, 2), "bytes_per_draft": bpd, "hbm_gbs": round(gbs, 1),
+        "verify_step_ms_M5": round(t5, 4), "plain_step_ms_M1": round(t1, 4),
+        "drafter_tax": round(ms_draft / t5, 4),
+        "tokens_per_s_plain": round(1e3 / t1, 1),
+        "tokens_per_s_spec": model,
+        "roofline": {"bound": "hbm", "kernel": "moe_draft_step (30 launches per draft)", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gamma * bpd, "avg_launch_us": round(ms_draft * 1e3, 2)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -288,6 +288,7 @@ static int check_draft_desc(const moe_draft_desc *d) {
     if (d->blocks < 0 || d->blocks > 64) return MOE_EINVAL;
     if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
     if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    if (!draft_splits(*d)) return MOE_EINVAL;
     return MOE_OK;
 }
 

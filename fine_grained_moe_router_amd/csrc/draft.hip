@@ -8,19 +8,22 @@
 // 1024-wide embedding table; "Lever 2": a 430M head proposes the tokens the target then
 // verifies in one pass. The rest of the head is a reading: a body of dense GELU-gated
 // blocks (pre-RMSNorm, residual) and a post-projection back to 2816 for the next draft.
-// Per draft:
-//   k_draft_embed   e = bf16(s_t * dec(Q[t])) (the product exact in fp64, one rounding),
-//                   x = [e | g]
-//   k_draft_gemv    z = bf16(pre_proj x)
+// Per draft (every kernel issues its weight loads first, so the weight stream overlaps
+// the wait for the vector it multiplies):
+//   k_draft_pre     x = [e | g], e = bf16(s_t * dec(E[t])) (the product exact in fp64, one
+//                   rounding), z = bf16(pre_proj x)
 //   per block       k_draft_gateup (u = rmsnorm(z; g_b) per workgroup, h = gelu(gate u) * up u)
 //                   k_draft_down   (z = bf16(z + down h))
-//   k_draft_norm    zf = rmsnorm(z; g_final)
+//   k_draft_post    zf = rmsnorm(z; g_final) per workgroup, g = bf16(post_proj zf) for the
+//                   next draft (k_draft_norm, zf alone, after the last)
 //   lm_head argmax  over the head's own table -> the draft
-//   k_draft_gemv    g = bf16(post_proj zf)
 // Every matrix is FP8 with per-row fp32 scales; arithmetic is fp32 (FP8 and bf16 products
-// are exact), the vectors between stages bf16 (h stays fp32).
+// are exact), the vectors between stages bf16 (h stays fp32). A matrix of N rows of K
+// codes is read by 16, 32 or 64 lanes per row, as many as give the launch 256 workgroups.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -29,8 +32,6 @@ namespace moe {
 namespace {
 
 using namespace dev;
-
-constexpr int kDraftRows = 16;   // output rows per workgroup: one per 16-lane group
 
 // bf16 (round to nearest even) of a double that is a product of an fp32 and an FP8 value
 // (at most 28 significant bits, normal range): round the mantissa at bit 45 in the integer
@@ -42,108 +43,208 @@ __device__ __forceinline__ uint16_t d2bf(double d) {
     return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)b)) >> 16);
 }
 
-// x = [bf16(s_t * dec(Q[t])) | g], t = *tok (the target's tied embedding row of the token)
-__global__ __launch_bounds__(256) void k_draft_embed(const int32_t *tok, const uint8_t *emb_w, const float *emb_s,
-                                                     const uint16_t *g, uint16_t *x, int H, int V) {
+// A workgroup's rows of an FP8 matrix [N][K] (K a multiple of 16 LPR): LPR lanes per row,
+// 256 / LPR rows per workgroup; lane li of a row's group holds the row's 16-byte pieces
+// li, li + LPR, ... (ch = K / (16 LPR) <= MAXCH of them). load() issues every piece at
+// once, ahead of the vector-dependent work, so the weight stream overlaps it.
+template <int LPR, int MAXCH>
+struct Pieces {
+    uint4 q[MAXCH];
+    __device__ __forceinline__ void load(const uint8_t *row, int li, int ch) {
+#pragma unroll
+        for (int k = 0; k < MAXCH; ++k)
+            if (k < ch) q[k] = *reinterpret_cast<const uint4 *>(row + (size_t)(k * LPR + li) * 16);
+    }
+    // sum_c dec(Q[c]) x[c] over this lane's pieces, x bf16 in LDS (two uint4 per piece)
+    __device__ __forceinline__ float dot_bf16(const uint4 *xs, int li, int ch) const {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < MAXCH; ++k)
+            if (k < ch) {
+                bf16x2 w[8];
+                decode16_bf16(q[k], w);
+                const int p = (k * LPR + li) * 2;
+                acc = dot16(w, xs[p], xs[p + 1], acc);
+            }
+        return acc;
+    }
+    // the same with an fp32 vector in LDS (four float4 per piece)
+    __device__ __forceinline__ float dot_f32(const float4 *hs, int li, int ch) const {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < MAXCH; ++k)
+            if (k < ch) {
+                const uint32_t qw[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+                const float4 *hp = hs + (k * LPR + li) * 4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x2 lo = fp8x2_to_f32<false>(qw[u]), hi = fp8x2_to_f32<true>(qw[u]);
+                    const float4 hv = hp[u];
+                    acc = fmaf(lo.x, hv.x, acc);
+                    acc = fmaf(lo.y, hv.y, acc);
+                    acc = fmaf(hi.x, hv.z, acc);
+                    acc = fmaf(hi.y, hv.w, acc);
+                }
+            }
+        return acc;
+    }
+};
+
+// Sum over a row's LPR lanes (aligned groups of a wave); every lane of the group gets it.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+    v = row16_sum(v);
+    if (LPR >= 32) v += __shfl_xor(v, 16);
+    if (LPR >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Copy n 16-byte words from global memory into LDS, four words a thread at a time: the
+// four loads are issued before the first store, so they are in flight together.
+__device__ __forceinline__ void stage16(uint4 *dst, const uint4 *src, int n) {
+    for (int b = threadIdx.x; b < n; b += 1024) {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = src[min(b + 256 * i, n - 1)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (b + 256 * i < n) dst[b + 256 * i] = v[i];
+    }
+}
+
+// z = bf16(pre_proj [e | g]), e = bf16(s_t * dec(E[t])) (the target's tied embedding row of
+// t = *tok, the product exact in fp64 and rounded once), g the hidden state.
+template <int LPR, int MAXCH>
+__global__ __launch_bounds__(256) void k_draft_pre(const int32_t *tok, const uint8_t *emb_w, const float *emb_s,
+                                                   const uint16_t *g, const uint8_t *Q, const float *s, uint16_t *z,
+                                                   int H, int V) {
+    extern __shared__ uint4 xs[];   // [2H / 8]
+    const int tid = threadIdx.x, li = tid & (LPR - 1), n = blockIdx.x * (256 / LPR) + tid / LPR;
+    const int K = 2 * H, ch = K / (16 * LPR);
+    Pieces<LPR, MAXCH> w;
+    w.load(Q + (size_t)n * K, li, ch);
     int t = *tok;
     t = t < 0 ? 0 : (t >= V ? V - 1 : t);
-    const double s = (double)emb_s[t];
-    for (int c = threadIdx.x; c < H; c += 256) {
-        const float dv = fp8x2_to_f32<false>((uint32_t)emb_w[(size_t)t * H + c]).x;
-        x[c] = d2bf(s * (double)dv);
-        x[H + c] = g[c];
-    }
-}
-
-// out[n] = bf16(s[n] * sum_c dec(Q[n][c]) x[c]) for rows n of this workgroup; lane li of
-// group r reads 16 bytes of every 256-column chunk of row 16 b + r, x in LDS.
-__global__ __launch_bounds__(256) void k_draft_gemv(const uint8_t *Q, const float *s, const uint16_t *x,
-                                                    uint16_t *out, int N, int K) {
-    extern __shared__ uint4 xs[];   // [K / 8]
-    const int tid = threadIdx.x;
-    for (int i = tid; i < K / 8; i += 256) xs[i] = reinterpret_cast<const uint4 *>(x)[i];
-    __syncthreads();
-    const int li = tid & 15, n = blockIdx.x * kDraftRows + (tid >> 4);
-    const uint8_t *wr = Q + (size_t)n * K + li * 16;
-    float acc = 0.0f;
-    for (int k = 0; k < K / 256; ++k) {
-        bf16x2 wv[8];
-        decode16_bf16(*reinterpret_cast<const uint4 *>(wr + (size_t)k * 256), wv);
-        acc = dot16(wv, xs[(k * 256 + li * 16) / 8], xs[(k * 256 + li * 16) / 8 + 1], acc);
-    }
-    acc = row16_sum(acc);
-    if (li == 0 && n < N) out[n] = f2bf(s[n] * acc);
-}
-
-// rmsnorm of one bf16 vector of D (a multiple of 256) elements into LDS, in the fixed order
-// of k_add_rmsnorm: per-thread sums, DPP rows, the rows of a wave, then the waves.
-__device__ __forceinline__ void rmsnorm_lds(const uint16_t *z, const uint16_t *gain, int D, float eps, uint16_t *u) {
-    __shared__ float wsum[4];
-    float ss = 0.0f;
-    for (int c = threadIdx.x; c < D; c += 256) {
-        const float v = bf2f(z[c]);
-        ss = fmaf(v, v, ss);
-    }
-    ss = row16_sum(ss);
-    ss += __shfl_xor(ss, 16);
-    ss += __shfl_xor(ss, 32);
-    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)D + eps);
-    for (int c = threadIdx.x; c < D; c += 256) u[c] = f2bf(bf2f(z[c]) * r * bf2f(gain[c]));
-    __syncthreads();
-}
-
-// h[j] = gelu_tanh(sg[j] (G_j . u)) * (su[j] (U_j . u)), u = rmsnorm(z; gain), rows j of
-// this workgroup (one per 16-lane group), the D columns in 256-column chunks.
-__global__ __launch_bounds__(256) void k_draft_gateup(const uint8_t *G, const float *sg, const uint8_t *U,
-                                                      const float *su, const uint16_t *z, const uint16_t *gain,
-                                                      float eps, float *h, int F, int D) {
-    extern __shared__ uint4 us[];   // [D / 8]
-    rmsnorm_lds(z, gain, D, eps, reinterpret_cast<uint16_t *>(us));
-    const int tid = threadIdx.x, li = tid & 15, j = blockIdx.x * kDraftRows + (tid >> 4);
-    const uint8_t *gr = G + (size_t)j * D + li * 16, *ur = U + (size_t)j * D + li * 16;
-    float ag = 0.0f, au = 0.0f;
-    for (int k = 0; k < D / 256; ++k) {
-        const uint4 x0 = us[(k * 256 + li * 16) / 8], x1 = us[(k * 256 + li * 16) / 8 + 1];
-        bf16x2 wg[8], wu[8];
-        decode16_bf16(*reinterpret_cast<const uint4 *>(gr + (size_t)k * 256), wg);
-        decode16_bf16(*reinterpret_cast<const uint4 *>(ur + (size_t)k * 256), wu);
-        ag = dot16(wg, x0, x1, ag);
-        au = dot16(wu, x0, x1, au);
-    }
-    ag = row16_sum(ag);
-    au = row16_sum(au);
-    if (li == 0 && j < F) h[j] = gelu_tanh(sg[j] * ag) * (su[j] * au);
-}
-
-// z[c] = bf16(z[c] + sd[c] (Dn_c . h)) for rows c of this workgroup, h fp32 [F] in LDS;
-// lane li reads 16 codes of every 256-column chunk of the row.
-__global__ __launch_bounds__(256) void k_draft_down(const uint8_t *Dn, const float *sd, const float *h, uint16_t *z,
-                                                    int D, int F) {
-    extern __shared__ float4 hs[];   // [F / 4]
-    const int tid = threadIdx.x;
-    for (int i = tid; i < F / 4; i += 256) hs[i] = reinterpret_cast<const float4 *>(h)[i];
-    __syncthreads();
-    const int li = tid & 15, c = blockIdx.x * kDraftRows + (tid >> 4);
-    const uint8_t *dr = Dn + (size_t)c * F + li * 16;
-    float acc = 0.0f;
-    for (int k = 0; k < F / 256; ++k) {
-        const uint4 q = *reinterpret_cast<const uint4 *>(dr + (size_t)k * 256);
+    // thread c < H / 16: codes 16 c .. 16 c + 15 of the row, two uint4 of e
+    const bool emb = tid < H / 16;
+    uint4 q = {0u, 0u, 0u, 0u};
+    if (emb) q = reinterpret_cast<const uint4 *>(emb_w + (size_t)t * H)[tid];
+    const double st = (double)emb_s[t];
+    stage16(xs + H / 8, reinterpret_cast<const uint4 *>(g), H / 8);
+    if (emb) {
         const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-        const float4 *hp = hs + (k * 256 + li * 16) / 4;
+        uint32_t e[8];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const f32x2 lo = fp8x2_to_f32<false>(qw[u]), hi = fp8x2_to_f32<true>(qw[u]);
-            const float4 hv = hp[u];
-            acc = fmaf(lo.x, hv.x, acc);
-            acc = fmaf(lo.y, hv.y, acc);
-            acc = fmaf(hi.x, hv.z, acc);
-            acc = fmaf(hi.y, hv.w, acc);
+            e[2 * u] = (uint32_t)d2bf(st * (double)lo.x) | ((uint32_t)d2bf(st * (double)lo.y) << 16);
+            e[2 * u + 1] = (uint32_t)d2bf(st * (double)hi.x) | ((uint32_t)d2bf(st * (double)hi.y) << 16);
         }
+        xs[2 * tid] = make_uint4(e[0], e[1], e[2], e[3]);
+        xs[2 * tid + 1] = make_uint4(e[4], e[5], e[6], e[7]);
     }
-    acc = row16_sum(acc);
-    if (li == 0 && c < D) z[c] = f2bf(bf2f(z[c]) + sd[c] * acc);
+    __syncthreads();
+    const float acc = group_sum<LPR>(w.dot_bf16(xs, li, ch));
+    if (li == 0) z[n] = f2bf(s[n] * acc);
+}
+
+// u = bf16(z * r * gain), r = 1 / sqrt(mean(z^2) + eps), for one bf16 vector of D (a
+// multiple of 256, at most 4096) elements, into LDS. z and the gain are read once, eight
+// elements a thread at a time; the sum of squares goes per thread in element order, then
+// over each 16-lane row, the wave and the four waves in a fixed order.
+__device__ __forceinline__ void rmsnorm_lds(const uint16_t *z, const uint16_t *gain, int D, float eps, uint16_t *u) {
+    __shared__ float wsum[4];
+    constexpr int MAXV = 2;
+    const int tid = threadIdx.x, nv = D / 8;
+    uint4 zv[MAXV], gv[MAXV];
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+        if (tid + 256 * i < nv) {
+            zv[i] = reinterpret_cast<const uint4 *>(z)[tid + 256 * i];
+            gv[i] = reinterpret_cast<const uint4 *>(gain)[tid + 256 * i];
+        }
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+        if (tid + 256 * i < nv) {
+            const uint32_t zw[4] = {zv[i].x, zv[i].y, zv[i].z, zv[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float a = bf2f(zw[k] & 0xffffu), b = bf2f(zw[k] >> 16);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        }
+    ss = row16_sum(ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+    __syncthreads();
+    const float r = rsqrtf(((wsum[0] + wsum[1]) + (wsum[2] + wsum[3])) / (float)D + eps);
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+        if (tid + 256 * i < nv) {
+            const uint32_t zw[4] = {zv[i].x, zv[i].y, zv[i].z, zv[i].w};
+            const uint32_t gw[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                o[k] = (uint32_t)f2bf(bf2f(zw[k] & 0xffffu) * r * bf2f(gw[k] & 0xffffu)) |
+                       ((uint32_t)f2bf(bf2f(zw[k] >> 16) * r * bf2f(gw[k] >> 16)) << 16);
+            reinterpret_cast<uint4 *>(u)[tid + 256 * i] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+    __syncthreads();
+}
+
+// h[j] = gelu_tanh(sg[j] (G_j . u)) * (su[j] (U_j . u)), u = rmsnorm(z; gain) (each
+// workgroup forms it in LDS while its gate and up pieces are in flight).
+template <int LPR, int MAXCH>
+__global__ __launch_bounds__(256) void k_draft_gateup(const uint8_t *G, const float *sg, const uint8_t *U,
+                                                      const float *su, const uint16_t *z, const uint16_t *gain,
+                                                      float eps, float *h, int D) {
+    extern __shared__ uint4 us[];   // [D / 8]
+    const int tid = threadIdx.x, li = tid & (LPR - 1), j = blockIdx.x * (256 / LPR) + tid / LPR;
+    const int ch = D / (16 * LPR);
+    Pieces<LPR, MAXCH> wg, wu;
+    wg.load(G + (size_t)j * D, li, ch);
+    wu.load(U + (size_t)j * D, li, ch);
+    rmsnorm_lds(z, gain, D, eps, reinterpret_cast<uint16_t *>(us));
+    const float ag = group_sum<LPR>(wg.dot_bf16(us, li, ch));
+    const float au = group_sum<LPR>(wu.dot_bf16(us, li, ch));
+    if (li == 0) h[j] = gelu_tanh(sg[j] * ag) * (su[j] * au);
+}
+
+// z[c] = bf16(z[c] + sd[c] (Dn_c . h)), h fp32 [F] in LDS.
+template <int LPR, int MAXCH>
+__global__ __launch_bounds__(256) void k_draft_down(const uint8_t *Dn, const float *sd, const float *h, uint16_t *z,
+                                                    int F) {
+    extern __shared__ float4 hs[];   // [F / 4]
+    const int tid = threadIdx.x, li = tid & (LPR - 1), c = blockIdx.x * (256 / LPR) + tid / LPR;
+    const int ch = F / (16 * LPR);
+    Pieces<LPR, MAXCH> w;
+    w.load(Dn + (size_t)c * F, li, ch);
+    stage16(reinterpret_cast<uint4 *>(hs), reinterpret_cast<const uint4 *>(h), F / 4);
+    __syncthreads();
+    const float acc = group_sum<LPR>(w.dot_f32(hs, li, ch));
+    if (li == 0) z[c] = f2bf(bf2f(z[c]) + sd[c] * acc);
+}
+
+// g = bf16(post_proj zf), zf = rmsnorm(z; final gain) formed by each workgroup in LDS;
+// workgroup 0 also stores zf for the table's argmax.
+template <int LPR, int MAXCH>
+__global__ __launch_bounds__(256) void k_draft_post(const uint8_t *P, const float *s, const uint16_t *z,
+                                                    const uint16_t *gain, float eps, uint16_t *zf, uint16_t *g,
+                                                    int D) {
+    extern __shared__ uint4 us[];   // [D / 8]
+    const int tid = threadIdx.x, li = tid & (LPR - 1), n = blockIdx.x * (256 / LPR) + tid / LPR;
+    const int ch = D / (16 * LPR);
+    Pieces<LPR, MAXCH> w;
+    w.load(P + (size_t)n * D, li, ch);
+    rmsnorm_lds(z, gain, D, eps, reinterpret_cast<uint16_t *>(us));
+    if (blockIdx.x == 0)
+        for (int i = tid; i < D / 8; i += 256) reinterpret_cast<uint4 *>(zf)[i] = us[i];
+    const float acc = group_sum<LPR>(w.dot_bf16(us, li, ch));
+    if (li == 0) g[n] = f2bf(s[n] * acc);
 }
 
 __global__ __launch_bounds__(256) void k_draft_norm(const uint16_t *z, const uint16_t *gain, float eps, uint16_t *zf,
@@ -156,6 +257,17 @@ __global__ __launch_bounds__(256) void k_draft_norm(const uint16_t *z, const uin
 
 inline hipStream_t S(void *p) { return reinterpret_cast<hipStream_t>(p); }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// f(IC<lpr>) for a lanes-per-row value from draft_lpr
+template <class F>
+void by_lpr(int lpr, F f) {
+    if (lpr == 16) f(IC<16>{});
+    else if (lpr == 32) f(IC<32>{});
+    else f(IC<64>{});
+}
+
 }  // namespace
 
 int launch_draft_step(const moe_draft_desc &d, const moe_draft_weights &w, int gamma, const int32_t *tok0,
@@ -163,34 +275,51 @@ int launch_draft_step(const moe_draft_desc &d, const moe_draft_weights &w, int g
                       char *ws, void *stream) {
     (void)hipGetLastError();
     const int H = d.hidden, D = d.width, F = d.ffn, B = d.blocks, V = d.vocab;
+    const int l_pre = draft_lpr(D, 2 * H, kDraftMaxCh), l_gu = draft_lpr(F, D, kDraftGateUpMaxCh),
+              l_dn = draft_lpr(D, F, kDraftMaxCh), l_post = draft_lpr(H, D, kDraftMaxCh);
+    if (!l_pre || !l_gu || !l_dn || !l_post) return MOE_EINVAL;
     const DraftWs W = draft_ws(d);
-    uint16_t *x = reinterpret_cast<uint16_t *>(ws + W.x);
     uint16_t *z = reinterpret_cast<uint16_t *>(ws + W.z);
     uint16_t *zf = reinterpret_cast<uint16_t *>(ws + W.zf);
     uint16_t *g = reinterpret_cast<uint16_t *>(ws + W.g);
     float *h = reinterpret_cast<float *>(ws + W.h);
     char *lmws = ws + W.lm;
+    hipStream_t st = S(stream);
     for (int i = 0; i < gamma; ++i) {
         const int32_t *tok = i == 0 ? tok0 : drafts + i - 1;
-        hipLaunchKernelGGL(k_draft_embed, dim3(1), dim3(256), 0, S(stream), tok, emb_w, emb_s, i == 0 ? hidden0 : g,
-                           x, H, V);
-        hipLaunchKernelGGL(k_draft_gemv, dim3(D / kDraftRows), dim3(256), (size_t)2 * H * 2, S(stream), w.pre_w,
-                           w.pre_s, x, z, D, 2 * H);
+        const uint16_t *gi = i == 0 ? hidden0 : g;
+        by_lpr(l_pre, [&](auto L) {
+            constexpr int lpr = decltype(L)::value;
+            hipLaunchKernelGGL((k_draft_pre<lpr, kDraftMaxCh>), dim3(D * lpr / 256), dim3(256), (size_t)4 * H, st,
+                               tok, emb_w, emb_s, gi, w.pre_w, w.pre_s, z, H, V);
+        });
         for (int b = 0; b < B; ++b) {
-            hipLaunchKernelGGL(k_draft_gateup, dim3(F / kDraftRows), dim3(256), (size_t)D * 2, S(stream),
-                               w.gate_w + (size_t)b * F * D, w.gate_s + (size_t)b * F, w.up_w + (size_t)b * F * D,
-                               w.up_s + (size_t)b * F, z, w.gains + (size_t)b * D, d.eps, h, F, D);
-            hipLaunchKernelGGL(k_draft_down, dim3(D / kDraftRows), dim3(256), (size_t)F * 4, S(stream),
-                               w.down_w + (size_t)b * D * F, w.down_s + (size_t)b * D, h, z, D, F);
+            by_lpr(l_gu, [&](auto L) {
+                constexpr int lpr = decltype(L)::value;
+                hipLaunchKernelGGL((k_draft_gateup<lpr, kDraftGateUpMaxCh>), dim3(F * lpr / 256), dim3(256),
+                                   (size_t)D * 2, st, w.gate_w + (size_t)b * F * D, w.gate_s + (size_t)b * F,
+                                   w.up_w + (size_t)b * F * D, w.up_s + (size_t)b * F, z, w.gains + (size_t)b * D,
+                                   d.eps, h, D);
+            });
+            by_lpr(l_dn, [&](auto L) {
+                constexpr int lpr = decltype(L)::value;
+                hipLaunchKernelGGL((k_draft_down<lpr, kDraftMaxCh>), dim3(D * lpr / 256), dim3(256), (size_t)F * 4,
+                                   st, w.down_w + (size_t)b * D * F, w.down_s + (size_t)b * D, h, z, F);
+            });
         }
-        hipLaunchKernelGGL(k_draft_norm, dim3(1), dim3(256), (size_t)D * 2, S(stream), z, w.gains + (size_t)B * D,
-                           d.eps, zf, D);
-        if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;   // launch_lm_head clears the error state
-        const int st = launch_lm_head(1, D, V, zf, w.table_w, w.table_s, drafts + i, nullptr, lmws, stream);
-        if (st != MOE_OK) return st;
+        // the final norm, with the post-projection for the next draft's hidden state
         if (i + 1 < gamma)
-            hipLaunchKernelGGL(k_draft_gemv, dim3(H / kDraftRows), dim3(256), (size_t)D * 2, S(stream), w.post_w,
-                               w.post_s, zf, g, H, D);
+            by_lpr(l_post, [&](auto L) {
+                constexpr int lpr = decltype(L)::value;
+                hipLaunchKernelGGL((k_draft_post<lpr, kDraftMaxCh>), dim3(H * lpr / 256), dim3(256), (size_t)D * 2,
+                                   st, w.post_w, w.post_s, z, w.gains + (size_t)B * D, d.eps, zf, g, D);
+            });
+        else
+            hipLaunchKernelGGL(k_draft_norm, dim3(1), dim3(256), (size_t)D * 2, st, z, w.gains + (size_t)B * D,
+                               d.eps, zf, D);
+        if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;   // launch_lm_head clears the error state
+        const int rc = launch_lm_head(1, D, V, zf, w.table_w, w.table_s, drafts + i, nullptr, lmws, stream);
+        if (rc != MOE_OK) return rc;
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

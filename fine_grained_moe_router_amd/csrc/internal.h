@@ -96,14 +96,32 @@ constexpr int kSampleMaxVocab = 1 << 24;
 
 // Workspace of moe_draft_step: the concatenated input, the head's vector and its norm,
 // the next hidden state, the blocks' inner vector, the argmax's per-workgroup bests.
+// Lanes per row (16, 32 or 64) for a drafter matrix of N rows (a multiple of 256) of K FP8
+// codes, each lane reading at most maxch 16-byte pieces of a row: the fewest lanes that
+// still give 256 workgroups of 256 threads, else the most workgroups; 0 when no split fits.
+constexpr int kDraftMaxCh = 16;       // pre_projection, down, post-projection pieces per lane
+constexpr int kDraftGateUpMaxCh = 8;  // gate and up pieces per lane (two rows per lane)
+inline int draft_lpr(int N, int K, int maxch) {
+    int best = 0;
+    for (int lpr = 16; lpr <= 64; lpr *= 2) {
+        if (K % (16 * lpr) || K / (16 * lpr) > maxch) continue;
+        best = lpr;
+        if ((long long)N * lpr / 256 >= 256) break;
+    }
+    return best;
+}
+inline bool draft_splits(const moe_draft_desc &d) {
+    return draft_lpr(d.width, 2 * d.hidden, kDraftMaxCh) && draft_lpr(d.ffn, d.width, kDraftGateUpMaxCh) &&
+           draft_lpr(d.width, d.ffn, kDraftMaxCh) && draft_lpr(d.hidden, d.width, kDraftMaxCh);
+}
+
 struct DraftWs {
-    size_t x, z, zf, g, h, lm, total;
+    size_t z, zf, g, h, lm, total;
 };
 inline DraftWs draft_ws(const moe_draft_desc &d) {
     DraftWs W{};
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
-    W.x = take(2 * 2 * (size_t)d.hidden);
     W.z = take(2 * (size_t)d.width);
     W.zf = take(2 * (size_t)d.width);
     W.g = take(2 * (size_t)d.hidden);

@@ -392,8 +392,10 @@ int moe_decode_step_status(const moe_step_desc *desc, void *workspace);
  * ---------------------------------------------------------------------------- */
 typedef struct moe_draft_desc {
     int hidden;   /* the target's width (2816): a multiple of 256, at most 4096            */
-    int width;    /* the head's width (1024): a multiple of 256, at most 4096               */
-    int ffn;      /* the blocks' inner width: a multiple of 256, at most 16384              */
+    int width;    /* the head's width (1024): a multiple of 256 up to 2048, or of 512 up
+                     to 4096                                                              */
+    int ffn;      /* the blocks' inner width: a multiple of 256 up to 4096, of 512 up to
+                     8192, or of 1024 up to 16384                                         */
     int blocks;   /* 0..64                                                                  */
     int vocab;    /* a multiple of 64, 64..2^30                                             */
     float eps;    /* RMSNorm epsilon, >= 0                                                  */

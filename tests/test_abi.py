@@ -201,10 +201,17 @@ def test_draft_step_validation():
     good = native.draft_desc(synth.MTP_HEAD)
     wsb = native.moe_draft_step_workspace(good)
     assert wsb > 0
-    for k, v in (("hidden", 100), ("width", 128), ("ffn", 0), ("blocks", 65), ("vocab", 100), ("eps", -1.0)):
+    for k, v in (("hidden", 100), ("width", 128), ("ffn", 0), ("blocks", 65), ("vocab", 100), ("eps", -1.0),
+                 ("width", 2304), ("width", 4352), ("ffn", 4352), ("ffn", 8704), ("ffn", 17408)):
         d = native.draft_desc(synth.MTP_HEAD)
         setattr(d, k, v)
-        assert native.moe_draft_step_workspace(d) == 0, k
+        assert native.moe_draft_step_workspace(d) == 0, (k, v)
+    # the largest splits: 32 lanes per gate/up row at width 4096, 64 lanes per down row
+    for k, v in (("width", 2048), ("width", 2560), ("width", 4096), ("ffn", 4096), ("ffn", 4608), ("ffn", 8192),
+                 ("ffn", 9216), ("ffn", 16384), ("hidden", 4096), ("hidden", 256)):
+        d = native.draft_desc(synth.MTP_HEAD)
+        setattr(d, k, v)
+        assert native.moe_draft_step_workspace(d) > 0, (k, v)
     w = native.DraftWeights(*([FAKE] * 13))
     args = lambda **o: [o.get(k, v) for k, v in (
         ("d", ctypes.byref(good)), ("w", ctypes.byref(w)), ("g", 4), ("t", FAKE), ("h", FAKE), ("e", FAKE),

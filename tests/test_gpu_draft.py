@@ -50,6 +50,21 @@ def test_draft_step_tiny(seed):
     assert (d == r["drafts"]).all(), (d, r["drafts"])
 
 
+# Shapes that make each kernel read its rows with 16, 32 and 64 lanes per row somewhere in
+# the set (pre_projection, gate/up, down, post-projection): the full-size head takes
+# 32/16/64/32, TINY_HEAD 32/16/32/16, and these:
+SPLIT_SHAPES = [synth.DraftShape(hidden=512, width=2048, ffn=1024, blocks=1, vocab=2048),    # 32/64/32/64
+                synth.DraftShape(hidden=256, width=4096, ffn=2048, blocks=1, vocab=1024),    # 16/32/16/64
+                synth.DraftShape(hidden=1024, width=256, ffn=8192, blocks=1, vocab=1024)]    # 64/16/64/16
+
+
+@pytest.mark.parametrize("hs", SPLIT_SHAPES, ids=lambda h: "h%d_w%d_f%d" % (h.hidden, h.width, h.ffn))
+def test_draft_step_row_splits(hs):
+    say("drafter %s" % (hs,))
+    d, r = run_case(hs, synth.TINY.with_(hidden=hs.hidden, vocab=hs.vocab), 7)
+    assert (d == r["drafts"]).all(), (d, r["drafts"])
+
+
 def test_draft_step_mtp_head_full_size():
     """The 430M head at the Gemma-4-26B-A4B shape: 2816-wide target, 1024-wide head, 12 blocks,
     262,144-row tables."""
