@@ -84,6 +84,13 @@ def lib():
             L.oracle_dense_mlp.argtypes = [I, I, P, P, P, P, P, P, P, P]
             L.oracle_bf16_round_n.restype = None
             L.oracle_bf16_round_n.argtypes = [I, P, P]
+            L.oracle_fp8_from_f32.restype = ctypes.c_uint8
+            L.oracle_fp8_from_f32.argtypes = [ctypes.c_float]
+            L.oracle_fp8_quant_row.restype = None
+            L.oracle_fp8_quant_row.argtypes = [I, P, P, P]
+            L.oracle_attn_decode.restype = I
+            L.oracle_attn_decode.argtypes = [I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, I, P, P, P, P, P, P,
+                                             P, P, P]
             L.oracle_num_threads.restype = I
             L.oracle_num_threads.argtypes = []
             L.oracle_set_num_threads.restype = None
@@ -398,3 +405,68 @@ def stack_step(x, layers, noise, gains, lm_w, lm_s, K, eps=1e-6, draft=None, lm_
         out["accepted"] = n
         out["out_tokens"] = acc
     return out
+
+
+def fp8_from_f32(v):
+    """E4M3FN code (round to nearest even, saturating at 448) of one fp32 value."""
+    return int(lib().oracle_fp8_from_f32(float(np.float32(v))))
+
+
+def fp8_quant_rows(x):
+    """The FP8 KV cache's quantiser over the last axis: x uint16 bf16 bits [..., n] ->
+    (codes uint8 [..., n], scales f32 [...]), each row scale max|x| / 448 (fp32)."""
+    x = _c(x, np.uint16)
+    n = x.shape[-1]
+    rows = x.reshape(-1, n)
+    codes = np.empty(rows.shape, np.uint8)
+    scales = np.empty(rows.shape[0], np.float32)
+    L = lib()
+    for i in range(rows.shape[0]):
+        r = np.ascontiguousarray(rows[i])
+        sc = np.empty(1, np.float32)
+        cd = np.empty(n, np.uint8)
+        L.oracle_fp8_quant_row(n, _p(r), _p(cd), _p(sc))
+        codes[i] = cd
+        scales[i] = sc[0]
+    return codes.reshape(x.shape), scales.reshape(x.shape[:-1])
+
+
+def decode_kv(keys, kv_fp8):
+    """Cached keys as the attention reads them, fp64: keys uint16 bf16 bits [..., dh] as
+    written into the cache; for an FP8 cache each row is quantised and decoded
+    (decode(code) * scale)."""
+    keys = _c(keys, np.uint16)
+    if not kv_fp8:
+        return _bf16_values(keys)
+    codes, scales = fp8_quant_rows(keys)
+    return _fp8_values()[codes] * scales.astype(np.float64)[..., None]
+
+
+def attn_decode(u, w, shape, M, pos, hist_keys, h0=0):
+    """One attention layer of the decode step (oracle_attn_decode).
+    u uint16 [M][H]; w: host dict q_w, q_s, k_w, k_s, o_w, o_s; shape with hidden, q_heads,
+    kv_heads, head_dim, window, kv_fp8; hist_keys uint16 bf16 bits [pos - h0][kv_heads][head_dim],
+    the keys written into the cache for positions h0 .. pos - 1 (decoded here as the cache
+    holds them). Returns q, k (bf16 bits), k_codes / k_scales (FP8 cache), o (fp64), o_bf16,
+    out (fp64), out_bf16."""
+    u = _c(u, np.uint16)
+    H, nq, nkv, dh = shape.hidden, shape.q_heads, shape.kv_heads, shape.head_dim
+    fp8 = int(bool(shape.kv_fp8))
+    hk = np.asarray(hist_keys, np.uint16).reshape(pos - h0, nkv, dh)
+    hist = np.ascontiguousarray(decode_kv(hk, fp8).transpose(1, 0, 2), np.float64)   # [nkv][pos - h0][dh]
+    NQ, NK = nq * dh, nkv * dh
+    q = np.empty((M, NQ), np.uint16)
+    k = np.empty((M, NK), np.uint16)
+    kc = np.zeros((M, nkv, dh), np.uint8)
+    ksc = np.zeros((M, nkv), np.float32)
+    o = np.empty((M, NQ), np.float64)
+    ob = np.empty((M, NQ), np.uint16)
+    out = np.empty((M, H), np.float64)
+    outb = np.empty((M, H), np.uint16)
+    W = {k_: _c(v, np.uint8 if v.dtype == np.uint8 else np.float32) for k_, v in w.items()}
+    rc = lib().oracle_attn_decode(M, H, nq, nkv, dh, shape.window, pos, fp8, _p(u), _p(W["q_w"]), _p(W["q_s"]),
+                                  _p(W["k_w"]), _p(W["k_s"]), _p(W["o_w"]), _p(W["o_s"]), h0, _p(hist), _p(q),
+                                  _p(k), _p(kc), _p(ksc), _p(o), _p(ob), _p(out), _p(outb))
+    if rc != 0:
+        raise ValueError("attn_decode: a position the tokens see lies below h0")
+    return {"q": q, "k": k, "k_codes": kc, "k_scales": ksc, "o": o, "o_bf16": ob, "out": out, "out_bf16": outb}

@@ -596,6 +596,179 @@ int oracle_spec_sample(int M, int V, const double *logits, double T, const int32
     return n;
 }
 
+/* --------------------------------------------------------- attention decode */
+
+/*
+ * E4M3FN code of an fp32 value, the FP8 KV cache's quantiser ([LLMD] "Lever 1" and "What
+ * we learned": an FP8 KV cache halves the KV reads): the nearest representable value, ties
+ * to the even mantissa, magnitudes from 448 up saturating to 448 (0x7E), NaN to 0x7F.
+ * Written from the format: below 2^-6 the values are m 2^-9 (m = 0..7); above, 2^E (1 +
+ * m/8) with E = -6..8 and m = 0..7 except m = 7 at E = 8. Both scalings are exact powers of
+ * two and the rounding is the default round-to-nearest-even, so the result is a function
+ * of the fp32 input alone.
+ */
+static uint8_t fp8_code_rne(float v)
+{
+    if (v != v)
+        return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const float a = fabsf(v);
+    if (a >= 448.0f)
+        return sign | 0x7E;
+    if (a < 0.015625f) {
+        const int m = (int)nearbyintf(a * 512.0f);
+        return sign | (uint8_t)m;             /* m == 8 is 0x08: the smallest normal, 2^-6 */
+    }
+    int e;
+    (void)frexpf(a, &e);                      /* a = f 2^e, f in [0.5, 1) */
+    int E = e - 1;
+    int r = (int)nearbyintf(ldexpf(a, 3 - E));  /* in [8, 16] */
+    if (r == 16) {
+        r = 8;
+        E += 1;
+    }
+    if (E > 8 || (E == 8 && r > 14))
+        return sign | 0x7E;
+    return sign | (uint8_t)(((E + 7) << 3) | (r - 8));
+}
+
+uint8_t oracle_fp8_from_f32(float v) { return fp8_code_rne(v); }
+
+/*
+ * One row of the FP8 KV cache (one position of one KV head): scale = max_i |x_i| / 448 in
+ * fp32, code_i = fp8_code_rne(x_i / scale) with an fp32 division; a row of zeros has scale
+ * 0 and codes 0. The decoded value is decode(code) * scale.
+ */
+void oracle_fp8_quant_row(int n, const uint16_t *x, uint8_t *codes, float *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i)
+        amax = fmaxf(amax, fabsf((float)oracle_bf16(x[i])));
+    const float s = amax / 448.0f;
+    *scale = s;
+    for (int i = 0; i < n; ++i)
+        codes[i] = s > 0.0f ? fp8_code_rne((float)oracle_bf16(x[i]) / s) : 0;
+}
+
+/*
+ * One attention layer of the decode step for M tokens at positions pos .. pos + M - 1
+ * ([LLMD] "The exact architecture": sliding-window and global layers, grouped-query
+ * attention; "Where the 7.36 GB goes": q, k and o projections, no v projection). Readings:
+ * the cached key is also the value; no positional rotation; scores scaled by
+ * 1/sqrt(dh); the vectors between stages are bf16 as elsewhere in the step.
+ *   q[m]   = bf16(qs * (Q_q u[m]))   [nq dh]        k[m] = bf16(ks * (Q_k u[m]))   [nkv dh]
+ *   the new key of head g at position pos + m: k[m][g dh ..] (bf16 cache) or its FP8 row
+ *   (oracle_fp8_quant_row) decoded (FP8 cache)
+ *   head h uses KV head g = h / (nq / nkv); token m sees positions p in [lo, pos + m],
+ *   lo = window > 0 ? max(0, pos + m - window + 1) : 0:
+ *     s_p = (q[m][h] . K_g[p]) / sqrt(dh), w = softmax(s), o[m][h] = sum_p w_p K_g[p]
+ *   o_bf16 = bf16(o); out[m] = os * (Q_o o_bf16[m]); out_bf16 = bf16(out)
+ * hist holds the decoded cached keys of positions h0 .. pos - 1, [nkv][pos - h0][dh]; every
+ * position a token sees below pos must be >= h0. Outputs: q_bf, k_bf (the projections),
+ * k_codes [M][nkv][dh] and k_scales [M][nkv] (FP8 cache only; may be NULL otherwise), o and
+ * o_bf [M][nq dh], out and out_bf [M][H]. Returns 0, or -1 if a needed position is below h0.
+ */
+int oracle_attn_decode(int M, int H, int nq, int nkv, int dh, int window, int pos, int kv_fp8,
+                       const uint16_t *u, const uint8_t *qw, const float *qs, const uint8_t *kw,
+                       const float *ks, const uint8_t *ow, const float *os, int h0, const double *hist,
+                       uint16_t *q_bf, uint16_t *k_bf, uint8_t *k_codes, float *k_scales, double *o,
+                       uint16_t *o_bf, double *out, uint16_t *out_bf)
+{
+    const int NQ = nq * dh, NK = nkv * dh, G = nq / nkv;
+    fp8_tab_init();
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *um = u + (size_t)m * H;
+        int r;
+#pragma omp parallel for schedule(static)
+        for (r = 0; r < NQ + NK; ++r) {
+            const uint8_t *row = r < NQ ? qw + (size_t)r * H : kw + (size_t)(r - NQ) * H;
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += fp8(row[c]) * oracle_bf16(um[c]);
+            if (r < NQ)
+                q_bf[(size_t)m * NQ + r] = oracle_bf16_round((double)qs[r] * acc);
+            else
+                k_bf[(size_t)m * NK + (r - NQ)] = oracle_bf16_round((double)ks[r - NQ] * acc);
+        }
+    }
+    /* the new keys as the cache holds them, decoded: [M][nkv][dh] */
+    double *newk = malloc(sizeof(double) * (size_t)M * NK);
+    for (int m = 0; m < M; ++m)
+        for (int g = 0; g < nkv; ++g) {
+            const uint16_t *kr = k_bf + (size_t)m * NK + (size_t)g * dh;
+            double *dst = newk + (size_t)m * NK + (size_t)g * dh;
+            if (kv_fp8) {
+                uint8_t *cd = k_codes + (size_t)m * NK + (size_t)g * dh;
+                float *sc = k_scales + (size_t)m * nkv + g;
+                oracle_fp8_quant_row(dh, kr, cd, sc);
+                for (int d = 0; d < dh; ++d)
+                    dst[d] = fp8(cd[d]) * (double)*sc;
+            } else {
+                for (int d = 0; d < dh; ++d)
+                    dst[d] = oracle_bf16(kr[d]);
+            }
+        }
+    const int span = pos + M;
+    double *sc = malloc(sizeof(double) * (size_t)span);
+    int bad = 0;
+    const double inv_sqrt = 1.0 / sqrt((double)dh);
+    for (int m = 0; m < M && !bad; ++m)
+        for (int h = 0; h < nq && !bad; ++h) {
+            const int g = h / G, pm = pos + m;
+            const int lo = window > 0 ? (pm - window + 1 > 0 ? pm - window + 1 : 0) : 0;
+            if (lo < pos && lo < h0) {
+                bad = 1;
+                break;
+            }
+            const uint16_t *qh = q_bf + (size_t)m * NQ + (size_t)h * dh;
+            double mx = -INFINITY;
+            for (int p = lo; p <= pm; ++p) {
+                const double *key = p < pos ? hist + ((size_t)g * (pos - h0) + (p - h0)) * dh
+                                            : newk + (size_t)(p - pos) * NK + (size_t)g * dh;
+                double acc = 0.0;
+                for (int d = 0; d < dh; ++d)
+                    acc += oracle_bf16(qh[d]) * key[d];
+                sc[p] = acc * inv_sqrt;
+                if (sc[p] > mx)
+                    mx = sc[p];
+            }
+            double z = 0.0;
+            for (int p = lo; p <= pm; ++p) {
+                sc[p] = exp(sc[p] - mx);
+                z += sc[p];
+            }
+            double *oh = o + (size_t)m * NQ + (size_t)h * dh;
+            for (int d = 0; d < dh; ++d)
+                oh[d] = 0.0;
+            for (int p = lo; p <= pm; ++p) {
+                const double *key = p < pos ? hist + ((size_t)g * (pos - h0) + (p - h0)) * dh
+                                            : newk + (size_t)(p - pos) * NK + (size_t)g * dh;
+                const double wgt = sc[p] / z;
+                for (int d = 0; d < dh; ++d)
+                    oh[d] += wgt * key[d];
+            }
+            for (int d = 0; d < dh; ++d)
+                o_bf[(size_t)m * NQ + (size_t)h * dh + d] = oracle_bf16_round(oh[d]);
+        }
+    free(sc);
+    free(newk);
+    if (bad)
+        return -1;
+    for (int m = 0; m < M; ++m) {
+        const uint16_t *om = o_bf + (size_t)m * NQ;
+        int c;
+#pragma omp parallel for schedule(static)
+        for (c = 0; c < H; ++c) {
+            double acc = 0.0;
+            for (int i = 0; i < NQ; ++i)
+                acc += fp8(ow[(size_t)c * NQ + i]) * oracle_bf16(om[i]);
+            out[(size_t)m * H + c] = (double)os[c] * acc;
+            out_bf[(size_t)m * H + c] = oracle_bf16_round(out[(size_t)m * H + c]);
+        }
+    }
+    return 0;
+}
+
 /* ----------------------------------------------------------- residual norm */
 
 /*

@@ -220,6 +220,63 @@ def draft_head_to_host(w: dict, shape: DraftShape) -> dict:
             "table_w": h["table_w"], "table_s": h["table_s"], "post_w": h["post_w"], "post_s": h["post_s"]}
 
 
+@dataclasses.dataclass(frozen=True)
+class AttnShape:
+    """One attention layer of the decode step (page 'LLM decoding', "The exact architecture":
+    25 sliding-window and 5 global layers, grouped-query attention; "Where the 7.36 GB goes":
+    q, k and o projections, about 966M parameters). The head counts and widths are the
+    reading that gives the page's count exactly: 16 query heads of 256 with 8 KV heads on
+    sliding layers, 16 query heads of 512 with 2 KV heads on global ones, the cached key
+    also the value. The 1024-position window is a reading too (the page gives none)."""
+    hidden: int = 2816
+    q_heads: int = 16
+    kv_heads: int = 8
+    head_dim: int = 256
+    window: int = 1024       # 0: global
+    capacity: int = 1032     # cache positions (a ring of window + 8 on sliding layers)
+    kv_fp8: bool = False
+
+    def params(self) -> int:
+        return self.hidden * (2 * self.q_heads * self.head_dim + self.kv_heads * self.head_dim)
+
+    def with_(self, **kw) -> "AttnShape":
+        return dataclasses.replace(self, **kw)
+
+
+GEMMA4_SLIDING = AttnShape()
+GEMMA4_GLOBAL = AttnShape(q_heads=16, kv_heads=2, head_dim=512, window=0, capacity=32768)
+GEMMA4_ATTN_LAYERS = [GEMMA4_GLOBAL if (l % 6) == 5 else GEMMA4_SLIDING for l in range(30)]   # 25 + 5, 5:1
+TINY_ATTN = AttnShape(hidden=256, q_heads=4, kv_heads=2, head_dim=64, window=16, capacity=24)
+KEY_STD = 1.0   # cached keys N(0, 1): the spread the projections give keys of normalised inputs
+
+
+def attn_weights(shape: AttnShape, device="cpu", seed: int = 0, tag: str = "attn", layer: int = 0) -> dict:
+    """FP8 q/k/o projections with per-row scales: q_w [nq dh][H], k_w [nkv dh][H],
+    o_w [H][nq dh], from N(0, 0.02) like the experts."""
+    H, NQ, NK = shape.hidden, shape.q_heads * shape.head_dim, shape.kv_heads * shape.head_dim
+    out = {}
+    out["q_w"], out["q_s"] = _fp8_matrix((NQ, H), EXPERT_STD, device, seed, tag, layer, "q")
+    out["k_w"], out["k_s"] = _fp8_matrix((NK, H), EXPERT_STD, device, seed, tag, layer, "k")
+    out["o_w"], out["o_s"] = _fp8_matrix((H, NQ), EXPERT_STD, device, seed, tag, layer, "o")
+    return out
+
+
+def kv_keys(shape: AttnShape, first_pos: int, n: int, device="cpu", seed: int = 0, tag: str = "kv",
+            layer: int = 0) -> torch.Tensor:
+    """Keys of positions first_pos .. first_pos + n - 1 as written into the cache: bf16
+    [n][kv_heads][head_dim], N(0, KEY_STD), drawn per position so a position's key does not
+    depend on n."""
+    out = torch.empty((n, shape.kv_heads, shape.head_dim), dtype=torch.bfloat16, device=device)
+    per = max(1, (1 << 24) // (shape.kv_heads * shape.head_dim))
+    for i0 in range(0, n, per):
+        i1 = min(n, i0 + per)
+        for b in range((first_pos + i0) // per, (first_pos + i1 - 1) // per + 1):
+            lo, hi = max(b * per, first_pos + i0), min((b + 1) * per, first_pos + i1)
+            blk = normal((per, shape.kv_heads, shape.head_dim), KEY_STD, device, seed, tag, layer, b)
+            out[lo - first_pos:hi - first_pos] = blk[lo - b * per:hi - b * per].to(torch.bfloat16)
+    return out
+
+
 def hidden_inputs(shape: Shape, M: int, step: int, sub: int = 0, device="cpu",
                   seed: int = 0, tag: str = "x") -> torch.Tensor:
     """M fresh bf16 hidden vectors N(0, 1) for one decode step (sub: resample index)."""
