@@ -1,6 +1,7 @@
 // api.cpp -- the C ABI: argument validation, workspace carving, and hand-off to
 // the launchers in kernels.hip. Plain C++ with no HIP headers, so the validation
 // can be built and exercised on a host without a GPU.
+#include <limits.h>
 #include <stdint.h>
 
 #include "internal.h"
@@ -324,6 +325,61 @@ int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int g
     if (((uintptr_t)tok0 | (uintptr_t)drafts) & 3u) return MOE_EALIGN;
     if (!ws_ok(workspace, workspace_bytes, draft_ws(*desc).total)) return MOE_EWORKSPACE;
     return launch_draft_step(*desc, *w, gamma, tok0, hidden0, emb_w, emb_s, drafts, (char *)workspace, stream);
+}
+
+static int check_attn_desc(const moe_attn_desc *d) {
+    if (!d) return MOE_EINVAL;
+    if (d->hidden < 256 || d->hidden > kMaxHidden || d->hidden % 256) return MOE_EINVAL;
+    if (d->q_heads < 1 || d->q_heads > 64 || d->kv_heads < 1 || d->kv_heads > 64) return MOE_EINVAL;
+    if (d->q_heads % d->kv_heads || d->q_heads / d->kv_heads > 16) return MOE_EINVAL;
+    if (d->head_dim != 128 && d->head_dim != 256 && d->head_dim != 512) return MOE_EINVAL;
+    if (d->q_heads * d->head_dim > 16384) return MOE_EINVAL;
+    if (d->window < 0 || d->window > (1 << 24) || d->capacity < 1 || d->capacity > (1 << 24))
+        return MOE_EINVAL;
+    if (d->window > 0 && d->capacity < d->window + kMaxM - 1) return MOE_EINVAL;
+    if (d->kv_type != MOE_KV_BF16 && d->kv_type != MOE_KV_FP8) return MOE_EINVAL;
+    return MOE_OK;
+}
+
+size_t moe_kv_cache_bytes(const moe_attn_desc *desc) {
+    if (check_attn_desc(desc) != MOE_OK) return 0;
+    return attn_cache(*desc).total;
+}
+
+int moe_kv_cache_write(const moe_attn_desc *desc, int first_pos, int n, const uint16_t *k, void *cache,
+                       void *stream) {
+    CHECK(check_attn_desc(desc));
+    if (first_pos < 0 || n < 1 || n > (1 << 24) || first_pos > INT_MAX - n) return MOE_EINVAL;
+    CHECK(need(k));
+    CHECK(need(cache));
+    if ((uintptr_t)cache & 255u) return MOE_EALIGN;
+    return launch_kv_write(*desc, first_pos, n, k, (char *)cache, stream);
+}
+
+size_t moe_attn_decode_workspace(const moe_attn_desc *desc, int max_M) {
+    if (check_attn_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
+    return attn_ws(*desc, max_M).total;
+}
+
+int moe_attn_decode(const moe_attn_desc *desc, const moe_attn_weights *w, int M, int pos, const uint16_t *u,
+                    void *cache, uint16_t *out, uint16_t *o, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    CHECK(check_attn_desc(desc));
+    if (!w || M < 1 || M > kMaxM || pos < 0 || pos > INT_MAX - M) return MOE_EINVAL;
+    if (desc->window == 0 && pos + M > desc->capacity) return MOE_EINVAL;
+    CHECK(need(w->q_w));
+    CHECK(need(w->q_s));
+    CHECK(need(w->k_w));
+    CHECK(need(w->k_s));
+    CHECK(need(w->o_w));
+    CHECK(need(w->o_s));
+    CHECK(need(u));
+    CHECK(need(cache));
+    CHECK(need(out));
+    if ((uintptr_t)cache & 255u) return MOE_EALIGN;
+    if (o && !aligned16(o)) return MOE_EALIGN;
+    if (!ws_ok(workspace, workspace_bytes, attn_ws(*desc, M).total)) return MOE_EWORKSPACE;
+    return launch_attn_decode(*desc, *w, M, pos, u, (char *)cache, out, o, (char *)workspace, stream);
 }
 
 int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_via_f32,

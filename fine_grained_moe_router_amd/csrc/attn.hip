@@ -1,0 +1,462 @@
+// attn.hip -- one attention layer of the decode step with a KV cache (gfx950).
+//
+// Page "LLM decoding", "The exact architecture": 25 sliding-window layers and 5 global
+// ones under grouped-query attention; "Where the 7.36 GB goes": q, k and o projections
+// (no v projection: the cached key is also the value) holding about 966M parameters;
+// "Lever 1" and "What we learned": an FP8 KV cache halves the KV reads. Per layer, four
+// launches:
+//   k_attn_proj    q = bf16(q_s (q_w u)) and k = bf16(k_s (k_w u)) for the M tokens, one
+//                  GEMV over the two matrices' rows; the bf16 cache takes the new keys here
+//   k_attn_part    per (KV head, tile of 16 queries, stripe of 16-position chunks): the
+//                  scores of the tile's queries against the chunk's keys, an online softmax
+//                  over the stripe, and the weighted key sum; a record (max, sum, 2 unused,
+//                  acc[dh]) per query and stripe. The FP8 cache takes the new keys here (quantised once
+//                  per (position, head) row by the workgroup whose chunk holds them).
+//   k_attn_combine one workgroup per query: the stripes' records in stripe order -> o
+//   k_attn_proj    out = bf16(o_s (o_w o))
+// Queries of KV head g are ordered qi = m G + (h - g G) (token-major); token m sees the
+// positions [lo_m, pos + m], lo_m = max(0, pos + m - window + 1) on sliding layers, 0 on
+// global ones. The cache is a ring: position p in slot p mod capacity.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+#include "pieces.h"
+
+namespace moe {
+namespace {
+
+using namespace dev;
+
+constexpr int kChunk = 16;       // positions per chunk: one per lane of a query's 16-lane row
+constexpr int kQTile = 16;       // queries per k_attn_part workgroup
+
+// E4M3FN code of an fp32 value: nearest, ties to even, saturating at 448 (0x7E); NaN 0x7F.
+// Below 2^-6 the codes are m 2^-9; above, 2^E (1 + r/8 - 1) with r = rint(a 2^(3 - E)) in
+// [8, 16]; both scalings are exact powers of two and rintf rounds to nearest even.
+__device__ __forceinline__ uint32_t fp8_encode(float v) {
+    if (v != v) return 0x7Fu;
+    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+    const float a = fabsf(v);
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);
+    int E = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;   // a is normal here
+    int r = (int)rintf(a * __uint_as_float((uint32_t)(127 + 3 - E) << 23));
+    if (r == 16) {
+        r = 8;
+        ++E;
+    }
+    if (E > 8 || (E == 8 && r > 14)) return sign | 0x7Eu;
+    return sign | (uint32_t)(((E + 7) << 3) | (r - 8));
+}
+
+// value of an E4M3FN code (scale 1), via the hardware conversion (exact)
+__device__ __forceinline__ float fp8_value(uint32_t code) { return fp8x2_to_f32<false>(code).x; }
+
+// -------------------------------------------------------------------- projections
+
+struct ProjArgs {
+    const uint8_t *wa;   // rows [0, na): [na][K] FP8
+    const float *sa;
+    const uint8_t *wb;   // rows [na, na + nb): [nb][K] FP8 (nb may be 0)
+    const float *sb;
+    int na, nb, K, M;
+    const uint16_t *x;   // [M][K] bf16
+    uint16_t *outa;      // [M][na]
+    uint16_t *outb;      // [M][nb]
+    uint16_t *cache;     // bf16 cache to append the b rows to (rows g dh + d), or null
+    int cap, dh, pos;
+};
+
+// Row n of the two stacked matrices against the M token vectors, staged in LDS a group of
+// tokens at a time (at most 32 KiB); the row's pieces stay in registers across groups.
+template <int LPR, int MAXCH>
+__global__ __launch_bounds__(256) void k_attn_proj(ProjArgs a) {
+    extern __shared__ uint4 xs[];
+    const int tid = threadIdx.x, li = tid & (LPR - 1), n = blockIdx.x * (256 / LPR) + tid / LPR;
+    const int ch = a.K / (16 * LPR);
+    const bool in_b = n >= a.na;
+    const uint8_t *row = in_b ? a.wb + (size_t)(n - a.na) * a.K : a.wa + (size_t)n * a.K;
+    Pieces<LPR, MAXCH> w;
+    w.load(row, li, ch);
+    const float sc = in_b ? a.sb[n - a.na] : a.sa[n];
+    const int tg = max(1, 16384 / a.K);   // tokens per LDS group (K bf16 each, 32 KiB)
+    for (int m0 = 0; m0 < a.M; m0 += tg) {
+        const int nt = min(tg, a.M - m0);
+        __syncthreads();
+        stage16(xs, reinterpret_cast<const uint4 *>(a.x + (size_t)m0 * a.K), nt * a.K / 8);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+            const float acc = group_sum<LPR>(w.dot_bf16(xs + (size_t)t * (a.K / 8), li, ch));
+            if (li == 0) {
+                const uint16_t v = f2bf(sc * acc);
+                const int m = m0 + t;
+                if (in_b) {
+                    const int r = n - a.na;
+                    a.outb[(size_t)m * a.nb + r] = v;
+                    if (a.cache) {
+                        const int g = r / a.dh, d = r - g * a.dh;
+                        const int slot = (a.pos + m) % a.cap;
+                        a.cache[((size_t)g * a.cap + slot) * a.dh + d] = v;
+                    }
+                } else {
+                    a.outa[(size_t)m * a.na + n] = v;
+                }
+            }
+        }
+    }
+}
+
+// -------------------------------------------------------------------- attention
+
+struct PartArgs {
+    const uint16_t *q;      // [M][NQ] bf16
+    const uint16_t *knew;   // [M][NK] bf16, the new keys
+    void *cache;            // bf16 [nkv][cap][dh], or FP8 codes of that shape
+    float *kscale;          // FP8: [nkv][cap]
+    int fp8;
+    int nkv, G, M, pos, window, cap, lo0, nch, nwg, Q, qsplit;
+    float inv_sqrt;
+    float *part;            // records [nkv][Q][nwg][dh + 4]: max, sum, -, -, acc[dh]
+};
+
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return v;
+}
+
+// The block-wide maximum of one value per thread (256 threads), every thread gets it.
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = row16_max(v);
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One (position, head) row of the FP8 cache, by the whole workgroup: thread t holds
+// elements t and t + 256 of the bf16 row src[0..n) (n <= 512) in x[]; returns the row's
+// scale max|x| / 448 (fp32 division), and code(i) = fp8_encode(x_i / scale) (0 when the
+// row is zero) gives its codes.
+__device__ __forceinline__ float fp8_row(const uint16_t *src, int n, float (&x)[2], float *red) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int d = threadIdx.x + 256 * e;
+        x[e] = d < n ? bf2f(src[d]) : 0.0f;
+        amax = fmaxf(amax, fabsf(x[e]));
+    }
+    return __fdiv_rn(block_max(amax, red), 448.0f);
+}
+__device__ __forceinline__ uint32_t fp8_row_code(float x, float scale) {
+    return scale > 0.0f ? fp8_encode(__fdiv_rn(x, scale)) : 0u;
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_part(PartArgs a) {
+    constexpr int KB = DH + 8;   // bf16 row stride of the staged keys (padding spreads the banks)
+    __shared__ uint4 qs4[kQTile * DH / 8];
+    __shared__ uint4 kb4[kChunk * KB / 8];
+    __shared__ float pw[kQTile][kChunk];
+    __shared__ float ksc[kChunk];
+    __shared__ float red[4];
+    uint16_t *kb = reinterpret_cast<uint16_t *>(kb4);
+
+    const int tid = threadIdx.x, ql = tid >> 4, l = tid & 15;
+    const int g = blockIdx.y / a.qsplit, s = blockIdx.y - g * a.qsplit, w = blockIdx.x;
+    const int qi0 = s * kQTile, nql = min(kQTile, a.Q - qi0);
+    const int NQ = a.G * a.nkv * DH, NK = a.nkv * DH;
+    const int last = a.pos + a.M - 1;
+
+    // the tile's queries
+    for (int i = tid; i < kQTile * DH / 8; i += 256) {
+        const int qq = i / (DH / 8), c = i - qq * (DH / 8);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (qq < nql) {
+            const int qi = qi0 + qq, m = qi / a.G, h = g * a.G + (qi - m * a.G);
+            v = reinterpret_cast<const uint4 *>(a.q + (size_t)m * NQ + (size_t)h * DH)[c];
+        }
+        qs4[i] = v;
+    }
+    const bool active = ql < nql;
+    const int my_m = active ? (qi0 + ql) / a.G : 0;
+    const int hi_m = a.pos + my_m;
+    const int lo_m = a.window > 0 ? max(0, hi_m - a.window + 1) : 0;
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    float acc[DH / 16];
+#pragma unroll
+    for (int i = 0; i < DH / 16; ++i) acc[i] = 0.0f;
+
+    const uint16_t *cb = reinterpret_cast<const uint16_t *>(a.cache);
+    uint8_t *c8 = reinterpret_cast<uint8_t *>(a.cache);
+    for (int c = w; c < a.nch; c += a.nwg) {
+        const int p0 = a.lo0 + c * kChunk;
+        __syncthreads();
+        // stage the chunk's keys as bf16 rows: as stored, or the FP8 codes' values (exact)
+        if (!a.fp8) {
+            for (int i = tid; i < kChunk * DH / 8; i += 256) {
+                const int j = i / (DH / 8), cc = i - j * (DH / 8), p = p0 + j;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (p <= last)
+                    v = reinterpret_cast<const uint4 *>(cb + ((size_t)g * a.cap + p % a.cap) * DH)[cc];
+                kb4[(j * KB) / 8 + cc] = v;
+            }
+            if (tid < kChunk) ksc[tid] = 1.0f;
+        } else {
+            // older positions: codes and scales from the cache
+            for (int i = tid; i < kChunk * DH / 16; i += 256) {
+                const int j = i / (DH / 16), cc = i - j * (DH / 16), p = p0 + j;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (p < a.pos) v = reinterpret_cast<const uint4 *>(c8 + ((size_t)g * a.cap + p % a.cap) * DH)[cc];
+                const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+                uint32_t bw[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x2 lo = fp8x2_to_f32<false>(vw[e]), hi = fp8x2_to_f32<true>(vw[e]);
+                    bw[2 * e] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                    bw[2 * e + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+                }
+                kb4[(j * KB) / 8 + 2 * cc] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+                kb4[(j * KB) / 8 + 2 * cc + 1] = make_uint4(bw[4], bw[5], bw[6], bw[7]);
+            }
+            if (tid < kChunk) {
+                const int p = p0 + tid;
+                ksc[tid] = p < a.pos ? a.kscale[(size_t)g * a.cap + p % a.cap] : 0.0f;
+            }
+            // new positions in this chunk: quantise the key rows, store them, stage them
+            const int jn0 = max(0, a.pos - p0), jn1 = min(kChunk, last - p0 + 1);
+            for (int j = jn0; j < jn1; ++j) {
+                const int p = p0 + j, m = p - a.pos;
+                float x[2];
+                const float scale = fp8_row(a.knew + (size_t)m * NK + (size_t)g * DH, DH, x, red);
+                const size_t slot = (size_t)g * a.cap + p % a.cap;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int d = tid + 256 * e;
+                    if (d < DH) {
+                        const uint32_t code = fp8_row_code(x[e], scale);
+                        const float v = fp8_value(code);
+                        if (s == 0) c8[slot * DH + d] = (uint8_t)code;
+                        kb[j * KB + d] = (uint16_t)(__float_as_uint(v) >> 16);
+                    }
+                }
+                if (tid == 0) {
+                    ksc[j] = scale;
+                    if (s == 0) a.kscale[slot] = scale;
+                }
+            }
+        }
+        __syncthreads();
+        // scores: lane l of query ql takes position p0 + l
+        float pj = 0.0f, alpha = 1.0f;
+        if (active) {
+            const uint4 *qr = qs4 + ql * (DH / 8);
+            const uint4 *kr = kb4 + (l * KB) / 8;
+            float d = 0.0f;
+#pragma unroll 8
+            for (int cc = 0; cc < DH / 8; ++cc) {
+                const uint4 qv = qr[cc], kv = kr[cc];
+                d = dot2(as_bf2(qv.x), as_bf2(kv.x), d);
+                d = dot2(as_bf2(qv.y), as_bf2(kv.y), d);
+                d = dot2(as_bf2(qv.z), as_bf2(kv.z), d);
+                d = dot2(as_bf2(qv.w), as_bf2(kv.w), d);
+            }
+            const int p = p0 + l;
+            const bool valid = p >= lo_m && p <= hi_m;
+            const float sc = valid ? d * ksc[l] * a.inv_sqrt : -INFINITY;
+            const float m_new = fmaxf(m_run, row16_max(sc));
+            if (m_new != -INFINITY) {
+                alpha = expf(m_run - m_new);
+                pj = valid ? expf(sc - m_new) : 0.0f;
+                l_run = l_run * alpha + row16_sum(pj);
+                m_run = m_new;
+            }
+            pw[ql][l] = pj * ksc[l];
+        }
+        __syncthreads();
+        // weighted key sum: lane l holds dims l 8 + 128 k + e (e < 8)
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < DH / 16; ++i) acc[i] *= alpha;
+            for (int j = 0; j < kChunk; ++j) {
+                const float wj = pw[ql][j];
+                const uint4 *kr = kb4 + (j * KB) / 8 + l;
+#pragma unroll
+                for (int k = 0; k < DH / 128; ++k) {
+                    const uint4 v = kr[16 * k];
+                    const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[8 * k + 2 * e] = fmaf(wj, __uint_as_float(vw[e] << 16), acc[8 * k + 2 * e]);
+                        acc[8 * k + 2 * e + 1] = fmaf(wj, __uint_as_float(vw[e] & 0xFFFF0000u), acc[8 * k + 2 * e + 1]);
+                    }
+                }
+            }
+        }
+    }
+    if (active) {
+        float *rec = a.part + (((size_t)g * a.Q + qi0 + ql) * a.nwg + w) * (DH + 4);
+        if (l == 0) {
+            rec[0] = m_run;
+            rec[1] = l_run;
+        }
+#pragma unroll
+        for (int k = 0; k < DH / 128; ++k) {
+            *reinterpret_cast<float4 *>(rec + 4 + l * 8 + 128 * k) =
+                make_float4(acc[8 * k], acc[8 * k + 1], acc[8 * k + 2], acc[8 * k + 3]);
+            *reinterpret_cast<float4 *>(rec + 4 + l * 8 + 128 * k + 4) =
+                make_float4(acc[8 * k + 4], acc[8 * k + 5], acc[8 * k + 6], acc[8 * k + 7]);
+        }
+    }
+}
+
+struct CombArgs {
+    const float *part;
+    int nkv, G, Q, nwg, dh;
+    uint16_t *o;       // [M][NQ] bf16 (workspace)
+    uint16_t *o_user;  // or null
+};
+
+// Query (g, qi): the stripes' records combined in stripe order:
+//   mx = max_w m_w, L = sum_w l_w e^(m_w - mx), o = sum_w acc_w e^(m_w - mx) / L
+__global__ __launch_bounds__(256) void k_attn_combine(CombArgs a) {
+    __shared__ float wt[512];
+    __shared__ float red[4];
+    const int tid = threadIdx.x;
+    const int g = blockIdx.x / a.Q, qi = blockIdx.x - g * a.Q;
+    const int R = a.dh + 4;
+    const float *rec = a.part + ((size_t)g * a.Q + qi) * a.nwg * R;
+    float mx = -INFINITY;
+    for (int w = tid; w < a.nwg; w += 256) mx = fmaxf(mx, rec[(size_t)w * R]);
+    mx = block_max(mx, red);
+    for (int w = tid; w < a.nwg; w += 256) {
+        const float m = rec[(size_t)w * R];
+        wt[w] = m == -INFINITY ? 0.0f : expf(m - mx);
+    }
+    __syncthreads();
+    float L = 0.0f;
+    for (int w = 0; w < a.nwg; ++w) L = fmaf(rec[(size_t)w * R + 1], wt[w], L);
+    const int m = qi / a.G, h = g * a.G + (qi - m * a.G), NQ = a.G * a.nkv * a.dh;
+    for (int d = tid; d < a.dh; d += 256) {
+        float o = 0.0f;
+        for (int w = 0; w < a.nwg; ++w) o = fmaf(rec[(size_t)w * R + 4 + d], wt[w], o);
+        const uint16_t v = f2bf(o / L);
+        a.o[(size_t)m * NQ + (size_t)h * a.dh + d] = v;
+        if (a.o_user) a.o_user[(size_t)m * NQ + (size_t)h * a.dh + d] = v;
+    }
+}
+
+// -------------------------------------------------------------------- cache writes
+
+// Row (position first + i, head g) of the cache from bf16 keys k [n][nkv][dh].
+__global__ __launch_bounds__(256) void k_kv_write(const uint16_t *k, int first, int nkv, int dh, int cap, int fp8,
+                                                  void *cache, float *kscale) {
+    __shared__ float red[4];
+    const int i = blockIdx.x / nkv, g = blockIdx.x - i * nkv, tid = threadIdx.x;
+    const uint16_t *src = k + ((size_t)i * nkv + g) * dh;
+    const size_t slot = (size_t)g * cap + (first + i) % cap;
+    if (!fp8) {
+        uint16_t *dst = reinterpret_cast<uint16_t *>(cache) + slot * dh;
+        for (int d = tid; d < dh; d += 256) dst[d] = src[d];
+        return;
+    }
+    float x[2];
+    const float scale = fp8_row(src, dh, x, red);
+    uint8_t *dst = reinterpret_cast<uint8_t *>(cache) + slot * dh;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int d = tid + 256 * e;
+        if (d < dh) dst[d] = (uint8_t)fp8_row_code(x[e], scale);
+    }
+    if (tid == 0) kscale[slot] = scale;
+}
+
+inline hipStream_t S(void *p) { return reinterpret_cast<hipStream_t>(p); }
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <class F>
+bool by_dh(int dh, F f) {
+    switch (dh) {
+        case 128: f(IC<128>{}); return true;
+        case 256: f(IC<256>{}); return true;
+        case 512: f(IC<512>{}); return true;
+        default: return false;
+    }
+}
+
+template <class F>
+void by_lpr(int lpr, F f) {
+    if (lpr == 16) f(IC<16>{});
+    else if (lpr == 32) f(IC<32>{});
+    else f(IC<64>{});
+}
+
+int launch_proj(const ProjArgs &a, void *stream) {
+    const int rows = a.na + a.nb;
+    const int lpr = draft_lpr(rows, a.K, kDraftMaxCh);
+    if (!lpr || rows % (256 / lpr)) return MOE_EINVAL;
+    const size_t lds = (size_t)min(a.M, max(1, 16384 / a.K)) * a.K * 2;
+    by_lpr(lpr, [&](auto L) {
+        constexpr int l = decltype(L)::value;
+        hipLaunchKernelGGL((k_attn_proj<l, kDraftMaxCh>), dim3(rows * l / 256), dim3(256), lds, S(stream), a);
+    });
+    return MOE_OK;
+}
+
+}  // namespace
+
+int launch_kv_write(const moe_attn_desc &d, int first_pos, int n, const uint16_t *k, char *cache, void *stream) {
+    (void)hipGetLastError();
+    const AttnCache C = attn_cache(d);
+    hipLaunchKernelGGL(k_kv_write, dim3(n * d.kv_heads), dim3(256), 0, S(stream), k, first_pos, d.kv_heads, d.head_dim,
+                       d.capacity, d.kv_type == MOE_KV_FP8 ? 1 : 0, (void *)cache,
+                       reinterpret_cast<float *>(cache + C.scales));
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M, int pos, const uint16_t *u,
+                       char *cache, uint16_t *out, uint16_t *o_user, char *ws, void *stream) {
+    (void)hipGetLastError();
+    const AttnPlan P = attn_plan(d, M, pos);
+    const AttnWs W = attn_ws(d, M);
+    const AttnCache C = attn_cache(d);
+    const int NQ = d.q_heads * d.head_dim, NK = d.kv_heads * d.head_dim;
+    const bool fp8 = d.kv_type == MOE_KV_FP8;
+    uint16_t *q = reinterpret_cast<uint16_t *>(ws + W.q), *k = reinterpret_cast<uint16_t *>(ws + W.k);
+    uint16_t *o = reinterpret_cast<uint16_t *>(ws + W.o);
+    float *part = reinterpret_cast<float *>(ws + W.part);
+
+    ProjArgs pa{w.q_w, w.q_s, w.k_w, w.k_s, NQ, NK, d.hidden, M, u, q, k,
+                fp8 ? nullptr : reinterpret_cast<uint16_t *>(cache), d.capacity, d.head_dim, pos};
+    int rc = launch_proj(pa, stream);
+    if (rc != MOE_OK) return rc;
+
+    PartArgs ta{q, k, cache, reinterpret_cast<float *>(cache + C.scales), fp8 ? 1 : 0, d.kv_heads, P.G, M, pos,
+                d.window, d.capacity, P.lo0, P.nch, P.nwg, P.Q, P.qsplit, 1.0f / sqrtf((float)d.head_dim), part};
+    if (!by_dh(d.head_dim, [&](auto D) {
+            constexpr int dh = decltype(D)::value;
+            hipLaunchKernelGGL((k_attn_part<dh>), dim3(P.nwg, d.kv_heads * P.qsplit), dim3(256), 0, S(stream), ta);
+        }))
+        return MOE_EINVAL;
+
+    CombArgs ca{part, d.kv_heads, P.G, P.Q, P.nwg, d.head_dim, o, o_user};
+    hipLaunchKernelGGL(k_attn_combine, dim3(d.kv_heads * P.Q), dim3(256), 0, S(stream), ca);
+
+    ProjArgs po{w.o_w, w.o_s, nullptr, nullptr, d.hidden, 0, NQ, M, o, out, nullptr, nullptr, 0, 0, 0};
+    rc = launch_proj(po, stream);
+    if (rc != MOE_OK) return rc;
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+}  // namespace moe

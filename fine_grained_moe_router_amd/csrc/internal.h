@@ -131,6 +131,62 @@ inline DraftWs draft_ws(const moe_draft_desc &d) {
     return W;
 }
 
+// ---------------------------------------------------------------- attention decode
+
+// Layout of one layer's KV cache: values (bf16 or FP8 codes) [kv_heads][capacity][head_dim],
+// then, for FP8, fp32 scales [kv_heads][capacity] at `scales`.
+struct AttnCache {
+    size_t scales, total;
+};
+inline AttnCache attn_cache(const moe_attn_desc &d) {
+    AttnCache C{};
+    const size_t n = (size_t)d.kv_heads * d.capacity * d.head_dim;
+    if (d.kv_type == MOE_KV_FP8) {
+        C.scales = align256(n);
+        C.total = C.scales + 4 * (size_t)d.kv_heads * d.capacity;
+    } else {
+        C.scales = 0;
+        C.total = 2 * n;
+    }
+    return C;
+}
+
+// The partial-softmax grid for M tokens at pos: G query heads per KV head, Q = G M queries
+// per KV head in tiles of 16, 16-position chunks from lo0 (token 0's first visible position)
+// to pos + M - 1, nwg stripes of chunks per (KV head, tile) so the grid stays <= 512
+// workgroups and the records (one per query and stripe) <= 16 x 512.
+constexpr int kAttnMaxWG = 512;
+constexpr int kAttnRecords = 16 * kAttnMaxWG;
+struct AttnPlan {
+    int G, Q, qsplit, lo0, nch, nwg;
+};
+inline AttnPlan attn_plan(const moe_attn_desc &d, int M, int pos) {
+    AttnPlan P{};
+    P.G = d.q_heads / d.kv_heads;
+    P.Q = P.G * M;
+    P.qsplit = (P.Q + 15) / 16;
+    P.lo0 = d.window > 0 ? (pos - d.window + 1 > 0 ? pos - d.window + 1 : 0) : 0;
+    P.nch = (pos + M - P.lo0 + 15) / 16;
+    const int cap = kAttnMaxWG / (d.kv_heads * P.qsplit);
+    P.nwg = P.nch < (cap > 1 ? cap : 1) ? P.nch : (cap > 1 ? cap : 1);
+    return P;
+}
+struct AttnWs {
+    size_t q, k, o, part, total;
+};
+inline AttnWs attn_ws(const moe_attn_desc &d, int max_M) {
+    AttnWs W{};
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o = align256(o + bytes); return r; };
+    const size_t NQ = (size_t)d.q_heads * d.head_dim, NK = (size_t)d.kv_heads * d.head_dim;
+    W.q = take(2 * NQ * max_M);
+    W.k = take(2 * NK * max_M);
+    W.o = take(2 * NQ * max_M);
+    W.part = take(4 * (size_t)kAttnRecords * (d.head_dim + 4));
+    W.total = o;
+    return W;
+}
+
 // Static scratch of lm_head_argmax_noalloc: the workspace of the largest call (M = 8,
 // the full lm_head grid), 128 KiB.
 constexpr size_t kLmNoallocScratch = 2 * (size_t)kLmMaxWG * kMaxM * 4;
@@ -262,6 +318,9 @@ int launch_layer_step(const moe_layer_desc &d, const moe_layer_weights &w, int M
 int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weights *layers, char *ws);
 int step_status(const StepWs &W, char *ws);
 int launch_fp8_decode(int n, const uint8_t *codes, float *via_bf16, float *via_f32, void *stream);
+int launch_kv_write(const moe_attn_desc &d, int first_pos, int n, const uint16_t *k, char *cache, void *stream);
+int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M, int pos, const uint16_t *u,
+                       char *cache, uint16_t *out, uint16_t *o_user, char *ws, void *stream);
 int launch_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 }  // namespace moe

@@ -18,13 +18,15 @@ _lib = None
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
 MOE_ETIMEOUT = -6
 MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
+MOE_KV_BF16, MOE_KV_FP8 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
            "lm_head_argmax", "lm_head_argmax_bf16", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
            "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
-           "moe_hbm_read_probe", "moe_draft_step_workspace", "moe_draft_step", "moe_strerror")
+           "moe_hbm_read_probe", "moe_draft_step_workspace", "moe_draft_step", "moe_kv_cache_bytes",
+           "moe_kv_cache_write", "moe_attn_decode_workspace", "moe_attn_decode", "moe_strerror")
 
 
 class MoeError(RuntimeError):
@@ -65,6 +67,15 @@ class DraftDesc(ctypes.Structure):
 class DraftWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("pre_w", "pre_s", "gate_w", "gate_s", "up_w", "up_s", "down_w", "down_s", "gains",
                                   "table_w", "table_s", "post_w", "post_s")]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("hidden", "q_heads", "kv_heads", "head_dim", "window", "capacity",
+                                            "kv_type")]
+
+
+class AttnWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("q_w", "q_s", "k_w", "k_s", "o_w", "o_s")]
 
 
 def lib() -> ctypes.CDLL:
@@ -116,6 +127,15 @@ def lib() -> ctypes.CDLL:
         L.moe_draft_step.restype = I
         L.moe_draft_step.argtypes = [ctypes.POINTER(DraftDesc), ctypes.POINTER(DraftWeights), I, _P, _P, _P, _P, _P,
                                      _P, S, _P]
+        L.moe_kv_cache_bytes.restype = S
+        L.moe_kv_cache_bytes.argtypes = [ctypes.POINTER(AttnDesc)]
+        L.moe_kv_cache_write.restype = I
+        L.moe_kv_cache_write.argtypes = [ctypes.POINTER(AttnDesc), I, I, _P, _P, _P]
+        L.moe_attn_decode_workspace.restype = S
+        L.moe_attn_decode_workspace.argtypes = [ctypes.POINTER(AttnDesc), I]
+        L.moe_attn_decode.restype = I
+        L.moe_attn_decode.argtypes = [ctypes.POINTER(AttnDesc), ctypes.POINTER(AttnWeights), I, I, _P, _P, _P, _P,
+                                      _P, S, _P]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_strerror.argtypes = [I]
         _lib = L
@@ -293,3 +313,34 @@ def moe_draft_step(desc: DraftDesc, weights: DraftWeights, gamma, tok0, hidden0,
                               _ptr(emb_w), _ptr(emb_s), _ptr(drafts), _ptr(workspace), int(workspace_bytes),
                               _stream(stream))
     _check("moe_draft_step", st)
+
+
+def attn_desc(shape) -> AttnDesc:
+    """AttnDesc from a synth.AttnShape."""
+    return AttnDesc(shape.hidden, shape.q_heads, shape.kv_heads, shape.head_dim, shape.window, shape.capacity,
+                    MOE_KV_FP8 if shape.kv_fp8 else MOE_KV_BF16)
+
+
+def attn_weights(w: dict) -> AttnWeights:
+    """AttnWeights from a dict of device tensors (keys as synth.attn_weights)."""
+    return AttnWeights(*[_ptr(w[k]) for k in ("q_w", "q_s", "k_w", "k_s", "o_w", "o_s")])
+
+
+def moe_kv_cache_bytes(desc: AttnDesc) -> int:
+    return lib().moe_kv_cache_bytes(ctypes.byref(desc))
+
+
+def moe_kv_cache_write(desc: AttnDesc, first_pos, n, k, cache, stream=None):
+    st = lib().moe_kv_cache_write(ctypes.byref(desc), int(first_pos), int(n), _ptr(k), _ptr(cache), _stream(stream))
+    _check("moe_kv_cache_write", st)
+
+
+def moe_attn_decode_workspace(desc: AttnDesc, max_M: int) -> int:
+    return lib().moe_attn_decode_workspace(ctypes.byref(desc), int(max_M))
+
+
+def moe_attn_decode(desc: AttnDesc, weights: AttnWeights, M, pos, u, cache, out, o, workspace, workspace_bytes,
+                    stream=None):
+    st = lib().moe_attn_decode(ctypes.byref(desc), ctypes.byref(weights), int(M), int(pos), _ptr(u), _ptr(cache),
+                               _ptr(out), _ptr(o), _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _check("moe_attn_decode", st)

@@ -425,6 +425,88 @@ int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int g
                    const float *emb_s, int32_t *drafts, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* ------------------------------------------------------------------------------
+ * Attention decode with a KV cache (page "LLM decoding", "The exact architecture": 25
+ * sliding-window layers and 5 global ones, grouped-query attention, a 256K context;
+ * "Where the 7.36 GB goes": the q/k/o projections, about 966M parameters, 26.3 % of the
+ * bytes, KV-cache reads not counted; "Lever 1" and "What we learned": an FP8 KV cache
+ * halves the KV reads). The page names q, k and o projections and no v projection: the
+ * reading taken is that the cached key is also the value, with 16 query heads of 256 and
+ * 8 KV heads on sliding layers and 16 query heads of 512 and 2 KV heads on global ones,
+ * which gives the page's 966,000,640 parameters exactly. No positional rotation is
+ * applied (none is on the page; it would add arithmetic, not bytes), and the score scale
+ * is 1/sqrt(head_dim). Per layer, for tokens m = 0..M-1 at positions pos + m:
+ *   q_m  = bf16(q_s * (q_w u_m))                 [q_heads * head_dim]
+ *   k_m  = bf16(k_s * (k_w u_m))                 [kv_heads * head_dim], appended to the cache
+ *   for query head h (KV head g = h / (q_heads / kv_heads)), over the positions
+ *   p in [lo_m, pos + m], lo_m = window ? max(0, pos + m - window + 1) : 0:
+ *        s_p  = (q_m,h . K_g[p]) / sqrt(head_dim);  w = softmax(s)
+ *        o_m,h = bf16(sum_p w_p K_g[p])          (the cached key is the value)
+ *   out_m = bf16(o_s * (o_w o_m))                [hidden]
+ * K_g[p] is the cached key as stored: bf16, or FP8 E4M3FN codes times a per-(position,
+ * head) fp32 scale.
+ * ---------------------------------------------------------------------------- */
+enum {
+    MOE_KV_BF16 = 0,   /* cache: bf16 [kv_heads][capacity][head_dim]                            */
+    MOE_KV_FP8 = 1     /* cache: FP8 codes [kv_heads][capacity][head_dim], then fp32 scales
+                          [kv_heads][capacity] at offset align256(kv_heads * capacity *
+                          head_dim); a row's scale is max|k| / 448 (fp32) and its codes are
+                          k / scale (fp32 division) rounded to nearest even, saturating at
+                          448; an all-zero row has scale 0                                      */
+};
+
+typedef struct moe_attn_desc {
+    int hidden;       /* model width (2816): a multiple of 256, at most 4096                    */
+    int q_heads;      /* 1..64, a multiple of kv_heads                                          */
+    int kv_heads;     /* 1..64; q_heads / kv_heads query heads share a KV head (at most 16)     */
+    int head_dim;     /* 128, 256 or 512; q_heads * head_dim at most 16384                      */
+    int window;       /* sliding window in positions (1024 on sliding layers), 0 for global;
+                         at most 2^24                                                          */
+    int capacity;     /* cache positions, 1..2^24; position p lives in slot p mod capacity. Sliding:
+                         capacity >= window + 7 (the ring holds every token's window); global:
+                         every call needs pos + M <= capacity                                  */
+    int kv_type;      /* MOE_KV_BF16 or MOE_KV_FP8                                              */
+} moe_attn_desc;
+
+typedef struct moe_attn_weights {      /* device pointers, 16-byte aligned; FP8 E4M3FN codes
+                                          with per-row fp32 scales                             */
+    const uint8_t *q_w; const float *q_s;   /* [q_heads * head_dim][hidden], [q_heads * head_dim] */
+    const uint8_t *k_w; const float *k_s;   /* [kv_heads * head_dim][hidden], [kv_heads * head_dim] */
+    const uint8_t *o_w; const float *o_s;   /* [hidden][q_heads * head_dim], [hidden]            */
+} moe_attn_weights;
+
+/* Bytes of one layer's KV cache for desc (0 if desc is invalid). */
+size_t moe_kv_cache_bytes(const moe_attn_desc *desc);
+
+/*
+ * Write keys of n positions first_pos .. first_pos + n - 1 into the cache (slot p mod
+ * capacity), quantising to FP8 for MOE_KV_FP8 exactly as the decode call does for the keys
+ * it appends. k bf16 [n][kv_heads][head_dim]; 1 <= n; first_pos >= 0. This is how a
+ * context is placed in the cache (prefill itself is not part of this library).
+ * Asynchronous on `stream`.
+ */
+int moe_kv_cache_write(const moe_attn_desc *desc, int first_pos, int n, const uint16_t *k, void *cache,
+                       void *stream);
+
+/* Bytes of workspace moe_attn_decode needs for up to max_M tokens (0 if invalid). */
+size_t moe_attn_decode_workspace(const moe_attn_desc *desc, int max_M);
+
+/*
+ * One layer's attention for M tokens (1..8) at positions pos .. pos + M - 1 (the decode
+ * step at M = 1, the speculative verify step at M = gamma + 1; each token attends to the
+ * others before it), as defined above. Positions below pos must already be in the cache
+ * (the last `window` of them on sliding layers); the call appends the M new keys.
+ *   u      bf16 [M][hidden], the (already normalised) layer input
+ *   cache  moe_kv_cache_bytes(desc) bytes, 256-byte aligned
+ *   out    bf16 [M][hidden], the attention branch output (the residual is NOT added)
+ *   o      bf16 [M][q_heads * head_dim], the heads' outputs before o_w, or NULL
+ * Asynchronous on `stream`, four launches (q/k projection and append, per-chunk partial
+ * softmax, combine, o projection); capturable.
+ */
+int moe_attn_decode(const moe_attn_desc *desc, const moe_attn_weights *w, int M, int pos, const uint16_t *u,
+                    void *cache, uint16_t *out, uint16_t *o, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
 /* A static string describing a moe_status value. */
 const char *moe_strerror(int status);
 

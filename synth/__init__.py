@@ -246,7 +246,7 @@ class AttnShape:
 GEMMA4_SLIDING = AttnShape()
 GEMMA4_GLOBAL = AttnShape(q_heads=16, kv_heads=2, head_dim=512, window=0, capacity=32768)
 GEMMA4_ATTN_LAYERS = [GEMMA4_GLOBAL if (l % 6) == 5 else GEMMA4_SLIDING for l in range(30)]   # 25 + 5, 5:1
-TINY_ATTN = AttnShape(hidden=256, q_heads=4, kv_heads=2, head_dim=64, window=16, capacity=24)
+TINY_ATTN = AttnShape(hidden=256, q_heads=4, kv_heads=2, head_dim=128, window=16, capacity=24)
 KEY_STD = 1.0   # cached keys N(0, 1): the spread the projections give keys of normalised inputs
 
 

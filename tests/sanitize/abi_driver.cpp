@@ -64,6 +64,9 @@ int step_prepare(const StepWs &W, const moe_layer_desc &, const moe_layer_weight
 int step_status(const StepWs &, char *) { return hit(0); }
 int launch_fp8_decode(int, const uint8_t *, float *, float *, void *) { return hit(0); }
 int launch_read_probe(const void *, size_t, uint32_t *, void *) { return hit(0); }
+int launch_kv_write(const moe_attn_desc &, int, int, const uint16_t *, char *, void *) { return hit(0); }
+int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &, int M, int, const uint16_t *, char *,
+                       uint16_t *, uint16_t *, char *, void *) { return hit(attn_ws(d, M).total); }
 }  // namespace moe
 
 // Device pointers are never dereferenced by the host code: distinct fake aligned addresses.
@@ -224,6 +227,35 @@ static void draft_sweep(const moe_draft_desc &dd, int gamma) {
     }
 }
 
+static void attn_sweep(const moe_attn_desc &ad, int M, int pos) {
+    moe_attn_weights w;
+    const void **p = reinterpret_cast<const void **>(&w);
+    for (size_t i = 0; i < sizeof w / sizeof(void *); ++i) p[i] = fake(110 + (int)i);
+    char *u = fake(120), *cache = fake(121), *out = fake(122), *WS = fake(123);
+    const size_t cb = moe_kv_cache_bytes(&ad), ws = moe_attn_decode_workspace(&ad, M);
+    if (cb) {
+        CHECK(moe_attn_decode_workspace(&ad, 1) > 0);
+        EXPECT_WS(0, moe_kv_cache_write(&ad, pos, 3, (uint16_t *)u, cache, nullptr),
+                  (pos >= 0 && pos <= INT_MAX - 3) ? MOE_OK : MOE_EINVAL);
+    } else {
+        g_calls = 0;
+        CHECK(moe_kv_cache_write(&ad, 0, 1, (uint16_t *)u, cache, nullptr) != MOE_OK && g_calls == 0);
+    }
+    if (ws) {
+        const bool ok = pos >= 0 && (long long)pos + M <= INT_MAX &&
+                        (ad.window > 0 || (long long)pos + M <= ad.capacity);
+        EXPECT_WS(ws, moe_attn_decode(&ad, &w, M, pos, (uint16_t *)u, cache, (uint16_t *)out, nullptr, WS, ws, nullptr),
+                  ok ? MOE_OK : MOE_EINVAL);
+        if (ok)
+            EXPECT_WS(ws - 1, moe_attn_decode(&ad, &w, M, pos, (uint16_t *)u, cache, (uint16_t *)out, nullptr, WS,
+                                              ws - 1, nullptr), MOE_EWORKSPACE);
+    } else {
+        g_calls = 0;
+        CHECK(moe_attn_decode(&ad, &w, M, pos, (uint16_t *)u, cache, (uint16_t *)out, nullptr, WS, (size_t)1 << 40,
+                              nullptr) != MOE_OK && g_calls == 0);
+    }
+}
+
 int main() {
     // known-good shapes
     const moe_layer_desc gemma = {2816, 128, 8, 704, 704, MOE_W_FP8_E4M3};
@@ -244,6 +276,12 @@ int main() {
     for (int M = 0; M <= 9; ++M) step_sweep(sd, M);
     const moe_draft_desc mtp = {2816, 1024, 4096, 12, 262144, 1e-6f};
     for (int g = 0; g <= 8; ++g) draft_sweep(mtp, g);
+    const moe_attn_desc sliding = {2816, 16, 8, 256, 1024, 1032, MOE_KV_BF16};
+    const moe_attn_desc global = {2816, 16, 2, 512, 0, 32768, MOE_KV_FP8};
+    for (int M = 0; M <= 9; ++M) {
+        attn_sweep(sliding, M, 5000);
+        attn_sweep(global, M, 32760);
+    }
 
     // pointer checks on one entry point each: NULL -> EINVAL, misaligned -> EALIGN
     {
@@ -302,6 +340,10 @@ int main() {
         *f = pick();
         if (rnd() % 8 == 0) dd = {pick(), pick(), pick(), pick(), pick(), 1e-6f};
         draft_sweep(dd, (int)(rnd() % 10) - 1);
+        moe_attn_desc ad = (rnd() & 1) ? sliding : global;
+        int *af = reinterpret_cast<int *>(&ad) + rnd() % 7;
+        *af = (rnd() % 7 == 6) ? (int)(rnd() % 3) - 1 : pick();
+        attn_sweep(ad, (int)(rnd() % 11) - 1, (rnd() & 1) ? pick() : (int)(rnd() % 40000));
     }
     if (failures) std::fprintf(stderr, "%d checks failed\n", failures);
     else std::printf("ABI sanitizer driver: ok (%ld accepted calls, %ld rejected)\n", n_ok, n_rejected);

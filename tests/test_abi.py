@@ -327,3 +327,38 @@ def test_step_call_validation_through_the_binding():
 def test_step_status_validation():
     assert native.lib().moe_decode_step_status(None, FAKE) == native.MOE_EINVAL
     assert native.moe_decode_step_status(step_desc(), None) == native.MOE_EWORKSPACE
+
+
+def test_attn_decode_validation():
+    import synth
+    L = native.lib()
+    good = native.attn_desc(synth.GEMMA4_SLIDING)
+    assert native.moe_kv_cache_bytes(good) == 2 * 8 * 1032 * 256
+    fp8 = native.attn_desc(synth.GEMMA4_GLOBAL.with_(kv_fp8=True))
+    n = 2 * 32768 * 512
+    assert native.moe_kv_cache_bytes(fp8) == (n + 255) // 256 * 256 + 4 * 2 * 32768
+    assert native.moe_attn_decode_workspace(good, 8) > 0 and native.moe_attn_decode_workspace(good, 9) == 0
+    for k, v in (("hidden", 100), ("q_heads", 0), ("kv_heads", 3), ("head_dim", 64), ("head_dim", 96),
+                 ("window", -1), ("capacity", 1030), ("kv_type", 2), ("window", 1 << 30)):
+        d = native.attn_desc(synth.GEMMA4_SLIDING)
+        setattr(d, k, v)
+        assert native.moe_kv_cache_bytes(d) == 0, (k, v)
+    d = native.attn_desc(synth.GEMMA4_SLIDING)
+    d.q_heads, d.kv_heads = 32, 1            # 32 query heads per KV head: above 16
+    assert native.moe_kv_cache_bytes(d) == 0
+    w = native.AttnWeights(*([FAKE] * 6))
+    wsb = native.moe_attn_decode_workspace(good, 5)
+    call = lambda **o: L.moe_attn_decode(ctypes.byref(o.get("d", good)), ctypes.byref(o.get("w", w)), o.get("M", 5),
+                                         o.get("pos", 100), o.get("u", FAKE), o.get("c", FAKE), o.get("out", FAKE),
+                                         o.get("o", None), o.get("ws", FAKE), o.get("wsb", wsb), None)
+    assert call(M=0) == native.MOE_EINVAL and call(M=9) == native.MOE_EINVAL and call(pos=-1) == native.MOE_EINVAL
+    assert call(u=None) == native.MOE_EINVAL and call(u=FAKE + 2) == native.MOE_EALIGN
+    assert call(c=FAKE + 16) == native.MOE_EALIGN           # the cache must be 256-byte aligned
+    assert call(o=FAKE + 2) == native.MOE_EALIGN and call(wsb=wsb - 1) == native.MOE_EWORKSPACE
+    assert call(w=native.AttnWeights(*([FAKE] * 5 + [None]))) == native.MOE_EINVAL
+    g = native.attn_desc(synth.GEMMA4_GLOBAL)
+    wsg = native.moe_attn_decode_workspace(g, 5)
+    assert call(d=g, pos=32768 - 4, wsb=wsg) == native.MOE_EINVAL      # pos + M beyond a global cache
+    assert L.moe_kv_cache_write(ctypes.byref(good), -1, 1, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_kv_cache_write(ctypes.byref(good), 0, 0, FAKE, FAKE, None) == native.MOE_EINVAL
+    assert L.moe_kv_cache_write(ctypes.byref(good), 0, 1, FAKE, FAKE + 16, None) == native.MOE_EALIGN
