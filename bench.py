@@ -109,6 +109,10 @@ def parse():
     ap.add_argument("--draft", action="store_true",
                     help="the MTP drafter step instead (moe_draft_step, 4 drafts of the 430M head), timed beside the "
                          "fused verify step, with the drafter tax and modelled tokens/s (its own JSON line)")
+    ap.add_argument("--attn", action="store_true",
+                    help="the attention half of the decode step instead (moe_attn_decode over the 30 layers, 25 "
+                         "sliding + 5 global, with a KV cache) at several contexts, M=1 and M=5, bf16 and FP8 KV "
+                         "caches (its own JSON line)")
     ap.add_argument("--ladder", action="store_true",
                     help="the precision ladder instead: the stack at M=1 and M=5 for FP8/bf16 experts x FP8/bf16 "
                          "lm_head, with tokens/s modelled from the acceptance rate (its own JSON line)")
@@ -147,6 +151,8 @@ def main():
         return ladder_main(args)
     if args.draft:
         return draft_main(args)
+    if args.attn:
+        return attn_main(args)
     if args.layer:
         return layer_main(args)
     import synth
@@ -617,6 +623,122 @@ def sample_main(args):
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_launch": int(bps),
                      "avg_launch_us": round(ms * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def attn_layer_bytes(sh, M, pos) -> int:
+    """Algorithmic bytes of one attention layer call: the q/k/o FP8 weights and row scales, the
+    cached key rows the M tokens see (each row once: the union of their windows), the M new key
+    rows written, and the M input and output rows."""
+    H, NQ, NK, dh = sh.hidden, sh.q_heads * sh.head_dim, sh.kv_heads * sh.head_dim, sh.head_dim
+    w = 2 * NQ * H + NK * H + 4 * (NQ + NK + H)
+    lo = max(0, pos - sh.window + 1) if sh.window else 0
+    row = dh * (1 if sh.kv_fp8 else 2) + (4 if sh.kv_fp8 else 0)
+    kv = (pos - lo) * sh.kv_heads * row + M * sh.kv_heads * row
+    return w + kv + 2 * M * H * 2
+
+
+def attn_main(args):
+    """The attention half of a decode step (page 'LLM decoding', "The exact architecture" and
+    "Where the 7.36 GB goes"): moe_attn_decode for each of the 30 layers (25 sliding-window
+    layers of 16 x 256 query heads over 8 KV heads with a 1024-position window, 5 global layers
+    of 16 x 512 over 2 KV heads), each on its own weights and KV cache, at contexts of 768
+    positions (the page's workload: 512 prompt + 256 generated tokens), 8K and 32K, for M = 1
+    and M = 5, with bf16 and with FP8 caches. The caches hold seeded synthetic keys of every
+    earlier position; each step appends the same M keys again, so replays do not drift. Steps
+    are captured into HIP graphs of 20 and replayed; bytes per step are the weights plus the
+    KV rows read (attn_layer_bytes)."""
+    import torch
+    import synth
+    from fine_grained_moe_router_amd import native
+
+    native.lib()   # fail loudly if the HIP library is missing
+    dev = "cuda"
+    K, W = args.steps, args.warmup
+    layers = synth.GEMMA4_ATTN_LAYERS
+    weights = [synth.attn_weights(sh, dev, seed=args.seed, layer=l) for l, sh in enumerate(layers)]
+    wd = [native.attn_weights(w) for w in weights]
+    H = layers[0].hidden
+    results = {}
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    for ctx in (768, 8192, 32768):
+        for fp8 in (False, True):
+            shapes = [sh.with_(kv_fp8=fp8, capacity=(sh.capacity if sh.window else ctx + 8)) for sh in layers]
+            descs = [native.attn_desc(sh) for sh in shapes]
+            caches = []
+            for l, (sh, d) in enumerate(zip(shapes, descs)):
+                c = native.workspace(native.moe_kv_cache_bytes(d))
+                lo = max(0, ctx - sh.window + 1) if sh.window else 0
+                for p0 in range(lo, ctx, 8192):
+                    n = min(8192, ctx - p0)
+                    native.moe_kv_cache_write(d, p0, n, synth.kv_keys(sh, p0, n, dev, seed=args.seed, layer=l), c)
+                caches.append(c)
+            torch.cuda.synchronize()
+            for M in (1, 5):
+                us = [synth.hidden_inputs(synth.GEMMA4_26B_A4B, M, l, device=dev, seed=args.seed, tag="attn_u")
+                      for l in range(len(layers))]
+                outs = [torch.empty(M, H, dtype=torch.bfloat16, device=dev) for _ in layers]
+                wsb = max(native.moe_attn_decode_workspace(d, M) for d in descs)
+                ws = native.workspace(wsb)
+
+                def step():
+                    for l in range(len(layers)):
+                        native.moe_attn_decode(descs[l], wd[l], M, ctx, us[l], caches[l], outs[l], None, ws, wsb,
+                                               stream)
+
+                with torch.cuda.stream(stream):
+                    for _ in range(W):
+                        step()
+                    torch.cuda.synchronize()
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr, stream=stream):
+                        for _ in range(20):
+                            step()
+                    torch.cuda.synchronize()
+                    blocks = []
+                    reps = max(1, K // 20)
+                    for b in range(5):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(reps):
+                            gr.replay()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        blocks.append(e0.elapsed_time(e1) / (20 * reps))
+                    del gr
+                ms = float(np.median(blocks))
+                bps = sum(attn_layer_bytes(sh, M, ctx) for sh in shapes)
+                gbs = bps / (ms / 1e3) / 1e9
+                key = "ctx%d_M%d_%s" % (ctx, M, "fp8kv" if fp8 else "bf16kv")
+                results[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": int(bps), "hbm_gbs": round(gbs, 1),
+                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                                "block_ms_per_step": [round(b, 5) for b in blocks]}
+                log("attention ctx %5d M=%d %s KV: %.1f us/step (%.1f us/layer), %.1f MB, %.1f GB/s (%.1f%%)" % (
+                    ctx, M, "FP8 " if fp8 else "bf16", ms * 1e3, ms * 1e3 / 30, bps / 1e6, gbs,
+                    100 * gbs / HBM_PEAK_GBS))
+            del caches
+            torch.cuda.empty_cache()
+    head = results["ctx8192_M1_bf16kv"]
+    line = {
+        "metric": "attention decode (30 layers: 25 sliding + 5 global, GQA) with a KV cache, steps/s and HBM GB/s",
+        "value": round(1e3 / head["ms_per_step"], 2), "unit": "steps/s (8K context, M=1, bf16 KV)", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 weights x bf16 activations, bf16 or FP8 KV cache, fp32 accumulate",
+        "data": "synthetic (seeded FP8 q/k/o projections, N(0,1) cached keys and inputs)",
+        "config": {"workload": "moe_attn_decode over the 30 layers of a Gemma-4-26B-A4B-shaped step: 25 sliding "
+                               "(16x256 q heads, 8 KV heads, window 1024, ring cache) + 5 global (16x512 q heads, "
+                               "2 KV heads); contexts 768 / 8K / 32K, M=1 and M=5, bf16 and FP8 KV",
+                   "hidden": H, "layers": len(layers), "params": sum(sh.params() for sh in layers)},
+        "per_config": results,
+        "fp8_kv_over_bf16_kv_ctx32768_M1": round(results["ctx32768_M1_bf16kv"]["ms_per_step"] /
+                                                 results["ctx32768_M1_fp8kv"]["ms_per_step"], 3),
+        "roofline": {"bound": "hbm", "kernel": "moe_attn_decode x 30 (4 launches each), 8K context, M=1, bf16 KV",
+                     "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": None, "bytes_per_launch": head["bytes_per_step"],
+                     "avg_launch_us": round(head["ms_per_step"] * 1e3, 2)},
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

@@ -160,6 +160,82 @@ __device__ __forceinline__ uint32_t fp8_row_code(float x, float scale) {
     return scale > 0.0f ? fp8_encode(__fdiv_rn(x, scale)) : 0u;
 }
 
+// A chunk's cached keys in registers: requested a chunk ahead of their use, so the loads of
+// chunk c + nwg are in flight while chunk c is computed. bf16 cache: 16 B of a row per
+// thread and request; FP8 cache: 16 codes per request and the row scale (threads 0..15).
+// Positions past the last token (bf16) or from pos on (FP8: the new rows, quantised in the
+// workgroup) read as zero; every address stays inside the cache (the position is clamped).
+template <int DH>
+struct KStage {
+    static constexpr int KB = DH + 8;
+    static constexpr int NB = (kChunk * DH / 8 + 255) / 256;
+    static constexpr int N8 = (kChunk * DH / 16 + 255) / 256;
+    static constexpr int NV = NB > N8 ? NB : N8;
+    uint4 v[NV];
+    float sc;
+    __device__ __forceinline__ void load(const PartArgs &a, int g, int p0, int last) {
+        const int tid = threadIdx.x;
+        const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+        if (!a.fp8) {
+            const uint16_t *cb = reinterpret_cast<const uint16_t *>(a.cache);
+#pragma unroll
+            for (int e = 0; e < NB; ++e) {
+                const int i = min(tid + 256 * e, kChunk * DH / 8 - 1);
+                const int j = i / (DH / 8), cc = i - j * (DH / 8), p = p0 + j;
+                const uint4 t = reinterpret_cast<const uint4 *>(cb + ((size_t)g * a.cap + min(p, last) % a.cap) * DH)[cc];
+                v[e] = p <= last ? t : zero;
+            }
+            sc = 1.0f;
+        } else {
+            const uint8_t *c8 = reinterpret_cast<const uint8_t *>(a.cache);
+            const int lim = a.pos > 0 ? a.pos - 1 : 0;
+#pragma unroll
+            for (int e = 0; e < N8; ++e) {
+                const int i = min(tid + 256 * e, kChunk * DH / 16 - 1);
+                const int j = i / (DH / 16), cc = i - j * (DH / 16), p = p0 + j;
+                const uint4 t = reinterpret_cast<const uint4 *>(c8 + ((size_t)g * a.cap + min(p, lim) % a.cap) * DH)[cc];
+                v[e] = p < a.pos ? t : zero;
+            }
+            const int p = p0 + (tid & (kChunk - 1));
+            const float t = a.kscale[(size_t)g * a.cap + min(p, lim) % a.cap];
+            sc = p < a.pos ? t : 0.0f;
+        }
+    }
+    // the chunk as bf16 rows in LDS (the FP8 codes' values are exact in bf16) and its scales
+    __device__ __forceinline__ void store(const PartArgs &a, uint4 *kb4, float *ksc) const {
+        const int tid = threadIdx.x;
+        if (!a.fp8) {
+#pragma unroll
+            for (int e = 0; e < NB; ++e) {
+                const int i = tid + 256 * e;
+                if (i < kChunk * DH / 8) {
+                    const int j = i / (DH / 8), cc = i - j * (DH / 8);
+                    kb4[(j * KB) / 8 + cc] = v[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < N8; ++e) {
+                const int i = tid + 256 * e;
+                if (i < kChunk * DH / 16) {
+                    const int j = i / (DH / 16), cc = i - j * (DH / 16);
+                    const uint32_t vw[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+                    uint32_t bw[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x2 lo = fp8x2_to_f32<false>(vw[q]), hi = fp8x2_to_f32<true>(vw[q]);
+                        bw[2 * q] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
+                        bw[2 * q + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
+                    }
+                    kb4[(j * KB) / 8 + 2 * cc] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
+                    kb4[(j * KB) / 8 + 2 * cc + 1] = make_uint4(bw[4], bw[5], bw[6], bw[7]);
+                }
+            }
+        }
+        if (tid < kChunk) ksc[tid] = sc;
+    }
+};
+
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_part(PartArgs a) {
     constexpr int KB = DH + 8;   // bf16 row stride of the staged keys (padding spreads the banks)
@@ -196,42 +272,14 @@ __global__ __launch_bounds__(256) void k_attn_part(PartArgs a) {
 #pragma unroll
     for (int i = 0; i < DH / 16; ++i) acc[i] = 0.0f;
 
-    const uint16_t *cb = reinterpret_cast<const uint16_t *>(a.cache);
     uint8_t *c8 = reinterpret_cast<uint8_t *>(a.cache);
+    KStage<DH> ks;
+    if (w < a.nch) ks.load(a, g, a.lo0 + w * kChunk, last);
     for (int c = w; c < a.nch; c += a.nwg) {
         const int p0 = a.lo0 + c * kChunk;
         __syncthreads();
-        // stage the chunk's keys as bf16 rows: as stored, or the FP8 codes' values (exact)
-        if (!a.fp8) {
-            for (int i = tid; i < kChunk * DH / 8; i += 256) {
-                const int j = i / (DH / 8), cc = i - j * (DH / 8), p = p0 + j;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (p <= last)
-                    v = reinterpret_cast<const uint4 *>(cb + ((size_t)g * a.cap + p % a.cap) * DH)[cc];
-                kb4[(j * KB) / 8 + cc] = v;
-            }
-            if (tid < kChunk) ksc[tid] = 1.0f;
-        } else {
-            // older positions: codes and scales from the cache
-            for (int i = tid; i < kChunk * DH / 16; i += 256) {
-                const int j = i / (DH / 16), cc = i - j * (DH / 16), p = p0 + j;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (p < a.pos) v = reinterpret_cast<const uint4 *>(c8 + ((size_t)g * a.cap + p % a.cap) * DH)[cc];
-                const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-                uint32_t bw[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const f32x2 lo = fp8x2_to_f32<false>(vw[e]), hi = fp8x2_to_f32<true>(vw[e]);
-                    bw[2 * e] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xFFFF0000u);
-                    bw[2 * e + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xFFFF0000u);
-                }
-                kb4[(j * KB) / 8 + 2 * cc] = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-                kb4[(j * KB) / 8 + 2 * cc + 1] = make_uint4(bw[4], bw[5], bw[6], bw[7]);
-            }
-            if (tid < kChunk) {
-                const int p = p0 + tid;
-                ksc[tid] = p < a.pos ? a.kscale[(size_t)g * a.cap + p % a.cap] : 0.0f;
-            }
+        ks.store(a, kb4, ksc);
+        if (a.fp8) {
             // new positions in this chunk: quantise the key rows, store them, stage them
             const int jn0 = max(0, a.pos - p0), jn1 = min(kChunk, last - p0 + 1);
             for (int j = jn0; j < jn1; ++j) {
@@ -256,6 +304,7 @@ __global__ __launch_bounds__(256) void k_attn_part(PartArgs a) {
             }
         }
         __syncthreads();
+        if (c + a.nwg < a.nch) ks.load(a, g, p0 + a.nwg * kChunk, last);
         // scores: lane l of query ql takes position p0 + l
         float pj = 0.0f, alpha = 1.0f;
         if (active) {
@@ -326,29 +375,52 @@ struct CombArgs {
     uint16_t *o_user;  // or null
 };
 
-// Query (g, qi): the stripes' records combined in stripe order:
-//   mx = max_w m_w, L = sum_w l_w e^(m_w - mx), o = sum_w acc_w e^(m_w - mx) / L
+// Query (g, qi), dims 64 b .. 64 b + 63 (b = blockIdx.y): the stripes' records combined,
+//   mx = max_w m_w, L = sum_w l_w e^(m_w - mx), o = sum_w acc_w e^(m_w - mx) / L,
+// every sum in a fixed order (thread t takes stripes t, t + 256, ... in turn, then a fixed
+// tree over the threads; wave v takes stripes v, v + 4, ... for the outputs, eight records
+// requested at a time, then the four waves in turn), so the result does not depend on timing.
 __global__ __launch_bounds__(256) void k_attn_combine(CombArgs a) {
-    __shared__ float wt[512];
+    __shared__ float wt[kAttnMaxWG];
+    __shared__ float po[4][64];
     __shared__ float red[4];
-    const int tid = threadIdx.x;
-    const int g = blockIdx.x / a.Q, qi = blockIdx.x - g * a.Q;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = blockIdx.x / a.Q, qi = blockIdx.x - g * a.Q, d = 64 * blockIdx.y + lane;
     const int R = a.dh + 4;
     const float *rec = a.part + ((size_t)g * a.Q + qi) * a.nwg * R;
     float mx = -INFINITY;
     for (int w = tid; w < a.nwg; w += 256) mx = fmaxf(mx, rec[(size_t)w * R]);
     mx = block_max(mx, red);
+    float ls = 0.0f;
     for (int w = tid; w < a.nwg; w += 256) {
         const float m = rec[(size_t)w * R];
-        wt[w] = m == -INFINITY ? 0.0f : expf(m - mx);
+        const float e = m == -INFINITY ? 0.0f : expf(m - mx);
+        wt[w] = e;
+        ls = fmaf(rec[(size_t)w * R + 1], e, ls);
     }
+    ls = row16_sum(ls);
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
     __syncthreads();
-    float L = 0.0f;
-    for (int w = 0; w < a.nwg; ++w) L = fmaf(rec[(size_t)w * R + 1], wt[w], L);
-    const int m = qi / a.G, h = g * a.G + (qi - m * a.G), NQ = a.G * a.nkv * a.dh;
-    for (int d = tid; d < a.dh; d += 256) {
-        float o = 0.0f;
-        for (int w = 0; w < a.nwg; ++w) o = fmaf(rec[(size_t)w * R + 4 + d], wt[w], o);
+    if (lane == 0) red[wv] = ls;
+    __syncthreads();
+    const float L = (red[0] + red[1]) + (red[2] + red[3]);
+    const float *col = rec + 4 + d;
+    float acc = 0.0f;
+    int w = wv;
+    for (; w + 28 < a.nwg; w += 32) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = col[(size_t)(w + 4 * k) * R];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc = fmaf(v[k], wt[w + 4 * k], acc);
+    }
+    for (; w < a.nwg; w += 4) acc = fmaf(col[(size_t)w * R], wt[w], acc);
+    po[wv][lane] = acc;
+    __syncthreads();
+    if (tid < 64) {
+        const int m = qi / a.G, h = g * a.G + (qi - m * a.G), NQ = a.G * a.nkv * a.dh;
+        const float o = ((po[0][tid] + po[1][tid]) + po[2][tid]) + po[3][tid];
         const uint16_t v = f2bf(o / L);
         a.o[(size_t)m * NQ + (size_t)h * a.dh + d] = v;
         if (a.o_user) a.o_user[(size_t)m * NQ + (size_t)h * a.dh + d] = v;
@@ -451,7 +523,7 @@ int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M,
         return MOE_EINVAL;
 
     CombArgs ca{part, d.kv_heads, P.G, P.Q, P.nwg, d.head_dim, o, o_user};
-    hipLaunchKernelGGL(k_attn_combine, dim3(d.kv_heads * P.Q), dim3(256), 0, S(stream), ca);
+    hipLaunchKernelGGL(k_attn_combine, dim3(d.kv_heads * P.Q, d.head_dim / 64), dim3(256), 0, S(stream), ca);
 
     ProjArgs po{w.o_w, w.o_s, nullptr, nullptr, d.hidden, 0, NQ, M, o, out, nullptr, nullptr, 0, 0, 0};
     rc = launch_proj(po, stream);
