@@ -459,15 +459,46 @@ __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]
 // step's, so both give the same logits for the same u.
 __device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
     const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
-    const int e = min(8 * j + (tid >> 5), E - 1);
-    const uint16_t *base = layer_w(a, 0)->router_w + e + (size_t)(tid & 31) * 8 * E;
+    if (E % 8) {
+        // rows not 16-byte aligned: one element per load
+        const int e = min(8 * j + (tid >> 5), E - 1);
+        const uint16_t *base = layer_w(a, 0)->router_w + e + (size_t)(tid & 31) * 8 * E;
+#pragma unroll
+        for (int k = 0; k < kNC; ++k) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = k < NC ? *glb(base + ((size_t)k * 256 + i) * E) : 0u;
+            wq[k] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        }
+        return;
+    }
+    // Pass k covers rows 256 k .. 256 k + 255: thread t requests the 16 bytes of row 256 k + t
+    // that hold experts 8 j .. 8 j + 7 (every pass's load is issued first); each pass then goes
+    // through an LDS tile (rows padded by 16 bytes every 8 rows, which spreads the banks), from
+    // which thread (expert tid / 32, lane l = tid % 32) takes rows 8 l .. 8 l + 7 of its expert.
+    // The tile lies in the u area, which layer_input fills only after this.
+    const uint16_t *col = layer_w(a, 0)->router_w + 8 * j;
+    uint4 r[kNC];
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) r[k] = ld16(col + ((size_t)min(k, NC - 1) * 256 + tid) * E);
+    uint4 *tile = reinterpret_cast<uint4 *>(ulds());   // 288 x 16 bytes
+    uint16_t *t16 = reinterpret_cast<uint16_t *>(ulds());
+    const int e = tid >> 5, l8 = (tid & 31) * 8;
 #pragma unroll
     for (int k = 0; k < kNC; ++k) {
-        uint32_t v[8];
+        if (k < NC) {
+            __syncthreads();
+            tile[tid + (tid >> 3)] = r[k];
+            __syncthreads();
+            uint32_t v[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = k < NC ? *glb(base + ((size_t)k * 256 + i) * E) : 0u;
-        wq[k] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+            for (int i = 0; i < 8; ++i) v[i] = t16[(l8 + i + ((l8 + i) >> 3)) * 8 + e];
+            wq[k] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
+        } else {
+            wq[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
     }
+    __syncthreads();
 }
 
 // Router workgroup j, layer l: u_l, then the logits of experts 8j .. 8j+7 for every
@@ -1354,11 +1385,10 @@ __device__ __forceinline__ void lm_phase(AP a0, int w, int G, uint32_t tgt) {
     }
 }
 
-// Layer mode, the end of the call: every workgroup signals; workgroup 0 waits for all of
-// them (so that every workgroup has read the epoch) and advances the epoch.
+// Layer mode, the end of the call: workgroup 0 waits for every workgroup's flag (raised
+// when it had read the epoch, at its start) and advances the epoch.
 __device__ __forceinline__ void layer_end(AP a0, int w, int G, uint32_t tgt) {
     const AP a = uniform(a0);
-    publish(flags(a) + a->f_lm + w, tgt);
     if (w != 0) return;
     wait_flags(a, flags(a) + a->f_lm, G, tgt);
     if (ltid() == 0) st32(flags(a) + a->f_epoch, tgt);
@@ -1383,6 +1413,9 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
     const AP base = (AP)__builtin_amdgcn_kernarg_segment_ptr();
     const int w = blockIdx.x, G = gridDim.x, GU = G - base->NR;
     const uint32_t tgt = __builtin_amdgcn_readfirstlane(ld32(flags(base) + base->f_epoch)) + 1u;
+    // one-layer mode: the step counter may advance once every workgroup has read it, so the
+    // flag workgroup 0 waits for at the end is raised here rather than after the work
+    if (base->layer_mode) publish(flags(base) + base->f_lm + w, tgt);
     if (w >= GU) {
         // router workgroup: each layer's weights are requested as soon as the previous
         // layer's logits are out
