@@ -696,7 +696,7 @@ int launch_moe_layer(const moe_layer_desc &d, const moe_layer_weights &w, int M,
                      char *ws, const LayerWs &L, void *stream) {
     (void)hipGetLastError();
     const int H = d.hidden, E = d.num_experts;
-    RouterArgs ra{x, w.router_w, reinterpret_cast<float *>(ws + L.partial), M, H, E};
+    RouterArgs ra{x, static_cast<const uint16_t *>(w.router_w), reinterpret_cast<float *>(ws + L.partial), M, H, E};
     hipLaunchKernelGGL(k_router, dim3(L.nb), dim3(256), 0, S(stream), ra);
     TopkArgs ta{reinterpret_cast<const float *>(ws + L.partial), w.router_bias, topk_idx, topk_w,
                 reinterpret_cast<int32_t *>(ws + L.n_slots), reinterpret_cast<int32_t *>(ws + L.slot_expert),

@@ -56,7 +56,7 @@ using namespace dev;
 
 struct StepArgs {
     const moe_layer_weights *layers;   // device table [L]
-    const uint16_t *rt;                // router weights re-laid out [L][E][H]
+    const uint16_t *rt;                // router weights re-laid out [L][E][H] (bf16, or FP8 codes)
     const uint16_t *gains;             // [L+1][H]
     const uint16_t *x;                 // [M][H]
     const uint16_t *noise;             // [L][M][H]
@@ -81,6 +81,7 @@ struct StepArgs {
     unsigned spin_limit;
     int layer_mode;                    // 1: one MoE layer from x (already normalised) to y (moe_decode_layer)
     int lm_bf;                         // 1: lm_w holds bf16 weights without scales
+    int router_fp8;                    // 1: FP8 router codes with per-expert scales (router_s)
     moe_layer_weights lw;              // layer mode: the layer's weights (router as given, [H][E])
 };
 
@@ -123,6 +124,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld16(const void *p) {
     const u32x4 v = *(const GAS u32x4 *)p;
     return make_uint4(v.x, v.y, v.z, v.w);
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld8(const void *p) {
+    const u32x2 v = *(const GAS u32x2 *)p;
+    return make_uint2(v.x, v.y);
+}
+// eight FP8 router codes (column order) -> eight bf16 (exact: scale 1)
+__device__ __forceinline__ uint4 widen8(uint2 q) {
+    return make_uint4(__builtin_bit_cast(uint32_t, fp8x2_to_bf16<false>(q.x)),
+                      __builtin_bit_cast(uint32_t, fp8x2_to_bf16<true>(q.x)),
+                      __builtin_bit_cast(uint32_t, fp8x2_to_bf16<false>(q.y)),
+                      __builtin_bit_cast(uint32_t, fp8x2_to_bf16<true>(q.y)));
 }
 
 // The thread index, made opaque so that values derived from it are formed where a
@@ -447,10 +460,58 @@ __device__ __forceinline__ void layer_input(AP a, int l, uint32_t tgt) {
 __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]) {
     const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
     const int e = min(8 * j + (tid >> 5), E - 1);
+    if (a->router_fp8) {   // codes [L][E][H]: eight per piece, widened to bf16
+        const uint8_t *wr8 = reinterpret_cast<const uint8_t *>(a->rt) + ((size_t)l * E + e) * H + (tid & 31) * 8;
+#pragma unroll
+        for (int k = 0; k < kNC; ++k) wq[k] = k < NC ? widen8(ld8(wr8 + k * 256)) : make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
     const uint16_t *wr = a->rt + ((size_t)l * E + e) * H + (tid & 31) * 8;
 #pragma unroll
     for (int k = 0; k < kNC; ++k)
         wq[k] = k < NC ? ld16(wr + k * 256) : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Layer mode, FP8 router codes [H][E] (bytes): as router_load_hxe with 8-byte loads (the
+// codes of experts 8 j .. 8 j + 7 in one row) through an LDS tile, the pieces widened to
+// bf16; rows that are not 8-byte aligned (E not a multiple of 8) take one byte per load.
+__device__ __forceinline__ void router_load_hxe8(AP a, int j, uint4 (&wq)[kNC]) {
+    const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
+    const uint8_t *w8 = static_cast<const uint8_t *>(layer_w(a, 0)->router_w);
+    const int e = tid >> 5, l8 = (tid & 31) * 8;
+    if (E % 8) {
+        const int ee = min(8 * j + e, E - 1);
+#pragma unroll
+        for (int k = 0; k < kNC; ++k) {
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = k < NC ? *glb(w8 + ((size_t)k * 256 + l8 + i) * E + ee) : 0u;
+            wq[k] = widen8(make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)));
+        }
+        return;
+    }
+    uint2 r[kNC];
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) r[k] = ld8(w8 + ((size_t)min(k, NC - 1) * 256 + tid) * E + 8 * j);
+    uint2 *tile = reinterpret_cast<uint2 *>(ulds());   // 288 x 8 bytes
+    const uint8_t *t8 = reinterpret_cast<const uint8_t *>(ulds());
+#pragma unroll
+    for (int k = 0; k < kNC; ++k) {
+        if (k < NC) {
+            __syncthreads();
+            tile[tid + (tid >> 3)] = r[k];
+            __syncthreads();
+            uint32_t c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[i] = t8[(l8 + i + ((l8 + i) >> 3)) * 8 + e];
+            wq[k] = widen8(make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
+                                      c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)));
+        } else {
+            wq[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    __syncthreads();
 }
 
 // Layer mode: the same per-lane pieces gathered from the router weights as given, [H][E]
@@ -459,10 +520,14 @@ __device__ __forceinline__ void router_load(AP a, int l, int j, uint4 (&wq)[kNC]
 // step's, so both give the same logits for the same u.
 __device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
     const int H = a->H, E = a->E, NC = H / 256, tid = ltid();
+    if (a->router_fp8) {
+        router_load_hxe8(a, j, wq);
+        return;
+    }
     if (E % 8) {
         // rows not 16-byte aligned: one element per load
         const int e = min(8 * j + (tid >> 5), E - 1);
-        const uint16_t *base = layer_w(a, 0)->router_w + e + (size_t)(tid & 31) * 8 * E;
+        const uint16_t *base = static_cast<const uint16_t *>(layer_w(a, 0)->router_w) + e + (size_t)(tid & 31) * 8 * E;
 #pragma unroll
         for (int k = 0; k < kNC; ++k) {
             uint32_t v[8];
@@ -477,7 +542,7 @@ __device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
     // through an LDS tile (rows padded by 16 bytes every 8 rows, which spreads the banks), from
     // which thread (expert tid / 32, lane l = tid % 32) takes rows 8 l .. 8 l + 7 of its expert.
     // The tile lies in the u area, which layer_input fills only after this.
-    const uint16_t *col = layer_w(a, 0)->router_w + 8 * j;
+    const uint16_t *col = static_cast<const uint16_t *>(layer_w(a, 0)->router_w) + 8 * j;
     uint4 r[kNC];
 #pragma unroll
     for (int k = 0; k < kNC; ++k) r[k] = ld16(col + ((size_t)min(k, NC - 1) * 256 + tid) * E);
@@ -511,6 +576,8 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
     const bool valid = e < E;
     const float *bias = layer_w(a, l)->router_bias;
     const float bv = (bias && valid) ? glb(bias)[e] : 0.0f;   // requested before the norm's polls
+    const float *rsp = layer_w(a, l)->router_s;
+    const float rs = (a->router_fp8 && valid) ? glb(rsp)[e] : 1.0f;   // FP8 router: the expert's scale
     layer_input<MT>(a, l, tgt);
     const uint16_t *u = ulds();
     float acc[MT];
@@ -543,7 +610,7 @@ __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&
     // for the first store to complete
     float v[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) v[m] = half_sum(acc[m]) + bv;
+    for (int m = 0; m < MT; ++m) v[m] = half_sum(acc[m]) * rs + bv;
     uint64_t *lg = logits(a, l);
     if (lane32 == 16 && valid) {
 #pragma unroll
@@ -1451,8 +1518,9 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
         lm_phase<MT, false>(a, w, G, tgt);
 }
 
-// Router weights [H][E] -> [E][H] (once, at prepare time).
-__global__ void k_router_transpose(const uint16_t *__restrict__ src, uint16_t *__restrict__ dst, int H, int E) {
+// Router weights [H][E] -> [E][H] (once, at prepare time); T is bf16 bits or FP8 codes.
+template <class T>
+__global__ void k_router_transpose(const T *__restrict__ src, T *__restrict__ dst, int H, int E) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (size_t)H * E) return;
     const int e = (int)(i / H), h = (int)(i % H);
@@ -1535,8 +1603,14 @@ int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weig
     const int H = ld.hidden, E = ld.num_experts;
     const size_t n = (size_t)H * E;
     for (int l = 0; l < W.L; ++l) {
-        hipLaunchKernelGGL(k_router_transpose, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr,
-                           layers[l].router_w, reinterpret_cast<uint16_t *>(ws + W.rt) + (size_t)l * n, H, E);
+        if (ld.router_type == MOE_ROUTER_FP8)
+            hipLaunchKernelGGL(k_router_transpose<uint8_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr,
+                               static_cast<const uint8_t *>(layers[l].router_w),
+                               reinterpret_cast<uint8_t *>(ws + W.rt) + (size_t)l * n, H, E);
+        else
+            hipLaunchKernelGGL(k_router_transpose<uint16_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr,
+                               static_cast<const uint16_t *>(layers[l].router_w),
+                               reinterpret_cast<uint16_t *>(ws + W.rt) + (size_t)l * n, H, E);
         if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
     }
     return hipDeviceSynchronize() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
@@ -1569,6 +1643,7 @@ int launch_layer_step(const moe_layer_desc &ld, const moe_layer_weights &w, int 
     const StepWs W = step_ws(d, false);
     StepArgs a{};
     a.layer_mode = 1;
+    a.router_fp8 = ld.router_type == MOE_ROUTER_FP8 ? 1 : 0;
     a.lw = w;
     a.x = x;
     a.y = y;
@@ -1624,6 +1699,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.lm_w = lm_w;
     a.lm_s = lm_s;
     a.lm_bf = (d.flags & MOE_STEP_LM_BF16) ? 1 : 0;
+    a.router_fp8 = d.layer.router_type == MOE_ROUTER_FP8 ? 1 : 0;
     a.draft = draft;
     a.token = token;
     a.max_logit = max_logit;

@@ -19,6 +19,7 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 
 MOE_ETIMEOUT = -6
 MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 MOE_KV_BF16, MOE_KV_FP8 = 0, 1
+MOE_ROUTER_BF16, MOE_ROUTER_FP8 = 0, 1
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
@@ -37,7 +38,8 @@ class MoeError(RuntimeError):
 
 class LayerDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int), ("num_experts", ctypes.c_int), ("top_k", ctypes.c_int),
-                ("expert_width", ctypes.c_int), ("shared_width", ctypes.c_int), ("wtype", ctypes.c_int)]
+                ("expert_width", ctypes.c_int), ("shared_width", ctypes.c_int), ("wtype", ctypes.c_int),
+                ("router_type", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p
@@ -46,7 +48,7 @@ _P = ctypes.c_void_p
 class LayerWeights(ctypes.Structure):
     _fields_ = [(n, _P) for n in ("router_w", "router_bias", "gate_w", "up_w", "down_w", "gate_s",
                                   "up_s", "down_s", "sh_gate_w", "sh_up_w", "sh_down_w",
-                                  "sh_gate_s", "sh_up_s", "sh_down_s")]
+                                  "sh_gate_s", "sh_up_s", "sh_down_s", "router_s")]
 
 
 class StepDesc(ctypes.Structure):
@@ -167,15 +169,16 @@ def _check(fn, st):
         raise MoeError(fn, st)
 
 
-def layer_desc(shape, expert_dtype: str = "fp8") -> LayerDesc:
+def layer_desc(shape, expert_dtype: str = "fp8", router_dtype: str = "bf16") -> LayerDesc:
     return LayerDesc(shape.hidden, shape.experts, shape.top_k, shape.width, shape.shared_width,
-                     MOE_W_FP8_E4M3 if expert_dtype == "fp8" else MOE_W_BF16)
+                     MOE_W_FP8_E4M3 if expert_dtype == "fp8" else MOE_W_BF16,
+                     MOE_ROUTER_FP8 if router_dtype == "fp8" else MOE_ROUTER_BF16)
 
 
 def layer_weights(w: dict) -> LayerWeights:
     """LayerWeights from a dict of device tensors (keys as synth.layer_weights)."""
     keys = ("router_w", "router_b", "gate_w", "up_w", "down_w", "gate_s", "up_s", "down_s",
-            "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s")
+            "sh_gate_w", "sh_up_w", "sh_down_w", "sh_gate_s", "sh_up_s", "sh_down_s", "router_s")
     return LayerWeights(*[_ptr(w.get(k)) for k in keys])
 
 
@@ -257,8 +260,10 @@ def moe_hbm_read_probe(src, nbytes, sink, stream=None):
 
 
 def step_desc(shape, max_tokens: int, eps: float = 1e-6, spin_limit: int = 0,
-              expert_dtype: str = "fp8", cooperative: bool = False, lm_bf16: bool = False) -> StepDesc:
-    return StepDesc(layer_desc(shape, expert_dtype), shape.layers, shape.vocab, max_tokens, eps, spin_limit,
+              expert_dtype: str = "fp8", cooperative: bool = False, lm_bf16: bool = False,
+              router_dtype: str = "bf16") -> StepDesc:
+    return StepDesc(layer_desc(shape, expert_dtype, router_dtype), shape.layers, shape.vocab, max_tokens, eps,
+                    spin_limit,
                     (MOE_STEP_COOPERATIVE if cooperative else 0) | (MOE_STEP_LM_BF16 if lm_bf16 else 0))
 
 

@@ -26,7 +26,7 @@ class DecodeStack:
         self.max_M = max_M
         self.eps = eps
         self.layers = layers                      # keep the tensors alive
-        self.desc = native.layer_desc(shape, expert_dtype)
+        self.desc = native.layer_desc(shape, expert_dtype, layers[0].get("router_dtype", "bf16"))
         self.lw = [native.layer_weights(w) for w in layers]
         self.gains = gains
         self.lm_w, self.lm_s = lm_w, lm_s
@@ -82,7 +82,7 @@ class FusedDecodeStep:
         expert_dtype = layers[0].get("expert_dtype", "fp8")
         self.lm_bf16 = lm_w.dtype == torch.bfloat16      # the BF16 rung: [V][H] bf16, no scales
         self.desc = native.step_desc(shape.with_(layers=self.L), max_M, eps, spin_limit, expert_dtype,
-                                     cooperative, self.lm_bf16)
+                                     cooperative, self.lm_bf16, layers[0].get("router_dtype", "bf16"))
         self.ws_bytes = native.moe_decode_step_workspace(self.desc)
         if self.ws_bytes == 0:
             raise ValueError("unsupported shape for the fused decode step")

@@ -59,6 +59,14 @@ typedef enum moe_wtype {
     MOE_W_BF16 = 1          /* expert weights: bf16, no scales                               */
 } moe_wtype;
 
+/* Router weights (page "LLM decoding", "Lever 1: fewer bytes" and "The ladder, every
+ * rung": the precision of each matrix is a rung of its own). */
+typedef enum moe_router_type {
+    MOE_ROUTER_BF16 = 0,    /* router_w bf16 [H][E]                                          */
+    MOE_ROUTER_FP8 = 1      /* router_w FP8 E4M3FN codes [H][E], router_s fp32 [E] (one scale
+                               per expert, applied to the finished logit)                     */
+} moe_router_type;
+
 /* Shape of one MoE layer.
  *   hidden        H: a multiple of 256, at most 4096            (Gemma-4-26B-A4B: 2816)
  *   num_experts   E: even, 2..256                                (128)
@@ -66,7 +74,9 @@ typedef enum moe_wtype {
  *   expert_width  D: a multiple of 64, 64..4096                  (704)
  *   shared_width  Ds: 0 (no shared expert) or a multiple of 64 up to 4096 (704; the
  *                 page's dense MLP is 2112 wide)
- *   wtype         a moe_wtype for the routed and shared expert matrices */
+ *   wtype         a moe_wtype for the routed and shared expert matrices
+ *   router_type   a moe_router_type (MOE_ROUTER_BF16 when zero-initialised); an FP8 router
+ *                 runs on the fused step and on moe_decode_layer's one-launch form only */
 typedef struct moe_layer_desc {
     int hidden;
     int num_experts;
@@ -74,17 +84,19 @@ typedef struct moe_layer_desc {
     int expert_width;
     int shared_width;
     int wtype;
+    int router_type;
 } moe_layer_desc;
 
 /* Weights of one MoE layer (device pointers, 16-byte aligned).
- *   router_w     bf16 [H][E]
+ *   router_w     [H][E]: bf16, or FP8 E4M3FN codes (router_type MOE_ROUTER_FP8)
  *   router_bias  fp32 [E], added to the logits before the softmax; NULL for none
  *   gate_w, up_w [E][D][H]   down_w [E][H][D]   (FP8 codes or bf16 per wtype)
  *   gate_s, up_s fp32 [E][D] down_s fp32 [E][H] (FP8 only; ignored for bf16)
  *   sh_*         the shared expert: gate/up [Ds][H], down [H][Ds], scales [Ds],[Ds],[H];
- *                ignored when shared_width == 0 */
+ *                ignored when shared_width == 0
+ *   router_s     fp32 [E], the FP8 router's per-expert scales (ignored for a bf16 router) */
 typedef struct moe_layer_weights {
-    const uint16_t *router_w;
+    const void *router_w;
     const float *router_bias;
     const void *gate_w;
     const void *up_w;
@@ -98,6 +110,7 @@ typedef struct moe_layer_weights {
     const float *sh_gate_s;
     const float *sh_up_s;
     const float *sh_down_s;
+    const float *router_s;
 } moe_layer_weights;
 
 /* Bytes of device workspace moe_decode_layer needs for up to max_M tokens
@@ -123,7 +136,8 @@ int moe_decode_layer_status(const moe_layer_desc *desc, void *workspace);
  * "Lever 1: fewer bytes (FP8 weights)" (8-bit weights, arithmetic in a wider type).
  * The gating (softmax over all experts, keep K, renormalise), the GELU-tanh gate and
  * the tie rule are readings the page leaves open.
- *   logits[m][e] = sum_c x[m][c] * router_w[c][e] (+ router_bias[e])
+ *   logits[m][e] = sum_c x[m][c] * router_w[c][e] (+ router_bias[e]); an FP8 router:
+ *                  router_s[e] * sum_c x[m][c] * decode(router_w[c][e]) (+ router_bias[e])
  *   S_m          = the K experts with the largest logits (equal logits: lower id)
  *   w[m][e]      = softmax(logits[m])[e] / sum_{j in S_m} softmax(logits[m])[j]
  *   expert_e(v)  = down_e( gelu_tanh(gate_e v) * (up_e v) ),

@@ -58,7 +58,9 @@ def lib():
             L.oracle_router.restype = None
             L.oracle_router.argtypes = [I, I, I, I, P, P, P, P, P, P, P]
             L.oracle_moe_layer.restype = None
-            L.oracle_moe_layer.argtypes = [I] * 7 + [P] * 21
+            L.oracle_moe_layer.argtypes = [I] * 7 + [P] * 22
+            L.oracle_router_fp8.restype = None
+            L.oracle_router_fp8.argtypes = [I, I, I, I, P, P, P, P, P, P, P, P]
             L.oracle_lm_head.restype = None
             L.oracle_lm_head.argtypes = [I, I, I, P, P, P, P, P, P]
             L.oracle_lm_head_bf16.restype = None
@@ -146,6 +148,23 @@ def router(u, W, bias, K):
     return {"idx": idx, "w": wts, "gap": gap, "logits": logits}
 
 
+def router_fp8(u, W8, s, bias, K):
+    """u uint16 [M][H], W8 uint8 FP8 codes [H][E], s f32 [E], bias f32 [E] or None ->
+    dict(idx, w, gap, logits) (oracle_router_fp8)."""
+    u = _c(u, np.uint16)
+    W8 = _c(W8, np.uint8)
+    s = _c(s, np.float32)
+    bias = _c(bias, np.float32)
+    M, H = u.shape
+    E = W8.shape[1]
+    logits = np.empty((M, E), np.float64)
+    idx = np.empty((M, K), np.int32)
+    wts = np.empty((M, K), np.float64)
+    gap = np.empty(M, np.float64)
+    lib().oracle_router_fp8(M, H, E, K, _p(u), _p(W8), _p(s), _p(bias), _p(logits), _p(idx), _p(wts), _p(gap))
+    return {"idx": idx, "w": wts, "gap": gap, "logits": logits}
+
+
 def moe_layer(u, w: dict, K: int):
     """One MoE layer. u uint16 [M][H]; w: synth.weights_to_host(layer_weights(...)).
 
@@ -160,8 +179,10 @@ def moe_layer(u, w: dict, K: int):
     E, D, _ = G.shape
     shG = _c(w["sh_gate_w"], edt)
     Ds = 0 if shG is None else shG.shape[0]
+    rfp8 = w.get("router_s") is not None
     args = dict(
-        router_w=_c(w["router_w"], np.uint16), router_b=_c(w["router_b"], np.float32),
+        router_w=_c(w["router_w"], np.uint8 if rfp8 else np.uint16),
+        router_s=_c(w.get("router_s"), np.float32), router_b=_c(w["router_b"], np.float32),
         G=G, U=_c(w["up_w"], edt), Dn=_c(w["down_w"], edt),
         gs=_c(w["gate_s"], np.float32), us=_c(w["up_s"], np.float32),
         ds=_c(w["down_s"], np.float32),
@@ -177,7 +198,7 @@ def moe_layer(u, w: dict, K: int):
     y = np.empty((M, H), np.float64)
     yb = np.empty((M, H), np.uint16)
     lib().oracle_moe_layer(
-        M, H, E, K, D, Ds, wtype, _p(u), _p(args["router_w"]), _p(args["router_b"]),
+        M, H, E, K, D, Ds, wtype, _p(u), _p(args["router_w"]), _p(args["router_s"]), _p(args["router_b"]),
         _p(args["G"]), _p(args["U"]), _p(args["Dn"]), _p(args["gs"]), _p(args["us"]),
         _p(args["ds"]), _p(args["shG"]), _p(args["shU"]), _p(args["shD"]),
         _p(args["shgs"]), _p(args["shus"]), _p(args["shds"]),

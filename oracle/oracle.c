@@ -161,6 +161,35 @@ static int int_asc(const void *a, const void *b)
  * with wts aligned to it. gap[m] = K-th largest logit minus (K+1)-th (INFINITY when
  * K == E): the margin of the selection decision.
  */
+/* Softmax, top-K and renormalisation of one token's logits l[0..E) (the selection of
+ * oracle_router; shared by the bf16 and FP8 routers). */
+static void router_select(int E, int K, const double *l, vi_t *order, int *sel, int32_t *idx, double *wts,
+                          double *gap)
+{
+    double lmax = l[0];
+    for (int e = 1; e < E; ++e)
+        if (l[e] > lmax) lmax = l[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e)
+        z += exp(l[e] - lmax);
+    for (int e = 0; e < E; ++e) {
+        order[e].v = l[e];
+        order[e].i = e;
+    }
+    qsort(order, (size_t)E, sizeof(vi_t), by_logit_desc);
+    for (int k = 0; k < K; ++k)
+        sel[k] = order[k].i;
+    *gap = (K < E) ? order[K - 1].v - order[K].v : INFINITY;
+    qsort(sel, (size_t)K, sizeof(int), int_asc);
+    double ps = 0.0;
+    for (int k = 0; k < K; ++k)
+        ps += exp(l[sel[k]] - lmax) / z;
+    for (int k = 0; k < K; ++k) {
+        idx[k] = sel[k];
+        wts[k] = (exp(l[sel[k]] - lmax) / z) / ps;
+    }
+}
+
 void oracle_router(int M, int H, int E, int K, const uint16_t *u, const uint16_t *W,
                    const float *bias, double *logits, int32_t *idx, double *wts,
                    double *gap)
@@ -177,28 +206,37 @@ void oracle_router(int M, int H, int E, int K, const uint16_t *u, const uint16_t
                 acc += (double)bias[e];
             l[e] = acc;
         }
-        double lmax = l[0];
-        for (int e = 1; e < E; ++e)
-            if (l[e] > lmax) lmax = l[e];
-        double z = 0.0;
-        for (int e = 0; e < E; ++e)
-            z += exp(l[e] - lmax);
+        router_select(E, K, l, order, sel, idx + (size_t)m * K, wts + (size_t)m * K, gap + m);
+    }
+    free(order);
+    free(sel);
+}
+
+/*
+ * The FP8 router (the precision ladder's FP8 router rung: [LLMD] "Lever 1: fewer bytes" and
+ * "The ladder, every rung"): W8 holds E4M3FN codes [H][E] and s one fp32 scale per expert,
+ * applied after the dot product as for the experts' rows:
+ *   logits[m][e] = s[e] * sum_c u[m][c] * decode(W8[c][e]) (+ bias[e])
+ * then the selection of oracle_router.
+ */
+void oracle_router_fp8(int M, int H, int E, int K, const uint16_t *u, const uint8_t *W8, const float *s,
+                       const float *bias, double *logits, int32_t *idx, double *wts, double *gap)
+{
+    vi_t *order = malloc(sizeof(vi_t) * (size_t)E);
+    int *sel = malloc(sizeof(int) * (size_t)K);
+    fp8_tab_init();
+    for (int m = 0; m < M; ++m) {
+        double *l = logits + (size_t)m * E;
         for (int e = 0; e < E; ++e) {
-            order[e].v = l[e];
-            order[e].i = e;
+            double acc = 0.0;
+            for (int c = 0; c < H; ++c)
+                acc += oracle_bf16(u[(size_t)m * H + c]) * fp8(W8[(size_t)c * E + e]);
+            acc *= (double)s[e];
+            if (bias)
+                acc += (double)bias[e];
+            l[e] = acc;
         }
-        qsort(order, (size_t)E, sizeof(vi_t), by_logit_desc);
-        for (int k = 0; k < K; ++k)
-            sel[k] = order[k].i;
-        gap[m] = (K < E) ? order[K - 1].v - order[K].v : INFINITY;
-        qsort(sel, (size_t)K, sizeof(int), int_asc);
-        double ps = 0.0;
-        for (int k = 0; k < K; ++k)
-            ps += exp(l[sel[k]] - lmax) / z;
-        for (int k = 0; k < K; ++k) {
-            idx[(size_t)m * K + k] = sel[k];
-            wts[(size_t)m * K + k] = (exp(l[sel[k]] - lmax) / z) / ps;
-        }
+        router_select(E, K, l, order, sel, idx + (size_t)m * K, wts + (size_t)m * K, gap + m);
     }
     free(order);
     free(sel);
@@ -251,10 +289,11 @@ static void expert_apply(int H, int F, int wtype, const uint16_t *u,
  * one always-on shared expert); it is not renormalised with the routed experts.
  * y is returned in fp64 and rounded once to bf16 (y_bf16), the boundary's type.
  * Expert weights: G, U [E][D][H], Dn [E][H][D]; shared [Ds][H], [Ds][H], [H][Ds]
- * (Ds == 0: no shared expert).
+ * (Ds == 0: no shared expert). router_w is bf16 [H][E], or FP8 codes [H][E] when
+ * router_s (fp32 [E]) is given (oracle_router_fp8).
  */
 void oracle_moe_layer(int M, int H, int E, int K, int D, int Ds, int wtype,
-                      const uint16_t *u, const uint16_t *router_w, const float *router_b,
+                      const uint16_t *u, const void *router_w, const float *router_s, const float *router_b,
                       const void *G, const void *U, const void *Dn,
                       const float *gs, const float *us, const float *ds,
                       const void *shG, const void *shU, const void *shD,
@@ -267,7 +306,10 @@ void oracle_moe_layer(int M, int H, int E, int K, int D, int Ds, int wtype,
     double *hbuf = malloc(sizeof(double) * (size_t)(F > 0 ? F : 1));
     double *o = malloc(sizeof(double) * (size_t)H);
     fp8_tab_init();
-    oracle_router(M, H, E, K, u, router_w, router_b, logits, idx, wts, gap);
+    if (router_s)
+        oracle_router_fp8(M, H, E, K, u, (const uint8_t *)router_w, router_s, router_b, logits, idx, wts, gap);
+    else
+        oracle_router(M, H, E, K, u, (const uint16_t *)router_w, router_b, logits, idx, wts, gap);
     for (int m = 0; m < M; ++m) {
         const uint16_t *um = u + (size_t)m * H;
         double *ym = y + (size_t)m * H;

@@ -113,10 +113,11 @@ def _fp8_matrix(shape, std, device, *key):
 
 def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
                   tag: str = "moe", expert_dtype: str = "fp8",
-                  router_bias: Optional[torch.Tensor] = None) -> dict:
+                  router_bias: Optional[torch.Tensor] = None, router_dtype: str = "bf16") -> dict:
     """Weights of one MoE layer in the boundary's logical row-major layout.
 
-    router_w  bf16 [H][E]            N(0, 0.05)
+    router_w  bf16 [H][E]            N(0, 0.05); with router_dtype="fp8" the same draws as
+              FP8 codes [H][E] quantised per expert (column), scales router_s fp32 [E]
     router_b  fp32 [E] or None
     gate_w/up_w  [E][D][H], down_w [E][H][D]: uint8 FP8 codes (expert_dtype="fp8",
               with fp32 per-row scales gate_s/up_s [E][D], down_s [E][H]) or bf16
@@ -125,8 +126,16 @@ def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
     """
     H, E, D, Ds = shape.hidden, shape.experts, shape.width, shape.shared_width
     k = (seed, tag, layer)
-    out = {"router_w": normal((H, E), ROUTER_STD, device, *k, "router").to(torch.bfloat16),
-           "router_b": None if router_bias is None else router_bias.to(device=device, dtype=torch.float32)}
+    rw = normal((H, E), ROUTER_STD, device, *k, "router")
+    out = {"router_b": None if router_bias is None else router_bias.to(device=device, dtype=torch.float32)}
+    if router_dtype == "fp8":
+        codes, rs = quantize_rows_fp8(rw.t().contiguous())
+        out["router_w"], out["router_s"] = codes.t().contiguous(), rs
+    elif router_dtype == "bf16":
+        out["router_w"], out["router_s"] = rw.to(torch.bfloat16), None
+    else:
+        raise ValueError(router_dtype)
+    del rw
 
     def mat(shp, name):
         if expert_dtype == "fp8":
@@ -151,6 +160,7 @@ def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
             out["sh_%s_w" % name] = None
             out["sh_%s_s" % name] = None
     out["expert_dtype"] = expert_dtype
+    out["router_dtype"] = router_dtype
     return out
 
 

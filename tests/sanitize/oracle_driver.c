@@ -19,8 +19,10 @@ uint16_t oracle_bf16_round(double v);
 double oracle_gelu_tanh(double z);
 void oracle_router(int M, int H, int E, int K, const uint16_t *u, const uint16_t *W, const float *bias,
                    double *logits, int32_t *idx, double *wts, double *gap);
+void oracle_router_fp8(int M, int H, int E, int K, const uint16_t *u, const uint8_t *W8, const float *s,
+                       const float *bias, double *logits, int32_t *idx, double *wts, double *gap);
 void oracle_moe_layer(int M, int H, int E, int K, int D, int Ds, int wtype, const uint16_t *u,
-                      const uint16_t *router_w, const float *router_b, const void *G, const void *U,
+                      const void *router_w, const float *router_s, const float *router_b, const void *G, const void *U,
                       const void *Dn, const float *gs, const float *us, const float *ds, const void *shG,
                       const void *shU, const void *shD, const float *shgs, const float *shus,
                       const float *shds, int32_t *idx, double *wts, double *gap, double *logits, double *y,
@@ -149,8 +151,15 @@ static void layer(int M, int H, int E, int K, int D, int Ds, int wtype) {
     double *w = blk(sizeof(double) * M * K), *gap = blk(sizeof(double) * M), *lg = blk(sizeof(double) * M * E);
     double *y = blk(sizeof(double) * M * H);
     uint16_t *yb = blk(2 * (size_t)M * H);
-    oracle_moe_layer(M, H, E, K, D, Ds, wtype, u, R, NULL, G, U, Dn, gs, us, ds, sG, sU, sD, sgs, sus, sds, idx, w,
-                     gap, lg, y, yb);
+    oracle_moe_layer(M, H, E, K, D, Ds, wtype, u, R, NULL, NULL, G, U, Dn, gs, us, ds, sG, sU, sD, sgs, sus, sds, idx,
+                     w, gap, lg, y, yb);
+    /* the same layer with an FP8 router: codes [H][E] and per-expert scales */
+    uint8_t *R8 = codes((size_t)H * E);
+    float *rs = scales((size_t)E);
+    oracle_moe_layer(M, H, E, K, D, Ds, wtype, u, R8, rs, NULL, G, U, Dn, gs, us, ds, sG, sU, sD, sgs, sus, sds, idx,
+                     w, gap, lg, y, yb);
+    free(R8);
+    free(rs);
     for (int i = 0; i < M * H; ++i) CHECK(isfinite(y[i]));
     free(u); free(R); free(G); free(U); free(Dn); free(sG); free(sU); free(sD); free(gs); free(us); free(ds);
     free(sgs); free(sus); free(sds); free(idx); free(w); free(gap); free(lg); free(y); free(yb);

@@ -362,3 +362,28 @@ def test_attn_decode_validation():
     assert L.moe_kv_cache_write(ctypes.byref(good), -1, 1, FAKE, FAKE, None) == native.MOE_EINVAL
     assert L.moe_kv_cache_write(ctypes.byref(good), 0, 0, FAKE, FAKE, None) == native.MOE_EINVAL
     assert L.moe_kv_cache_write(ctypes.byref(good), 0, 1, FAKE, FAKE + 16, None) == native.MOE_EALIGN
+
+
+def test_fp8_router_validation():
+    import synth
+    L = native.lib()
+    d = native.layer_desc(synth.TINY, "fp8", "fp8")
+    assert native.moe_decode_layer_workspace(d, 1) > 0
+    bad = native.layer_desc(synth.TINY, "fp8", "fp8")
+    bad.router_type = 2
+    assert native.moe_decode_layer_workspace(bad, 1) == 0
+    # beyond the fused geometry: the per-layer kernels read a bf16 router only
+    wide = native.layer_desc(synth.TINY.with_(hidden=512, width=768, shared_width=128), "fp8", "fp8")
+    assert native.moe_decode_layer_workspace(wide, 1) == 0
+    w = native.LayerWeights(*([FAKE] * 14 + [None]))        # FP8 router without its scales
+    wsb = native.moe_decode_layer_workspace(d, 1)
+    st = L.moe_decode_layer(ctypes.byref(d), ctypes.byref(w), 1, FAKE, FAKE, None, None, FAKE, wsb, None)
+    assert st == native.MOE_EINVAL
+    w.router_s = FAKE + 2
+    st = L.moe_decode_layer(ctypes.byref(d), ctypes.byref(w), 1, FAKE, FAKE, None, None, FAKE, wsb, None)
+    assert st == native.MOE_EALIGN
+    st = L.moe_decode_layer(ctypes.byref(wide), ctypes.byref(native.LayerWeights(*([FAKE] * 15))), 1, FAKE, FAKE,
+                            None, None, FAKE, 1 << 30, None)
+    assert st == native.MOE_EUNSUPPORTED
+    sd = native.step_desc(synth.TINY.with_(layers=2), 8, router_dtype="fp8")
+    assert native.moe_decode_step_workspace(sd) > 0

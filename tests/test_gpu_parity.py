@@ -26,13 +26,14 @@ def say(*a):
 class Layer:
     """Device weights of one layer plus a host copy for the oracle."""
 
-    def __init__(self, shape, layer=0, seed=0, device_gen="cpu", router_bias=None, expert_dtype="fp8"):
+    def __init__(self, shape, layer=0, seed=0, device_gen="cpu", router_bias=None, expert_dtype="fp8",
+                 router_dtype="bf16"):
         w = synth.layer_weights(shape, layer, device_gen, seed=seed, router_bias=router_bias,
-                                expert_dtype=expert_dtype)
+                                expert_dtype=expert_dtype, router_dtype=router_dtype)
         self.shape = shape
         self.dev = to_device(w, DEV)
         self.host = synth.weights_to_host(w)
-        self.desc = native.layer_desc(shape, expert_dtype)
+        self.desc = native.layer_desc(shape, expert_dtype, router_dtype)
         self.lw = native.layer_weights(self.dev)
 
     def run(self, x_bits_dev, M):
@@ -95,6 +96,8 @@ VARIANTS = {
     "e256_k8": synth.TINY.with_(experts=256, top_k=8, hidden=512, width=128, shared_width=64),
     "e128_k16": synth.TINY.with_(experts=128, top_k=16, hidden=768),
     "e48": synth.TINY.with_(experts=48, top_k=6),
+    # E not a multiple of 8: the one-launch form gathers the router one element per load
+    "e18": synth.TINY.with_(experts=18, top_k=3),
     "wide_d": synth.TINY.with_(hidden=1024, width=320, shared_width=128),
     # beyond the fused kernel's unit geometry (H > 2816, D > 704): the separate per-layer kernels
     "beyond_fused_h": synth.TINY.with_(hidden=3072, experts=16, top_k=2, width=64, shared_width=64),
@@ -110,6 +113,30 @@ def test_layer_shape_variants(name, M):
     L = Layer(sh, seed=3)
     x, r = unambiguous_layer_input(sh, M, L.host, 100)
     check_layer(L, x, r, "%s M=%d" % (name, M))
+
+
+FP8_ROUTER_SHAPES = {"tiny": synth.TINY, "e18": VARIANTS["e18"], "e48": VARIANTS["e48"],
+                     "h2816": synth.TINY.with_(hidden=2816, experts=32, top_k=4, width=704, shared_width=704)}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_ROUTER_SHAPES))
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_layer_fp8_router(name, M):
+    """The precision ladder's FP8 router rung: router codes [H][E] with per-expert scales,
+    gathered by the one-launch form of moe_decode_layer (16-byte tile or, for E = 18, one
+    code per load)."""
+    sh = FP8_ROUTER_SHAPES[name]
+    say("fp8 router %s M=%d" % (name, M))
+    L = Layer(sh, seed=6, router_dtype="fp8")
+    x, r = unambiguous_layer_input(sh, M, L.host, 300 + M)
+    check_layer(L, x, r, "fp8 router %s M=%d" % (name, M))
+
+
+def test_layer_fp8_router_needs_the_one_launch_form():
+    """The separate per-layer kernels read a bf16 router: a layer beyond the fused geometry
+    with an FP8 router is refused (no workspace size, MOE_EUNSUPPORTED)."""
+    d = native.layer_desc(VARIANTS["beyond_fused_d"], "fp8", "fp8")
+    assert native.moe_decode_layer_workspace(d, 1) == 0
 
 
 def test_layer_with_zipf_router_bias():
@@ -206,7 +233,7 @@ def _unit_rms_inputs(shape, M, seed):
     return sign.to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("where", ["tiny", "gemma"])
+@pytest.mark.parametrize("where", ["tiny", "gemma", "tiny_fp8_router"])
 @pytest.mark.parametrize("M", [1, 5, 8])
 def test_layer_entry_point_is_bit_identical_to_the_fused_step_layer(gemma_layer, where, M):
     """moe_decode_layer and the fused step's layer share the routing, the units and the
@@ -216,6 +243,8 @@ def test_layer_entry_point_is_bit_identical_to_the_fused_step_layer(gemma_layer,
     from fine_grained_moe_router_amd.stack import FusedDecodeStep
     if where == "gemma":
         layer = gemma_layer
+    elif where == "tiny_fp8_router":   # the router gathered from [H][E] vs the prepared [E][H] copy
+        layer = Layer(synth.TINY, seed=12, router_dtype="fp8")
     else:
         layer = Layer(synth.TINY, seed=12)
     sh = layer.shape.with_(layers=1)

@@ -21,9 +21,9 @@ def say(*a):
     print(*a, flush=True)
 
 
-def make(shape, seed=0, expert_dtype="fp8", router_bias=None, lm_bf16=False):
+def make(shape, seed=0, expert_dtype="fp8", router_bias=None, lm_bf16=False, router_dtype="bf16"):
     layers = [synth.layer_weights(shape, l, "cpu", seed=seed, tag="fused", expert_dtype=expert_dtype,
-                                  router_bias=router_bias) for l in range(shape.layers)]
+                                  router_bias=router_bias, router_dtype=router_dtype) for l in range(shape.layers)]
     host = [synth.weights_to_host(w) for w in layers]
     gains = synth.rmsnorm_gains(shape, seed=seed)
     if lm_bf16:   # the BF16 lm_head rung: bf16 weights, no scales (s stays None)
@@ -48,8 +48,8 @@ def oracle_step(shape, host, gains, Q, s, M, step):
 
 
 def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bias=None, cooperative=False,
-                  lm_bf16=False):
-    layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias, lm_bf16)
+                  lm_bf16=False, router_dtype="bf16"):
+    layers, host, gains, Q, s, dev = make(shape, seed, expert_dtype, router_bias, lm_bf16, router_dtype)
     x, noise, res = oracle_step(shape, host, gains, Q, s, M, step)
     drafts = synth.drafts(res["tok"], 0.7, shape.vocab, step)
     n_ref, out_ref = oracle.spec_accept(drafts, res["tok"])
@@ -92,6 +92,17 @@ def test_fused_step_bf16_lm_head(M, experts):
     say("fused bf16 lm_head M=%d experts %s" % (M, experts))
     run_and_check(FUSED_VARIANTS["h2816"], M, step=70 + M, seed=8, what="bf16 lm_head M=%d" % M,
                   expert_dtype=experts, lm_bf16=True)
+
+
+@pytest.mark.parametrize("name", ["tiny", "e48_k6", "h2816"])
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_fused_step_fp8_router(name, M):
+    """The precision ladder's FP8 router rung in the fused step: codes re-laid out one expert
+    per row at prepare, widened to bf16 in the router workgroups, the expert's scale applied to
+    the finished logit."""
+    sh = synth.TINY.with_(layers=2) if name == "tiny" else FUSED_VARIANTS[name]
+    say("fused fp8 router %s M=%d" % (name, M))
+    run_and_check(sh, M, step=90 + M, seed=9, what="fp8 router %s M=%d" % (name, M), router_dtype="fp8")
 
 
 @pytest.mark.parametrize("M", [1, 5, 8])

@@ -606,3 +606,29 @@ def test_lm_head_bf16_vs_numpy_and_planted_winner():
     Q, s = synth.lm_head(sh, seed=3)
     deq = FP8_TABLE[synth.bytes8(Q)] * synth.f32(s)[:, None].astype(np.float64)
     assert np.abs(deq - bf16_np(W)).max() < 0.1 * np.abs(bf16_np(W)).max()
+
+
+def test_router_fp8_against_numpy():
+    """The FP8 router rung (oracle_router_fp8): logits = s_e (u . decode(W8[:, e])) (+ b_e),
+    against numpy's decode of the same codes; the selection as the bf16 router's; and
+    moe_layer with router_s routes exactly as router_fp8."""
+    shape = synth.TINY
+    w = synth.weights_to_host(synth.layer_weights(shape, seed=4, router_dtype="fp8"))
+    assert w["router_w"].dtype == np.uint8 and w["router_w"].shape == (shape.hidden, shape.experts)
+    u = synth.bits16(torch.randn(5, shape.hidden, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16))
+    b = np.linspace(-0.5, 0.5, shape.experts).astype(np.float32)
+    r = oracle.router_fp8(u, w["router_w"], w["router_s"], b, shape.top_k)
+    dec = FP8_TABLE[w["router_w"]] * w["router_s"].astype(np.float64)[None, :]
+    logits = bf16_np(u) @ dec + b.astype(np.float64)
+    np.testing.assert_allclose(r["logits"], logits, rtol=1e-12, atol=1e-12)
+    for m in range(u.shape[0]):
+        order = sorted(range(shape.experts), key=lambda e: (-logits[m, e], e))
+        assert list(r["idx"][m]) == sorted(order[:shape.top_k])
+        sel = np.exp(logits[m, r["idx"][m]] - logits[m].max())
+        np.testing.assert_allclose(r["w"][m], sel / sel.sum(), rtol=1e-12)
+    # the codes are the per-expert quantisation of the bf16 rung's draws: within half an FP8 step
+    wb = synth.weights_to_host(synth.layer_weights(shape, seed=4))
+    ref = bf16_np(wb["router_w"])
+    assert np.abs(dec - ref).max() <= (np.abs(ref).max(axis=0) / 448 * 16).max()
+    lay = oracle.moe_layer(u, dict(w, router_b=b), shape.top_k)
+    assert (lay["idx"] == r["idx"]).all() and (lay["logits"] == r["logits"]).all()
