@@ -280,7 +280,7 @@ def read_probe(nbytes=4 << 30, reps=10):
             "read_gbs": round(nbytes / (us / 1e6) / 1e9, 1)}
 
 
-def measure(args, runner, sh, M, expert_dtype="fp8", bias=False, lm_dtype="fp8"):
+def measure(args, runner, sh, M, expert_dtype="fp8", bias=False, lm_dtype="fp8", router_dtype="bf16"):
     """Warm up, then time exactly args.steps steps of the runner at M tokens (HIP events
     on the launch stream, bracketed by device synchronisations); then record each timed
     step's routing to count the bytes it needed."""
@@ -354,7 +354,7 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False, lm_dtype="fp8")
         if st_code != native.MOE_OK:
             raise RuntimeError("fused step reported %s" % native.strerror(st_code))
 
-    bytes_steps = [budget.step_bytes(sh, u, M, expert_dtype, bias, lm_dtype) for u in uniq]
+    bytes_steps = [budget.step_bytes(sh, u, M, expert_dtype, bias, lm_dtype, router_dtype) for u in uniq]
     ms = ms_total / K
     bps = float(np.mean(bytes_steps))
     r = {
@@ -852,7 +852,8 @@ def ladder_main(args):
     """The precision ladder (page "LLM decoding", "Lever 1: fewer bytes" and the table "The
     ladder, every rung"): the 30-layer stack on the fused step at M=1 (plain decoding) and M=5
     (the verify step with 4 drafts), for FP8 or bf16 expert weights (routed and shared) and
-    an FP8 or bf16 lm_head; the router is bf16 in every rung. Per rung: bytes/step and
+    an FP8 or bf16 lm_head with a bf16 router, and the all-FP8 rung (FP8 router too). Per
+    rung: bytes/step and
     steps/s at both M, and tokens/s = steps/s(M=1) for plain decoding and steps/s(M=5) x
     E[n+1] for speculative decoding at the page's acceptance rates (E[n+1] = sum_j alpha^j,
     j = 0..4). The drafter's own cost is not in these figures."""
@@ -874,19 +875,23 @@ def ladder_main(args):
         torch.cuda.synchronize()
         log("%s experts generated in %.1fs (%.2f GB resident)" % (edt, time.time() - t0,
                                                                  torch.cuda.memory_allocated() / 1e9))
-        for ldt in ("bf16", "fp8"):
+        plan = [("bf16", "bf16"), ("fp8", "bf16")] + ([("fp8", "fp8")] if edt == "fp8" else [])
+        for ldt, rdt in plan:
             Q, s = lm[ldt]
+            if rdt == "fp8":   # the same layers with the router swapped for its FP8 rung
+                layers = [dict(w, **synth.router_weights(sh, l, dev, seed=args.seed, tag="stack", router_dtype="fp8"))
+                          for l, w in enumerate(layers)]
             runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=5)
             r = {}
             for M in (1, 5):
-                m = measure(args, runner, sh, M, edt, lm_dtype=ldt)
+                m = measure(args, runner, sh, M, edt, lm_dtype=ldt, router_dtype=rdt)
                 r["M%d" % M] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in m.items()
                                 if k in ("steps_per_s", "ms_per_step", "bytes_per_step", "hbm_gbs", "hbm_frac",
                                          "median_block_ms_per_step")}
             r["tokens_per_s_plain"] = round(r["M1"]["steps_per_s"], 1)
             for alpha in (0.87, 0.90):
                 r["tokens_per_s_spec_alpha%.2f" % alpha] = round(r["M5"]["steps_per_s"] * expected_emitted(alpha, 4), 1)
-            name = "experts_%s+lm_head_%s" % (edt, ldt)
+            name = "experts_%s+lm_head_%s" % (edt, ldt) + ("+router_fp8" if rdt == "fp8" else "")
             rungs[name] = r
             log("%s: M=1 %.3f ms, M=5 %.3f ms, plain %.0f tok/s, spec(0.87) %.0f tok/s" % (
                 name, r["M1"]["ms_per_step"], r["M5"]["ms_per_step"], r["tokens_per_s_plain"],
@@ -898,7 +903,7 @@ def ladder_main(args):
     top, base = rungs["experts_fp8+lm_head_fp8"], rungs["experts_bf16+lm_head_bf16"]
     line = {
         "metric": "precision ladder: decode steps/s and modelled tokens/s, 26B-A4B MoE stack, FP8/bf16 experts x "
-                  "FP8/bf16 lm_head, M=1 and M=5",
+                  "FP8/bf16 lm_head (bf16 router), and all-FP8 (FP8 router too), M=1 and M=5",
         "value": top["tokens_per_s_plain"], "unit": "tokens/s (FP8 rung, plain decoding)", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": top["M1"]["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -910,6 +915,8 @@ def ladder_main(args):
         "rungs": rungs,
         "fp8_over_bf16_plain": round(top["tokens_per_s_plain"] / base["tokens_per_s_plain"], 3),
         "fp8_spec_over_bf16_plain_alpha0.87": round(top["tokens_per_s_spec_alpha0.87"] / base["tokens_per_s_plain"], 3),
+        "router_fp8_over_bf16_plain": round(rungs["experts_fp8+lm_head_fp8+router_fp8"]["tokens_per_s_plain"] /
+                                            top["tokens_per_s_plain"], 3),
         "roofline": None, "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

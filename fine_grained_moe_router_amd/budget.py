@@ -21,8 +21,10 @@ def expert_bytes(hidden: int, width: int, weight_bytes: int = 1, scales: bool = 
     return b
 
 
-def router_bytes(hidden: int, experts: int, bias: bool = False) -> int:
-    return hidden * experts * 2 + (experts * 4 if bias else 0)
+def router_bytes(hidden: int, experts: int, bias: bool = False, router_dtype: str = "bf16") -> int:
+    """bf16 [H][E], or FP8 codes [H][E] with one fp32 scale per expert; the bias if any."""
+    w = hidden * experts * 2 if router_dtype == "bf16" else hidden * experts + experts * 4
+    return w + (experts * 4 if bias else 0)
 
 
 def lm_head_bytes(vocab: int, hidden: int) -> int:
@@ -31,14 +33,14 @@ def lm_head_bytes(vocab: int, hidden: int) -> int:
 
 
 def layer_bytes(shape, unique_routed: int, M: int, expert_dtype: str = "fp8",
-                bias: bool = False, norm: bool = False) -> int:
+                bias: bool = False, norm: bool = False, router_dtype: str = "bf16") -> int:
     """One MoE layer: the router, each expert in the union once, the shared expert,
     and the bf16 activations (input read, output written; with the residual norm
     also the residual, the noise and the gain)."""
     wb = 1 if expert_dtype == "fp8" else 2
     sc = expert_dtype == "fp8"
     H = shape.hidden
-    b = router_bytes(H, shape.experts, bias)
+    b = router_bytes(H, shape.experts, bias, router_dtype)
     b += unique_routed * expert_bytes(H, shape.width, wb, sc)
     if shape.shared_width:
         b += expert_bytes(H, shape.shared_width, wb, sc)
@@ -49,13 +51,13 @@ def layer_bytes(shape, unique_routed: int, M: int, expert_dtype: str = "fp8",
 
 
 def step_bytes(shape, unique_routed_per_layer, M: int, expert_dtype: str = "fp8",
-               bias: bool = False, lm_dtype: str = "fp8") -> int:
+               bias: bool = False, lm_dtype: str = "fp8", router_dtype: str = "bf16") -> int:
     """Whole stacked step: every layer (with its residual norm), the final norm, the
     lm_head (FP8 codes and row scales, or bf16), and the argmax / acceptance outputs
     (negligible, counted as 16 B/token)."""
     b = 0
     for u in unique_routed_per_layer:
-        b += layer_bytes(shape, int(u), M, expert_dtype, bias, norm=True)
+        b += layer_bytes(shape, int(u), M, expert_dtype, bias, norm=True, router_dtype=router_dtype)
     H = shape.hidden
     b += 3 * M * H * 2 + H * 2            # final residual add + norm
     b += lm_head_bytes(shape.vocab, H) if lm_dtype == "fp8" else 2 * shape.vocab * H

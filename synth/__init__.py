@@ -111,6 +111,20 @@ def _fp8_matrix(shape, std, device, *key):
     return codes, scales
 
 
+def router_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0, tag: str = "moe",
+                   router_dtype: str = "bf16") -> dict:
+    """The router of layer_weights() alone: router_w (bf16 [H][E], or FP8 codes [H][E] quantised
+    per expert from the same draws), router_s (fp32 [E] or None) and router_dtype."""
+    H, E = shape.hidden, shape.experts
+    rw = normal((H, E), ROUTER_STD, device, seed, tag, layer, "router")
+    if router_dtype == "fp8":
+        codes, rs = quantize_rows_fp8(rw.t().contiguous())
+        return {"router_w": codes.t().contiguous(), "router_s": rs, "router_dtype": "fp8"}
+    if router_dtype == "bf16":
+        return {"router_w": rw.to(torch.bfloat16), "router_s": None, "router_dtype": "bf16"}
+    raise ValueError(router_dtype)
+
+
 def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
                   tag: str = "moe", expert_dtype: str = "fp8",
                   router_bias: Optional[torch.Tensor] = None, router_dtype: str = "bf16") -> dict:
@@ -126,16 +140,8 @@ def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
     """
     H, E, D, Ds = shape.hidden, shape.experts, shape.width, shape.shared_width
     k = (seed, tag, layer)
-    rw = normal((H, E), ROUTER_STD, device, *k, "router")
     out = {"router_b": None if router_bias is None else router_bias.to(device=device, dtype=torch.float32)}
-    if router_dtype == "fp8":
-        codes, rs = quantize_rows_fp8(rw.t().contiguous())
-        out["router_w"], out["router_s"] = codes.t().contiguous(), rs
-    elif router_dtype == "bf16":
-        out["router_w"], out["router_s"] = rw.to(torch.bfloat16), None
-    else:
-        raise ValueError(router_dtype)
-    del rw
+    out.update(router_weights(shape, layer, device, seed, tag, router_dtype))
 
     def mat(shp, name):
         if expert_dtype == "fp8":
@@ -160,7 +166,6 @@ def layer_weights(shape: Shape, layer: int = 0, device="cpu", seed: int = 0,
             out["sh_%s_w" % name] = None
             out["sh_%s_s" % name] = None
     out["expert_dtype"] = expert_dtype
-    out["router_dtype"] = router_dtype
     return out
 
 
