@@ -754,7 +754,8 @@ def draft_bytes(hs) -> int:
 
 def draft_main(args):
     """The MTP drafter's step (moe_draft_step): gamma = 4 drafts of the 430M head, each chained on
-    the previous one on the device, graph-captured in groups of 10 steps; timed beside the fused
+    the previous one on the device, graph-captured in groups of 10 steps, in the one-launch form
+    (the value) and as the chain of launches (for comparison); timed beside the fused
     verify step (M = 5) and plain decoding (M = 1) of the 30-layer stack in the same process.
     Reports the drafter tax (drafter time / verify time) and tokens/s = E[n+1] / (t_verify +
     t_draft) at acceptance rates from the page (39 % on random prompts, 87 % and 94 % on
@@ -770,45 +771,59 @@ def draft_main(args):
     sh = synth.GEMMA4_26B_A4B.with_(layers=args.layers)
     head = synth.draft_head(hs, dev, seed=args.seed)
     Q, s = synth.lm_head(sh, dev, seed=args.seed)
-    desc = native.draft_desc(hs)
     dw = native.draft_weights(head)
-    wsb = native.moe_draft_step_workspace(desc)
-    ws = native.workspace(wsb)
     n = K + W
     g0 = [synth.hidden_inputs(sh, 1, i, device=dev, seed=args.seed, tag="draft_g")[0].contiguous() for i in range(n)]
     t0 = torch.randint(0, sh.vocab, (n, 1), generator=torch.Generator().manual_seed(args.seed),
                        dtype=torch.int32).to(dev)
-    drafts = torch.zeros(n, gamma, dtype=torch.int32, device=dev)
-    stream = torch.cuda.Stream()
-    stream.wait_stream(torch.cuda.current_stream())
-
-    def launch(i):
-        native.moe_draft_step(desc, dw, gamma, t0[i], g0[i], Q, s, drafts[i], ws, wsb, stream)
-
-    with torch.cuda.stream(stream):
-        for i in range(W):
-            launch(i)
-        torch.cuda.synchronize()
-        graphs = []
-        for c0 in range(W, n, 10):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr, stream=stream):
-                for i in range(c0, min(n, c0 + 10)):
-                    launch(i)
-            graphs.append(gr)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for gr in graphs:
-            gr.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-    ms_draft = e0.elapsed_time(e1) / K
-    del graphs
     bpd = draft_bytes(hs)
+
+    def time_form(chain):
+        """ms per drafter step of one form: W eager warm-up calls, then K calls replayed from
+        graphs of 10 (the drafts of every call kept apart)."""
+        desc = native.draft_desc(hs, chain=chain)
+        wsb = native.moe_draft_step_workspace(desc)
+        ws = native.workspace(wsb)
+        drafts = torch.zeros(n, gamma, dtype=torch.int32, device=dev)
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+
+        def launch(i):
+            native.moe_draft_step(desc, dw, gamma, t0[i], g0[i], Q, s, drafts[i], ws, wsb, stream)
+
+        with torch.cuda.stream(stream):
+            for i in range(W):
+                launch(i)
+            torch.cuda.synchronize()
+            graphs = []
+            for c0 in range(W, n, 10):
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr, stream=stream):
+                    for i in range(c0, min(n, c0 + 10)):
+                        launch(i)
+                graphs.append(gr)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for gr in graphs:
+                gr.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+        if native.moe_draft_step_status(desc, ws) != native.MOE_OK:
+            raise RuntimeError("drafter: a device-side wait gave up")
+        ms = e0.elapsed_time(e1) / K
+        del graphs
+        log("drafter step, %s (%d drafts): %.1f us (%.1f us per draft), %.1f GB/s over %.1f MB per draft" % (
+            "chain of launches" if chain else "one launch", gamma, ms * 1e3, ms * 1e3 / gamma,
+            gamma * bpd / (ms / 1e3) / 1e9, bpd / 1e6))
+        return ms, drafts
+
+    ms_draft, d_fused = time_form(False)
+    ms_chain, d_chain = time_form(True)
+    # the two forms differ only in the order of fp32 sums; report how often a draft differs
+    differ = int((d_fused[W:] != d_chain[W:]).sum())
+    log("drafts that differ between the two forms: %d of %d" % (differ, K * gamma))
     gbs = gamma * bpd / (ms_draft / 1e3) / 1e9
-    log("drafter step (%d drafts): %.1f us (%.1f us per draft), %.1f GB/s over %.1f MB per draft" % (
-        gamma, ms_draft * 1e3, ms_draft * 1e3 / gamma, gbs, bpd / 1e6))
     layers = [synth.layer_weights(sh, l, dev, seed=args.seed, tag="stack") for l in range(sh.layers)]
     gains = synth.rmsnorm_gains(sh, dev, seed=args.seed)
     runner = FusedDecodeStep(sh, layers, gains, Q, s, max_M=5)
@@ -830,11 +845,13 @@ def draft_main(args):
                                "norm + 262144-row argmax + post-projection each)", "hidden": hs.hidden,
                    "width": hs.width, "ffn": hs.ffn, "blocks": hs.blocks, "vocab": hs.vocab, "params": hs.params()},
         "us_per_draft": round(ms_draft * 1e3 / gamma, 2), "bytes_per_draft": bpd, "hbm_gbs": round(gbs, 1),
+        "chain_ms_per_step": round(ms_chain, 5), "chain_us_per_draft": round(ms_chain * 1e3 / gamma, 2),
+        "drafts_differing_between_forms": differ,
         "verify_step_ms_M5": round(t5, 4), "plain_step_ms_M1": round(t1, 4),
         "drafter_tax": round(ms_draft / t5, 4),
         "tokens_per_s_plain": round(1e3 / t1, 1),
         "tokens_per_s_spec": model,
-        "roofline": {"bound": "hbm", "kernel": "moe_draft_step (30 launches per draft)", "achieved": round(gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_draft_fused (one launch per step)", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": gamma * bpd, "avg_launch_us": round(ms_draft * 1e3, 2)},
         "cpu_baseline": None,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoedecode.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, f) for f in ("api.cpp", "kernels.hip", "step.hip", "sample.hip", "draft.hip", "attn.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("api.cpp", "kernels.hip", "step.hip", "sample.hip", "draft.hip", "draft_fused.hip", "attn.hip")]
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -293,6 +293,7 @@ static int check_draft_desc(const moe_draft_desc *d) {
     if (d->blocks < 0 || d->blocks > 64) return MOE_EINVAL;
     if (d->vocab < 64 || d->vocab % 64 || d->vocab > (1 << 30)) return MOE_EINVAL;
     if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    if (d->flags & ~MOE_DRAFT_CHAIN) return MOE_EINVAL;
     if (!draft_splits(*d)) return MOE_EINVAL;
     return MOE_OK;
 }
@@ -329,6 +330,12 @@ int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int g
     if (((uintptr_t)tok0 | (uintptr_t)drafts) & 3u) return MOE_EALIGN;
     if (!ws_ok(workspace, workspace_bytes, draft_ws(*desc).total)) return MOE_EWORKSPACE;
     return launch_draft_step(*desc, *w, gamma, tok0, hidden0, emb_w, emb_s, drafts, (char *)workspace, stream);
+}
+
+int moe_draft_step_status(const moe_draft_desc *desc, void *workspace) {
+    CHECK(check_draft_desc(desc));
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MOE_EWORKSPACE;
+    return draft_status(*desc, (char *)workspace);
 }
 
 static int check_attn_desc(const moe_attn_desc *d) {

@@ -108,6 +108,29 @@ __device__ __forceinline__ uint32_t dppu(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
+__device__ __forceinline__ void kmax_step(uint32_t &hi, uint32_t &lo, uint32_t oh, uint32_t ol) {
+    const bool gt = oh > hi || (oh == hi && ol > lo);
+    hi = gt ? oh : hi;
+    lo = gt ? ol : lo;
+}
+
+// Largest 64-bit key over the 64 lanes (all lanes active); wave-uniform result.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+    kmax_step(hi, lo, dppu<0xB1>(hi), dppu<0xB1>(lo));     // quad_perm [1,0,3,2]
+    kmax_step(hi, lo, dppu<0x4E>(hi), dppu<0x4E>(lo));     // quad_perm [2,3,0,1]
+    kmax_step(hi, lo, dppu<0x141>(hi), dppu<0x141>(lo));   // row_half_mirror
+    kmax_step(hi, lo, dppu<0x140>(hi), dppu<0x140>(lo));   // row_mirror
+    uint64_t best = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+        best = v > best ? v : best;
+    }
+    return best;
+}
+
 __device__ __forceinline__ int lanes_below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
 }

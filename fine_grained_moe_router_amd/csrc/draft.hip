@@ -1,6 +1,7 @@
-// draft.hip -- the MTP drafter's step on gfx950: gamma drafts in sequence, each a chain of
-// small launches (graph-capturable; the drafted token stays on the device and feeds the
-// next draft's embedding row).
+// draft.hip -- the MTP drafter's step on gfx950 as a chain of launches: gamma drafts in
+// sequence, each a chain of small launches (graph-capturable; the drafted token stays on
+// the device and feeds the next draft's embedding row). Heads and devices that fit it run
+// the one-launch form of draft_fused.hip instead.
 //
 // Page "LLM decoding", "The one-line shape bug that disabled the model's own drafter": the
 // head's pre_projection takes 5632 = 2 x 2816 inputs (the target's embedding of the token
@@ -205,6 +206,9 @@ void by_lpr(int lpr, F f) {
 int launch_draft_step(const moe_draft_desc &d, const moe_draft_weights &w, int gamma, const int32_t *tok0,
                       const uint16_t *hidden0, const uint8_t *emb_w, const float *emb_s, int32_t *drafts,
                       char *ws, void *stream) {
+    // the one-launch form where the shape and the device fit it
+    const int rc = launch_draft_fused(d, w, gamma, tok0, hidden0, emb_w, emb_s, drafts, ws, stream);
+    if (rc != MOE_EUNSUPPORTED) return rc;
     (void)hipGetLastError();
     const int H = d.hidden, D = d.width, F = d.ffn, B = d.blocks, V = d.vocab;
     const int l_pre = draft_lpr(D, 2 * H, kDraftMaxCh), l_gu = draft_lpr(F, D, kDraftGateUpMaxCh),

@@ -2,6 +2,7 @@
 // validation, no HIP headers) and kernels.hip (device code).
 #pragma once
 #include <stddef.h>
+#include <algorithm>
 #include <stdint.h>
 
 #include "moe_decode.h"
@@ -115,8 +116,48 @@ inline bool draft_splits(const moe_draft_desc &d) {
            draft_lpr(d.width, d.ffn, kDraftMaxCh) && draft_lpr(d.hidden, d.width, kDraftMaxCh);
 }
 
+// The persistent drafter: all gamma drafts in one launch of kDraftPG workgroups of 256
+// threads (two per compute unit), each matrix's rows spread over the workgroups with
+// R rows per workgroup (a power of two) and L = 256 / R lanes per row; a lane holds at
+// most the given number of 16-byte pieces of a row in registers.
+constexpr int kDraftPG = 512;
+constexpr int kDpPreC = 3, kDpGuC = 2, kDpDnC = 8, kDpPoC = 2;
+constexpr int kDraftMaxGamma = kMaxM - 1;
+struct DraftGeo {
+    int lp, lgu, ld, lpo;   // lanes per row: pre-projection, gate/up, down, post-projection
+    bool ok;                // the shape fits the persistent kernel
+};
+inline int pow2_at_least(int v) {
+    int p = 1;
+    while (p < v) p *= 2;
+    return p;
+}
+inline DraftGeo draft_geo(const moe_draft_desc &d) {
+    DraftGeo g{};
+    const int H = d.hidden, D = d.width, F = d.ffn;
+    if (D > 1024 || F > 8192 || H > 4096) return g;
+    // rows per workgroup: at least rmin, and enough that N rows take at most kDraftPG
+    auto lanes = [](int N, int rmin) {
+        const int R = std::max(rmin, pow2_at_least((N + kDraftPG - 1) / kDraftPG));
+        return R <= 256 ? 256 / R : 0;
+    };
+    auto pieces = [](int K, int L) { return (K / 16 + L - 1) / L; };
+    g.lp = lanes(D, 2);                 // bf16 results go out in pairs
+    g.lgu = lanes(F, 1);
+    // down: the fewest workgroups whose rows still fit kDpDnC pieces a lane (fewer
+    // workgroups poll the blocks' inner vector)
+    const int ld_want = std::min(128, std::max(16, pow2_at_least(F / (16 * kDpDnC))));
+    g.ld = std::min(lanes(D, 2), ld_want);
+    g.lpo = lanes(H, 2);
+    g.ok = g.lp && g.lgu && g.ld && g.lpo && pieces(2 * H, g.lp) <= kDpPreC && pieces(D, g.lgu) <= kDpGuC &&
+           pieces(F, g.ld) <= kDpDnC && pieces(D, g.lpo) <= kDpPoC;
+    return g;
+}
+
 struct DraftWs {
-    size_t z, zf, g, h, lm, total;
+    size_t z, zf, g, h, lm;                 // the chain of launches
+    size_t ctr, epoch, zw, hw, gw, kw;      // the persistent kernel (when draft_geo().ok)
+    size_t total;
 };
 inline DraftWs draft_ws(const moe_draft_desc &d) {
     DraftWs W{};
@@ -127,6 +168,15 @@ inline DraftWs draft_ws(const moe_draft_desc &d) {
     W.g = take(2 * (size_t)d.hidden);
     W.h = take(4 * (size_t)d.ffn);
     W.lm = take(lm_ws_bytes(1, d.vocab));
+    if (draft_geo(d).ok) {
+        const size_t G7 = kDraftMaxGamma;
+        W.ctr = take(4);
+        W.epoch = take(4);
+        W.zw = take(8 * G7 * (size_t)(d.blocks + 1) * (size_t)(d.width / 2));
+        W.hw = take(8 * G7 * (size_t)d.blocks * (size_t)d.ffn);
+        W.gw = take(8 * G7 * (size_t)(d.hidden / 2));
+        W.kw = take(8 * G7 * (size_t)kDraftPG * 2);
+    }
     W.total = o;
     return W;
 }
@@ -302,6 +352,12 @@ int launch_lm_head_bf16(int M, int H, int V, const uint16_t *x, const uint16_t *
 int launch_draft_step(const moe_draft_desc &d, const moe_draft_weights &w, int gamma, const int32_t *tok0,
                       const uint16_t *hidden0, const uint8_t *emb_w, const float *emb_s, int32_t *drafts,
                       char *ws, void *stream);
+// The persistent drafter (MOE_EUNSUPPORTED when the shape or the device does not fit it)
+// and the status of its bounded waits.
+int launch_draft_fused(const moe_draft_desc &d, const moe_draft_weights &w, int gamma, const int32_t *tok0,
+                       const uint16_t *hidden0, const uint8_t *emb_w, const float *emb_s, int32_t *drafts,
+                       char *ws, void *stream);
+int draft_status(const moe_draft_desc &d, char *ws);
 int launch_lm_head_noalloc(int M, int H, int V, const uint16_t *x, const uint8_t *w, const float *s,
                            int32_t *token, float *max_logit, void *stream);
 int launch_spec_accept(int gamma, const int32_t *draft, const int32_t *target,

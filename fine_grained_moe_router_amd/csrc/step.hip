@@ -47,6 +47,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "handoff.h"
 #include "internal.h"
 
 namespace moe {
@@ -112,24 +113,6 @@ __device__ __forceinline__ AP uniform(AP p) {
 
 extern __shared__ __align__(16) char smem[];
 
-// Every access to device memory goes through the global address space: the pointers
-// here arrive as generic pointers (from the argument block and the weight table), and
-// generic (flat) accesses also count against the LDS wait counter, so an LDS wait would
-// otherwise wait for weight loads and hand-off stores still in flight.
-#define GAS __attribute__((address_space(1)))
-template <class T>
-__device__ __forceinline__ GAS T *glb(T *p) { return (GAS T *)p; }
-// A 16-byte load through the global address space.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 ld16(const void *p) {
-    const u32x4 v = *(const GAS u32x4 *)p;
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint2 ld8(const void *p) {
-    const u32x2 v = *(const GAS u32x2 *)p;
-    return make_uint2(v.x, v.y);
-}
 // eight FP8 router codes (column order) -> eight bf16 (exact: scale 1)
 __device__ __forceinline__ uint4 widen8(uint2 q) {
     return make_uint4(__builtin_bit_cast(uint32_t, fp8x2_to_bf16<false>(q.x)),
@@ -146,29 +129,6 @@ __device__ __forceinline__ int ltid() {
     asm volatile("" : "+v"(t));
     return t;
 }
-
-// -------------------------------------------------------- coherent hand-off access
-
-__device__ __forceinline__ void st32(void *p, uint32_t v) {
-    __hip_atomic_store(glb(reinterpret_cast<uint32_t *>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st64(void *p, uint64_t v) {
-    __hip_atomic_store(glb(reinterpret_cast<uint64_t *>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t ld32(const void *p) {
-    return __hip_atomic_load(glb(reinterpret_cast<const uint32_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ld64(const void *p) {
-    return __hip_atomic_load(glb(reinterpret_cast<const uint64_t *>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Hand-off words are read with these atomic loads: a plain load can hit a line that the
-// reading XCD's L2 still holds from before the write (the L2s of different XCDs are not
-// kept coherent). The compiler waits for each atomic load before its first use, so the
-// code below issues them in unrolled batches (loads first, uses after): a batch costs
-// one memory latency.
-__device__ __forceinline__ uint64_t tagged(uint32_t v, uint32_t tag) { return ((uint64_t)tag << 32) | v; }
-__device__ __forceinline__ bool current(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
-__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) { return (uint32_t)lo | ((uint32_t)hi << 16); }
 
 // ------------------------------------------------------------ workspace views
 
@@ -277,30 +237,6 @@ __device__ __forceinline__ float half_sum(float v) {
     // row_bcast:15 into rows 1 and 3 only: lane 15 of the row below
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
 }
-
-__device__ __forceinline__ void kmax_step(uint32_t &hi, uint32_t &lo, uint32_t oh, uint32_t ol) {
-    const bool gt = oh > hi || (oh == hi && ol > lo);
-    hi = gt ? oh : hi;
-    lo = gt ? ol : lo;
-}
-
-// Largest 64-bit key over the 64 lanes (all lanes active); wave-uniform result.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-    uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
-    kmax_step(hi, lo, dppu<0xB1>(hi), dppu<0xB1>(lo));     // quad_perm [1,0,3,2]
-    kmax_step(hi, lo, dppu<0x4E>(hi), dppu<0x4E>(lo));     // quad_perm [2,3,0,1]
-    kmax_step(hi, lo, dppu<0x141>(hi), dppu<0x141>(lo));   // row_half_mirror
-    kmax_step(hi, lo, dppu<0x140>(hi), dppu<0x140>(lo));   // row_mirror
-    uint64_t best = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint64_t v = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-        best = v > best ? v : best;
-    }
-    return best;
-}
-
 
 // ------------------------------------------------------------ norm
 

@@ -26,7 +26,7 @@ EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_s
            "lm_head_argmax", "lm_head_argmax_bf16", "lm_head_argmax_noalloc", "lm_head_spec_sample_workspace", "lm_head_spec_sample",
            "spec_accept", "moe_add_rmsnorm", "moe_decode_step_workspace",
            "moe_decode_step_prepare", "moe_decode_step", "moe_decode_step_status", "moe_fp8_decode",
-           "moe_hbm_read_probe", "moe_draft_step_workspace", "moe_draft_step", "moe_kv_cache_bytes",
+           "moe_hbm_read_probe", "moe_draft_step_workspace", "moe_draft_step", "moe_draft_step_status", "moe_kv_cache_bytes",
            "moe_kv_cache_write", "moe_attn_decode_workspace", "moe_attn_decode", "moe_strerror")
 
 
@@ -63,7 +63,11 @@ MOE_STEP_LM_BF16 = 2
 
 class DraftDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int), ("width", ctypes.c_int), ("ffn", ctypes.c_int), ("blocks", ctypes.c_int),
-                ("vocab", ctypes.c_int), ("eps", ctypes.c_float)]
+                ("vocab", ctypes.c_int), ("eps", ctypes.c_float), ("flags", ctypes.c_uint),
+                ("spin_limit", ctypes.c_uint)]
+
+
+MOE_DRAFT_CHAIN = 1
 
 
 class DraftWeights(ctypes.Structure):
@@ -127,6 +131,8 @@ def lib() -> ctypes.CDLL:
         L.moe_draft_step_workspace.restype = S
         L.moe_draft_step_workspace.argtypes = [ctypes.POINTER(DraftDesc)]
         L.moe_draft_step.restype = I
+        L.moe_draft_step_status.restype = I
+        L.moe_draft_step_status.argtypes = [ctypes.POINTER(DraftDesc), _P]
         L.moe_draft_step.argtypes = [ctypes.POINTER(DraftDesc), ctypes.POINTER(DraftWeights), I, _P, _P, _P, _P, _P,
                                      _P, S, _P]
         L.moe_kv_cache_bytes.restype = S
@@ -298,8 +304,10 @@ def workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def draft_desc(shape, eps: float = 1e-6) -> DraftDesc:
-    return DraftDesc(shape.hidden, shape.width, shape.ffn, shape.blocks, shape.vocab, eps)
+def draft_desc(shape, eps: float = 1e-6, chain: bool = False, spin_limit: int = 0) -> DraftDesc:
+    """chain: always run the chain of launches (MOE_DRAFT_CHAIN) instead of the one-launch form."""
+    return DraftDesc(shape.hidden, shape.width, shape.ffn, shape.blocks, shape.vocab, eps,
+                     MOE_DRAFT_CHAIN if chain else 0, int(spin_limit))
 
 
 def draft_weights(w: dict) -> DraftWeights:
@@ -318,6 +326,10 @@ def moe_draft_step(desc: DraftDesc, weights: DraftWeights, gamma, tok0, hidden0,
                               _ptr(emb_w), _ptr(emb_s), _ptr(drafts), _ptr(workspace), int(workspace_bytes),
                               _stream(stream))
     _check("moe_draft_step", st)
+
+
+def moe_draft_step_status(desc: DraftDesc, workspace) -> int:
+    return lib().moe_draft_step_status(ctypes.byref(desc), _ptr(workspace))
 
 
 def attn_desc(shape) -> AttnDesc:

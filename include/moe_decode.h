@@ -413,7 +413,12 @@ typedef struct moe_draft_desc {
     int blocks;   /* 0..64                                                                  */
     int vocab;    /* a multiple of 64, 64..2^30                                             */
     float eps;    /* RMSNorm epsilon, >= 0                                                  */
+    unsigned flags;       /* MOE_DRAFT_* bits (0 when zero-initialised)                     */
+    unsigned spin_limit;  /* polls before a device-side wait of the one-launch form gives up
+                             (0: the library's default, about a quarter second)             */
 } moe_draft_desc;
+
+#define MOE_DRAFT_CHAIN 1u   /* always run the chain of launches, never the one-launch form  */
 
 typedef struct moe_draft_weights {     /* device pointers, 16-byte aligned                  */
     const uint8_t *pre_w;   const float *pre_s;    /* [width][2 hidden], [width]            */
@@ -432,12 +437,32 @@ size_t moe_draft_step_workspace(const moe_draft_desc *desc);
  * gamma drafts (1..7) of the head above. tok0 int32 [1] and hidden0 bf16 [hidden] are
  * device arrays (the target's last token and its hidden state); emb_w FP8 [vocab][hidden]
  * with emb_s fp32 [vocab] is the target's tied embedding table (the lm_head); drafts
- * int32 [gamma]. Asynchronous on `stream`, one short chain of launches per draft.
+ * int32 [gamma]. Asynchronous on `stream` and capturable. The workspace (at least
+ * moe_draft_step_workspace(desc) bytes, 256-byte aligned) is zero-filled before its first
+ * use and then left to the library: it keeps a call counter and tagged hand-off words
+ * between calls, and concurrent calls must use distinct workspaces.
+ * Heads with width <= 1024, ffn <= 8192 and pieces that fit its register budget (the
+ * 430M head among them) run as ONE launch of 512 co-resident workgroups on a device that
+ * holds them (two per compute unit on MI355X), unless MOE_DRAFT_CHAIN is set: the
+ * workgroups pass z, the blocks' inner vectors, g and their argmax keys to one another
+ * through tagged words in the workspace, with bounded waits (see moe_draft_step_status).
+ * Like moe_decode_step, it relies on the caller not running other work on the device
+ * meanwhile. Other heads, and other devices, run a short chain of launches per draft.
+ * Both forms compute the formulas above; they may differ in the last bits of fp32 sums.
  */
 int moe_draft_step(const moe_draft_desc *desc, const moe_draft_weights *w, int gamma,
                    const int32_t *tok0, const uint16_t *hidden0, const uint8_t *emb_w,
                    const float *emb_s, int32_t *drafts, void *workspace, size_t workspace_bytes,
                    void *stream);
+
+/*
+ * Synchronous: MOE_OK, or MOE_ETIMEOUT if a device-side wait of a one-launch drafter call
+ * on this workspace gave up since the last status call (those calls' drafts are then
+ * invalid). It then clears the flag and moves the workspace's call counter past every
+ * tag a hand-off word can hold, so the next call runs normally. Call with no drafter call
+ * in flight on the workspace.
+ */
+int moe_draft_step_status(const moe_draft_desc *desc, void *workspace);
 
 /* ------------------------------------------------------------------------------
  * Attention decode with a KV cache (page "LLM decoding", "The exact architecture": 25

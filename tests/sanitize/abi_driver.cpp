@@ -62,6 +62,7 @@ int launch_layer_step(const moe_layer_desc &d, const moe_layer_weights &, int M,
                       int32_t *, float *, char *, void *) { return hit(layer_step_ws(d, M).total); }
 int step_prepare(const StepWs &W, const moe_layer_desc &, const moe_layer_weights *, char *) { return hit(W.total); }
 int step_status(const StepWs &, char *) { return hit(0); }
+int draft_status(const moe_draft_desc &, char *) { return hit(0); }
 int launch_fp8_decode(int, const uint8_t *, float *, float *, void *) { return hit(0); }
 int launch_read_probe(const void *, size_t, uint32_t *, void *) { return hit(0); }
 int launch_kv_write(const moe_attn_desc &, int, int, const uint16_t *, char *, void *) { return hit(0); }
@@ -219,11 +220,16 @@ static void draft_sweep(const moe_draft_desc &dd, int gamma) {
         if (g_ok)
             EXPECT_WS(ws - 1, moe_draft_step(&dd, &w, gamma, (int32_t *)t, (uint16_t *)h, (uint8_t *)e, (float *)s,
                                              (int32_t *)out, WS, ws - 1, nullptr), MOE_EWORKSPACE);
+        g_calls = 0;
+        CHECK(moe_draft_step_status(&dd, WS) == MOE_OK && g_calls == 1);
+        CHECK(moe_draft_step_status(&dd, nullptr) == MOE_EWORKSPACE && moe_draft_step_status(&dd, WS + 16) ==
+              MOE_EWORKSPACE && g_calls == 1);
     } else {
         g_ws_bytes = 0;
         g_calls = 0;
         CHECK(moe_draft_step(&dd, &w, gamma, (int32_t *)t, (uint16_t *)h, (uint8_t *)e, (float *)s, (int32_t *)out,
                              WS, (size_t)1 << 40, nullptr) != MOE_OK && g_calls == 0);
+        CHECK(moe_draft_step_status(&dd, WS) != MOE_OK && g_calls == 0);
     }
 }
 
@@ -274,8 +280,11 @@ int main() {
     sd.max_tokens = 8;
     sd.eps = 1e-6f;
     for (int M = 0; M <= 9; ++M) step_sweep(sd, M);
-    const moe_draft_desc mtp = {2816, 1024, 4096, 12, 262144, 1e-6f};
+    const moe_draft_desc mtp = {2816, 1024, 4096, 12, 262144, 1e-6f, 0u, 0u};
     for (int g = 0; g <= 8; ++g) draft_sweep(mtp, g);
+    moe_draft_desc mtp_chain = mtp;
+    mtp_chain.flags = MOE_DRAFT_CHAIN;
+    draft_sweep(mtp_chain, 4);
     const moe_attn_desc sliding = {2816, 16, 8, 256, 1024, 1032, MOE_KV_BF16};
     const moe_attn_desc global = {2816, 16, 2, 512, 0, 32768, MOE_KV_FP8};
     for (int M = 0; M <= 9; ++M) {
@@ -338,7 +347,9 @@ int main() {
         moe_draft_desc dd = mtp;
         int *f = reinterpret_cast<int *>(&dd) + rnd() % 5;
         *f = pick();
-        if (rnd() % 8 == 0) dd = {pick(), pick(), pick(), pick(), pick(), 1e-6f};
+        if (rnd() % 8 == 0) dd = {pick(), pick(), pick(), pick(), pick(), 1e-6f, 0u, 0u};
+        if (rnd() % 8 == 0) dd.flags = (unsigned)(rnd() % 4);   // bit 1 is not a flag
+        dd.spin_limit = (unsigned)rnd();
         draft_sweep(dd, (int)(rnd() % 10) - 1);
         moe_attn_desc ad = (rnd() & 1) ? sliding : global;
         int *af = reinterpret_cast<int *>(&ad) + rnd() % 7;
