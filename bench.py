@@ -39,31 +39,33 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, vendor figure
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# the sources the fused step kernel is compiled from
-STEP_SOURCES = [os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc", f)
-                for f in ("step.hip", "device_common.h", "internal.h")]
+CSRC = os.path.join(ROOT, "fine_grained_moe_router_amd", "csrc")
+# the sources each persistent kernel is compiled from, and its hardware-counter summary
+STEP_SOURCES = [os.path.join(CSRC, f) for f in ("step.hip", "device_common.h", "handoff.h", "internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_step_traffic.txt")
+DRAFT_SOURCES = [os.path.join(CSRC, f) for f in ("draft_fused.hip", "device_common.h", "handoff.h", "internal.h")]
+DRAFT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_draft_fused_traffic.txt")
 
 
-def step_source_hash():
-    """sha256 over the fused step kernel's sources, in a fixed order."""
+def source_hash(paths=None):
+    """sha256 over a kernel's sources, in a fixed order (the fused step's by default)."""
     import hashlib
     h = hashlib.sha256()
-    for path in STEP_SOURCES:
+    for path in paths or STEP_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic(M):
-    """HBM bytes per k_step launch at M tokens from the committed hardware-counter
-    summary (FETCH_SIZE and WRITE_SIZE, each from its own rocprofv3 --pmc run, scaled by
-    the factors a plain copy of known size gives), or None when there is no summary for
-    this M or the kernel source has changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_from(path, sources, key):
+    """HBM bytes per launch from a committed hardware-counter summary (FETCH_SIZE and
+    WRITE_SIZE in KiB, each from its own rocprofv3 --pmc run, scaled by the factors a plain
+    copy of known size gives) for the row named `key`, or None when there is no such row or
+    the kernel's sources have changed since the counters were taken."""
+    if not os.path.exists(path):
         return None
     sha, scale, rows = None, {}, {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         f = line.split()
         if not f or f[0].startswith("#"):
             continue
@@ -71,12 +73,17 @@ def measured_traffic(M):
             sha = f[1]
         elif f[0] == "scale":
             scale = dict(kv.split("=") for kv in f[1:])
-        elif f[0].startswith("M="):
-            rows[int(f[0][2:])] = dict(kv.split("=") for kv in f[1:])
-    if sha != step_source_hash() or M not in rows or not scale:
+        elif "=" in f[0]:
+            rows[f[0]] = dict(kv.split("=") for kv in f[1:])
+    if sha != source_hash(sources) or key not in rows or not scale:
         return None
-    r = rows[M]
+    r = rows[key]
     return int(float(r["fetch_kib"]) * 1024 * float(scale["fetch"]) + float(r["write_kib"]) * 1024 * float(scale["write"]))
+
+
+def measured_traffic(M):
+    """HBM bytes per k_step launch at M tokens (see traffic_from)."""
+    return traffic_from(TRAFFIC_FILE, STEP_SOURCES, "M=%d" % M)
 
 
 def parse():
@@ -470,9 +477,10 @@ def layer_main(args):
                                "greedy accept", "path": "layers", "hidden": sh.hidden, "experts": sh.experts,
                    "top_k": sh.top_k, "expert_width": sh.width, "vocab": sh.vocab},
         "per_config": out,
-        "roofline": {"bound": "hbm", "kernel": "moe_decode_layer (5 launches, M=1)",
+        "roofline": {"bound": "hbm", "kernel": "moe_decode_layer (one k_step<1> launch, one-layer mode, M=1)",
                      "achieved": head["hbm_gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac"], "traffic": None, "bytes_per_launch": head["bytes_per_step"],
+                     "frac": head["hbm_frac"], "traffic": traffic_from(TRAFFIC_FILE, STEP_SOURCES, "layer_M=1"),
+                     "bytes_per_launch": head["bytes_per_step"],
                      "avg_launch_us": head["us_per_step"]},
         "cpu_baseline": None,
     }
@@ -852,7 +860,8 @@ def draft_main(args):
         "tokens_per_s_plain": round(1e3 / t1, 1),
         "tokens_per_s_spec": model,
         "roofline": {"bound": "hbm", "kernel": "k_draft_fused (one launch per step)", "achieved": round(gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from(DRAFT_TRAFFIC_FILE, DRAFT_SOURCES, "gamma=%d" % gamma),
                      "bytes_per_launch": gamma * bpd, "avg_launch_us": round(ms_draft * 1e3, 2)},
         "cpu_baseline": None,
     }

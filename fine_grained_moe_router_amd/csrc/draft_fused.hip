@@ -368,14 +368,13 @@ __device__ __forceinline__ void dn_phase(DA a, DfLds &s, const Row<kDpDnC> &Dn, 
     a = opaque(a);
     const int tid = threadIdx.x, L = a->ld, R = 256 / L, li = tid & (L - 1), c = w * R + tid / L;
     const float sd = *glb(a->w.down_s + (size_t)b * a->D + c);
-    poll_to_lds<16>(a, hwords(a, i, b), a->F, tag, s.xh);
-    // the row's residual, from the stage's z words
+    // the row's residual, from the stage's z words: requested with the scale, before the
+    // wait for h (it is current by then, as h depends on it), checked after it
     const uint64_t *zp = zwords(a, i, b) + c / 2;
-    uint64_t zw;
+    uint64_t zw = ld64(zp);
+    poll_to_lds<16>(a, hwords(a, i, b), a->F, tag, s.xh);
     Spin sp;
-    do {
-        zw = ld64(zp);
-    } while (!sp.done(a, current(zw, tag)));
+    while (!sp.done(a, current(zw, tag))) zw = ld64(zp);
     const float zc = bf2f((c & 1) ? ((uint32_t)zw >> 16) : ((uint32_t)zw & 0xffffu));
     const float acc = rows_sum(Dn.dot_f32(reinterpret_cast<const float4 *>(s.xh), a->F, L, li), L, s);
     publish_pairs(s, f2bf(zc + sd * acc), li == 0, tid / L, R, zwords(a, i, b + 1) + w * R / 2, tag);

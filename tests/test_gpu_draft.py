@@ -93,14 +93,20 @@ def test_draft_step_no_blocks(chain):
     assert (d == r["drafts"]).all(), (d, r["drafts"])
 
 
-# Shapes that make each kernel read its rows with 16, 32 and 64 lanes per row somewhere in
-# the set (pre_projection, gate/up, down, post-projection): the full-size head takes
-# 32/16/64/32, TINY_HEAD 32/16/32/16, and these (the first two are wider than the
-# one-launch form takes and run the chain; the third runs the one-launch form with 128,
-# 16, 64 and 128 lanes per row):
+# Shapes that make each kernel of the chain read its rows with 16, 32 and 64 lanes per row
+# somewhere in the set (pre_projection, gate/up, down, post-projection): the full-size head
+# takes 32/16/64/32 and TINY_HEAD 32/16/32/16 there; the first two here are wider than the
+# one-launch form takes and run the chain (32/64/32/64 and 16/32/16/64). The others run the
+# one-launch form, whose lanes per row (pre, gate/up, down, post) are 128/32/32/32 for the
+# full-size head and 128/256/16/128 for TINY_HEAD: 128/16/64/128 (64 down workgroups of
+# four rows), 128/64/16/128 (two blocks), 128/32/32/128 (a 768-wide head: three 256-column
+# table chunks, 384 pre-projection workgroups) and 128/16/64/128 with an inner width of 6144.
 SPLIT_SHAPES = [synth.DraftShape(hidden=512, width=2048, ffn=1024, blocks=1, vocab=2048),    # 32/64/32/64
                 synth.DraftShape(hidden=256, width=4096, ffn=2048, blocks=1, vocab=1024),    # 16/32/16/64
-                synth.DraftShape(hidden=1024, width=256, ffn=8192, blocks=1, vocab=1024)]    # 64/16/64/16
+                synth.DraftShape(hidden=1024, width=256, ffn=8192, blocks=1, vocab=1024),
+                synth.DraftShape(hidden=512, width=512, ffn=2048, blocks=2, vocab=2048),
+                synth.DraftShape(hidden=1024, width=768, ffn=3072, blocks=1, vocab=1024),
+                synth.DraftShape(hidden=512, width=256, ffn=6144, blocks=1, vocab=1024)]
 
 
 @pytest.mark.parametrize("hs", SPLIT_SHAPES, ids=lambda h: "h%d_w%d_f%d" % (h.hidden, h.width, h.ffn))
