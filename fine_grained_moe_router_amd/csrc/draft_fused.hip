@@ -45,6 +45,11 @@ using namespace dev;
 
 constexpr unsigned kDraftSpin = 1u << 18;   // default polls before a wait gives up
 constexpr int kTabRows = 4;                 // table rows per lane (one 256-column chunk each)
+// A gate/up-only workgroup requests its next block's rows this long (in 100 MHz ticks of
+// the constant clock) after writing its h: by then the down workgroups' wait for h is
+// over, so the 8 MB burst of gate/up rows does not queue ahead of those polls, and the
+// rows still arrive before the next z does.
+constexpr unsigned long long kPrefetchDelay = 260;
 
 struct DfArgs {
     moe_draft_weights w;
@@ -101,6 +106,11 @@ __device__ __forceinline__ uint32_t *epoch(DA a) { return reinterpret_cast<uint3
 // A wave's polling loop: done() is true once every lane's words are current, or once the
 // spin limit is reached (which raises the error flag), or within 256 polls of any other
 // wait having given up; otherwise it sleeps 64 cycles and the loop reloads.
+// Sleep until `ticks` of the constant 100 MHz clock have passed since t0.
+__device__ __forceinline__ void sleep_until(unsigned long long t0, unsigned long long ticks) {
+    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(2);
+}
+
 struct Spin {
     unsigned spins = 0;
     __device__ __forceinline__ bool done(DA a, bool ok) {
@@ -518,16 +528,24 @@ __global__ __launch_bounds__(256, 2) void k_draft_fused(DfArgs args) {
             // the rows used next: the following block's, or block 0's for the next draft
             const int nb = b + 1 < a->B ? b + 1 : 0;
             const bool more = b + 1 < a->B || i + 1 < a->gamma;
+            // The next rows are requested where their burst does not queue ahead of a
+            // critical poll (loads return in order, so a poll also waits for every load
+            // issued before it): a gate/up-only workgroup waits kPrefetchDelay after its h;
+            // a down workgroup requests its next gate/up rows before its wait for h and
+            // this block's down rows after its gate/up (they arrive during that wait).
             if (w < NG) {
                 gu_phase(a, s, G, U, i, b, w, tag);
                 if (more) {
+                    if (w >= ND) sleep_until(wall_clock64(), kPrefetchDelay);
                     G.load(a->w.gate_w, nb * a->F + rg, a->D, Lg, tid & (Lg - 1));
                     U.load(a->w.up_w, nb * a->F + rg, a->D, Lg, tid & (Lg - 1));
                 }
             }
+            if (w < ND && b > 0) Dn.load(a->w.down_w, b * a->D + rd, a->F, Ld, tid & (Ld - 1));
             if (w < ND) {
                 dn_phase(a, s, Dn, i, b, w, tag);
-                if (more) Dn.load(a->w.down_w, nb * a->D + rd, a->F, Ld, tid & (Ld - 1));
+                // block 0's down rows for the next draft
+                if (more && nb == 0) Dn.load(a->w.down_w, rd, a->F, Ld, tid & (Ld - 1));
             }
         }
         final_phase(a, s, PO, i, w, tag);
