@@ -262,7 +262,70 @@ static void attn_sweep(const moe_attn_desc &ad, int M, int pos) {
     }
 }
 
+// The one-launch drafter's geometry against what its kernel assumes (kDraftPG workgroups of
+// 256 threads; a matrix of N rows of K codes at L lanes per row, R = 256 / L rows per
+// workgroup, lane li holding pieces li, li + L, ... clamped to the row's last): every
+// workgroup count fits the grid, the rows split evenly, the pieces cover every 16-code
+// chunk of a row, the matrices whose bf16 results go out in pairs have an even R of at
+// most 16 (the kernel's staging), the vectors fit its LDS arrays (x or h: 8192 words; z and
+// u: 512 pairs), and the hand-off words of every draft and stage fit their workspace
+// regions. Shapes that fail any of these must run the chain instead (ok false).
+static void draft_geo_check(const moe_draft_desc &d) {
+    using namespace moe;
+    const DraftGeo g = draft_geo(d);
+    if (!g.ok) return;
+    const int H = d.hidden, D = d.width, F = d.ffn, B = d.blocks;
+    auto matrix = [&](int N, int K, int L, int maxc, bool pairs) {
+        CHECK(L >= 16 && L <= 256 && (L & (L - 1)) == 0);
+        const int R = 256 / L, nc = K / 16;
+        CHECK(K % 16 == 0 && N % R == 0 && N / R <= kDraftPG);
+        if (pairs) CHECK(R % 2 == 0 && R <= 16);
+        CHECK((nc + L - 1) / L <= maxc);   // every chunk k L + li < nc is held by some piece
+        return N / R;
+    };
+    matrix(D, 2 * H, g.lp, kDpPreC, true);
+    matrix(H, D, g.lpo, kDpPoC, true);
+    if (B > 0) {
+        matrix(F, D, g.lgu, kDpGuC, false);
+        matrix(D, F, g.ld, kDpDnC, true);
+    }
+    CHECK(H <= 4096 && F <= 8192 && D / 2 <= 512 && D % 256 == 0);   // LDS arrays, 256-column table chunks
+    const DraftWs W = draft_ws(d);
+    const size_t G7 = kDraftMaxGamma;
+    CHECK(W.ctr < W.epoch && W.epoch < W.zw && W.zw <= W.hw && W.hw <= W.gw && W.gw < W.kw);
+    CHECK(W.hw - W.zw >= 8 * G7 * (size_t)(B + 1) * (size_t)(D / 2));
+    CHECK(W.gw - W.hw >= 8 * G7 * (size_t)B * (size_t)F);
+    CHECK(W.kw - W.gw >= 8 * G7 * (size_t)(H / 2));
+    CHECK(W.total - W.kw >= 8 * G7 * (size_t)kDraftPG * 2);
+    // the table: 64-row units shared out, every unit's four-row lane groups inside the vocabulary
+    const int NU = d.vocab / 64;
+    long covered = 0;
+    for (int w = 0; w < kDraftPG; ++w) {
+        const int u0 = (int)((long long)w * NU / kDraftPG), u1 = (int)((long long)(w + 1) * NU / kDraftPG);
+        CHECK(u0 <= u1 && u1 <= NU);
+        covered += u1 - u0;
+    }
+    CHECK(covered == NU);
+}
+
+static void draft_geo_sweep() {
+    long n_fused = 0;
+    for (int H = 256; H <= 4096; H += 256)
+        for (int D = 256; D <= 2048; D += 256)
+            for (int F = 256; F <= 9216; F += 256)
+                for (int B : {0, 1, 12}) {
+                    const moe_draft_desc d = {H, D, F, B, 64 * (1 + (H + D + F) % 997), 1e-6f, 0u, 0u};
+                    draft_geo_check(d);
+                    n_fused += moe::draft_geo(d).ok;
+                }
+    // the 430M head takes the one-launch form
+    const moe_draft_desc mtp = {2816, 1024, 4096, 12, 262144, 1e-6f, 0u, 0u};
+    CHECK(moe::draft_geo(mtp).ok);
+    CHECK(n_fused > 1000);
+}
+
 int main() {
+    draft_geo_sweep();
     // known-good shapes
     const moe_layer_desc gemma = {2816, 128, 8, 704, 704, MOE_W_FP8_E4M3};
     for (int M = 0; M <= 9; ++M) layer_sweep(gemma, M);

@@ -226,6 +226,34 @@ def test_draft_step_validation():
     assert L.moe_draft_step(*args(w=ctypes.byref(wbad))) == native.MOE_EINVAL
 
 
+def test_draft_step_flags_and_status_validation():
+    """MOE_DRAFT_CHAIN is the only flag; the workspace does not depend on it (a workspace
+    serves both forms); the status call validates its arguments like the step's."""
+    import synth
+    L = native.lib()
+    fused = native.draft_desc(synth.MTP_HEAD)
+    chain = native.draft_desc(synth.MTP_HEAD, chain=True)
+    assert chain.flags == native.MOE_DRAFT_CHAIN
+    assert native.moe_draft_step_workspace(chain) == native.moe_draft_step_workspace(fused) > 0
+    for bad in (2, 4, 0x80000000, 3):
+        d = native.draft_desc(synth.MTP_HEAD)
+        d.flags = bad
+        assert native.moe_draft_step_workspace(d) == 0, bad
+    # a spin limit is any value (0: the default)
+    d = native.draft_desc(synth.MTP_HEAD, spin_limit=1)
+    assert native.moe_draft_step_workspace(d) == native.moe_draft_step_workspace(fused)
+    # the one-launch form's words and counter make the workspace larger than the chain alone
+    # needs: a head the one-launch form does not take (width 2048) has none of them
+    wide = native.draft_desc(synth.MTP_HEAD.__class__(hidden=2816, width=2048, ffn=4096, blocks=12, vocab=262144))
+    assert 0 < native.moe_draft_step_workspace(wide)
+    assert L.moe_draft_step_status(None, FAKE) == native.MOE_EINVAL
+    assert native.moe_draft_step_status(fused, None) == native.MOE_EWORKSPACE
+    assert native.moe_draft_step_status(fused, FAKE + 16) == native.MOE_EWORKSPACE
+    d = native.draft_desc(synth.MTP_HEAD)
+    d.flags = 2
+    assert native.moe_draft_step_status(d, FAKE) == native.MOE_EINVAL
+
+
 def test_spec_accept_validation():
     L = native.lib()
     assert L.spec_accept(-1, FAKE, FAKE, FAKE, FAKE, None) == native.MOE_EINVAL

@@ -6,9 +6,12 @@ Two drivers in tests/sanitize/ are built with gcc/g++ and -fsanitize=address,und
   over edge-case shapes, with LeakSanitizer on;
 - abi_driver.cpp with the library's host code (csrc/api.cpp) and stub launchers in place of
   the device code: every entry point on valid, invalid and swept edge-case arguments, with
-  the workspace-query/call contract checked.
+  the workspace-query/call contract checked; it also sweeps the one-launch drafter's
+  geometry (draft_geo) over head shapes against what that kernel assumes of it (grid,
+  row splits, piece coverage, LDS sizes, hand-off word regions).
 A planted overrun in the oracle and a workspace check off by one byte in api.cpp are each
-caught by these drivers (the second through the stub launchers' layout check)."""
+caught by these drivers (the second through the stub launchers' layout check), and so is
+a drafter geometry that admits one piece too many per lane."""
 import os
 import shutil
 import subprocess
