@@ -157,6 +157,28 @@ __device__ __forceinline__ float fp8_row(const uint16_t *src, int n, float (&x)[
     }
     return __fdiv_rn(block_max(amax, red), 448.0f);
 }
+// The same for a workgroup of NT threads (NT / 64 waves, red[] one entry per wave): thread t
+// holds elements t, t + NT, ... (n <= 512).
+template <int NT>
+__device__ __forceinline__ float fp8_row_t(const uint16_t *src, int n, float (&x)[512 / NT], float *red) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 512 / NT; ++e) {
+        const int d = threadIdx.x + NT * e;
+        x[e] = d < n ? bf2f(src[d]) : 0.0f;
+        amax = fmaxf(amax, fabsf(x[e]));
+    }
+    amax = row16_max(amax);
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, red[w]);
+    return __fdiv_rn(m, 448.0f);
+}
 __device__ __forceinline__ uint32_t fp8_row_code(float x, float scale) {
     return scale > 0.0f ? fp8_encode(__fdiv_rn(x, scale)) : 0u;
 }
@@ -166,11 +188,11 @@ __device__ __forceinline__ uint32_t fp8_row_code(float x, float scale) {
 // thread and request; FP8 cache: 16 codes per request and the row scale (threads 0..15).
 // Positions past the last token (bf16) or from pos on (FP8: the new rows, quantised in the
 // workgroup) read as zero; every address stays inside the cache (the position is clamped).
-template <int DH>
+template <int DH, int NT = 256>
 struct KStage {
     static constexpr int KB = DH + 8;
-    static constexpr int NB = (kChunk * DH / 8 + 255) / 256;
-    static constexpr int N8 = (kChunk * DH / 16 + 255) / 256;
+    static constexpr int NB = (kChunk * DH / 8 + NT - 1) / NT;
+    static constexpr int N8 = (kChunk * DH / 16 + NT - 1) / NT;
     static constexpr int NV = NB > N8 ? NB : N8;
     uint4 v[NV];
     float sc;
@@ -181,7 +203,7 @@ struct KStage {
             const uint16_t *cb = reinterpret_cast<const uint16_t *>(a.cache);
 #pragma unroll
             for (int e = 0; e < NB; ++e) {
-                const int i = min(tid + 256 * e, kChunk * DH / 8 - 1);
+                const int i = min(tid + NT * e, kChunk * DH / 8 - 1);
                 const int j = i / (DH / 8), cc = i - j * (DH / 8), p = p0 + j;
                 const uint4 t = reinterpret_cast<const uint4 *>(cb + ((size_t)g * a.cap + min(p, last) % a.cap) * DH)[cc];
                 v[e] = p <= last ? t : zero;
@@ -192,7 +214,7 @@ struct KStage {
             const int lim = a.pos > 0 ? a.pos - 1 : 0;
 #pragma unroll
             for (int e = 0; e < N8; ++e) {
-                const int i = min(tid + 256 * e, kChunk * DH / 16 - 1);
+                const int i = min(tid + NT * e, kChunk * DH / 16 - 1);
                 const int j = i / (DH / 16), cc = i - j * (DH / 16), p = p0 + j;
                 const uint4 t = reinterpret_cast<const uint4 *>(c8 + ((size_t)g * a.cap + min(p, lim) % a.cap) * DH)[cc];
                 v[e] = p < a.pos ? t : zero;
@@ -208,7 +230,7 @@ struct KStage {
         if (!a.fp8) {
 #pragma unroll
             for (int e = 0; e < NB; ++e) {
-                const int i = tid + 256 * e;
+                const int i = tid + NT * e;
                 if (i < kChunk * DH / 8) {
                     const int j = i / (DH / 8), cc = i - j * (DH / 8);
                     kb4[(j * KB) / 8 + cc] = v[e];
@@ -217,7 +239,7 @@ struct KStage {
         } else {
 #pragma unroll
             for (int e = 0; e < N8; ++e) {
-                const int i = tid + 256 * e;
+                const int i = tid + NT * e;
                 if (i < kChunk * DH / 16) {
                     const int j = i / (DH / 16), cc = i - j * (DH / 16);
                     const uint32_t vw[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
@@ -375,14 +397,17 @@ __global__ __launch_bounds__(256) void k_attn_part(PartArgs a) {
 // dense contractions on gfx950's matrix cores (v_mfma_f32_16x16x32_bf16: lane l holds row
 // l % 16, k 8 (l / 16) .. + 7 of A, k 8 (l / 16) .. + 7, column l % 16 of B, and rows
 // 4 (l / 16) .. + 3, column l % 16 of C). Per 32-position chunk of the stripe:
-//   S = Q K^T        wave v takes query tile v (16 queries, its A operands held in registers
-//                    for the whole stripe) against both 16-position halves of the chunk
+//   S = Q K^T        wave v < 4 takes query tile v (16 queries, its A operands held in
+//                    registers for the whole stripe) against both 16-position halves of the
+//                    chunk, while waves 4..7 write the transposed copy of the chunk
 //   softmax          each lane owns four query rows of S; the row maximum and sum go over the
 //                    16 lanes of its DPP row; the weights p (times the FP8 row scale) are
 //                    split into bf16 high and low parts (16 bits of mantissa together)
-//   O += P V         wave v takes a quarter of the head's 16-dimension tiles for every query
+//   O += P V         wave v takes an eighth of the head's 16-dimension tiles for every query
 //                    tile, V being the chunk's keys (the cached key is also the value), read
-//                    from a transposed copy of the chunk in LDS
+//                    from the transposed copy; a tile's accumulators are rescaled only when
+//                    one of its rows' maxima moved
+// Eight waves (two per SIMD) so that one wave's LDS and matrix latencies hide behind another's.
 // The records have k_attn_part's layout, so k_attn_combine finishes both. Bf16 products are
 // exact in fp32; the sums run in the matrix cores' order (fixed, so the result does not
 // depend on timing).
@@ -405,13 +430,14 @@ struct MmaLds {
     uint16_t pl[16 * kMmaMaxQt * TB];
     float al[16 * kMmaMaxQt];
     float ksc[kMmaChunk];
-    float red[4];
+    float red[8];
 };
+constexpr int kMmaThreads = 512;
 
 template <int DH>
-__global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
+__global__ __launch_bounds__(kMmaThreads, 1) void k_attn_part_mma(PartArgs a) {
     using LDS = MmaLds<DH>;
-    constexpr int KB = LDS::KB, TB = LDS::TB, NKK = DH / 32, DTW = DH / 64;
+    constexpr int NT = kMmaThreads, KB = LDS::KB, TB = LDS::TB, NKK = DH / 32, DTW = DH / 16 / (NT / 64);
     __shared__ __align__(16) LDS L;
     uint4 *kb4 = reinterpret_cast<uint4 *>(L.kp);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r16 = lane & 15, k8 = lane >> 4;
@@ -420,6 +446,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
     const int NQ = a.G * a.nkv * DH, NK = a.nkv * DH;
     const int last = a.pos + a.M - 1;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    const bool sw = wave < Qt;   // this wave scores query tile `wave`
 
     // query tile `wave`: A operands of every 32-dimension step, and the rows' token bounds
     uint4 qa[NKK];
@@ -428,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
     bool rv[4];
     {
         const int qi = wave * 16 + r16;
-        const bool on = wave < Qt && qi < Q;
+        const bool on = sw && qi < Q;
         const int m = on ? qi / a.G : 0, h = g * a.G + (on ? qi - m * a.G : 0);
         const uint16_t *qp = a.q + (size_t)m * NQ + (size_t)h * DH + 8 * k8;
 #pragma unroll
@@ -436,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wave * 16 + 4 * k8 + i;
-            rv[i] = wave < Qt && r < Q;
+            rv[i] = sw && r < Q;
             const int tok = rv[i] ? r / a.G : 0;
             hi_r[i] = a.pos + tok;
             lo_r[i] = a.window > 0 ? max(0, hi_r[i] - a.window + 1) : 0;
@@ -451,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
         for (int j = 0; j < DTW; ++j) o[mt][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     uint8_t *c8 = reinterpret_cast<uint8_t *>(a.cache);
-    KStage<DH> k0, k1;
+    KStage<DH, NT> k0, k1;
     if (w < a.nch) {
         k0.load(a, g, a.lo0 + w * kMmaChunk, last);
         k1.load(a, g, a.lo0 + w * kMmaChunk + kChunk, last);
@@ -467,12 +494,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
             const int jn0 = max(0, a.pos - p0), jn1 = min(kMmaChunk, last - p0 + 1);
             for (int j = jn0; j < jn1; ++j) {
                 const int p = p0 + j, m = p - a.pos;
-                float x[2];
-                const float scale = fp8_row(a.knew + (size_t)m * NK + (size_t)g * DH, DH, x, L.red);
+                float x[512 / NT];
+                const float scale = fp8_row_t<NT>(a.knew + (size_t)m * NK + (size_t)g * DH, DH, x, L.red);
                 const size_t slot = (size_t)g * a.cap + p % a.cap;
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int d = tid + 256 * e;
+                for (int e = 0; e < 512 / NT; ++e) {
+                    const int d = tid + NT * e;
                     if (d < DH) {
                         const uint32_t code = fp8_row_code(x[e], scale);
                         c8[slot * DH + d] = (uint8_t)code;
@@ -486,24 +513,24 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
             }
         }
         __syncthreads();
-        // the transposed copy [dimension][position] for the V operand
-        for (int i = tid; i < kMmaChunk * DH / 8; i += 256) {
-            const int pp = i % kMmaChunk, d0 = 8 * (i / kMmaChunk);
-            const uint4 v = *reinterpret_cast<const uint4 *>(L.kp + pp * KB + d0);
-            const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                L.kt[(d0 + 2 * e) * TB + pp] = (uint16_t)(vw[e] & 0xffffu);
-                L.kt[(d0 + 2 * e + 1) * TB + pp] = (uint16_t)(vw[e] >> 16);
-            }
-        }
         // the next chunk's keys are requested now, so they arrive during this one
         if (c + a.nwg < a.nch) {
             k0.load(a, g, p0 + a.nwg * kMmaChunk, last);
             k1.load(a, g, p0 + a.nwg * kMmaChunk + kChunk, last);
         }
-        __syncthreads();
-        if (wave < Qt) {
+        if (wave >= 4) {
+            // the transposed copy [dimension][position] for the V operand
+            for (int i = tid - 256; i < kMmaChunk * DH / 8; i += NT - 256) {
+                const int pp = i % kMmaChunk, d0 = 8 * (i / kMmaChunk);
+                const uint4 v = *reinterpret_cast<const uint4 *>(L.kp + pp * KB + d0);
+                const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    L.kt[(d0 + 2 * e) * TB + pp] = (uint16_t)(vw[e] & 0xffffu);
+                    L.kt[(d0 + 2 * e + 1) * TB + pp] = (uint16_t)(vw[e] >> 16);
+                }
+            }
+        } else if (sw) {
             // scores of query tile `wave` against positions p0 + r16 and p0 + 16 + r16
             f32x4_t s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -546,15 +573,19 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
                 const float4 al = *reinterpret_cast<const float4 *>(L.al + mt * 16 + 4 * k8);
                 const uint4 ah = *reinterpret_cast<const uint4 *>(L.ph + (mt * 16 + r16) * TB + 8 * k8);
                 const uint4 alo = *reinterpret_cast<const uint4 *>(L.pl + (mt * 16 + r16) * TB + 8 * k8);
+                // a row's accumulators change only when its maximum moved (alpha != 1)
+                const bool rescale = __any(al.x != 1.0f || al.y != 1.0f || al.z != 1.0f || al.w != 1.0f);
 #pragma unroll
                 for (int j = 0; j < DTW; ++j) {
                     const int dt = wave * DTW + j;
                     const uint4 bv = *reinterpret_cast<const uint4 *>(L.kt + (dt * 16 + r16) * TB + 8 * k8);
                     f32x4_t acc = o[mt][j];
-                    acc[0] *= al.x;
-                    acc[1] *= al.y;
-                    acc[2] *= al.z;
-                    acc[3] *= al.w;
+                    if (rescale) {
+                        acc[0] *= al.x;
+                        acc[1] *= al.y;
+                        acc[2] *= al.z;
+                        acc[3] *= al.w;
+                    }
                     acc = mma16(ah, bv, acc);
                     o[mt][j] = mma16(alo, bv, acc);
                 }
@@ -565,7 +596,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_part_mma(PartArgs a) {
     // records: (max, sum, -, -, acc[DH]) per query, in k_attn_part's layout
     const size_t R = DH + 4;
     float *recs = a.part + ((size_t)g * a.Q * a.nwg + w) * R;   // query q at recs + q nwg R
-    if (wave < Qt && r16 == 0) {
+    if (sw && r16 == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = wave * 16 + 4 * k8 + i;
@@ -752,7 +783,7 @@ int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M,
         ta.nch = nch;
         ta.nwg = nwg;
         ta.qsplit = 1;
-        hipLaunchKernelGGL((k_attn_part_mma<512>), dim3(nwg, d.kv_heads), dim3(256), 0, S(stream), ta);
+        hipLaunchKernelGGL((k_attn_part_mma<512>), dim3(nwg, d.kv_heads), dim3(kMmaThreads), 0, S(stream), ta);
     } else if (!by_dh(d.head_dim, [&](auto D) {
                    constexpr int dh = decltype(D)::value;
                    hipLaunchKernelGGL((k_attn_part<dh>), dim3(P.nwg, d.kv_heads * P.qsplit), dim3(256), 0, S(stream), ta);
