@@ -771,14 +771,19 @@ int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M,
     PartArgs ta{q, k, cache, reinterpret_cast<float *>(cache + C.scales), fp8 ? 1 : 0, d.kv_heads, P.G, M, pos,
                 d.window, d.capacity, P.lo0, P.nch, P.nwg, P.Q, P.qsplit, 1.0f / sqrtf((float)d.head_dim), part};
     int nwg = P.nwg;
-    if (d.head_dim == 512 && P.Q >= 16 && P.Q <= 16 * kMmaMaxQt) {
-        // 512-wide heads (the global layers) with at least a full tile of queries per KV head
-        // (a verify batch): every query of a KV head in one workgroup, on the matrix cores,
-        // 32-position chunks; as many stripes per KV head as the records allow. A single
-        // token's 8 queries per KV head measured no faster there than on the vector units
-        // (32K context: 86.1 against 84.3 us per layer), so they stay on k_attn_part.
+    if (d.head_dim == 512 && P.Q <= 16 * kMmaMaxQt) {
+        // 512-wide heads (the global layers) with at most four tiles of queries per KV head:
+        // every query of a KV head in one workgroup, on the matrix cores, 32-position chunks;
+        // as many stripes per KV head as the records allow. A single token's 8 queries per KV
+        // head fill half a tile and still run faster here than on the vector units (32K
+        // context: 55.3 against 85.5 us per layer).
+        // One workgroup fills a compute unit (85 KB of LDS), so the stripes per KV head are
+        // also capped at the compute units over the KV heads: one round of workgroups.
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return MOE_ELAUNCH;
         const int nch = (pos + M - P.lo0 + kMmaChunk - 1) / kMmaChunk;
-        const int cap = std::max(1, std::min(kAttnMaxWG, kAttnRecords / (d.kv_heads * P.Q)));
+        const int cap = std::max(1, std::min({kAttnMaxWG, kAttnRecords / (d.kv_heads * P.Q), cus / d.kv_heads}));
         nwg = std::min(nch, cap);
         ta.nch = nch;
         ta.nwg = nwg;

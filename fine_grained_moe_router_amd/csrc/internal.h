@@ -204,9 +204,11 @@ inline AttnCache attn_cache(const moe_attn_desc &d) {
 // The partial-softmax grid for M tokens at pos: G query heads per KV head, Q = G M queries
 // per KV head in tiles of 16, 16-position chunks from lo0 (token 0's first visible position)
 // to pos + M - 1, nwg stripes of chunks per (KV head, tile) so the grid stays <= 512
-// workgroups and the records (one per query and stripe) <= 16 x 512.
+// workgroups and the records (one per query and stripe) <= 16 x 512. The matrix-core form
+// (all of a KV head's queries in one workgroup) takes up to 32 x 512 records: a stripe per
+// compute unit for 2 KV heads of 64 queries.
 constexpr int kAttnMaxWG = 512;
-constexpr int kAttnRecords = 16 * kAttnMaxWG;
+constexpr int kAttnRecords = 32 * kAttnMaxWG;
 struct AttnPlan {
     int G, Q, qsplit, lo0, nch, nwg;
 };
