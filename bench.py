@@ -657,7 +657,7 @@ def attn_main(args):
     and M = 5, with bf16 and with FP8 caches. The caches hold seeded synthetic keys of every
     earlier position; each step appends the same M keys again, so replays do not drift. Steps
     are captured into HIP graphs of 20 and replayed; bytes per step are the weights plus the
-    KV rows read (attn_layer_bytes)."""
+    KV rows read (attn_layer_bytes). One global layer is also timed alone (global_layer_us)."""
     import torch
     import synth
     from fine_grained_moe_router_amd import native
@@ -717,16 +717,36 @@ def attn_main(args):
                         torch.cuda.synchronize()
                         blocks.append(e0.elapsed_time(e1) / (20 * reps))
                     del gr
+                    # one global layer alone, the same way
+                    gl = next(l for l, sh in enumerate(shapes) if not sh.window)
+                    gr = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(gr, stream=stream):
+                        for _ in range(20):
+                            native.moe_attn_decode(descs[gl], wd[gl], M, ctx, us[gl], caches[gl], outs[gl], None, ws,
+                                                   wsb, stream)
+                    torch.cuda.synchronize()
+                    gblocks = []
+                    for b in range(5):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(reps):
+                            gr.replay()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        gblocks.append(e0.elapsed_time(e1) / (20 * reps))
+                    del gr
                 ms = float(np.median(blocks))
+                g_us = float(np.median(gblocks)) * 1e3
                 bps = sum(attn_layer_bytes(sh, M, ctx) for sh in shapes)
                 gbs = bps / (ms / 1e3) / 1e9
                 key = "ctx%d_M%d_%s" % (ctx, M, "fp8kv" if fp8 else "bf16kv")
                 results[key] = {"ms_per_step": round(ms, 5), "bytes_per_step": int(bps), "hbm_gbs": round(gbs, 1),
                                 "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                                "block_ms_per_step": [round(b, 5) for b in blocks]}
-                log("attention ctx %5d M=%d %s KV: %.1f us/step (%.1f us/layer), %.1f MB, %.1f GB/s (%.1f%%)" % (
-                    ctx, M, "FP8 " if fp8 else "bf16", ms * 1e3, ms * 1e3 / 30, bps / 1e6, gbs,
-                    100 * gbs / HBM_PEAK_GBS))
+                                "block_ms_per_step": [round(b, 5) for b in blocks],
+                                "global_layer_us": round(g_us, 2)}
+                log("attention ctx %5d M=%d %s KV: %.1f us/step (%.1f us/layer), %.1f MB, %.1f GB/s (%.1f%%); "
+                    "one global layer %.1f us" % (ctx, M, "FP8 " if fp8 else "bf16", ms * 1e3, ms * 1e3 / 30, bps / 1e6,
+                                                  gbs, 100 * gbs / HBM_PEAK_GBS, g_us))
             del caches
             torch.cuda.empty_cache()
     head = results["ctx8192_M1_bf16kv"]
