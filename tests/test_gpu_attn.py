@@ -13,8 +13,10 @@ against the oracle's attention layer, through the C ABI.
 - Shapes: a tiny layer (sliding with the ring wrapped, and global), and the Gemma-4-26B-A4B
   sliding (16 x 256, 8 KV heads, window 1024) and global (16 x 512, 2 KV heads) layers at
   long contexts, M = 1, 5 and 8 (the global layer also at M = 2 and 3 and at its first
-  positions: from M = 2 its partial softmax runs on the matrix cores), bf16 and FP8
-  caches; determinism of both global paths.
+  positions), bf16 and FP8 caches. 512-wide heads with up to 64 queries per KV head run the
+  partial softmax on the matrix cores (one to four query tiles); a layer with 16 query heads
+  per KV head at M = 5 (80 queries) runs it on the vector units, and a 512-wide sliding
+  layer checks the matrix-core path's window and ring. Determinism of both paths.
 """
 import numpy as np
 import pytest
@@ -147,22 +149,44 @@ def test_attn_gemma_sliding_layer(kv_fp8, M):
 @pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
 @pytest.mark.parametrize("M", [1, 2, 3, 5, 8])
 def test_attn_gemma_global_layer(kv_fp8, M):
-    """The Gemma global layer at an 8K context (16 query heads of 512, 2 KV heads). From
-    M = 2 (16 queries per KV head) the partial softmax runs on the matrix cores: one full
-    query tile (M = 2), a partial second one (M = 3), three (M = 5) and four (M = 8)."""
+    """The Gemma global layer at an 8K context (16 query heads of 512, 2 KV heads), its
+    partial softmax on the matrix cores: half a query tile (M = 1), one full tile (M = 2), a
+    partial second one (M = 3), three (M = 5) and four (M = 8)."""
     shape = synth.GEMMA4_GLOBAL.with_(kv_fp8=kv_fp8, capacity=8200)
     g, r = run_layer(shape, M, 8000, 14)
     check(shape, M, 8000, g, r, "gemma global")
 
 
 @pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("M,pos", [(2, 0), (5, 5), (8, 31), (5, 40)])
+@pytest.mark.parametrize("M,pos", [(1, 0), (2, 0), (5, 5), (8, 31), (5, 40), (1, 33)])
 def test_attn_gemma_global_short(kv_fp8, M, pos):
     """The matrix-core path at the first positions: one or two 32-position chunks, most of
     them masked (a query sees only the positions up to its own), the new keys inside them."""
     shape = synth.GEMMA4_GLOBAL.with_(kv_fp8=kv_fp8, capacity=128)
     g, r = run_layer(shape, M, pos, 17)
     check(shape, M, pos, g, r, "gemma global short")
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("M", [4, 5])
+def test_attn_global_wide_group(kv_fp8, M):
+    """512-wide heads with 16 query heads per KV head: 64 queries per KV head at M = 4 (four
+    tiles on the matrix cores) and 80 at M = 5 (more than one workgroup of the matrix-core
+    form holds, so the vector-unit kernel runs)."""
+    shape = synth.GEMMA4_GLOBAL.with_(q_heads=32, kv_fp8=kv_fp8, capacity=2100)
+    g, r = run_layer(shape, M, 2000, 18)
+    check(shape, M, 2000, g, r, "global G=16")
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 5])
+def test_attn_512_wide_sliding(kv_fp8, M):
+    """512-wide heads with a window on the matrix cores: a 300-position window over a ring of
+    308 slots, wrapped several times; the masks of the window's first position and of the
+    verify batch's later tokens fall inside the chunks."""
+    shape = synth.GEMMA4_GLOBAL.with_(window=300, capacity=308, kv_fp8=kv_fp8)
+    g, r = run_layer(shape, M, 1000, 19)
+    check(shape, M, 1000, g, r, "512-wide sliding")
 
 
 def test_attn_gemma_global_full_context_fp8():
