@@ -175,7 +175,7 @@ struct Row {
         const int nc = K >> 4;
         const uint8_t *p = m + (size_t)row * K;
 #pragma unroll
-        for (int k = 0; k < MAXC; ++k) q[k] = ld16(p + (size_t)min(k * L + li, nc - 1) * 16);
+        for (int k = 0; k < MAXC; ++k) q[k] = ld16nt(p + (size_t)min(k * L + li, nc - 1) * 16);
     }
     // sum of dec(q) x over the lane's pieces, x bf16 in LDS (two uint4 per piece)
     __device__ __forceinline__ float dot_bf16(const uint4 *xs, int K, int L, int li) const {
@@ -403,7 +403,7 @@ __device__ __forceinline__ void tab_load(DA a, int u0, int nst, int st, TabBuf &
         const size_t row = (size_t)unit * 64 + wave * 16 + (lane >> 4) * kTabRows;
         const uint8_t *p = a->w.table_w + row * a->D + k * 256 + (lane & 15) * 16;
 #pragma unroll
-        for (int r = 0; r < kTabRows; ++r) b.q[r] = ld16(p + (size_t)r * a->D);
+        for (int r = 0; r < kTabRows; ++r) b.q[r] = ld16nt(p + (size_t)r * a->D);
     }
 }
 

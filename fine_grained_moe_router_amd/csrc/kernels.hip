@@ -15,6 +15,7 @@
 #include <mutex>
 
 #include "device_common.h"
+#include "handoff.h"
 #include "internal.h"
 
 namespace moe {
@@ -256,8 +257,8 @@ __global__ __launch_bounds__(256) void k_gateup(ExpertArgs a) {
 #pragma unroll
         for (int k = 0; k < kGateUpUnroll; ++k) {
             if (i0 + k < NC) {
-                qg[k] = *reinterpret_cast<const uint4 *>(gw + (size_t)(i0 + k) * 256);
-                qu[k] = *reinterpret_cast<const uint4 *>(uw + (size_t)(i0 + k) * 256);
+                qg[k] = ld16nt(gw + (size_t)(i0 + k) * 256);
+                qu[k] = ld16nt(uw + (size_t)(i0 + k) * 256);
             }
         }
 #pragma unroll
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void k_down(ExpertArgs a) {
             uint4 qd[kDownUnroll];
 #pragma unroll
             for (int k = 0; k < kDownUnroll; ++k)
-                if (i0 + k < NI) qd[k] = *reinterpret_cast<const uint4 *>(dw + (size_t)(i0 + k) * 64);
+                if (i0 + k < NI) qd[k] = ld16nt(dw + (size_t)(i0 + k) * 64);
 #pragma unroll
             for (int k = 0; k < kDownUnroll; ++k) {
                 if (i0 + k < NI) {
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(256) void k_lmhead(LmArgs a) {
 #pragma unroll
                 for (int r = 0; r < kLmRowsPerLane; ++r)
                     if (i0 + k < NC)
-                        q[k][r] = *reinterpret_cast<const uint4 *>(wr + (size_t)r * H * EB + (size_t)(i0 + k) * 256);
+                        q[k][r] = ld16nt(wr + (size_t)r * H * EB + (size_t)(i0 + k) * 256);
 #pragma unroll
             for (int k = 0; k < kLmUnroll; ++k) {
                 if (i0 + k < NC) {
@@ -825,12 +826,12 @@ __global__ __launch_bounds__(256) void k_read_probe(const uint4 *__restrict__ sr
     for (; i + (kProbeDepth - 1) * T < n; i += kProbeDepth * T) {
         uint4 p[kProbeDepth];
 #pragma unroll
-        for (int k = 0; k < kProbeDepth; ++k) p[k] = src[i + k * T];
+        for (int k = 0; k < kProbeDepth; ++k) p[k] = ld16nt(src + i + k * T);
 #pragma unroll
         for (int k = 0; k < kProbeDepth; ++k) acc ^= p[k].x ^ p[k].y ^ p[k].z ^ p[k].w;
     }
     for (; i < n; i += T) {
-        const uint4 p0 = src[i];
+        const uint4 p0 = ld16nt(src + i);
         acc ^= p0.x ^ p0.y ^ p0.z ^ p0.w;
     }
     red[threadIdx.x] = acc;

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "device_common.h"
+#include "handoff.h"
 
 namespace moe {
 namespace dev {
@@ -20,7 +21,7 @@ struct Pieces {
     __device__ __forceinline__ void load(const uint8_t *row, int li, int ch) {
 #pragma unroll
         for (int k = 0; k < MAXCH; ++k)
-            if (k < ch) q[k] = *reinterpret_cast<const uint4 *>(row + (size_t)(k * LPR + li) * 16);
+            if (k < ch) q[k] = ld16nt(row + (size_t)(k * LPR + li) * 16);
     }
     // sum_c dec(Q[c]) x[c] over this lane's pieces, x bf16 in LDS (two uint4 per piece)
     __device__ __forceinline__ float dot_bf16(const uint4 *xs, int li, int ch) const {

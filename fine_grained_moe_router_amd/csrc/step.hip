@@ -841,9 +841,9 @@ __device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf
         const uint4 *vp = reinterpret_cast<const uint4 *>(
             (shared ? (const uint8_t *)wp->sh_up_w : (const uint8_t *)wp->up_w + eoff * H * g::EB) + (size_t)row * H * g::EB);
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(gp + min(j + g::LG * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16nt(gp + min(j + g::LG * i, NP - 1));
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(vp + min(j + g::LG * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16nt(vp + min(j + g::LG * i, NP - 1));
         b.sc[0] = BF ? 1.0f : *glb((shared ? wp->sh_gate_s : wp->gate_s + eoff) + row);
         b.sc[1] = BF ? 1.0f : *glb((shared ? wp->sh_up_s : wp->up_s + eoff) + row);
     } else {
@@ -854,9 +854,9 @@ __device__ __forceinline__ void load_unit(AP a, int l, const UnitRef &u, UnitBuf
         const uint4 *d0 = reinterpret_cast<const uint4 *>(dp);
         const uint4 *d1 = reinterpret_cast<const uint4 *>(dp + (size_t)(g::RD / 2) * F * g::EB);
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[i] = ld16(d0 + min(j + g::LD * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[i] = ld16nt(d0 + min(j + g::LD * i, NP - 1));
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16(d1 + min(j + g::LD * i, NP - 1));
+        for (int i = 0; i < kPc; ++i) b.w[kPc + i] = ld16nt(d1 + min(j + g::LD * i, NP - 1));
         const float *ds = shared ? wp->sh_down_s : wp->down_s + (size_t)e * H;
         b.sc[0] = BF ? 1.0f : *glb(ds + c0);
         b.sc[1] = BF ? 1.0f : *glb(ds + c0 + g::RD / 2);
@@ -1214,7 +1214,7 @@ __device__ __forceinline__ void lm_load(AP a, int u0, int nst, int st, LmBuf &b)
         const size_t row = (size_t)unit * 64 + wave * 16 + (lane >> 4) * kLmRows;
         const uint8_t *p = a->lm_w + row * a->H * EB + k * 256 + (lane & 15) * 16;
 #pragma unroll
-        for (int r = 0; r < kLmRows; ++r) b.q[r] = ld16(p + (size_t)r * a->H * EB);
+        for (int r = 0; r < kLmRows; ++r) b.q[r] = ld16nt(p + (size_t)r * a->H * EB);
     }
 }
 

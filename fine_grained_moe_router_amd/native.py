@@ -257,7 +257,7 @@ def moe_fp8_decode(n, codes, out_via_bf16, out_via_f32, stream=None):
     _check("moe_fp8_decode", st)
 
 
-PROBE_GRID = 4096   # MOE_PROBE_GRID: words of the read probe's sink
+PROBE_GRID = 8192   # MOE_PROBE_GRID: words of the read probe's sink
 
 
 def moe_hbm_read_probe(src, nbytes, sink, stream=None):

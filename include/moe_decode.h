@@ -283,12 +283,13 @@ int moe_fp8_decode(int n, const uint8_t *codes, float *out_via_bf16, float *out_
 /*
  * Diagnostic: the streaming-read rate a kernel of this library gets from HBM, the
  * practical ceiling to set beside the nominal 8 TB/s. Reads `bytes` bytes from src once,
- * with 16-byte loads spread over MOE_PROBE_GRID workgroups of 256 threads, and folds them
- * into one word per workgroup (sink[w] = XOR of the 32-bit words workgroup w read), so
- * that the loads are kept. bytes a positive multiple of 16; src and sink 16-byte aligned;
- * sink holds MOE_PROBE_GRID words. Asynchronous on `stream`.
+ * with 16-byte loads carrying the nontemporal hint (as the library's weight streams do)
+ * spread over MOE_PROBE_GRID workgroups of 256 threads, and folds them into one word per
+ * workgroup (sink[w] = XOR of the 32-bit words workgroup w read), so that the loads are
+ * kept. bytes a positive multiple of 16; src and sink 16-byte aligned; sink holds
+ * MOE_PROBE_GRID words. Asynchronous on `stream`.
  */
-#define MOE_PROBE_GRID 4096
+#define MOE_PROBE_GRID 8192
 int moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
 
 /* ------------------------------------------------------------------------------
