@@ -507,7 +507,7 @@ __device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
 template <int MT>
 __device__ __forceinline__ void router_phase(AP a0, int l, int j, const uint4 (&wq)[kNC], uint32_t tgt) {
     const AP a = uniform(a0);
-    const int H = a->H, E = a->E, tid = ltid(), lane32 = tid & 31;
+    const int E = a->E, tid = ltid(), lane32 = tid & 31;
     const int e = 8 * j + (tid >> 5);
     const bool valid = e < E;
     const float *bias = layer_w(a, l)->router_bias;
