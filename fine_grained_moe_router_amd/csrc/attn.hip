@@ -435,7 +435,7 @@ struct MmaLds {
 constexpr int kMmaThreads = 512;
 
 template <int DH>
-__global__ __launch_bounds__(kMmaThreads, 1) void k_attn_part_mma(PartArgs a) {
+__global__ __launch_bounds__(kMmaThreads, 2) void k_attn_part_mma(PartArgs a) {
     using LDS = MmaLds<DH>;
     constexpr int NT = kMmaThreads, KB = LDS::KB, TB = LDS::TB, NKK = DH / 32, DTW = DH / 16 / (NT / 64);
     __shared__ __align__(16) LDS L;
@@ -771,14 +771,14 @@ int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M,
     PartArgs ta{q, k, cache, reinterpret_cast<float *>(cache + C.scales), fp8 ? 1 : 0, d.kv_heads, P.G, M, pos,
                 d.window, d.capacity, P.lo0, P.nch, P.nwg, P.Q, P.qsplit, 1.0f / sqrtf((float)d.head_dim), part};
     int nwg = P.nwg;
-    if (d.head_dim == 512 && P.Q <= 16 * kMmaMaxQt) {
+    if (P.Q <= 16 * kMmaMaxQt && (d.head_dim == 512 || (d.head_dim == 256 && P.Q >= 8))) {
         // 512-wide heads (the global layers) with at most four tiles of queries per KV head:
         // every query of a KV head in one workgroup, on the matrix cores, 32-position chunks;
         // as many stripes per KV head as the records allow. A single token's 8 queries per KV
         // head fill half a tile and still run faster here than on the vector units (32K
-        // context: 55.3 against 85.5 us per layer).
-        // One workgroup fills a compute unit (85 KB of LDS), so the stripes per KV head are
-        // also capped at the compute units over the KV heads: one round of workgroups.
+        // context: 55.3 against 85.5 us per layer). 256-wide heads (the sliding layers, 2 query
+        // heads per KV head) take it from 8 queries per KV head (M >= 4): at M = 5 the 30-layer
+        // attention step measured 2-3 % faster with it, at M = 1 (2 queries) 2-4 % slower.
         int dev = 0, cus = 0;
         if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return MOE_ELAUNCH;
@@ -788,7 +788,10 @@ int launch_attn_decode(const moe_attn_desc &d, const moe_attn_weights &w, int M,
         ta.nch = nch;
         ta.nwg = nwg;
         ta.qsplit = 1;
-        hipLaunchKernelGGL((k_attn_part_mma<512>), dim3(nwg, d.kv_heads), dim3(kMmaThreads), 0, S(stream), ta);
+        if (d.head_dim == 512)
+            hipLaunchKernelGGL((k_attn_part_mma<512>), dim3(nwg, d.kv_heads), dim3(kMmaThreads), 0, S(stream), ta);
+        else
+            hipLaunchKernelGGL((k_attn_part_mma<256>), dim3(nwg, d.kv_heads), dim3(kMmaThreads), 0, S(stream), ta);
     } else if (!by_dh(d.head_dim, [&](auto D) {
                    constexpr int dh = decltype(D)::value;
                    hipLaunchKernelGGL((k_attn_part<dh>), dim3(P.nwg, d.kv_heads * P.qsplit), dim3(256), 0, S(stream), ta);

@@ -13,10 +13,11 @@ against the oracle's attention layer, through the C ABI.
 - Shapes: a tiny layer (sliding with the ring wrapped, and global), and the Gemma-4-26B-A4B
   sliding (16 x 256, 8 KV heads, window 1024) and global (16 x 512, 2 KV heads) layers at
   long contexts, M = 1, 5 and 8 (the global layer also at M = 2 and 3 and at its first
-  positions), bf16 and FP8 caches. 512-wide heads with up to 64 queries per KV head run the
-  partial softmax on the matrix cores (one to four query tiles); a layer with 16 query heads
-  per KV head at M = 5 (80 queries) runs it on the vector units, and a 512-wide sliding
-  layer checks the matrix-core path's window and ring. Determinism of both paths.
+  positions), bf16 and FP8 caches. 512-wide heads with up to 64 queries per KV head, and
+  256-wide heads with 8 to 64, run the partial softmax on the matrix cores (one to four query
+  tiles); a layer with 16 query heads per KV head at M = 5 (80 queries) and the sliding layer
+  below 8 queries per KV head run it on the vector units, and a 512-wide sliding layer checks
+  the matrix-core path's window and ring. Determinism of both paths.
 """
 import numpy as np
 import pytest
@@ -138,9 +139,11 @@ def test_attn_tiny_global(kv_fp8, M, pos):
 
 
 @pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
-@pytest.mark.parametrize("M", [1, 5, 8])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8])
 def test_attn_gemma_sliding_layer(kv_fp8, M):
-    """The Gemma sliding layer with the ring wrapped several times (pos 5000, capacity 1032)."""
+    """The Gemma sliding layer with the ring wrapped several times (pos 5000, capacity 1032):
+    2 and 6 queries per KV head on the vector units (M = 1, 3), 8, 10 and 16 on the matrix
+    cores (M = 4, 5, 8)."""
     shape = synth.GEMMA4_SLIDING.with_(kv_fp8=kv_fp8)
     g, r = run_layer(shape, M, 5000, 13)
     check(shape, M, 5000, g, r, "gemma sliding")
