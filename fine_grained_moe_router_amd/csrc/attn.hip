@@ -642,15 +642,33 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombArgs a) {
     const int g = blockIdx.x / a.Q, qi = blockIdx.x - g * a.Q, d = 64 * blockIdx.y + lane;
     const int R = a.dh + 4;
     const float *rec = a.part + ((size_t)g * a.Q + qi) * a.nwg * R;
-    float mx = -INFINITY;
-    for (int w = tid; w < a.nwg; w += 256) mx = fmaxf(mx, rec[(size_t)w * R]);
-    mx = block_max(mx, red);
+    const float *col = rec + 4 + d;
+    // Every load of the first pass is issued at once: this thread's stripes' (max, sum) pairs
+    // (stripes t and t + 256) and the wave's first eight output values (stripes v, v + 4, ...,
+    // v + 28), so that a stripe count up to 32 costs one memory latency.
+    static_assert(kAttnMaxWG <= 512, "two stripes per thread");
+    float mv[2], lv[2], v0[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int w = wv + 4 * k;
+        v0[k] = w < a.nwg ? col[(size_t)w * R] : 0.0f;
+    }
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+        const int w = tid + 256 * j2;
+        mv[j2] = w < a.nwg ? rec[(size_t)w * R] : -INFINITY;
+        lv[j2] = w < a.nwg ? rec[(size_t)w * R + 1] : 0.0f;
+    }
+    const float mx = block_max(fmaxf(mv[0], mv[1]), red);
     float ls = 0.0f;
-    for (int w = tid; w < a.nwg; w += 256) {
-        const float m = rec[(size_t)w * R];
-        const float e = m == -INFINITY ? 0.0f : expf(m - mx);
-        wt[w] = e;
-        ls = fmaf(rec[(size_t)w * R + 1], e, ls);
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+        const int w = tid + 256 * j2;
+        if (w < a.nwg) {
+            const float e = mv[j2] == -INFINITY ? 0.0f : expf(mv[j2] - mx);
+            wt[w] = e;
+            ls = fmaf(lv[j2], e, ls);
+        }
     }
     ls = row16_sum(ls);
     ls += __shfl_xor(ls, 16);
@@ -659,9 +677,15 @@ __global__ __launch_bounds__(256) void k_attn_combine(CombArgs a) {
     if (lane == 0) red[wv] = ls;
     __syncthreads();
     const float L = (red[0] + red[1]) + (red[2] + red[3]);
-    const float *col = rec + 4 + d;
+    // the weighted sum over the wave's stripes, in stripe order: the prefetched eight, then
+    // eight records requested at a time
     float acc = 0.0f;
-    int w = wv;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int w = wv + 4 * k;
+        if (w < a.nwg) acc = fmaf(v0[k], wt[w], acc);
+    }
+    int w = wv + 32;
     for (; w + 28 < a.nwg; w += 32) {
         float v[8];
 #pragma unroll
