@@ -49,7 +49,7 @@ typedef enum moe_status {
     MOE_EINVAL = -1,        /* a size or count out of range, or a required pointer is NULL */
     MOE_EALIGN = -2,        /* a pointer is not 16-byte aligned                              */
     MOE_EWORKSPACE = -3,    /* workspace NULL or smaller than the *_workspace() size         */
-    MOE_EUNSUPPORTED = -4,  /* a valid request this build does not implement                 */
+    MOE_EUNSUPPORTED = -4,  /* a valid request the library does not implement               */
     MOE_ELAUNCH = -5,       /* the HIP runtime rejected a kernel launch                      */
     MOE_ETIMEOUT = -6       /* a device-side wait of moe_decode_step gave up                 */
 } moe_status;

@@ -2,7 +2,7 @@
 // with this file under AddressSanitizer and UndefinedBehaviorSanitizer by
 // tests/test_sanitizers.py, without the device code: the kernel launchers below are stubs
 // that count their calls and check that the workspace layout the entry point hands them
-// fits the workspace the caller passed. The driver runs every entry point on valid
+// fits the workspace the caller passed. This program runs every entry point on valid
 // arguments, on each kind of invalid argument, and on a seeded sweep of descriptor values
 // from edge-case pools (negative, zero, off-by-one, power-of-two and INT_MAX sizes), so
 // that an overflow in the size arithmetic, an out-of-bounds access or any undefined
