@@ -192,6 +192,28 @@ def test_attn_512_wide_sliding(kv_fp8, M):
     check(shape, M, 1000, g, r, "512-wide sliding")
 
 
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 8])
+def test_attn_widest_call(kv_fp8, M):
+    """The largest widths the call accepts: hidden 4096 and q_heads x head_dim = 16,384 (32
+    heads of 512 over 2 KV heads, 16 per group). The o projection then takes 64 lanes per row
+    and one token per LDS group; at M = 8 the 128 queries per KV head exceed the matrix-core
+    form, so the 512-wide vector kernel runs with eight query tiles."""
+    shape = synth.AttnShape(hidden=4096, q_heads=32, kv_heads=2, head_dim=512, window=0, capacity=520, kv_fp8=kv_fp8)
+    g, r = run_layer(shape, M, 500, 21)
+    check(shape, M, 500, g, r, "widest")
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 5])
+def test_attn_many_narrow_heads(kv_fp8, M):
+    """The most query heads (64 of 128 over 4 KV heads, 16 per group) with a 64-position window
+    on a 72-slot ring that has wrapped four times: five query tiles per KV head at M = 5."""
+    shape = synth.AttnShape(q_heads=64, kv_heads=4, head_dim=128, window=64, capacity=72, kv_fp8=kv_fp8)
+    g, r = run_layer(shape, M, 300, 22)
+    check(shape, M, 300, g, r, "narrow heads")
+
+
 def test_attn_gemma_global_full_context_fp8():
     """The last positions of a 32K-slot global cache (FP8), one token; the oracle sees every
     position, so this is the largest case it evaluates."""
