@@ -430,17 +430,18 @@ __device__ __forceinline__ void router_load_hxe8(AP a, int j, uint4 (&wq)[kNC]) 
     uint2 r[kNC];
 #pragma unroll
     for (int k = 0; k < kNC; ++k) r[k] = ld8(w8 + ((size_t)min(k, NC - 1) * 256 + tid) * E + 8 * j);
-    uint2 *tile = reinterpret_cast<uint2 *>(ulds());   // 288 x 8 bytes
+    uint2 *tile = reinterpret_cast<uint2 *>(ulds());   // kNC x 288 x 8 bytes
     const uint8_t *t8 = reinterpret_cast<const uint8_t *>(ulds());
+#pragma unroll
+    for (int k = 0; k < kNC; ++k)
+        if (k < NC) tile[k * 288 + tid + (tid >> 3)] = r[k];
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kNC; ++k) {
         if (k < NC) {
-            __syncthreads();
-            tile[tid + (tid >> 3)] = r[k];
-            __syncthreads();
             uint32_t c[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = t8[(l8 + i + ((l8 + i) >> 3)) * 8 + e];
+            for (int i = 0; i < 8; ++i) c[i] = t8[(k * 288 + l8 + i + ((l8 + i) >> 3)) * 8 + e];
             wq[k] = widen8(make_uint2(c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24),
                                       c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24)));
         } else {
@@ -473,27 +474,29 @@ __device__ __forceinline__ void router_load_hxe(AP a, int j, uint4 (&wq)[kNC]) {
         }
         return;
     }
-    // Pass k covers rows 256 k .. 256 k + 255: thread t requests the 16 bytes of row 256 k + t
-    // that hold experts 8 j .. 8 j + 7 (every pass's load is issued first); each pass then goes
-    // through an LDS tile (rows padded by 16 bytes every 8 rows, which spreads the banks), from
-    // which thread (expert tid / 32, lane l = tid % 32) takes rows 8 l .. 8 l + 7 of its expert.
-    // The tile lies in the u area, which layer_input fills only after this.
+    // Block k covers rows 256 k .. 256 k + 255: thread t requests the 16 bytes of row 256 k + t
+    // that hold experts 8 j .. 8 j + 7 (every block's load is issued first); all blocks then go
+    // into one LDS tile (H / 256 blocks of 288 x 16 bytes at the head of LDS, which the one-layer launch provides;
+    // rows padded by 16 bytes every 8 rows, which spreads the banks), from which thread (expert
+    // tid / 32, lane l = tid % 32) takes rows 8 l .. 8 l + 7 of its expert in every block. The
+    // tile lies in LDS that layer_input and the routing fill only after this.
     const uint16_t *col = static_cast<const uint16_t *>(layer_w(a, 0)->router_w) + 8 * j;
     uint4 r[kNC];
 #pragma unroll
     for (int k = 0; k < kNC; ++k) r[k] = ld16(col + ((size_t)min(k, NC - 1) * 256 + tid) * E);
-    uint4 *tile = reinterpret_cast<uint4 *>(ulds());   // 288 x 16 bytes
-    uint16_t *t16 = reinterpret_cast<uint16_t *>(ulds());
+    uint4 *tile = reinterpret_cast<uint4 *>(ulds());   // kNC x 288 x 16 bytes
+    const uint16_t *t16 = reinterpret_cast<const uint16_t *>(ulds());
     const int e = tid >> 5, l8 = (tid & 31) * 8;
+#pragma unroll
+    for (int k = 0; k < kNC; ++k)
+        if (k < NC) tile[k * 288 + tid + (tid >> 3)] = r[k];
+    __syncthreads();
 #pragma unroll
     for (int k = 0; k < kNC; ++k) {
         if (k < NC) {
-            __syncthreads();
-            tile[tid + (tid >> 3)] = r[k];
-            __syncthreads();
             uint32_t v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = t16[(l8 + i + ((l8 + i) >> 3)) * 8 + e];
+            for (int i = 0; i < 8; ++i) v[i] = t16[(k * 288 + l8 + i + ((l8 + i) >> 3)) * 8 + e];
             wq[k] = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16));
         } else {
             wq[k] = make_uint4(0u, 0u, 0u, 0u);
@@ -1614,7 +1617,9 @@ int launch_layer_step(const moe_layer_desc &ld, const moe_layer_weights &w, int 
     a.nseg_s = W.nseg_s;
     a.NLU = 0;
     a.spin_limit = kDefaultSpin;
-    const size_t lds = step_lds_bytes(d, M, &a.l_scr, &a.l_slot);
+    // the router workgroups stage the whole [H][E] block of their experts in LDS at once
+    const size_t tile = (size_t)(ld.hidden / 256) * 288 * (a.router_fp8 ? 8 : 16);
+    const size_t lds = std::max(step_lds_bytes(d, M, &a.l_scr, &a.l_slot), tile);
     return ld.wtype == MOE_W_BF16 ? launch_m<true>(M, a, lds, W.NR, false, stream)
                                   : launch_m<false>(M, a, lds, W.NR, false, stream);
 }
