@@ -104,6 +104,9 @@ def parse():
                     help="the one-layer configurations instead, through the per-layer entry points: "
                          "a Gemma-shaped MoE layer at M=1, and at M=5 followed by the lm_head, argmax "
                          "and acceptance; --steps fresh inputs each (its own JSON line)")
+    ap.add_argument("--layer-configs", type=str, default="m1,m5,m1em",
+                    help="--layer: which of m1 (M=1), m5 (M=5 + lm_head + accept), m1em (M=1, expert-major "
+                         "router) to run")
     ap.add_argument("--copies", type=int, default=8,
                     help="--layer: weight copies rotated step by step, so that an expert's reuse "
                          "distance exceeds the Infinity Cache")
@@ -383,7 +386,8 @@ def measure(args, runner, sh, M, expert_dtype="fp8", bias=False, lm_dtype="fp8",
 def layer_main(args):
     """The one-layer configurations, through the boundary's per-layer entry points:
     (a) one Gemma-4-26B-A4B-shaped MoE layer at M=1 (moe_decode_layer), and (b) the same
-    layer at M=5 followed by lm_head_argmax and spec_accept (the verify step). Each step
+    layer at M=5 followed by lm_head_argmax and spec_accept (the verify step), and (c) (a) with
+    the router passed expert-major ([E][H], MOE_ROUTER_EXPERT_MAJOR). Each step
     takes a fresh seeded input; the layer's weights rotate over args.copies copies (8 x
     0.77 GB) and the lm_head over 2, so no step finds its weights in the 256 MB Infinity
     Cache. The timed steps are captured into HIP graphs of 100 steps each (a step is a
@@ -399,15 +403,20 @@ def layer_main(args):
     desc = native.layer_desc(sh)
     copies = [synth.layer_weights(sh, 0, dev, seed=args.seed + c, tag="layer") for c in range(R)]
     lws = [native.layer_weights(w) for w in copies]
+    em_copies = [dict(w, router_w=w["router_w"].t().contiguous()) for w in copies]
+    lws_em = [native.layer_weights(w) for w in em_copies]
+    desc_em = native.layer_desc(sh, expert_major=True)
     lms = [synth.lm_head(sh, dev, seed=args.seed + c) for c in range(2)]
     torch.cuda.synchronize()
     log("layer copies: %d x %.2f GB, lm_head copies: 2 (%.2f GB resident)" % (
         R, budget.expert_bytes(sh.hidden, sh.width) * sh.experts / 1e9, torch.cuda.memory_allocated() / 1e9))
     out = {}
-    for M, with_lm in ((1, False), (5, True)):
+    configs = {"m1": (1, False, False), "m5": (5, True, False), "m1em": (1, False, True)}
+    for M, with_lm, em in [configs[c] for c in args.layer_configs.split(",")]:
         n = K + W
         xs = [synth.hidden_inputs(sh, M, i, device=dev, seed=args.seed, tag="layer_x") for i in range(n)]
-        wsb = native.moe_decode_layer_workspace(desc, M)
+        ld, lw = (desc_em, lws_em) if em else (desc, lws)
+        wsb = native.moe_decode_layer_workspace(ld, M)
         ws = native.workspace(wsb)
         lwsb = native.lm_head_argmax_workspace(M, sh.hidden, sh.vocab)
         lws_ = native.workspace(lwsb)
@@ -423,7 +432,7 @@ def layer_main(args):
         stream.wait_stream(torch.cuda.current_stream())
 
         def launch(i):
-            native.moe_decode_layer(desc, lws[i % R], M, xs[i], y, idx[i], wts, ws, wsb, stream)
+            native.moe_decode_layer(ld, lw[i % R], M, xs[i], y, idx[i], wts, ws, wsb, stream)
             if with_lm:
                 Q, s = lms[i % 2]
                 native.lm_head_argmax(M, sh.hidden, sh.vocab, y, Q, s, tok, None, lws_, lwsb, stream)
@@ -456,14 +465,14 @@ def layer_main(args):
         bps = float(np.mean([budget.layer_bytes(sh, u, M) for u in uniq]))
         if with_lm:
             bps += budget.lm_head_bytes(sh.vocab, sh.hidden) + 16 * M
-        name = "layer_m1" if not with_lm else "verify_m5_lm_head"
+        name = "verify_m5_lm_head" if with_lm else ("layer_m1_expert_major_router" if em else "layer_m1")
         out[name] = {"us_per_step": round(ms * 1e3, 2), "steps_per_s": round(1e3 / ms, 1),
                      "bytes_per_step": int(bps), "hbm_gbs": round(bps / (ms / 1e3) / 1e9, 1),
                      "hbm_frac": round(bps / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                      "mean_unique_experts": round(float(np.mean(uniq)), 2)}
         log("%s: %.1f us/step, %.1f GB/s (%.1f%% of 8 TB/s), %.2f MB/step, union %.2f" % (
             name, ms * 1e3, out[name]["hbm_gbs"], 100 * out[name]["hbm_frac"], bps / 1e6, np.mean(uniq)))
-    head = out["layer_m1"]
+    head = out["layer_m1"] if "layer_m1" in out else next(iter(out.values()))
     line = {
         "metric": "per-step latency + achieved HBM GB/s, one 26B-A4B MoE layer (M=1) and its verify step "
                   "with lm_head (M=5)",

@@ -20,7 +20,8 @@ int check_layer_desc(const moe_layer_desc *d) {
     if (d->expert_width < 64 || d->expert_width > kMaxWidth || d->expert_width % 64) return MOE_EINVAL;
     if (d->shared_width < 0 || d->shared_width > kMaxWidth || d->shared_width % 64) return MOE_EINVAL;
     if (d->wtype != MOE_W_FP8_E4M3 && d->wtype != MOE_W_BF16) return MOE_EINVAL;
-    if (d->router_type != MOE_ROUTER_BF16 && d->router_type != MOE_ROUTER_FP8) return MOE_EINVAL;
+    const int rt = d->router_type & ~(int)MOE_ROUTER_EXPERT_MAJOR;
+    if (rt != MOE_ROUTER_BF16 && rt != MOE_ROUTER_FP8) return MOE_EINVAL;
     return MOE_OK;
 }
 
@@ -40,7 +41,7 @@ int check_weights(const moe_layer_desc *desc, const moe_layer_weights *w) {
     if (!w) return MOE_EINVAL;
     const bool fp8 = desc->wtype == MOE_W_FP8_E4M3;
     CHECK(need(w->router_w));
-    if (desc->router_type == MOE_ROUTER_FP8) CHECK(need(w->router_s));
+    if (desc->router_type & MOE_ROUTER_FP8) CHECK(need(w->router_s));
     if (w->router_bias && !aligned16(w->router_bias)) return MOE_EALIGN;
     CHECK(need(w->gate_w));
     CHECK(need(w->up_w));
@@ -100,7 +101,7 @@ const char *moe_strerror(int status) {
 
 size_t moe_decode_layer_workspace(const moe_layer_desc *desc, int max_M) {
     if (check_layer_desc(desc) != MOE_OK || max_M < 1 || max_M > kMaxM) return 0;
-    if (!layer_fits_step(*desc) && desc->router_type == MOE_ROUTER_FP8) return 0;
+    if (!layer_fits_step(*desc) && desc->router_type != MOE_ROUTER_BF16) return 0;
     return layer_fits_step(*desc) ? layer_step_ws(*desc, max_M).total : layer_ws(*desc, max_M).total;
 }
 
@@ -117,7 +118,8 @@ int moe_decode_layer(const moe_layer_desc *desc, const moe_layer_weights *w, int
         if (!ws_ok(workspace, workspace_bytes, layer_step_ws(*desc, M).total)) return MOE_EWORKSPACE;
         return launch_layer_step(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, stream);
     }
-    if (desc->router_type == MOE_ROUTER_FP8) return MOE_EUNSUPPORTED;   // the per-layer kernels read a bf16 router
+    // the per-layer kernels read a bf16 router laid out [H][E]
+    if (desc->router_type != MOE_ROUTER_BF16) return MOE_EUNSUPPORTED;
     const LayerWs L = layer_ws(*desc, M);
     if (!ws_ok(workspace, workspace_bytes, L.total)) return MOE_EWORKSPACE;
     return launch_moe_layer(*desc, *w, M, x, y, topk_idx, topk_w, (char *)workspace, L, stream);

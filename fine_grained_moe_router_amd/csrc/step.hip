@@ -57,7 +57,8 @@ using namespace dev;
 
 struct StepArgs {
     const moe_layer_weights *layers;   // device table [L]
-    const uint16_t *rt;                // router weights re-laid out [L][E][H] (bf16, or FP8 codes)
+    const uint16_t *rt;                // router weights [L][E][H] (bf16, or FP8 codes): the prepared copy;
+                                       // layer mode: the caller's expert-major router, or null for [H][E]
     const uint16_t *gains;             // [L+1][H]
     const uint16_t *x;                 // [M][H]
     const uint16_t *noise;             // [L][M][H]
@@ -1426,7 +1427,7 @@ __global__ __launch_bounds__(256, step_min_blocks<MT>()) void k_step(StepArgs ar
         // router workgroup: each layer's weights are requested as soon as the previous
         // layer's logits are out
         uint4 wq[kNC];
-        if (base->layer_mode)
+        if (base->layer_mode && !base->rt)
             router_load_hxe(base, w - GU, wq);
         else
             router_load(base, 0, w - GU, wq);
@@ -1542,7 +1543,13 @@ int step_prepare(const StepWs &W, const moe_layer_desc &ld, const moe_layer_weig
     const int H = ld.hidden, E = ld.num_experts;
     const size_t n = (size_t)H * E;
     for (int l = 0; l < W.L; ++l) {
-        if (ld.router_type == MOE_ROUTER_FP8)
+        if (ld.router_type & MOE_ROUTER_EXPERT_MAJOR) {   // already [E][H]: copied as it is
+            if (hipMemcpy(ws + W.rt + (size_t)l * n * (ld.router_type & MOE_ROUTER_FP8 ? 1 : 2), layers[l].router_w,
+                          n * (ld.router_type & MOE_ROUTER_FP8 ? 1 : 2), hipMemcpyDeviceToDevice) != hipSuccess)
+                return MOE_ELAUNCH;
+            continue;
+        }
+        if (ld.router_type & MOE_ROUTER_FP8)
             hipLaunchKernelGGL(k_router_transpose<uint8_t>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, nullptr,
                                static_cast<const uint8_t *>(layers[l].router_w),
                                reinterpret_cast<uint8_t *>(ws + W.rt) + (size_t)l * n, H, E);
@@ -1582,7 +1589,8 @@ int launch_layer_step(const moe_layer_desc &ld, const moe_layer_weights &w, int 
     const StepWs W = step_ws(d, false);
     StepArgs a{};
     a.layer_mode = 1;
-    a.router_fp8 = ld.router_type == MOE_ROUTER_FP8 ? 1 : 0;
+    a.router_fp8 = ld.router_type & MOE_ROUTER_FP8 ? 1 : 0;
+    a.rt = ld.router_type & MOE_ROUTER_EXPERT_MAJOR ? static_cast<const uint16_t *>(w.router_w) : nullptr;
     a.lw = w;
     a.x = x;
     a.y = y;
@@ -1640,7 +1648,7 @@ int launch_step(const moe_step_desc &d, const StepWs &W, int M, const uint16_t *
     a.lm_w = lm_w;
     a.lm_s = lm_s;
     a.lm_bf = (d.flags & MOE_STEP_LM_BF16) ? 1 : 0;
-    a.router_fp8 = d.layer.router_type == MOE_ROUTER_FP8 ? 1 : 0;
+    a.router_fp8 = d.layer.router_type & MOE_ROUTER_FP8 ? 1 : 0;
     a.draft = draft;
     a.token = token;
     a.max_logit = max_logit;

@@ -19,7 +19,7 @@ MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 
 MOE_ETIMEOUT = -6
 MOE_W_FP8_E4M3, MOE_W_BF16 = 0, 1
 MOE_KV_BF16, MOE_KV_FP8 = 0, 1
-MOE_ROUTER_BF16, MOE_ROUTER_FP8 = 0, 1
+MOE_ROUTER_BF16, MOE_ROUTER_FP8, MOE_ROUTER_EXPERT_MAJOR = 0, 1, 2
 
 # Every symbol include/moe_decode.h declares.
 EXPORTS = ("moe_decode_layer_workspace", "moe_decode_layer", "moe_decode_layer_status", "lm_head_argmax_workspace",
@@ -175,10 +175,12 @@ def _check(fn, st):
         raise MoeError(fn, st)
 
 
-def layer_desc(shape, expert_dtype: str = "fp8", router_dtype: str = "bf16") -> LayerDesc:
+def layer_desc(shape, expert_dtype: str = "fp8", router_dtype: str = "bf16", expert_major: bool = False) -> LayerDesc:
+    """expert_major: the router weights are passed [E][H] (MOE_ROUTER_EXPERT_MAJOR)."""
+    rt = MOE_ROUTER_FP8 if router_dtype == "fp8" else MOE_ROUTER_BF16
     return LayerDesc(shape.hidden, shape.experts, shape.top_k, shape.width, shape.shared_width,
                      MOE_W_FP8_E4M3 if expert_dtype == "fp8" else MOE_W_BF16,
-                     MOE_ROUTER_FP8 if router_dtype == "fp8" else MOE_ROUTER_BF16)
+                     rt | (MOE_ROUTER_EXPERT_MAJOR if expert_major else 0))
 
 
 def layer_weights(w: dict) -> LayerWeights:

@@ -63,8 +63,14 @@ typedef enum moe_wtype {
  * rung": the precision of each matrix is a rung of its own). */
 typedef enum moe_router_type {
     MOE_ROUTER_BF16 = 0,    /* router_w bf16 [H][E]                                          */
-    MOE_ROUTER_FP8 = 1      /* router_w FP8 E4M3FN codes [H][E], router_s fp32 [E] (one scale
+    MOE_ROUTER_FP8 = 1,     /* router_w FP8 E4M3FN codes [H][E], router_s fp32 [E] (one scale
                                per expert, applied to the finished logit)                     */
+    MOE_ROUTER_EXPERT_MAJOR = 2  /* flag, OR-ed with either type: router_w laid out [E][H]
+                               (row e = expert e's H weights) instead of [H][E]; the same
+                               values give the same results bit for bit. moe_decode_layer's
+                               one-launch form then reads each expert's row whole instead of
+                               gathering it from [H][E] (about 5 us less per call at the
+                               Gemma shape); the per-layer kernels do not take it          */
 } moe_router_type;
 
 /* Shape of one MoE layer.
@@ -75,8 +81,9 @@ typedef enum moe_router_type {
  *   shared_width  Ds: 0 (no shared expert) or a multiple of 64 up to 4096 (704; the
  *                 page's dense MLP is 2112 wide)
  *   wtype         a moe_wtype for the routed and shared expert matrices
- *   router_type   a moe_router_type (MOE_ROUTER_BF16 when zero-initialised); an FP8 router
- *                 runs on the fused step and on moe_decode_layer's one-launch form only */
+ *   router_type   a moe_router_type (MOE_ROUTER_BF16 when zero-initialised), optionally OR-ed
+ *                 with MOE_ROUTER_EXPERT_MAJOR; an FP8 or expert-major router runs on the
+ *                 fused step and on moe_decode_layer's one-launch form only */
 typedef struct moe_layer_desc {
     int hidden;
     int num_experts;
@@ -88,7 +95,8 @@ typedef struct moe_layer_desc {
 } moe_layer_desc;
 
 /* Weights of one MoE layer (device pointers, 16-byte aligned).
- *   router_w     [H][E]: bf16, or FP8 E4M3FN codes (router_type MOE_ROUTER_FP8)
+ *   router_w     [H][E] ([E][H] with MOE_ROUTER_EXPERT_MAJOR): bf16, or FP8 E4M3FN codes
+ *                (MOE_ROUTER_FP8)
  *   router_bias  fp32 [E], added to the logits before the softmax; NULL for none
  *   gate_w, up_w [E][D][H]   down_w [E][H][D]   (FP8 codes or bf16 per wtype)
  *   gate_s, up_s fp32 [E][D] down_s fp32 [E][H] (FP8 only; ignored for bf16)

@@ -398,11 +398,19 @@ def test_fp8_router_validation():
     d = native.layer_desc(synth.TINY, "fp8", "fp8")
     assert native.moe_decode_layer_workspace(d, 1) > 0
     bad = native.layer_desc(synth.TINY, "fp8", "fp8")
-    bad.router_type = 2
-    assert native.moe_decode_layer_workspace(bad, 1) == 0
-    # beyond the fused geometry: the per-layer kernels read a bf16 router only
-    wide = native.layer_desc(synth.TINY.with_(hidden=512, width=768, shared_width=128), "fp8", "fp8")
+    for rt in (4, 5, -1, 1 << 30):
+        bad.router_type = rt
+        assert native.moe_decode_layer_workspace(bad, 1) == 0
+    # either type, expert-major: accepted on the fused geometry
+    for rdt in ("bf16", "fp8"):
+        assert native.moe_decode_layer_workspace(native.layer_desc(synth.TINY, "fp8", rdt, expert_major=True), 1) > 0
+    # beyond the fused geometry: the per-layer kernels read a bf16 [H][E] router only
+    wide_shape = synth.TINY.with_(hidden=512, width=768, shared_width=128)
+    wide = native.layer_desc(wide_shape, "fp8", "fp8")
     assert native.moe_decode_layer_workspace(wide, 1) == 0
+    wide_em = native.layer_desc(wide_shape, "fp8", "bf16", expert_major=True)
+    assert native.moe_decode_layer_workspace(wide_em, 1) == 0
+    assert native.moe_decode_layer_workspace(native.layer_desc(wide_shape, "fp8", "bf16"), 1) > 0
     w = native.LayerWeights(*([FAKE] * 14 + [None]))        # FP8 router without its scales
     wsb = native.moe_decode_layer_workspace(d, 1)
     st = L.moe_decode_layer(ctypes.byref(d), ctypes.byref(w), 1, FAKE, FAKE, None, None, FAKE, wsb, None)
@@ -411,6 +419,9 @@ def test_fp8_router_validation():
     st = L.moe_decode_layer(ctypes.byref(d), ctypes.byref(w), 1, FAKE, FAKE, None, None, FAKE, wsb, None)
     assert st == native.MOE_EALIGN
     st = L.moe_decode_layer(ctypes.byref(wide), ctypes.byref(native.LayerWeights(*([FAKE] * 15))), 1, FAKE, FAKE,
+                            None, None, FAKE, 1 << 30, None)
+    assert st == native.MOE_EUNSUPPORTED
+    st = L.moe_decode_layer(ctypes.byref(wide_em), ctypes.byref(native.LayerWeights(*([FAKE] * 15))), 1, FAKE, FAKE,
                             None, None, FAKE, 1 << 30, None)
     assert st == native.MOE_EUNSUPPORTED
     sd = native.step_desc(synth.TINY.with_(layers=2), 8, router_dtype="fp8")

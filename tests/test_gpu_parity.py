@@ -226,6 +226,38 @@ def test_gemma_layer_shared_2112(gemma_layer):
         check_layer(L, x, r, "shared2112 M=%d" % M)
 
 
+@pytest.mark.parametrize("where", ["gemma", "tiny_fp8_router", "e18_fp8_router"])
+@pytest.mark.parametrize("M", [1, 5, 8])
+def test_layer_expert_major_router_is_bit_identical(gemma_layer, where, M):
+    """MOE_ROUTER_EXPERT_MAJOR: the same router values passed [E][H] (transposed on the
+    device) give the same expert ids, weights and y bit for bit as the [H][E] call, since the
+    router workgroups then hold the same values in the same lanes; E = 18 covers rows that
+    are not 16-byte aligned in the [H][E] layout."""
+    if where == "gemma":
+        L, rdt = gemma_layer, "bf16"
+    else:
+        rdt = "fp8"
+        L = Layer(synth.TINY if where.startswith("tiny") else VARIANTS["e18"], seed=6, router_dtype="fp8")
+    sh = L.shape
+    em = dict(L.dev)
+    em["router_w"] = L.dev["router_w"].t().contiguous()
+    desc = native.layer_desc(sh, "fp8", rdt, expert_major=True)
+    lw = native.layer_weights(em)
+    x = synth.hidden_inputs(sh, M, 600 + M).to(DEV)
+    y0, i0, w0 = L.run(x, M)
+    wsb = native.moe_decode_layer_workspace(desc, M)
+    ws = native.workspace(wsb)
+    y = torch.empty(M, sh.hidden, dtype=torch.bfloat16, device=DEV)
+    idx = torch.full((M, sh.top_k), -7, dtype=torch.int32, device=DEV)
+    wts = torch.zeros(M, sh.top_k, dtype=torch.float32, device=DEV)
+    native.moe_decode_layer(desc, lw, M, x, y, idx, wts, ws, wsb)
+    torch.cuda.synchronize()
+    assert native.moe_decode_layer_status(desc, ws) == native.MOE_OK
+    say("%s M=%d: expert-major router" % (where, M))
+    assert (idx.cpu().numpy() == i0).all() and (wts.cpu().numpy() == w0).all()
+    assert (synth.bits16(y) == y0).all()
+
+
 def _unit_rms_inputs(shape, M, seed):
     """bf16 +-1 vectors: with unit gains and eps 0 their RMSNorm is themselves."""
     g = torch.Generator().manual_seed(seed)

@@ -78,6 +78,31 @@ def run_and_check(shape, M, step, seed=0, what="", expert_dtype="fp8", router_bi
     return fs, x, noise, dd
 
 
+@pytest.mark.parametrize("router_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("M", [1, 5])
+def test_fused_step_expert_major_router(router_dtype, M):
+    """MOE_ROUTER_EXPERT_MAJOR in the fused step: prepare copies the [E][H] routers as they
+    are instead of transposing them, and the step is bit-identical to the [H][E] one."""
+    sh = synth.TINY.with_(layers=2)
+    layers, host, gains, Q, s, dev = make(sh, 4, "fp8", None, False, router_dtype)
+    x, noise, res = oracle_step(sh, host, gains, Q, s, M, 40 + M)
+    drafts = synth.drafts(res["tok"], 0.7, sh.vocab, 40 + M)
+    dd = torch.from_numpy(drafts.astype(np.int32)).to(DEV) if M > 1 else None
+    a = FusedDecodeStep(sh, dev, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8)
+    em = [dict(w, router_w=w["router_w"].t().contiguous()) for w in dev]
+    b = FusedDecodeStep(sh, em, gains.to(DEV), Q.to(DEV), s.to(DEV), max_M=8)
+    b.desc.layer.router_type |= native.MOE_ROUTER_EXPERT_MAJOR
+    native.moe_decode_step_prepare(b.desc, [native.layer_weights(w) for w in em], b.ws, b.ws_bytes)
+    for f in (a, b):
+        f.step(x.to(DEV), noise.to(DEV), dd, M)
+    torch.cuda.synchronize()
+    assert a.status() == native.MOE_OK and b.status() == native.MOE_OK
+    assert (a.topk_idx(M).cpu() == b.topk_idx(M).cpu()).all()
+    assert (a.topk_w(M).cpu() == b.topk_w(M).cpu()).all()
+    assert (synth.bits16(a.y(M)) == synth.bits16(b.y(M))).all()
+    assert (a.tok[:M].cpu() == b.tok[:M].cpu()).all() and (a.tok[:M].cpu().numpy() == res["tok"]).all()
+
+
 @pytest.mark.parametrize("L", [1, 2, 3])
 @pytest.mark.parametrize("M", [1, 5, 8])
 def test_fused_step_tiny(L, M):
